@@ -1,0 +1,327 @@
+/*
+ * CPU ORACLE for the CSA2 global-attention path — TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+ * load or call this library. The HIP library never does, and shares no code,
+ * header, table or constant with it.
+ *
+ * Plain, slow, obviously-correct C in fp64. Each function names the passage
+ * it follows. Pages:
+ *   [ATLAS]  "An infra-oriented diagram of the DeepSeek-V4.1-Flash
+ *            architecture" — Reading notes (KV-latent bullet, Full-layer cache
+ *            bullet, indexer bullet, role bullet) and section "The KV cache".
+ *   [HELIX]  "DeepSeek V4.1 Flash: Why Its Encoder, Engram and KV Cache
+ *            Matter" — section "CSA2 makes long context cheaper to retain".
+ *   [PERCHY] "DeepSeek V4.1 Flash" model guide — "A closer look: Full.
+ *            Reindex. Reuse."
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *   R1 code byte j holds channel 2j in the low nibble, 2j+1 in the high one;
+ *      codes precede scales inside an entry.
+ *   R2 the E4M3 flavour is OCP E4M3FN (bias 7, no inf, S.1111.111 = NaN).
+ *   R3 the indexer query is MXFP4 like the keys (E2M1, E8M0 per 32).
+ *   R4 indexer score = sum_h w_h * max(q_h . k, 0): no extra constant factor.
+ *   R5 top-k order is (score descending, entry index ascending); -0 == +0;
+ *      NaN ranks below every number.
+ *   R6 Reindex pools are aligned blocks: block b covers entries 8b..8b+7.
+ *   R7 attention runs over the selected entries followed by the SWA rows, one
+ *      softmax over the joint set, no de-duplication, no sink, no bias; the
+ *      latent is both key and value; RoPE is outside this path.
+ *   R8 selected ids outside [0, n_entries) (the -1 padding) are skipped; an
+ *      empty joint set gives a zero output and lse = -inf.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_API __attribute__((visibility("default")))
+
+/* ------------------------------------------------------------------ O1 --- */
+/* Element formats named in [ATLAS] Full-layer cache bullet ("E2M1, one E4M3
+ * scale per 16 channels") and "The KV cache" ("one E8M0 scale per 32"). The
+ * value definitions are those of the OCP Microscaling (MX) formats spec. */
+
+/* FP4 E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa bit; no inf/NaN. */
+ORC_API double orc_e2m1(unsigned code) {
+  unsigned s = (code >> 3) & 1u, e = (code >> 1) & 3u, m = code & 1u;
+  double mag = (e == 0) ? 0.5 * (double)m : ldexp(1.0 + 0.5 * (double)m, (int)e - 1);
+  return s ? -mag : mag;
+}
+
+/* FP8 E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa; S.1111.111 is NaN. */
+ORC_API double orc_e4m3(unsigned byte) {
+  unsigned s = (byte >> 7) & 1u, e = (byte >> 3) & 15u, m = byte & 7u;
+  if (e == 15 && m == 7) return NAN;
+  double mag = (e == 0) ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, (int)e - 7);
+  return s ? -mag : mag;
+}
+
+/* E8M0: unsigned power of two 2^(b-127); 0xFF is NaN. */
+ORC_API double orc_e8m0(unsigned byte) {
+  if ((byte & 0xFFu) == 0xFFu) return NAN;
+  return ldexp(1.0, (int)(byte & 0xFFu) - 127);
+}
+
+static double nib(const uint8_t* codes, int ch) { /* R1 */
+  unsigned b = codes[ch >> 1];
+  return orc_e2m1((ch & 1) ? (b >> 4) : (b & 15u));
+}
+
+/* Main entry: 256 code bytes then 32 E4M3 scales ([ATLAS] "The KV cache":
+ * 512 FP4 values with an E4M3 scale per 16 channels, 288 bytes). */
+static void main_entry_f64(const uint8_t* entry, double* out512) {
+  for (int c = 0; c < 512; ++c) out512[c] = nib(entry, c) * orc_e4m3(entry[256 + c / 16]);
+}
+
+/* Indexer key: 64 code bytes + 4 E8M0 scales (68 bytes, [ATLAS] "The KV cache"). */
+static void index_row_f64(const uint8_t* codes, const uint8_t* scales, double* out128) {
+  for (int c = 0; c < 128; ++c) out128[c] = nib(codes, c) * orc_e8m0(scales[c / 32]);
+}
+
+ORC_API int orc_main_entry_bytes(void) { return 512 / 2 + 512 / 16; }  /* 288 */
+ORC_API int orc_index_entry_bytes(void) { return 128 / 2 + 128 / 32; } /* 68 */
+
+static uint16_t f64_to_bf16(double v) {
+  float f = (float)v; /* RNE */
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0x007FFFFFu) ? 0x40u : 0u));
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+static double bf16_to_f64(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* Dequantise n main entries to fp32 [n][512] and/or bf16 [n][512]. */
+ORC_API void orc_dequant_main(const uint8_t* entries, int64_t n, float* out_f32, uint16_t* out_bf16) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    double v[512];
+    main_entry_f64(entries + (size_t)i * 288, v);
+    for (int c = 0; c < 512; ++c) {
+      if (out_f32) out_f32[(size_t)i * 512 + c] = (float)v[c];
+      if (out_bf16) out_bf16[(size_t)i * 512 + c] = f64_to_bf16(v[c]);
+    }
+  }
+}
+
+/* Dequantise n indexer keys to fp32 [n][128] and/or bf16. */
+ORC_API void orc_dequant_index(const uint8_t* codes, const uint8_t* scales, int64_t n, float* out_f32,
+                               uint16_t* out_bf16) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    double v[128];
+    index_row_f64(codes + (size_t)i * 64, scales + (size_t)i * 4, v);
+    for (int c = 0; c < 128; ++c) {
+      if (out_f32) out_f32[(size_t)i * 128 + c] = (float)v[c];
+      if (out_bf16) out_bf16[(size_t)i * 128 + c] = f64_to_bf16(v[c]);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------ O3 --- */
+/* Candidate set. Full layers score every cache entry ([HELIX] CSA2 section:
+ * Full layers "search the full sparse index"); Reindex layers score only a
+ * pool built from blocks of 8 ([ATLAS] indexer bullet). Position p of the
+ * candidate list maps to a global entry id; n_valid (if given) excludes ids
+ * >= n_valid[q] (causal limit). */
+static int64_t cand_entry(const int32_t* blocks_q, int64_t p) {
+  if (!blocks_q) return p;
+  return 8 * (int64_t)blocks_q[p / 8] + p % 8; /* R6 */
+}
+
+/* ------------------------------------------------------------------ O2 --- */
+/* Lightning indexer, [ATLAS] indexer bullet: 32 FP4 query heads of 128 dims
+ * against one shared key per entry, ReLU'd scores summed with per-head
+ * weights. d_h = q_h . k is exact in fp64 for these formats; the weighted sum
+ * is formed in fp64 and rounded once to fp32. Entries outside the candidate
+ * set get -inf. dots_out (optional) receives d as [Q][32][n_cand] fp64. */
+ORC_API void orc_index_score(int Q, int64_t n_entries, int64_t cache_q_stride, const uint8_t* key_codes,
+                             const uint8_t* key_scales, const uint8_t* iq_codes, const uint8_t* iq_scales,
+                             const float* w, const int32_t* cand_blocks, int n_blocks, const int32_t* n_valid,
+                             float* scores, double* dots_out) {
+  int64_t n_cand = cand_blocks ? 8 * (int64_t)n_blocks : n_entries;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int q = 0; q < Q; ++q) {
+    double qv[32][128];
+    for (int h = 0; h < 32; ++h)
+      index_row_f64(iq_codes + ((size_t)q * 32 + h) * 64, iq_scales + ((size_t)q * 32 + h) * 4, qv[h]);
+    const int32_t* blk = cand_blocks ? cand_blocks + (size_t)q * n_blocks : NULL;
+    int64_t limit = n_valid ? (int64_t)n_valid[q] : n_entries;
+    if (limit > n_entries) limit = n_entries;
+    for (int64_t p = 0; p < n_cand; ++p) {
+      int64_t e = cand_entry(blk, p);
+      if (e < 0 || e >= limit) {
+        scores[(size_t)q * n_cand + p] = -INFINITY;
+        continue;
+      }
+      int64_t row = (int64_t)q * cache_q_stride + e;
+      double kv[128];
+      index_row_f64(key_codes + (size_t)row * 64, key_scales + (size_t)row * 4, kv);
+      double acc = 0.0;
+      for (int h = 0; h < 32; ++h) {
+        double d = 0.0;
+        for (int c = 0; c < 128; ++c) d += qv[h][c] * kv[c];
+        if (dots_out) dots_out[((size_t)q * 32 + h) * n_cand + p] = d;
+        double r = d > 0.0 ? d : 0.0; /* ReLU before the head weighting */
+        acc += (double)w[q * 32 + h] * r;
+      }
+      scores[(size_t)q * n_cand + p] = (float)acc;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------ O4 --- */
+/* Top-k per query ([PERCHY] "Main sparse selection: 512 entries"; [ATLAS]
+ * indexer bullet "top-512"). Sort the candidates by R5 and keep the first
+ * min(k, n). idx gets global entry ids, padded with -1; top_scores (optional)
+ * gets the scores, padded with -inf. */
+typedef struct {
+  float s;
+  int64_t e;
+} orc_pair;
+
+static int rank_cmp(const void* a, const void* b) {
+  const orc_pair* x = (const orc_pair*)a;
+  const orc_pair* y = (const orc_pair*)b;
+  int xn = isnan(x->s), yn = isnan(y->s);
+  if (xn != yn) return xn ? 1 : -1;
+  if (!xn && x->s != y->s) return (x->s > y->s) ? -1 : 1; /* -0 == +0 here */
+  return (x->e < y->e) ? -1 : (x->e > y->e) ? 1 : 0;
+}
+
+ORC_API void orc_topk(const float* scores, int Q, int64_t n_cand, const int32_t* n_valid, int64_t n_entries,
+                      const int32_t* cand_blocks, int n_blocks, int k, int32_t* idx, float* top_scores) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int q = 0; q < Q; ++q) {
+    const int32_t* blk = cand_blocks ? cand_blocks + (size_t)q * n_blocks : NULL;
+    int64_t limit = n_valid ? (int64_t)n_valid[q] : n_entries;
+    if (limit > n_entries) limit = n_entries;
+    orc_pair* v = (orc_pair*)malloc(sizeof(orc_pair) * (size_t)(n_cand > 0 ? n_cand : 1));
+    int64_t m = 0;
+    for (int64_t p = 0; p < n_cand; ++p) {
+      int64_t e = cand_entry(blk, p);
+      if (e < 0 || e >= limit) continue;
+      v[m].s = scores[(size_t)q * n_cand + p];
+      v[m].e = e;
+      ++m;
+    }
+    qsort(v, (size_t)m, sizeof(orc_pair), rank_cmp);
+    for (int j = 0; j < k; ++j) {
+      idx[(size_t)q * k + j] = (j < m) ? (int32_t)v[j].e : -1;
+      if (top_scores) top_scores[(size_t)q * k + j] = (j < m) ? v[j].s : -INFINITY;
+    }
+    free(v);
+  }
+}
+
+/* ------------------------------------------------------------------ O5 --- */
+/* Sparse attention, [ATLAS] role bullet (every non-SWA-only layer attends
+ * over the 128-token window plus 512 selected entries) and KV-latent bullet
+ * (one 512-wide latent per entry, k = v, shared by all 64 query heads).
+ * J = valid selected ids in idx order, then the n_swa window rows (R7, R8).
+ * logits l_hj = scale * q_h . K_j; p = softmax_j(l) in max-subtracted form;
+ * o_h = sum_j p_hj V_j, all in fp64. Outputs: bf16 (RNE) and/or fp32 of the
+ * fp64 result, and optional lse_h = m_h + log(sum_j exp(l_hj - m_h)).
+ * probs_out (optional, for tests): [Q][64][k_sel + n_swa] softmax weights in
+ * joint-list order, with skipped slots left at 0. */
+ORC_API void orc_sparse_attn(int Q, int64_t n_entries, int64_t cache_q_stride, const uint8_t* main_cache,
+                             const int32_t* idx, int k_sel, const uint16_t* q_bf16, const uint16_t* swa,
+                             int64_t swa_q_stride, int n_swa, double scale, uint16_t* out_bf16, float* out_f32,
+                             float* lse, double* probs_out) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int qi = 0; qi < Q; ++qi) {
+    int jmax = k_sel + n_swa;
+    double* kv = (double*)malloc(sizeof(double) * (size_t)(jmax > 0 ? jmax : 1) * 512);
+    int* slot = (int*)malloc(sizeof(int) * (size_t)(jmax > 0 ? jmax : 1));
+    int nj = 0;
+    for (int j = 0; j < k_sel; ++j) {
+      int64_t e = idx[(size_t)qi * k_sel + j];
+      if (e < 0 || e >= n_entries) continue; /* R8 */
+      main_entry_f64(main_cache + (size_t)((int64_t)qi * cache_q_stride + e) * 288, kv + (size_t)nj * 512);
+      slot[nj++] = j;
+    }
+    for (int r = 0; r < n_swa; ++r) {
+      const uint16_t* row = swa + (size_t)((int64_t)qi * swa_q_stride + r) * 512;
+      for (int c = 0; c < 512; ++c) kv[(size_t)nj * 512 + c] = bf16_to_f64(row[c]);
+      slot[nj++] = k_sel + r;
+    }
+    double* lg = (double*)malloc(sizeof(double) * (size_t)(nj > 0 ? nj : 1));
+    for (int h = 0; h < 64; ++h) {
+      double qh[512];
+      for (int c = 0; c < 512; ++c) qh[c] = bf16_to_f64(q_bf16[((size_t)qi * 64 + h) * 512 + c]);
+      double o[512];
+      for (int c = 0; c < 512; ++c) o[c] = 0.0;
+      double mx = -INFINITY, z = 0.0;
+      for (int j = 0; j < nj; ++j) {
+        double d = 0.0;
+        for (int c = 0; c < 512; ++c) d += qh[c] * kv[(size_t)j * 512 + c];
+        lg[j] = scale * d;
+        if (lg[j] > mx) mx = lg[j];
+      }
+      for (int j = 0; j < nj; ++j) z += exp(lg[j] - mx);
+      if (probs_out)
+        for (int j = 0; j < jmax; ++j) probs_out[((size_t)qi * 64 + h) * jmax + j] = 0.0;
+      for (int j = 0; j < nj; ++j) {
+        double p = exp(lg[j] - mx) / z;
+        if (probs_out) probs_out[((size_t)qi * 64 + h) * jmax + slot[j]] = p;
+        for (int c = 0; c < 512; ++c) o[c] += p * kv[(size_t)j * 512 + c];
+      }
+      for (int c = 0; c < 512; ++c) {
+        size_t at = ((size_t)qi * 64 + h) * 512 + c;
+        if (out_bf16) out_bf16[at] = f64_to_bf16(o[c]);
+        if (out_f32) out_f32[at] = (float)o[c];
+      }
+      if (lse) lse[qi * 64 + h] = (nj > 0) ? (float)(mx + log(z)) : -INFINITY;
+    }
+    free(lg);
+    free(slot);
+    free(kv);
+  }
+}
+
+/* ------------------------------------------------------------------ O6 --- */
+/* Fused decode: O2 -> O4 -> O5 ([PERCHY] "shared KV -> candidate pool ->
+ * top 512 -> attention"). scores_out/idx_out (optional) expose the stages. */
+ORC_API void orc_decode(int Q, int64_t n_entries, int64_t cache_q_stride, const uint8_t* key_codes,
+                        const uint8_t* key_scales, const uint8_t* iq_codes, const uint8_t* iq_scales,
+                        const float* w, const int32_t* cand_blocks, int n_blocks, const int32_t* n_valid, int k,
+                        const uint8_t* main_cache, const uint16_t* q_bf16, const uint16_t* swa,
+                        int64_t swa_q_stride, int n_swa, double scale, uint16_t* out_bf16, float* out_f32,
+                        float* lse, int32_t* idx_out, float* scores_out) {
+  int64_t n_cand = cand_blocks ? 8 * (int64_t)n_blocks : n_entries;
+  float* sc = scores_out ? scores_out : (float*)malloc(sizeof(float) * (size_t)Q * (size_t)(n_cand > 0 ? n_cand : 1));
+  int32_t* id = idx_out ? idx_out : (int32_t*)malloc(sizeof(int32_t) * (size_t)Q * (size_t)(k > 0 ? k : 1));
+  orc_index_score(Q, n_entries, cache_q_stride, key_codes, key_scales, iq_codes, iq_scales, w, cand_blocks, n_blocks,
+                  n_valid, sc, NULL);
+  orc_topk(sc, Q, n_cand, n_valid, n_entries, cand_blocks, n_blocks, k, id, NULL);
+  orc_sparse_attn(Q, n_entries, cache_q_stride, main_cache, id, k, q_bf16, swa, swa_q_stride, n_swa, scale, out_bf16,
+                  out_f32, lse, NULL);
+  if (!scores_out) free(sc);
+  if (!idx_out) free(id);
+}
+
+ORC_API void orc_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
+ORC_API int orc_get_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

@@ -1,0 +1,277 @@
+"""Seeded synthetic inputs for the CSA2 path (shared by the oracle and the HIP side).
+
+The C source ``csa2_synth.c`` defines the random streams and the storage
+quantisation of the inputs; this module builds it with gcc, loads it, and
+assembles whole workloads as numpy arrays. Nothing here scores, selects or
+attends.
+
+Stream ids (the ``tensor_id`` of the counter): 0 main latents, 1 indexer keys,
+2 indexer queries, 3 head weights, 4 attention queries, 5 SWA rows, 6 pool blocks.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "csa2_synth.c")
+_LIB = os.path.join(_HERE, "libcsa2synth.so")
+
+TID_MAIN, TID_IKEY, TID_IQ, TID_W, TID_Q, TID_SWA, TID_POOL = range(7)
+
+MAIN_BYTES = 288
+IKEY_CODE_BYTES = 64
+IKEY_SCALE_BYTES = 4
+N_IHEADS = 32
+N_HEADS = 64
+HEAD_DIM = 512
+TOPK = 512
+N_SWA = 128
+BLOCK = 8
+
+
+def build(force: bool = True) -> str:
+    if force or not os.path.exists(_LIB):
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-fvisibility=hidden", _SRC, "-o", _LIB + ".tmp", "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        u64, i64, i32, vp = ctypes.c_uint64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        L.syn_normal.restype = ctypes.c_double
+        L.syn_normal.argtypes = [u64, i32, u64, u64]
+        L.syn_bits.restype = u64
+        L.syn_bits.argtypes = [u64, i32, u64, u64]
+        L.syn_main_latents.argtypes = [u64, u64, i64, i64, vp]
+        L.syn_main_latents_list.argtypes = [u64, u64, vp, i64, vp]
+        L.syn_index_keys.argtypes = [u64, u64, i64, i64, vp, vp]
+        L.syn_index_keys_list.argtypes = [u64, u64, vp, i64, vp, vp]
+        L.syn_index_queries.argtypes = [u64, i64, i64, vp, vp]
+        L.syn_head_weights.argtypes = [u64, i64, i64, vp]
+        L.syn_bf16_normal.argtypes = [u64, i32, u64, i64, i64, vp]
+        L.syn_pool_blocks.argtypes = [u64, u64, i64, i64, vp]
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def main_latents(seed: int, seq: int, first: int, n: int) -> np.ndarray:
+    out = np.empty((n, MAIN_BYTES), np.uint8)
+    lib().syn_main_latents(seed, seq, first, n, _p(out))
+    return out
+
+
+def main_latents_list(seed: int, seq: int, ids: np.ndarray) -> np.ndarray:
+    ids = np.ascontiguousarray(ids, dtype=np.int64)
+    out = np.empty((len(ids), MAIN_BYTES), np.uint8)
+    lib().syn_main_latents_list(seed, seq, _p(ids), len(ids), _p(out))
+    return out
+
+
+def index_keys(seed: int, seq: int, first: int, n: int):
+    codes = np.empty((n, IKEY_CODE_BYTES), np.uint8)
+    scales = np.empty((n, IKEY_SCALE_BYTES), np.uint8)
+    lib().syn_index_keys(seed, seq, first, n, _p(codes), _p(scales))
+    return codes, scales
+
+
+def index_keys_list(seed: int, seq: int, ids: np.ndarray):
+    ids = np.ascontiguousarray(ids, dtype=np.int64)
+    codes = np.empty((len(ids), IKEY_CODE_BYTES), np.uint8)
+    scales = np.empty((len(ids), IKEY_SCALE_BYTES), np.uint8)
+    lib().syn_index_keys_list(seed, seq, _p(ids), len(ids), _p(codes), _p(scales))
+    return codes, scales
+
+
+def index_queries(seed: int, first: int, n: int):
+    codes = np.empty((n, N_IHEADS, IKEY_CODE_BYTES), np.uint8)
+    scales = np.empty((n, N_IHEADS, IKEY_SCALE_BYTES), np.uint8)
+    lib().syn_index_queries(seed, first, n, _p(codes), _p(scales))
+    return codes, scales
+
+
+def head_weights(seed: int, first: int, n: int) -> np.ndarray:
+    w = np.empty((n, N_IHEADS), np.float32)
+    lib().syn_head_weights(seed, first, n, _p(w))
+    return w
+
+
+def bf16_normal(seed: int, tid: int, seq: int, first: int, n: int) -> np.ndarray:
+    out = np.empty((n,), np.uint16)
+    lib().syn_bf16_normal(seed, tid, seq, first, n, _p(out))
+    return out
+
+
+def pool_blocks(seed: int, seq: int, n_pick: int, n_total: int) -> np.ndarray:
+    out = np.empty((n_pick,), np.int32)
+    lib().syn_pool_blocks(seed, seq, n_pick, n_total, _p(out))
+    return out
+
+
+# Poison bytes for cache entries that a kernel must never read: NaN scales
+# (E4M3 0x7F, E8M0 0xFF) so any stray read turns outputs into NaN.
+POISON_E4M3 = 0x7F
+POISON_E8M0 = 0xFF
+
+
+@dataclass
+class Workload:
+    """One batch of the CSA2 path, all host arrays.
+
+    Layouts (C-contiguous):
+      main_cache  uint8 [rows][288]     key_codes uint8 [rows][64]   key_scales uint8 [rows][4]
+      iq_codes    uint8 [Q][32][64]     iq_scales uint8 [Q][32][4]   w float32 [Q][32]
+      q           uint16(bf16) [Q][64][512]
+      swa         uint16(bf16) [swa_rows][512]; query i's window starts at row i*swa_q_stride
+      cand_blocks int32 [Q][n_blocks] or None   n_valid int32 [Q] or None
+    Query i's cache occupies rows [i*cache_q_stride, i*cache_q_stride + n_entries).
+    Entries listed in ``sparse_rows`` (if not None) are the only ones holding data;
+    all other rows are poison.
+    """
+
+    name: str
+    Q: int
+    n_entries: int
+    cache_q_stride: int
+    main_cache: np.ndarray
+    key_codes: np.ndarray
+    key_scales: np.ndarray
+    iq_codes: np.ndarray
+    iq_scales: np.ndarray
+    w: np.ndarray
+    q: np.ndarray
+    swa: np.ndarray
+    swa_q_stride: int
+    n_swa: int
+    cand_blocks: Optional[np.ndarray] = None
+    n_valid: Optional[np.ndarray] = None
+    k: int = TOPK
+    scale: float = 1.0 / np.sqrt(512.0)
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def n_blocks(self) -> int:
+        return 0 if self.cand_blocks is None else int(self.cand_blocks.shape[1])
+
+    @property
+    def n_cand(self) -> int:
+        return self.n_blocks * BLOCK if self.cand_blocks is not None else self.n_entries
+
+
+def _queries(seed, Q, swa_rows_per_query, shared_swa_rows=None):
+    iq_codes, iq_scales = index_queries(seed, 0, Q)
+    w = head_weights(seed, 0, Q)
+    q = np.stack([bf16_normal(seed, TID_Q, i, 0, N_HEADS * HEAD_DIM) for i in range(Q)]).reshape(Q, N_HEADS, HEAD_DIM)
+    if shared_swa_rows is None:
+        swa = np.stack([bf16_normal(seed, TID_SWA, i, 0, swa_rows_per_query * HEAD_DIM) for i in range(Q)])
+        swa = swa.reshape(Q * swa_rows_per_query, HEAD_DIM)
+    else:
+        swa = bf16_normal(seed, TID_SWA, 0, 0, shared_swa_rows * HEAD_DIM).reshape(shared_swa_rows, HEAD_DIM)
+    return iq_codes, iq_scales, w, q, swa
+
+
+def full_decode(Q: int, N: int, seed: int = 0, n_swa: int = N_SWA, name: str = "full_decode") -> Workload:
+    """Full-layer decode: Q queries, each with its own cache of N entries (m=1)."""
+    main = np.concatenate([main_latents(seed, i, 0, N) for i in range(Q)]) if N else np.zeros((0, MAIN_BYTES), np.uint8)
+    kc, ks = zip(*[index_keys(seed, i, 0, N) for i in range(Q)]) if N else ((np.zeros((0, 64), np.uint8),), (np.zeros((0, 4), np.uint8),))
+    iq_codes, iq_scales, w, q, swa = _queries(seed, Q, n_swa)
+    return Workload(name, Q, N, N, main, np.concatenate(kc), np.concatenate(ks), iq_codes, iq_scales, w, q,
+                    swa, n_swa, n_swa)
+
+
+def reindex_decode(Q: int, N: int, n_blocks: int, seed: int = 0, dense_rows: bool = True,
+                   name: str = "reindex_decode") -> Workload:
+    """Reindex-layer decode: each query's cache has N entries; a pool of n_blocks
+    distinct aligned blocks of 8 is drawn per query. Only pool entries hold data,
+    every other entry is poison.
+
+    dense_rows=True materialises the full Q*N-row cache on the host (small N only);
+    otherwise ``extra['pool_rows']`` lists the pool rows and ``main_cache`` etc.
+    hold only those rows (the caller scatters them into a poisoned device cache).
+    """
+    blocks = np.stack([pool_blocks(seed, i, n_blocks, N // BLOCK) for i in range(Q)])
+    ids = [(BLOCK * blocks[i][:, None] + np.arange(BLOCK)[None, :]).reshape(-1).astype(np.int64) for i in range(Q)]
+    main_rows = [main_latents_list(seed, i, ids[i]) for i in range(Q)]
+    key_rows = [index_keys_list(seed, i, ids[i]) for i in range(Q)]
+    iq_codes, iq_scales, w, q, swa = _queries(seed, Q, N_SWA)
+    pool_rows = np.concatenate([i * N + ids[i] for i in range(Q)])
+    pm = np.concatenate(main_rows)
+    pkc = np.concatenate([k[0] for k in key_rows])
+    pks = np.concatenate([k[1] for k in key_rows])
+    if dense_rows:
+        main = np.zeros((Q * N, MAIN_BYTES), np.uint8)
+        main[:, 256:] = POISON_E4M3
+        kc = np.zeros((Q * N, IKEY_CODE_BYTES), np.uint8)
+        ks = np.full((Q * N, IKEY_SCALE_BYTES), POISON_E8M0, np.uint8)
+        main[pool_rows] = pm
+        kc[pool_rows] = pkc
+        ks[pool_rows] = pks
+        wl = Workload(name, Q, N, N, main, kc, ks, iq_codes, iq_scales, w, q, swa, N_SWA, N_SWA,
+                      cand_blocks=blocks.astype(np.int32))
+    else:
+        wl = Workload(name, Q, N, N, pm, pkc, pks, iq_codes, iq_scales, w, q, swa, N_SWA, N_SWA,
+                      cand_blocks=blocks.astype(np.int32))
+    wl.extra["pool_rows"] = pool_rows
+    wl.extra["dense_rows"] = dense_rows
+    return wl
+
+
+def prefill(T: int, n_cache: int, t0: int, seed: int = 0, m: int = 2, name: str = "prefill") -> Workload:
+    """Encoder Full-layer prefill chunk: T queries at positions t0..t0+T-1 against a
+    shared m-pooled cache of n_cache entries; query at position t sees entries
+    with index < floor(t/m) and its own 128-token window, rows i..i+127 of a
+    shared chunk buffer of T+127 bf16 rows."""
+    main = main_latents(seed, 0, 0, n_cache)
+    kc, ks = index_keys(seed, 0, 0, n_cache)
+    iq_codes, iq_scales, w, q, swa = _queries(seed, T, 0, shared_swa_rows=T + N_SWA - 1)
+    n_valid = np.array([(t0 + i) // m for i in range(T)], np.int64)
+    n_valid = np.minimum(n_valid, n_cache).astype(np.int32)
+    wl = Workload(name, T, n_cache, 0, main, kc, ks, iq_codes, iq_scales, w, q, swa, 1, N_SWA, n_valid=n_valid)
+    wl.extra["t0"] = t0
+    return wl
+
+
+# The five workload shapes of the CSA2 decode/prefill hot path.
+CONFIGS = {
+    0: dict(kind="full_decode", Q=1, N=4096),
+    1: dict(kind="full_decode", Q=16, N=65536),
+    2: dict(kind="reindex_decode", Q=64, N=1 << 20, n_blocks=2048),
+    3: dict(kind="prefill", T=4096, n_cache=131072, t0=258048),
+    4: dict(kind="full_decode", Q=4, N=1 << 20),
+}
+
+CONFIG_NAMES = {
+    0: "full-layer decode, 1 query x 4,096 entries",
+    1: "full-layer decode, batch 16 x 65,536 entries",
+    2: "reindex-layer decode, batch 64, 16,384-entry pool of a 1,048,576-entry cache",
+    3: "encoder full-layer prefill, 4,096 queries x 131,072-entry m=2 cache (causal)",
+    4: "long-context full-layer decode, batch 4 x 1,048,576 entries",
+}
+
+
+def make_config(i: int, seed: int = 0, dense_rows: Optional[bool] = None) -> Workload:
+    c = CONFIGS[i]
+    if c["kind"] == "full_decode":
+        return full_decode(c["Q"], c["N"], seed, name=f"config{i}")
+    if c["kind"] == "reindex_decode":
+        return reindex_decode(c["Q"], c["N"], c["n_blocks"], seed, dense_rows=bool(dense_rows), name=f"config{i}")
+    return prefill(c["T"], c["n_cache"], c["t0"], seed, name=f"config{i}")

@@ -1,0 +1,356 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each ``check_*`` takes an oracle library handle ``L`` (the real build, or a
+build with a planted mistake) and raises AssertionError when the oracle
+disagrees with:
+  * the element-format definitions (golden E2M1 table; torch's own
+    float8_e4m3fn / float8_e8m0fnu conversions),
+  * the byte figures the pages print (tests/golden/kv_layout.txt),
+  * independent numpy / torch computations of the same closed forms
+    (matmul-based indexer scores, library sort for top-k, library SDPA for
+    select-all attention),
+  * invariants (ReLU before weighting, exact dots, tie order, permutation
+    invariance, softmax weights summing to 1, single-entry and zero-query cases).
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden_e2m1() -> np.ndarray:
+    vals = np.zeros(16, np.float64)
+    with open(os.path.join(GOLDEN, "e2m1_values.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            c, v = line.split()
+            vals[int(c)] = float(v)
+    return vals
+
+
+def golden_layout() -> dict:
+    out = {}
+    with open(os.path.join(GOLDEN, "kv_layout.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, v = line.split()
+            out[k] = float(v)
+    return out
+
+
+def lib_e4m3(b: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(b, np.uint8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def lib_e8m0(b: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(b, np.uint8)).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+
+
+def nibbles(codes: np.ndarray) -> np.ndarray:
+    """[..., B] bytes -> [..., 2B] 4-bit codes, channel 2j = low nibble of byte j."""
+    lo = codes & 0x0F
+    hi = codes >> 4
+    return np.stack([lo, hi], axis=-1).reshape(*codes.shape[:-1], codes.shape[-1] * 2)
+
+
+def ref_dequant_main(entries: np.ndarray) -> np.ndarray:
+    e = np.asarray(entries, np.uint8).reshape(-1, 288)
+    vals = golden_e2m1()[nibbles(e[:, :256])]
+    sc = lib_e4m3(e[:, 256:])
+    return vals * np.repeat(sc, 16, axis=1)
+
+
+def ref_dequant_index(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    c = np.asarray(codes, np.uint8).reshape(-1, 64)
+    s = np.asarray(scales, np.uint8).reshape(-1, 4)
+    return golden_e2m1()[nibbles(c)] * np.repeat(lib_e8m0(s), 32, axis=1)
+
+
+def bf16_to_f64(h: np.ndarray) -> np.ndarray:
+    return (np.asarray(h, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------- formats ---
+
+def check_format_tables(L):
+    g = golden_e2m1()
+    for c in range(16):
+        v = oracle.e2m1(c, L)
+        assert v == g[c] and math.copysign(1, v) == math.copysign(1, g[c]), (c, v, g[c])
+    ref4 = lib_e4m3(np.arange(256, dtype=np.uint8))
+    ref8 = lib_e8m0(np.arange(256, dtype=np.uint8))
+    for b in range(256):
+        v4, v8 = oracle.e4m3(b, L), oracle.e8m0(b, L)
+        if math.isnan(ref4[b]):
+            assert math.isnan(v4), b
+        else:
+            assert v4 == ref4[b] and math.copysign(1, v4) == math.copysign(1, ref4[b]), (b, v4, ref4[b])
+        if math.isnan(ref8[b]):
+            assert math.isnan(v8), b
+        else:
+            assert v8 == ref8[b], (b, v8, ref8[b])
+
+
+def check_layout(L):
+    g = golden_layout()
+    assert L.orc_main_entry_bytes() == g["main_entry_bytes"]
+    assert L.orc_index_entry_bytes() == g["index_entry_bytes"]
+    per_entry = L.orc_main_entry_bytes() + L.orc_index_entry_bytes()
+    # three m=2 encoder caches and one m=1 decoder cache
+    entries_per_token = 3 * 0.5 + 1 * 1.0
+    assert entries_per_token == g["entries_per_token"]
+    assert entries_per_token * per_entry == g["kv_bytes_per_token"]
+    gib = g["kv_bytes_per_token"] * g["context_limit_tokens"] / 2**30
+    assert round(gib, 2) == g["kv_gib_at_limit"]
+
+
+def check_dequant(L, seed=3):
+    main = synth.main_latents(seed, 0, 0, 300)
+    kc, ks = synth.index_keys(seed, 0, 0, 300)
+    # hand-built entry: byte 0x71 -> channel 0 code 1 (0.5), channel 1 code 7 (6.0)
+    hand = np.zeros((1, 288), np.uint8)
+    hand[0, 0] = 0x71
+    hand[0, 1] = 0x9A  # channel 2 code 0xA (-1.0), channel 3 code 9 (-0.5)
+    hand[0, 256] = 0x38  # E4M3 1.0 for channels 0..15
+    hand[0, 257] = 0x40  # E4M3 2.0 for channels 16..31
+    hand[0, 8] = 0x0F  # channel 16 code 0xF (-6.0) -> -12.0
+    # all E4M3 scale codes incl. subnormals and NaN, all nibbles
+    sweep = np.zeros((256, 288), np.uint8)
+    sweep[:, :256] = np.arange(256, dtype=np.uint8)[None, :]
+    sweep[:, 256:] = np.arange(256, dtype=np.uint8)[:, None]
+    for ent in (main, hand, sweep):
+        f, b = oracle.dequant_main(ent, L)
+        ref = ref_dequant_main(ent)
+        ref32 = ref.astype(np.float32)
+        nan = np.isnan(ref32)
+        assert np.array_equal(np.isnan(f), nan)
+        assert np.array_equal(f[~nan].view(np.uint32), ref32[~nan].view(np.uint32))
+        # bf16 output equals the exact value (products have <= 6 significant bits)
+        bb = bf16_to_f64(b)
+        assert np.array_equal(np.isnan(bb), nan)
+        assert np.array_equal(bb[~nan], ref[~nan])
+    f, _ = oracle.dequant_main(hand, L)
+    assert f[0, 0] == 0.5 and f[0, 1] == 6.0 and f[0, 2] == -1.0 and f[0, 3] == -0.5 and f[0, 16] == -12.0
+    # indexer keys, plus all E8M0 scales
+    sweep_c = np.tile(np.arange(64, dtype=np.uint8) * 4 + 1, (256, 1)).astype(np.uint8)
+    sweep_s = np.repeat(np.arange(256, dtype=np.uint8)[:, None], 4, axis=1)
+    for c, s in ((kc, ks), (sweep_c, sweep_s)):
+        f, _ = oracle.dequant_index(c, s, L)
+        ref = ref_dequant_index(c, s)
+        with np.errstate(over="ignore"):
+            ref32 = ref.astype(np.float32)
+        nan = np.isnan(ref32)
+        assert np.array_equal(np.isnan(f), nan)
+        assert np.array_equal(f[~nan].view(np.uint32), ref32[~nan].view(np.uint32))
+
+
+# ---------------------------------------------------------------- indexer ---
+
+def _ref_scores(wl, queries=None):
+    """Independent indexer scores: numpy dequant + matmul + ReLU + weighted sum."""
+    qs = range(wl.Q) if queries is None else queries
+    out = []
+    for i in qs:
+        qd = ref_dequant_index(wl.iq_codes[i], wl.iq_scales[i])  # [32][128]
+        if wl.cand_blocks is None:
+            ents = np.arange(wl.n_entries)
+        else:
+            ents = (8 * wl.cand_blocks[i][:, None] + np.arange(8)[None, :]).reshape(-1)
+        rows = i * wl.cache_q_stride + ents
+        kd = ref_dequant_index(wl.key_codes[rows], wl.key_scales[rows])  # [n][128]
+        d = qd @ kd.T  # [32][n]
+        s = (wl.w[i].astype(np.float64)[:, None] * np.maximum(d, 0.0)).sum(axis=0)
+        lim = wl.n_entries if wl.n_valid is None else min(int(wl.n_valid[i]), wl.n_entries)
+        s = np.where(ents < lim, s, -np.inf)
+        out.append(s)
+    return np.stack(out)
+
+
+def check_index_scores(L, seed=5):
+    wl = synth.full_decode(3, 700, seed)
+    sc, dots = oracle.index_score(wl, want_dots=True, L=L)
+    ref = _ref_scores(wl)
+    assert np.allclose(sc, ref, rtol=2e-7, atol=1e-30), np.abs(sc - ref).max()
+    # exact dots: an exactly-rounded sum in a different (reversed) order agrees bit for bit
+    for i in range(wl.Q):
+        qd = ref_dequant_index(wl.iq_codes[i], wl.iq_scales[i])
+        for e in (0, 17, 699):
+            kd = ref_dequant_index(wl.key_codes[i * 700 + e], wl.key_scales[i * 700 + e])[0]
+            for h in (0, 13, 31):
+                exact = math.fsum(list((qd[h] * kd)[::-1]))
+                assert dots[i, h, e] == exact, (i, h, e)
+    # one-hot weights -> score = ReLU(d_h)
+    for h in (0, 7, 31):
+        wl1 = synth.full_decode(1, 200, seed)
+        wl1.w[:] = 0
+        wl1.w[0, h] = 1.0
+        s1, d1 = oracle.index_score(wl1, want_dots=True, L=L)
+        assert np.array_equal(s1[0], np.maximum(d1[0, h], 0).astype(np.float32)), h
+    # zero keys -> score 0
+    wl0 = synth.full_decode(1, 64, seed)
+    wl0.key_codes[:] = 0
+    s0 = oracle.index_score(wl0, L=L)
+    assert np.all(s0 == 0)
+    # ReLU comes before weighting: negative weight on a negative dot contributes 0
+    wln = synth.full_decode(1, 256, seed)
+    wln.w[:] = -1.0
+    sn, dn = oracle.index_score(wln, want_dots=True, L=L)
+    expect = -np.maximum(dn[0], 0).sum(axis=0)
+    assert np.allclose(sn[0], expect, rtol=1e-6)
+    assert np.all(sn[0] <= 0)
+
+
+def check_candidate_sets(L, seed=9):
+    # Reindex pool scores equal the Full-layer scores at entries 8b+r
+    wlr = synth.reindex_decode(2, 4096, 64, seed, dense_rows=True)
+    sr = oracle.index_score(wlr, L=L)
+    assert np.allclose(sr, _ref_scores(wlr), rtol=2e-7)
+    full = synth.Workload("f", wlr.Q, wlr.n_entries, wlr.cache_q_stride, wlr.main_cache, wlr.key_codes,
+                          wlr.key_scales, wlr.iq_codes, wlr.iq_scales, wlr.w, wlr.q, wlr.swa, wlr.swa_q_stride,
+                          wlr.n_swa)
+    with np.errstate(invalid="ignore"):
+        sf = oracle.index_score(full, L=L)
+    for i in range(wlr.Q):
+        ents = (8 * wlr.cand_blocks[i][:, None] + np.arange(8)[None, :]).reshape(-1)
+        assert np.array_equal(sr[i], sf[i][ents])
+    # causal limit: entries >= n_valid are -inf, the rest unchanged
+    wlc = synth.prefill(5, 300, 40, seed, m=2)  # n_valid = 20..22
+    sc = oracle.index_score(wlc, L=L)
+    assert np.allclose(sc, _ref_scores(wlc), rtol=2e-7)
+    for i in range(5):
+        nv = wlc.n_valid[i]
+        assert np.all(np.isneginf(sc[i, nv:])) and np.all(np.isfinite(sc[i, :nv]))
+
+
+# ---------------------------------------------------------------- top-k ----
+
+def _ref_topk(scores_row, ents, k):
+    pairs = [(float(s), int(e)) for s, e in zip(scores_row, ents)]
+    pairs.sort(key=lambda t: (0 if not math.isnan(t[0]) else 1, -t[0] if not math.isnan(t[0]) else 0, t[1]))
+    top = pairs[:k]
+    return [e for _, e in top] + [-1] * (k - len(top))
+
+
+def check_topk(L, seed=11):
+    rng = np.random.default_rng(seed)
+    for n in (1, 511, 512, 513, 2048):
+        s = rng.standard_normal((2, n)).astype(np.float32)
+        idx, ts = oracle.topk(s, k=512, L=L)
+        for i in range(2):
+            assert list(idx[i]) == _ref_topk(s[i], range(n), 512), n
+            m = min(n, 512)
+            assert np.array_equal(ts[i, :m], s[i][idx[i, :m]])
+            assert np.all(np.isneginf(ts[i, m:]))
+    # ties: equal keys go to the lower index; -0 == +0
+    s = np.zeros((1, 3000), np.float32)
+    s[0, ::3] = 1.0
+    s[0, 1::3] = -0.0
+    idx, _ = oracle.topk(s, k=512, L=L)
+    assert list(idx[0]) == list(range(0, 1536, 3))
+    s2 = np.zeros((1, 1200), np.float32)
+    s2[0, 600:] = 1.0
+    s2[0, :600:2] = -0.0
+    idx2, _ = oracle.topk(s2, k=700, L=L)
+    assert list(idx2[0]) == list(range(600, 1200)) + list(range(100))
+    # quantised scores with many duplicates, brute force
+    s3 = np.round(rng.standard_normal((3, 4000)) * 4).astype(np.float32)
+    idx3, _ = oracle.topk(s3, k=512, L=L)
+    for i in range(3):
+        assert list(idx3[i]) == _ref_topk(s3[i], range(4000), 512)
+    # NaN ranks below every number
+    s4 = rng.standard_normal((1, 600)).astype(np.float32)
+    s4[0, :200] = np.nan
+    idx4, _ = oracle.topk(s4, k=512, L=L)
+    assert set(idx4[0, :400].tolist()) == set(range(200, 600)) and set(idx4[0, 400:].tolist()) <= set(range(200))
+    # n_valid and pool translation
+    s5 = rng.standard_normal((2, 64)).astype(np.float32)
+    blocks = np.array([[3, 9, 10, 40, 41, 50, 60, 70], [0, 1, 2, 3, 4, 5, 6, 7]], np.int32)
+    idx5, _ = oracle.topk(s5, k=16, n_valid=np.array([400, 30], np.int32), n_entries=1000, cand_blocks=blocks, L=L)
+    for i in range(2):
+        ents = (8 * blocks[i][:, None] + np.arange(8)[None, :]).reshape(-1)
+        lim = [400, 30][i]
+        keep = ents < lim
+        assert list(idx5[i]) == _ref_topk(s5[i][keep], ents[keep], 16)
+
+
+# ------------------------------------------------------------ attention ----
+
+def _dense_ref(q_bf16, kv_f64, scale):
+    """Library SDPA in fp64 (torch CPU math path)."""
+    qq = torch.from_numpy(bf16_to_f64(q_bf16))[:, None, :]  # [64 heads][1][512]
+    kk = torch.from_numpy(kv_f64)[None].expand(64, *kv_f64.shape).contiguous()  # [64][J][512]
+    o = torch.nn.functional.scaled_dot_product_attention(qq, kk, kk, scale=scale)
+    logits = (qq @ kk.transpose(1, 2)) * scale
+    lse = torch.logsumexp(logits[:, 0, :], dim=-1)
+    return o[:, 0, :].numpy(), lse.numpy()
+
+
+def check_attention(L, seed=13):
+    n = 200
+    wl = synth.full_decode(2, n, seed)
+    idx = np.tile(np.arange(n, dtype=np.int32), (2, 1))
+    ob, of, lse, probs = oracle.sparse_attn(wl, idx, want_probs=True, L=L)
+    for i in range(2):
+        kv = np.concatenate([ref_dequant_main(wl.main_cache[i * n:(i + 1) * n]),
+                             bf16_to_f64(wl.swa[i * 128:(i + 1) * 128])])
+        o_ref, lse_ref = _dense_ref(wl.q[i], kv, wl.scale)
+        assert np.allclose(of[i], o_ref, rtol=1e-6, atol=1e-7), np.abs(of[i] - o_ref).max()
+        assert np.allclose(lse[i], lse_ref, rtol=1e-6)
+        assert np.allclose(bf16_to_f64(ob[i]), o_ref, rtol=8e-3, atol=1e-6)
+    assert np.allclose(probs.sum(axis=-1), 1.0, atol=1e-12)
+    # permutation invariance of the selected list
+    perm = np.random.default_rng(seed).permutation(n)
+    _, of2, lse2 = oracle.sparse_attn(wl, idx[:, perm].copy(), L=L)
+    assert np.allclose(of2, of, rtol=1e-6, atol=1e-7) and np.allclose(lse2, lse, rtol=1e-6)
+    # padding (-1) and out-of-range ids are skipped
+    idx_pad = np.full((2, 300), -1, np.int32)
+    idx_pad[:, :n] = idx
+    idx_pad[:, n] = n + 5
+    _, of3, _ = oracle.sparse_attn(wl, idx_pad, L=L)
+    assert np.allclose(of3, of, rtol=1e-6, atol=1e-7)
+    # a single entry: o = v exactly
+    one = np.full((2, 4), -1, np.int32)
+    one[:, 2] = 7
+    _, of4, _ = oracle.sparse_attn(wl, one, n_swa=0, L=L)
+    for i in range(2):
+        v = ref_dequant_main(wl.main_cache[i * n + 7])[0]
+        assert np.array_equal(of4[i], np.broadcast_to(v.astype(np.float32), (64, 512)))
+    # zero query: o = mean of the values
+    wlz = synth.full_decode(1, n, seed)
+    wlz.q[:] = 0
+    _, of5, _ = oracle.sparse_attn(wlz, idx[:1], L=L)
+    kv = np.concatenate([ref_dequant_main(wlz.main_cache[:n]), bf16_to_f64(wlz.swa[:128])])
+    assert np.allclose(of5[0], np.broadcast_to(kv.mean(axis=0), (64, 512)), rtol=1e-6, atol=1e-7)
+    # empty joint set: zeros and lse = -inf
+    _, of6, lse6 = oracle.sparse_attn(wl, np.full((2, 8), -1, np.int32), n_swa=0, L=L)
+    assert np.all(of6 == 0) and np.all(np.isneginf(lse6))
+
+
+def check_decode_composition(L, seed=17):
+    wl = synth.full_decode(2, 1500, seed)
+    r = oracle.decode(wl, L=L)
+    sc = oracle.index_score(wl, L=L)
+    idx, _ = oracle.topk(sc, wl, L=L)
+    ob, of, lse = oracle.sparse_attn(wl, idx, L=L)
+    assert np.array_equal(r["scores"], sc) and np.array_equal(r["idx"], idx)
+    assert np.array_equal(r["out_bf16"], ob) and np.array_equal(r["lse"], lse)
+    # the selection is the true top-512 of the independent scores
+    ref = _ref_scores(wl)
+    for i in range(wl.Q):
+        assert list(idx[i]) == _ref_topk(ref[i].astype(np.float32), range(wl.n_entries), 512)
+
+
+ALL_CHECKS = [check_format_tables, check_layout, check_dequant, check_index_scores, check_candidate_sets,
+              check_topk, check_attention, check_decode_composition]

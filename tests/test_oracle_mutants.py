@@ -1,0 +1,56 @@
+"""Pin strength: plant a plausible mistake in a copy of the oracle source,
+build it, and require at least one pin to catch it (CPU only)."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "csa2_oracle.c")
+
+# (name, original text, mistaken text)
+MUTANTS = [
+    ("nibble_order", "return orc_e2m1((ch & 1) ? (b >> 4) : (b & 15u));",
+     "return orc_e2m1((ch & 1) ? (b & 15u) : (b >> 4));"),
+    ("e4m3_bias", "ldexp(1.0 + (double)m / 8.0, (int)e - 7)", "ldexp(1.0 + (double)m / 8.0, (int)e - 8)"),
+    ("e8m0_bias", "(int)(byte & 0xFFu) - 127", "(int)(byte & 0xFFu) - 128"),
+    ("e2m1_subnormal", "(e == 0) ? 0.5 * (double)m", "(e == 0) ? 1.0 * (double)m"),
+    ("main_scale_group", "orc_e4m3(entry[256 + c / 16])", "orc_e4m3(entry[256 + c / 32])"),
+    ("index_scale_group", "orc_e8m0(scales[c / 32])", "orc_e8m0(scales[c / 16 % 4])"),
+    ("relu_after_weight", "acc += (double)w[q * 32 + h] * r;", "acc += fmax((double)w[q * 32 + h] * d, 0.0);"),
+    ("dropped_head", "acc += (double)w[q * 32 + h] * r;", "if (h != 31) acc += (double)w[q * 32 + h] * r;"),
+    ("reversed_key", "d += qv[h][c] * kv[c];", "d += qv[h][c] * kv[127 - c];"),
+    ("pool_block_scale", "return 8 * (int64_t)blocks_q[p / 8] + p % 8;", "return (int64_t)blocks_q[p / 8] + p % 8;"),
+    ("causal_off_by_one", "if (e < 0 || e >= limit) {\n        scores", "if (e < 0 || e >= limit - 1) {\n        scores"),
+    ("tie_break_high_index", "return (x->e < y->e) ? -1 : (x->e > y->e) ? 1 : 0;",
+     "return (x->e > y->e) ? -1 : (x->e < y->e) ? 1 : 0;"),
+    ("ascending_scores", "return (x->s > y->s) ? -1 : 1;", "return (x->s < y->s) ? -1 : 1;"),
+    ("no_softmax_scale", "lg[j] = scale * d;", "lg[j] = d;"),
+    ("no_normalisation", "double p = exp(lg[j] - mx) / z;", "double p = exp(lg[j] - mx);"),
+    ("swa_dropped", "for (int r = 0; r < n_swa; ++r) {", "for (int r = 0; r < n_swa - 1; ++r) {"),
+    ("swa_row_stride", "swa + (size_t)((int64_t)qi * swa_q_stride + r) * 512", "swa + (size_t)((int64_t)qi * swa_q_stride) * 512"),
+    ("wrong_head_query", "q_bf16[((size_t)qi * 64 + h) * 512 + c]", "q_bf16[((size_t)qi * 64 + (h ^ 1)) * 512 + c]"),
+    ("lse_missing_max", "(float)(mx + log(z))", "(float)(log(z))"),
+]
+
+
+@pytest.mark.parametrize("name,orig,bad", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(name, orig, bad, tmp_path):
+    src = open(SRC).read()
+    assert src.count(orig) == 1, f"mutation anchor for {name} not unique"
+    mut = tmp_path / f"mut_{name}.c"
+    mut.write_text(src.replace(orig, bad))
+    so = str(tmp_path / f"libmut_{name}.so")
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-fvisibility=hidden", str(mut), "-o", so, "-lm"],
+                   check=True)
+    L = oracle.load_variant(so)
+    caught = []
+    for check in pins.ALL_CHECKS:
+        try:
+            check(L)
+        except AssertionError:
+            caught.append(check.__name__)
+            break
+    assert caught, f"no pin caught the planted mistake {name}"
