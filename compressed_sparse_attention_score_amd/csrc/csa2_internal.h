@@ -1,0 +1,85 @@
+// Internal launch interface between the C-ABI front end (capi.hip) and the
+// kernels. Host code only; every launcher enqueues on `stream` and returns the
+// hipGetLastError() of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+struct IndexLaunch {
+  int Q;
+  int64_t n_entries, cache_q_stride, n_cand;
+  const uint8_t *key_codes, *key_scales, *iq_codes, *iq_scales;
+  const float* w;
+  const int32_t* cand_blocks;
+  int n_blocks;
+  const int32_t* n_valid;
+};
+
+// Work decomposition of the scoring pass, shared by the selection pass.
+struct ScorePlan {
+  int wave_span;    // entries per wave (power of two, multiple of 16)
+  int group;        // sub-chunk size whose maximum key is recorded (16..wave_span)
+  int64_t n_groups; // sub-chunks per query
+  int n_wg;         // scoring workgroups per query
+};
+ScorePlan plan_score(int64_t n_cand, int Q, int k);
+
+// Selection pass layout.
+struct SelectPlan {
+  int chunk;        // scores per selection workgroup
+  int n_chunks;     // selection workgroups per query
+};
+SelectPlan plan_select(int64_t n_cand);
+
+// Attention split layout.
+struct AttnPlan {
+  int n_tiles;      // 32-slot tiles of the joint list
+  int tiles_per_split;
+  int n_splits;
+};
+AttnPlan plan_attn(int Q, int nj);
+
+hipError_t launch_dequant(int kind, const uint8_t* codes, const uint8_t* scales, int64_t n, int out_bf16, void* out,
+                          hipStream_t s);
+
+// Scores [Q][n_cand] and, if gmax != NULL, the maximum selection key of each
+// sub-chunk [Q][plan.n_groups]; zeroes ctrl[0 .. 2*Q) when ctrl != NULL.
+hipError_t launch_index_score(const IndexLaunch& a, const ScorePlan& plan, float* scores, unsigned* gmax,
+                              unsigned* ctrl, hipStream_t s);
+
+// Sub-chunk maxima straight from a score array (standalone top-k); zeroes ctrl.
+hipError_t launch_score_maxima(const float* scores, int Q, int64_t n_cand, int64_t n_entries,
+                               const int32_t* cand_blocks, int n_blocks, const int32_t* n_valid,
+                               const ScorePlan& plan, unsigned* gmax, unsigned* ctrl, hipStream_t s);
+
+// Threshold + compaction + (last workgroup per query) exact final selection.
+hipError_t launch_select(const float* scores, int Q, int64_t n_cand, int64_t n_entries, const int32_t* cand_blocks,
+                         int n_blocks, const int32_t* n_valid, int k, const ScorePlan& sp, const unsigned* gmax,
+                         unsigned* ctrl, unsigned long long* cand, int32_t* idx, float* top_scores, hipStream_t s);
+
+struct AttnLaunch {
+  int Q;
+  int64_t n_entries, cache_q_stride;
+  const uint8_t* main_cache;
+  const int32_t* idx;
+  int k_sel;
+  const uint16_t* q;
+  const uint16_t* swa;
+  int64_t swa_q_stride;
+  int n_swa;
+  float scale;
+  uint16_t* out;
+  float* lse;
+};
+
+// ws: partials (plan.n_splits > 1); ctrl: Q tickets, zero on entry.
+hipError_t launch_attn(const AttnLaunch& a, const AttnPlan& plan, float* partial, unsigned* ctrl, hipStream_t s);
+hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t s);
+
+size_t attn_partial_bytes(int Q, const AttnPlan& plan);
+
+}  // namespace csa2

@@ -1,0 +1,220 @@
+/*
+ * csa2.h — C ABI of the CSA2 global-attention hot path on AMD Instinct MI355X
+ * (gfx950): lightning-indexer scoring, top-k selection and sparse attention
+ * over FP4 latents plus a sliding window.
+ *
+ * Source of the method: "An infra-oriented diagram of the DeepSeek-V4.1-Flash
+ * architecture" (Reading notes: KV-latent bullet, Full-layer cache bullet,
+ * indexer bullet, role bullet; section "The KV cache"), "DeepSeek V4.1 Flash:
+ * Why Its Encoder, Engram and KV Cache Matter" (section "CSA2 makes long
+ * context cheaper to retain") and the "DeepSeek V4.1 Flash" model guide
+ * ("A closer look": shared KV -> candidate pool -> top 512 -> attention).
+ *
+ * Conventions for every entry point
+ *  - All data pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors),
+ *    C-contiguous, owned by the caller. The library allocates nothing, keeps no
+ *    pointer after a call returns and holds no mutable global state; calls are
+ *    thread-safe and reentrant.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work
+ *    is enqueued asynchronously on it; outputs are valid once it synchronises.
+ *  - Arguments are validated on the host before anything is enqueued: a
+ *    non-zero status means no work was launched. Data contents (NaN scores,
+ *    unsorted block lists) are preconditions and are not checked on the host;
+ *    kernels never read outside the buffers the arguments describe (selected
+ *    ids outside [0, n_entries) are skipped, out-of-range block ids are treated
+ *    as absent). Launch failures surface as CSA2_ERR_HIP.
+ *  - Argument structs begin with `struct_size` (set it to sizeof the struct).
+ *
+ * Storage layouts (one "row" = one cache entry)
+ *  main cache   uint8 [rows][288]: bytes 0..255 hold 512 FP4 E2M1 codes, byte j
+ *               = channel 2j (low nibble) and 2j+1 (high nibble); bytes 256..287
+ *               hold 32 E4M3 (OCP E4M3FN) scales, scale g for channels 16g..16g+15.
+ *  index codes  uint8 [rows][64]: 128 FP4 E2M1 codes, same nibble order.
+ *  index scales uint8 [rows][4]:  E8M0 scales, scale b for channels 32b..32b+31.
+ *  Query i's cache is rows [i*cache_q_stride, i*cache_q_stride + n_entries)
+ *  (cache_q_stride = n_entries for independent per-sequence caches, 0 for one
+ *  cache shared by all queries, as in a prefill chunk). Entry ids returned and
+ *  consumed by the library are relative to the query's cache.
+ */
+#ifndef CSA2_H_
+#define CSA2_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef CSA2_API
+#define CSA2_API __attribute__((visibility("default")))
+#endif
+
+/* ---------------------------------------------------------------- status */
+enum {
+  CSA2_OK = 0,
+  CSA2_ERR_NULL = 1,      /* a required pointer is NULL                        */
+  CSA2_ERR_SHAPE = 2,     /* unsupported size (k, counts, ranges)               */
+  CSA2_ERR_ALIGN = 3,     /* a pointer is not aligned as documented             */
+  CSA2_ERR_WORKSPACE = 4, /* workspace NULL or smaller than csa2_workspace_size */
+  CSA2_ERR_HIP = 5,       /* a HIP launch or runtime call failed                */
+  CSA2_ERR_ARG = 6        /* struct_size mismatch or bad enum value             */
+};
+
+/* Fixed shapes of the method ("An infra-oriented diagram ...", Reading notes). */
+#define CSA2_MAIN_ENTRY_BYTES 288  /* 256 B codes + 32 E4M3 scales               */
+#define CSA2_INDEX_CODE_BYTES 64   /* 128 FP4 codes                              */
+#define CSA2_INDEX_SCALE_BYTES 4   /* 4 E8M0 scales                              */
+#define CSA2_INDEX_HEADS 32        /* indexer query heads                        */
+#define CSA2_INDEX_DIM 128         /* indexer head dim                           */
+#define CSA2_HEADS 64              /* attention query heads                      */
+#define CSA2_LATENT_DIM 512        /* shared k = v latent width                  */
+#define CSA2_POOL_BLOCK 8          /* Reindex pools are built from blocks of 8   */
+#define CSA2_MAX_K 1024            /* largest supported top-k                    */
+#define CSA2_MAX_SWA 128           /* sliding-window rows per query              */
+
+/* ------------------------------------------------------------- dequant */
+enum { CSA2_KIND_MAIN = 0, CSA2_KIND_INDEX = 1 };
+enum { CSA2_OUT_F32 = 0, CSA2_OUT_BF16 = 1 };
+
+/* csa2_dequant — decode stored entries to real values (FP4 E2M1 times its
+ * block scale: E4M3 per 16 channels for main entries, E8M0 per 32 for indexer
+ * keys; "An infra-oriented diagram ...", Full-layer cache bullet and "The KV
+ * cache"). The result is the exact product (it fits both fp32 and bf16; E8M0
+ * extremes may give fp32 subnormals or inf, NaN scale codes give NaN).
+ *   kind      CSA2_KIND_MAIN:  codes = main cache [n][288], scales ignored;
+ *                              out = [n][512].
+ *             CSA2_KIND_INDEX: codes = [n][64], scales = [n][4]; out = [n][128].
+ *   out_dtype CSA2_OUT_F32 (float) or CSA2_OUT_BF16 (bf16 bits, uint16).
+ *   Alignment: codes and out 16 B; scales 4 B. n_entries >= 0 (0 = no-op). */
+CSA2_API int csa2_dequant(int kind, const void* codes, const void* scales, int64_t n_entries, int out_dtype, void* out,
+                 void* stream);
+
+/* --------------------------------------------------------- index score */
+typedef struct csa2_index_args {
+  size_t struct_size;
+  int32_t n_queries;          /* Q >= 0                                         */
+  int64_t n_entries;          /* entries per query cache, 0 <= N < 2^31         */
+  int64_t cache_q_stride;     /* rows between consecutive queries' caches       */
+  const uint8_t* key_codes;   /* [rows][64]   16-B aligned                       */
+  const uint8_t* key_scales;  /* [rows][4]    4-B aligned                        */
+  const uint8_t* iq_codes;    /* [Q][32][64]  indexer query, MXFP4, 16-B aligned */
+  const uint8_t* iq_scales;   /* [Q][32][4]   E8M0, 4-B aligned                  */
+  const float* head_weights;  /* [Q][32]      per-head weights                   */
+  const int32_t* cand_blocks; /* [Q][n_blocks] Reindex pool block ids, or NULL  */
+  int32_t n_blocks;           /* pool blocks per query (0 when cand_blocks NULL) */
+  const int32_t* n_valid;     /* [Q] causal limit (ids >= n_valid[q] excluded) or NULL */
+} csa2_index_args;
+
+/* csa2_index_score — lightning-indexer scores ("An infra-oriented diagram ...",
+ * indexer bullet): for query q and candidate entry e,
+ *     score = sum_{h<32} w[q][h] * max(0, iq_h . key_e)
+ * over 32 MXFP4 heads of 128 dims against the entry's one shared MXFP4 key.
+ * Candidates (Full layer, "search the full sparse index"): entries 0..N-1;
+ * (Reindex layer, pool of blocks of 8): position p -> entry
+ * 8*cand_blocks[q][p/8] + p%8, with block ids ascending and distinct
+ * (precondition). Entries outside [0, min(N, n_valid[q])) score -inf.
+ *   scores: [Q][n_cand] float, n_cand = N (Full) or 8*n_blocks (Reindex); 4-B aligned.
+ * The dot products are exact (FP4 products, power-of-two scales); the weighted
+ * sum is accumulated in fp32. */
+CSA2_API int csa2_index_score(const csa2_index_args* args, float* scores, void* stream);
+
+/* ---------------------------------------------------------------- topk */
+typedef struct csa2_topk_args {
+  size_t struct_size;
+  int32_t n_queries;          /* Q >= 0                                          */
+  int64_t n_cand;             /* scores per query, < 2^31                        */
+  int64_t n_entries;          /* cache size; candidate ids >= n_entries excluded */
+  const float* scores;        /* [Q][n_cand]                                     */
+  const int32_t* cand_blocks; /* [Q][n_blocks] or NULL (then id = position)      */
+  int32_t n_blocks;           /* n_cand == 8*n_blocks when cand_blocks != NULL   */
+  const int32_t* n_valid;     /* [Q] causal limit or NULL                        */
+  int32_t k;                  /* 1 <= k <= CSA2_MAX_K (the method uses 512)      */
+  int32_t* idx;               /* out [Q][k] entry ids, -1 padded                 */
+  float* top_scores;          /* out [Q][k] scores (-inf padded), or NULL        */
+} csa2_topk_args;
+
+/* csa2_topk — per-query top-k of the candidate scores ("DeepSeek V4.1 Flash"
+ * guide, "A closer look": main sparse selection of 512 entries). Output order
+ * is (score descending, entry id ascending); equal scores go to the lower id,
+ * -0 equals +0, NaN ranks below every number. When fewer than k candidates are
+ * valid the tail is -1. Needs a workspace of csa2_workspace_size(CSA2_WS_TOPK,
+ * args) bytes, 256-B aligned, contents ignored on entry. */
+CSA2_API int csa2_topk(const csa2_topk_args* args, void* workspace, size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------------- sparse attn */
+typedef struct csa2_attn_args {
+  size_t struct_size;
+  int32_t n_queries;          /* Q >= 0                                          */
+  int64_t n_entries;          /* entries per query cache                         */
+  int64_t cache_q_stride;     /* rows between consecutive queries' caches        */
+  const uint8_t* main_cache;  /* [rows][288], 16-B aligned                       */
+  const int32_t* idx;         /* [Q][k_sel] selected ids; ids outside [0,N) skipped */
+  int32_t k_sel;              /* 0 <= k_sel <= CSA2_MAX_K                        */
+  const uint16_t* q;          /* [Q][64][512] bf16, 16-B aligned                 */
+  const uint16_t* swa;        /* bf16 rows [..][512], 16-B aligned (NULL iff n_swa == 0) */
+  int64_t swa_q_stride;       /* query i's window = rows i*swa_q_stride + 0..n_swa-1 */
+  int32_t n_swa;              /* 0 <= n_swa <= 128                               */
+  float softmax_scale;        /* e.g. 1/sqrt(512)                                */
+  uint16_t* out;              /* out [Q][64][512] bf16, 16-B aligned             */
+  float* lse;                 /* out [Q][64] natural-log sum-exp of scaled logits, or NULL */
+} csa2_attn_args;
+
+/* csa2_sparse_attn — attention of 64 query heads over one shared k = v latent
+ * per entry ("An infra-oriented diagram ...", KV-latent bullet), for the joint
+ * set J = selected entries (in idx order) followed by the n_swa window rows
+ * (role bullet: the 128-token window plus 512 selected entries):
+ *     o_h = sum_{j in J} softmax_j(scale * q_h . x_j) x_j
+ * with x_j the dequantised latent (exact in bf16) or the bf16 SWA row. bf16
+ * matrix-core products, fp32 accumulation and softmax, bf16 output. An empty
+ * J gives zeros and lse = -inf. Also the whole path of a Reuse layer (given
+ * ids) and of an SWA-only layer (k_sel = 0). Workspace:
+ * csa2_workspace_size(CSA2_WS_ATTN, args) bytes, 256-B aligned. */
+CSA2_API int csa2_sparse_attn(const csa2_attn_args* args, void* workspace, size_t ws_bytes, void* stream);
+
+/* -------------------------------------------------------- fused decode */
+typedef struct csa2_decode_args {
+  size_t struct_size;
+  csa2_index_args index;      /* struct_size inside must also be set             */
+  int32_t k;                  /* top-k, 1..CSA2_MAX_K                            */
+  const uint8_t* main_cache;  /* [rows][288], same row indexing as the keys      */
+  const uint16_t* q;          /* [Q][64][512] bf16                               */
+  const uint16_t* swa;        /* bf16 window rows                                */
+  int64_t swa_q_stride;
+  int32_t n_swa;
+  float softmax_scale;
+  uint16_t* out;              /* out [Q][64][512] bf16                           */
+  float* lse;                 /* out [Q][64] or NULL                             */
+  int32_t* idx_out;           /* out [Q][k] selected ids, or NULL                */
+  void* stage_events[4];      /* optional hipEvent_t (as void*) recorded on the stream
+                                 before scoring [0], after scoring [1], after
+                                 selection [2] and after attention [3]; NULL = skip */
+} csa2_decode_args;
+
+/* csa2_decode — the whole path for one batch: csa2_index_score ->
+ * csa2_topk -> csa2_sparse_attn ("DeepSeek V4.1 Flash" guide: shared KV ->
+ * candidate pool -> top 512 -> attention), enqueued back to back with
+ * no host round trip; scores and ids live in the workspace. Same results as
+ * the three calls in sequence. Workspace: csa2_workspace_size(CSA2_WS_DECODE,
+ * args) bytes, 256-B aligned. */
+CSA2_API int csa2_decode(const csa2_decode_args* args, void* workspace, size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------------- utilities */
+enum { CSA2_WS_TOPK = 0, CSA2_WS_ATTN = 1, CSA2_WS_DECODE = 2 };
+
+/* Bytes of workspace the call `which` needs for `args` (a csa2_topk_args*,
+ * csa2_attn_args* or csa2_decode_args*); 0 if none; SIZE_MAX if the args are
+ * invalid. */
+CSA2_API size_t csa2_workspace_size(int which, const void* args);
+
+/* Static, human-readable text for a status code. */
+CSA2_API const char* csa2_status_string(int status);
+
+/* ABI version of this header (major*10000 + minor*100 + patch). */
+CSA2_API int csa2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H_ */

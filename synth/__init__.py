@@ -65,6 +65,7 @@ def lib():
         L.syn_head_weights.argtypes = [u64, i64, i64, vp]
         L.syn_bf16_normal.argtypes = [u64, i32, u64, i64, i64, vp]
         L.syn_pool_blocks.argtypes = [u64, u64, i64, i64, vp]
+        L.syn_bf16_rows.argtypes = [u64, i32, u64, i64, i64, i32, vp]
         _lib = L
     return _lib
 
@@ -118,6 +119,12 @@ def head_weights(seed: int, first: int, n: int) -> np.ndarray:
 def bf16_normal(seed: int, tid: int, seq: int, first: int, n: int) -> np.ndarray:
     out = np.empty((n,), np.uint16)
     lib().syn_bf16_normal(seed, tid, seq, first, n, _p(out))
+    return out
+
+
+def bf16_rows(seed: int, tid: int, seq: int, first_row: int, n_rows: int, width: int) -> np.ndarray:
+    out = np.empty((n_rows, width), np.uint16)
+    lib().syn_bf16_rows(seed, tid, seq, first_row, n_rows, width, _p(out))
     return out
 
 
@@ -180,12 +187,12 @@ class Workload:
 def _queries(seed, Q, swa_rows_per_query, shared_swa_rows=None):
     iq_codes, iq_scales = index_queries(seed, 0, Q)
     w = head_weights(seed, 0, Q)
-    q = np.stack([bf16_normal(seed, TID_Q, i, 0, N_HEADS * HEAD_DIM) for i in range(Q)]).reshape(Q, N_HEADS, HEAD_DIM)
+    q = np.stack([bf16_rows(seed, TID_Q, i, 0, N_HEADS, HEAD_DIM) for i in range(Q)])
     if shared_swa_rows is None:
-        swa = np.stack([bf16_normal(seed, TID_SWA, i, 0, swa_rows_per_query * HEAD_DIM) for i in range(Q)])
+        swa = np.stack([bf16_rows(seed, TID_SWA, i, 0, swa_rows_per_query, HEAD_DIM) for i in range(Q)])
         swa = swa.reshape(Q * swa_rows_per_query, HEAD_DIM)
     else:
-        swa = bf16_normal(seed, TID_SWA, 0, 0, shared_swa_rows * HEAD_DIM).reshape(shared_swa_rows, HEAD_DIM)
+        swa = bf16_rows(seed, TID_SWA, 0, 0, shared_swa_rows, HEAD_DIM)
     return iq_codes, iq_scales, w, q, swa
 
 

@@ -11,7 +11,8 @@
  * generators", OOPSLA 2014) applied to
  *     seed ^ (tensor_id << 56) ^ (seq << 40) ^ counter
  * so any element of any tensor can be produced independently and in parallel.
- * Normals use the cosine branch of Box-Muller on two consecutive counters.
+ * Normals come in Box-Muller pairs: element 2j uses the cosine and 2j+1 the
+ * sine branch of the transform of counters 2j and 2j+1.
  *
  * Storage formats follow "An infra-oriented diagram of the DeepSeek-V4.1-Flash
  * architecture" (Reading notes, the Full-layer cache bullet; section "The KV
@@ -50,10 +51,23 @@ static double ctr_uniform(uint64_t seed, uint64_t tid, uint64_t seq, uint64_t ct
   return (double)(ctr_bits(seed, tid, seq, ctr) >> 11) * (1.0 / 9007199254740992.0);
 }
 
+static void ctr_normal_pair(uint64_t seed, uint64_t tid, uint64_t seq, uint64_t pair, double* z) {
+  double u1 = 1.0 - ctr_uniform(seed, tid, seq, 2 * pair); /* (0,1] */
+  double u2 = ctr_uniform(seed, tid, seq, 2 * pair + 1);
+  double r = sqrt(-2.0 * log(u1)), t = 6.283185307179586476925 * u2;
+  z[0] = r * cos(t);
+  z[1] = r * sin(t);
+}
+
 static double ctr_normal(uint64_t seed, uint64_t tid, uint64_t seq, uint64_t elem) {
-  double u1 = 1.0 - ctr_uniform(seed, tid, seq, 2 * elem); /* (0,1] */
-  double u2 = ctr_uniform(seed, tid, seq, 2 * elem + 1);
-  return sqrt(-2.0 * log(u1)) * cos(6.283185307179586476925 * u2);
+  double z[2];
+  ctr_normal_pair(seed, tid, seq, elem >> 1, z);
+  return z[elem & 1];
+}
+
+/* n (even) consecutive normals starting at an even element */
+static void ctr_normals(uint64_t seed, uint64_t tid, uint64_t seq, uint64_t first, int n, double* out) {
+  for (int i = 0; i < n; i += 2) ctr_normal_pair(seed, tid, seq, (first >> 1) + (uint64_t)(i >> 1), out + i);
 }
 
 SYN_API double syn_normal(uint64_t seed, int tid, uint64_t seq, uint64_t elem) {
@@ -157,7 +171,7 @@ SYN_API void syn_main_latents(uint64_t seed, uint64_t seq, int64_t first, int64_
   for (int64_t i = 0; i < n; ++i) {
     double x[512];
     uint64_t e = (uint64_t)(first + i);
-    for (int c = 0; c < 512; ++c) x[c] = ctr_normal(seed, TID_MAIN, seq, e * 512u + (uint64_t)c);
+    ctr_normals(seed, TID_MAIN, seq, e * 512u, 512, x);
     quant_main_entry(x, out + (size_t)i * 288);
   }
 }
@@ -169,7 +183,7 @@ SYN_API void syn_main_latents_list(uint64_t seed, uint64_t seq, const int64_t* i
   for (int64_t i = 0; i < n; ++i) {
     double x[512];
     uint64_t e = (uint64_t)ids[i];
-    for (int c = 0; c < 512; ++c) x[c] = ctr_normal(seed, TID_MAIN, seq, e * 512u + (uint64_t)c);
+    ctr_normals(seed, TID_MAIN, seq, e * 512u, 512, x);
     quant_main_entry(x, out + (size_t)i * 288);
   }
 }
@@ -181,7 +195,7 @@ SYN_API void syn_index_keys(uint64_t seed, uint64_t seq, int64_t first, int64_t 
   for (int64_t i = 0; i < n; ++i) {
     double x[128];
     uint64_t e = (uint64_t)(first + i);
-    for (int c = 0; c < 128; ++c) x[c] = ctr_normal(seed, TID_IKEY, seq, e * 128u + (uint64_t)c);
+    ctr_normals(seed, TID_IKEY, seq, e * 128u, 128, x);
     quant_mx_row(x, 128, codes + (size_t)i * 64, scales + (size_t)i * 4);
   }
 }
@@ -192,7 +206,7 @@ SYN_API void syn_index_keys_list(uint64_t seed, uint64_t seq, const int64_t* ids
   for (int64_t i = 0; i < n; ++i) {
     double x[128];
     uint64_t e = (uint64_t)ids[i];
-    for (int c = 0; c < 128; ++c) x[c] = ctr_normal(seed, TID_IKEY, seq, e * 128u + (uint64_t)c);
+    ctr_normals(seed, TID_IKEY, seq, e * 128u, 128, x);
     quant_mx_row(x, 128, codes + (size_t)i * 64, scales + (size_t)i * 4);
   }
 }
@@ -204,8 +218,7 @@ SYN_API void syn_index_queries(uint64_t seed, int64_t first, int64_t n, uint8_t*
   for (int64_t i = 0; i < n; ++i) {
     for (int h = 0; h < 32; ++h) {
       double x[128];
-      for (int c = 0; c < 128; ++c)
-        x[c] = ctr_normal(seed, TID_IQ, (uint64_t)(first + i), (uint64_t)(h * 128 + c));
+      ctr_normals(seed, TID_IQ, (uint64_t)(first + i), (uint64_t)(h * 128), 128, x);
       quant_mx_row(x, 128, codes + ((size_t)i * 32 + h) * 64, scales + ((size_t)i * 32 + h) * 4);
     }
   }
@@ -232,6 +245,21 @@ SYN_API void syn_bf16_normal(uint64_t seed, int tid, uint64_t seq, int64_t first
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i)
     out[i] = f32_to_bf16_rne((float)ctr_normal(seed, (uint64_t)tid, seq, (uint64_t)(first + i)));
+}
+
+/* bf16 N(0,1) rows: rows [first_row, first_row + n_rows) of width `width`
+ * (even) of stream (tid, seq); row r uses elements r*width + c. */
+SYN_API void syn_bf16_rows(uint64_t seed, int tid, uint64_t seq, int64_t first_row, int64_t n_rows, int width,
+                           uint16_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    double z[2];
+    for (int c = 0; c < width; c += 2) {
+      ctr_normal_pair(seed, (uint64_t)tid, seq, ((uint64_t)(first_row + r) * (uint64_t)width + (uint64_t)c) >> 1, z);
+      out[r * width + c] = f32_to_bf16_rne((float)z[0]);
+      out[r * width + c + 1] = f32_to_bf16_rne((float)z[1]);
+    }
+  }
 }
 
 /* Candidate pool: n_pick distinct block ids out of [0, n_total), ascending,

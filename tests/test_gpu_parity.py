@@ -1,0 +1,291 @@
+"""GPU parity: every C-ABI entry point against the CPU oracle on the same
+seeded inputs (small ragged cases spanning several tiles, edge cases, and the
+five workload shapes at full size)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import (announce, bf16_np_to_f64, check_attn, check_lse, check_scores, check_topk_band, gpu_attn,
+                      gpu_decode, gpu_scores, gpu_topk, oracle, to_device)
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import compressed_sparse_attention_score_amd as csa
+
+
+@pytest.fixture(autouse=True)
+def _name(request):
+    announce(request.node.nodeid)
+    yield
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ dequant
+
+def _dq(kind, codes, scales, n, bf16):
+    width = 512 if kind == 0 else 128
+    out = torch.empty((n, width), dtype=torch.int16 if bf16 else torch.float32, device="cuda")
+    c = torch.from_numpy(np.ascontiguousarray(codes)).cuda()
+    s = None if scales is None else torch.from_numpy(np.ascontiguousarray(scales)).cuda()
+    csa.csa2_dequant(kind, c, s, n, 1 if bf16 else 0, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _bits_equal_nan(a32, b32):
+    an, bn = np.isnan(a32), np.isnan(b32)
+    assert np.array_equal(an, bn)
+    assert np.array_equal(a32[~an].view(np.uint32), b32[~bn].view(np.uint32))
+
+
+def test_dequant_main_bitexact():
+    main = synth.main_latents(7, 0, 0, 1001)
+    sweep = np.zeros((256, 288), np.uint8)
+    sweep[:, :256] = np.arange(256, dtype=np.uint8)[None, :]
+    sweep[:, 256:] = np.arange(256, dtype=np.uint8)[:, None]
+    ent = np.concatenate([main, sweep])
+    f_ref, b_ref = oracle.dequant_main(ent)
+    f = _dq(0, ent, None, len(ent), False)
+    _bits_equal_nan(f, f_ref)
+    b = _dq(0, ent, None, len(ent), True).view(np.uint16)
+    bn = np.isnan(bf16_np_to_f64(b))
+    assert np.array_equal(bn, np.isnan(f_ref))
+    assert np.array_equal(b[~bn], b_ref[~bn])
+
+
+def test_dequant_index_bitexact():
+    kc, ks = synth.index_keys(7, 0, 0, 999)
+    sc = np.tile(np.arange(64, dtype=np.uint8) * 4 + 1, (256, 1)).astype(np.uint8)
+    ss = np.repeat(np.arange(256, dtype=np.uint8)[:, None], 4, axis=1)
+    codes, scales = np.concatenate([kc, sc]), np.concatenate([ks, ss])
+    with np.errstate(over="ignore"):
+        f_ref, b_ref = oracle.dequant_index(codes, scales)
+    f = _dq(1, codes, scales, len(codes), False)
+    _bits_equal_nan(f, f_ref)
+    b = _dq(1, codes, scales, len(codes), True).view(np.uint16)
+    bn = np.isnan(bf16_np_to_f64(b))
+    assert np.array_equal(b[~bn], b_ref[~bn])
+
+
+# ------------------------------------------------------------ index scores
+
+@pytest.mark.parametrize("Q,N", [(3, 5000), (1, 17), (2, 16), (1, 4096 + 37)])
+def test_index_score_full(Q, N):
+    wl = synth.full_decode(Q, N, seed=N)
+    ref, dots = oracle.index_score(wl, want_dots=True)
+    got = gpu_scores(to_device(wl))
+    check_scores(got, ref, dots, wl.w, f"full Q{Q} N{N}")
+
+
+def test_index_score_reindex_pool_and_bad_blocks():
+    wl = synth.reindex_decode(4, 65536, 300, seed=3, dense_rows=True)
+    wl.cand_blocks = wl.cand_blocks.copy()
+    wl.cand_blocks[1, 5] = -1          # absent block
+    wl.cand_blocks[2, 7] = 65536 // 8  # beyond the cache
+    ref, dots = oracle.index_score(wl, want_dots=True)
+    got = gpu_scores(to_device(wl))
+    check_scores(got, ref, dots, wl.w, "reindex")
+    assert np.all(np.isneginf(got[1, 40:48])) and np.all(np.isneginf(got[2, 56:64]))
+
+
+def test_index_score_causal_prefill():
+    wl = synth.prefill(40, 3000, 5000, seed=4)
+    ref, dots = oracle.index_score(wl, want_dots=True)
+    got = gpu_scores(to_device(wl))
+    check_scores(got, ref, dots, wl.w, "causal")
+
+
+# ------------------------------------------------------------------- top-k
+
+def _assert_topk_exact(scores, k, n_entries, cand_blocks=None, n_valid=None, what=""):
+    ref_i, ref_s = oracle.topk(scores, k=k, n_valid=n_valid, n_entries=n_entries, cand_blocks=cand_blocks)
+    gi, gs = gpu_topk(scores, k, n_entries, cand_blocks, n_valid)
+    assert np.array_equal(gi, ref_i), f"{what}: ids differ at {np.argwhere(gi != ref_i)[:5].tolist()}"
+    assert np.array_equal(np.isnan(gs), np.isnan(ref_s))
+    m = ~np.isnan(ref_s)
+    assert np.array_equal(gs[m].view(np.uint32), ref_s[m].view(np.uint32)), what
+
+
+@pytest.mark.parametrize("n", [1, 100, 511, 512, 513, 4096, 4097, 70001])
+@pytest.mark.parametrize("k", [1, 7, 512, 1024])
+def test_topk_exact_random(n, k):
+    rng = np.random.default_rng(n * 31 + k)
+    s = rng.standard_normal((3, n)).astype(np.float32)
+    _assert_topk_exact(s, k, n, what=f"n{n} k{k}")
+
+
+def test_topk_ties_nan_negzero():
+    rng = np.random.default_rng(1)
+    s = np.round(rng.standard_normal((4, 20000)) * 3).astype(np.float32)  # heavy ties
+    s[1, ::7] = -0.0
+    s[1, 1::7] = 0.0
+    s[2, :300] = np.nan
+    s[3, :] = 2.5  # all equal: the whole list is one tie set
+    _assert_topk_exact(s, 512, 20000, what="ties")
+
+
+def test_topk_pool_and_causal():
+    rng = np.random.default_rng(2)
+    blocks = np.stack([np.sort(rng.choice(50000, 700, replace=False)) for _ in range(3)]).astype(np.int32)
+    s = rng.standard_normal((3, 5600)).astype(np.float32)
+    _assert_topk_exact(s, 512, 400000, cand_blocks=blocks, what="pool")
+    s2 = rng.standard_normal((5, 9000)).astype(np.float32)
+    nv = np.array([0, 1, 511, 512, 8999], np.int32)
+    _assert_topk_exact(s2, 512, 9000, n_valid=nv, what="causal")
+
+
+def test_topk_empty_candidates():
+    s = np.zeros((2, 0), np.float32)
+    gi, _ = gpu_topk(s, 512, 0)
+    assert np.all(gi == -1)
+
+
+# --------------------------------------------------------------- attention
+
+def test_sparse_attn_with_oracle_ids():
+    wl = synth.full_decode(3, 2000, seed=11)
+    sc = oracle.index_score(wl)
+    idx, _ = oracle.topk(sc, wl)
+    _, of, lse = oracle.sparse_attn(wl, idx)
+    ob, glse = gpu_attn(to_device(wl), idx)
+    check_attn(ob, of, "attn")
+    check_lse(glse, lse, "attn lse")
+
+
+@pytest.mark.parametrize("Q", [1, 40, 700])
+def test_sparse_attn_split_layouts(Q):
+    """Q=1 splits the slot list over many workgroups, Q=700 over one."""
+    wl = synth.full_decode(Q, 600, seed=Q)
+    rng = np.random.default_rng(Q)
+    idx = np.stack([rng.choice(600, 512, replace=False) for _ in range(Q)]).astype(np.int32)
+    _, of, lse = oracle.sparse_attn(wl, idx)
+    ob, glse = gpu_attn(to_device(wl), idx)
+    check_attn(ob, of, f"attn Q{Q}")
+    check_lse(glse, lse, f"attn Q{Q} lse")
+
+
+def test_sparse_attn_edge_cases():
+    wl = synth.full_decode(2, 300, seed=5, n_swa=37)
+    db = to_device(wl)
+    rng = np.random.default_rng(5)
+    # -1 padding and out-of-range ids are skipped; ragged k_sel and window
+    idx = np.full((2, 77), -1, np.int32)
+    idx[:, :50] = rng.choice(300, 50, replace=False)
+    idx[0, 60] = 300
+    idx[1, 61] = 10 ** 6
+    _, of, lse = oracle.sparse_attn(wl, idx)
+    ob, glse = gpu_attn(db, idx)
+    check_attn(ob, of, "padded")
+    check_lse(glse, lse, "padded lse")
+    # SWA only (k_sel = 0)
+    _, of, lse = oracle.sparse_attn(wl, np.zeros((2, 0), np.int32))
+    ob, glse = gpu_attn(db, None)
+    check_attn(ob, of, "swa only")
+    # selection only (no window)
+    _, of, lse = oracle.sparse_attn(wl, idx, n_swa=0)
+    ob, glse = gpu_attn(db, idx, n_swa=0)
+    check_attn(ob, of, "no window")
+    # empty joint set: zeros, lse = -inf
+    ob, glse = gpu_attn(db, np.full((2, 8), -1, np.int32), n_swa=0)
+    assert np.all(ob == 0) and np.all(np.isneginf(glse))
+
+
+# ------------------------------------------------------------ fused decode
+
+def _check_decode(wl, queries=None, what=""):
+    db = to_device(wl)
+    ob, glse, gidx = gpu_decode(db)
+    ref = oracle.decode(wl, queries=queries)
+    qs = list(range(wl.Q)) if queries is None else list(queries)
+    check_topk_band(gidx[qs], ref["scores"], ref["idx"], _sub(wl, qs), wl.k, what)
+    # attention with the GPU's own selection isolates the attention step
+    _, of_own, lse_own = oracle.sparse_attn(wl, gidx[qs], queries=qs)
+    check_attn(ob[qs], of_own, what + " (own ids)")
+    check_lse(glse[qs], lse_own, what + " lse")
+    # end to end against the oracle's selection (differences only from band swaps)
+    check_attn(ob[qs], ref["out_f32"], what + " (oracle ids)")
+    return gidx
+
+
+def _sub(wl, qs):
+    class V:  # the fields check_topk_band reads, restricted to qs
+        pass
+    v = V()
+    v.n_entries = wl.n_entries
+    v.cand_blocks = None if wl.cand_blocks is None else wl.cand_blocks[qs]
+    v.n_valid = None if wl.n_valid is None else wl.n_valid[qs]
+    return v
+
+
+def test_decode_full_small():
+    _check_decode(synth.full_decode(2, 4096 + 300, seed=21), what="full small")
+
+
+def test_decode_reindex_small_poisoned():
+    wl = synth.reindex_decode(3, 1 << 16, 2048, seed=22, dense_rows=True)
+    gidx = _check_decode(wl, what="reindex small")
+    for qi in range(wl.Q):
+        pool = set((8 * wl.cand_blocks[qi][:, None] + np.arange(8)[None, :]).reshape(-1).tolist())
+        assert set(gidx[qi].tolist()) <= pool
+
+
+def test_decode_prefill_small():
+    _check_decode(synth.prefill(50, 2048, 3000, seed=23), what="prefill small")
+
+
+def test_decode_fewer_than_k_entries():
+    _check_decode(synth.full_decode(2, 300, seed=24), what="n<k")
+
+
+def test_decode_deterministic():
+    wl = synth.full_decode(4, 9000, seed=25)
+    db = to_device(wl)
+    a = gpu_decode(db)
+    b = gpu_decode(db)
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+
+
+# ------------------------------------------------- full-size workload shapes
+
+def test_config0_full():
+    _check_decode(synth.make_config(0), what="config0")
+
+
+def test_config1_full():
+    _check_decode(synth.make_config(1), what="config1")
+
+
+def test_config4_full():
+    _check_decode(synth.make_config(4), what="config4")
+
+
+def test_config2_full_pool():
+    """1,048,576-entry caches, 2,048 random blocks of 8 per query; the oracle
+    runs on the pool rows re-indexed into a compact cache."""
+    wl = synth.make_config(2, dense_rows=False)
+    db = to_device(wl)
+    ob, glse, gidx = gpu_decode(db)
+    # compact view: query i's pool becomes entries 0..16383 of its own cache
+    Q, nb = wl.Q, wl.n_blocks
+    comp = synth.Workload("c2c", Q, 8 * nb, 8 * nb, wl.main_cache, wl.key_codes, wl.key_scales, wl.iq_codes,
+                          wl.iq_scales, wl.w, wl.q, wl.swa, wl.swa_q_stride, wl.n_swa,
+                          cand_blocks=np.tile(np.arange(nb, dtype=np.int32), (Q, 1)))
+    ref = oracle.decode(comp)
+    pools = [(8 * wl.cand_blocks[i][:, None].astype(np.int64) + np.arange(8)[None, :]).reshape(-1) for i in range(Q)]
+    # map the GPU's global ids back to compact ids
+    comp_gidx = np.stack([np.searchsorted(pools[i], gidx[i]) for i in range(Q)]).astype(np.int32)
+    for i in range(Q):
+        assert np.array_equal(pools[i][comp_gidx[i]], gidx[i]), "GPU selected an entry outside the pool"
+    check_topk_band(comp_gidx, ref["scores"], ref["idx"], comp, wl.k, "config2")
+    _, of_own, _ = oracle.sparse_attn(comp, comp_gidx)
+    check_attn(ob, of_own, "config2 (own ids)")
+    check_attn(ob, ref["out_f32"], "config2 (oracle ids)")
+
+
+def test_config3_sampled_queries():
+    wl = synth.make_config(3)
+    qs = [0, 1, 1000, 2047, 2048, 3001, 4094, 4095]
+    _check_decode(wl, queries=qs, what="config3")
