@@ -21,8 +21,9 @@
  *   R2 the E4M3 flavour is OCP E4M3FN (bias 7, no inf, S.1111.111 = NaN).
  *   R3 the indexer query is MXFP4 like the keys (E2M1, E8M0 per 32).
  *   R4 indexer score = sum_h w_h * max(q_h . k, 0): no extra constant factor.
- *   R5 top-k order is (score descending, entry index ascending); -0 == +0;
- *      NaN ranks below every number.
+ *   R5 top-k ranks candidates by (score descending, entry index ascending),
+ *      -0 == +0, NaN below every number; the selected set is returned in
+ *      ascending entry index (the pages fix the set, not an order).
  *   R6 Reindex pools are aligned blocks: block b covers entries 8b..8b+7.
  *   R7 attention runs over the selected entries followed by the SWA rows, one
  *      softmax over the joint set, no de-duplication, no sink, no bias; the
@@ -182,9 +183,9 @@ ORC_API void orc_index_score(int Q, int64_t n_entries, int64_t cache_q_stride, c
 
 /* ------------------------------------------------------------------ O4 --- */
 /* Top-k per query ([PERCHY] "Main sparse selection: 512 entries"; [ATLAS]
- * indexer bullet "top-512"). Sort the candidates by R5 and keep the first
- * min(k, n). idx gets global entry ids, padded with -1; top_scores (optional)
- * gets the scores, padded with -inf. */
+ * indexer bullet "top-512"). Sort the candidates by the R5 ranking, keep the
+ * first min(k, n), and list them by ascending entry id. idx gets entry ids,
+ * padded with -1; top_scores (optional) gets their scores, padded with -inf. */
 typedef struct {
   float s;
   int64_t e;
@@ -197,6 +198,12 @@ static int rank_cmp(const void* a, const void* b) {
   if (xn != yn) return xn ? 1 : -1;
   if (!xn && x->s != y->s) return (x->s > y->s) ? -1 : 1; /* -0 == +0 here */
   return (x->e < y->e) ? -1 : (x->e > y->e) ? 1 : 0;
+}
+
+static int id_cmp(const void* a, const void* b) {
+  int64_t ea = ((const orc_pair*)a)->e, eb = ((const orc_pair*)b)->e;
+  if (ea == eb) return 0;
+  return ea < eb ? -1 : 1;
 }
 
 ORC_API void orc_topk(const float* scores, int Q, int64_t n_cand, const int32_t* n_valid, int64_t n_entries,
@@ -216,6 +223,8 @@ ORC_API void orc_topk(const float* scores, int Q, int64_t n_cand, const int32_t*
       ++m;
     }
     qsort(v, (size_t)m, sizeof(orc_pair), rank_cmp);
+    int64_t keep = m < k ? m : k;
+    qsort(v, (size_t)keep, sizeof(orc_pair), id_cmp);
     for (int j = 0; j < k; ++j) {
       idx[(size_t)q * k + j] = (j < m) ? (int32_t)v[j].e : -1;
       if (top_scores) top_scores[(size_t)q * k + j] = (j < m) ? v[j].s : -INFINITY;
