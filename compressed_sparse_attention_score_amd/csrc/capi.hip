@@ -109,16 +109,16 @@ int check_decode(const csa2_decode_args* a, int64_t* n_cand) {
 
 // Workspace layouts (each region 256-byte aligned).
 struct TopkWs {
-  unsigned* ctrl;  // [3][Q]: candidate counts, selection tickets, attention tickets
-  unsigned* gmax;  // [Q][n_groups]
-  unsigned long long* cand;  // [Q][n_cand]
+  unsigned* counts;          // [Q][n_chunks] candidates kept per compaction chunk
+  unsigned* gmax;            // [Q][n_groups] sub-chunk maximum keys
+  unsigned long long* cand;  // [Q][n_cand] kept composites
   size_t bytes;
 };
 
 TopkWs carve_topk(void* ws, int Q, int64_t n_cand, const ScorePlan& sp, Carve& c) {
   TopkWs w;
-  w.ctrl = c.take<unsigned>((size_t)3 * Q);
-  w.gmax = c.take<unsigned>((size_t)Q * (size_t)sp.n_groups);
+  w.counts = c.take<unsigned>((size_t)Q * (size_t)plan_select(n_cand).n_chunks);
+  w.gmax = c.take<unsigned>((size_t)Q * (size_t)(sp.n_groups > 0 ? sp.n_groups : 1));
   w.cand = c.take<unsigned long long>((size_t)Q * (size_t)(n_cand > 0 ? n_cand : 1));
   w.bytes = c.off;
   (void)ws;
@@ -137,7 +137,6 @@ size_t ws_attn(int Q, int nj) {
   AttnPlan ap = plan_attn(Q, nj);
   if (ap.n_splits <= 1) return 0;
   Carve c(nullptr);
-  c.take<unsigned>((size_t)Q);
   c.take<char>(attn_partial_bytes(Q, ap));
   return c.off;
 }
@@ -215,7 +214,7 @@ int csa2_index_score(const csa2_index_args* a, float* scores, void* stream) {
   IndexLaunch L{a->n_queries, a->n_entries, a->cache_q_stride, n_cand,       a->key_codes, a->key_scales,
                 a->iq_codes,  a->iq_scales, a->head_weights,   a->cand_blocks, a->n_blocks, a->n_valid};
   ScorePlan sp = plan_score(n_cand, a->n_queries, 512);
-  return hip_status(launch_index_score(L, sp, scores, nullptr, nullptr, (hipStream_t)stream));
+  return hip_status(launch_index_score(L, sp, scores, nullptr, (hipStream_t)stream));
 }
 
 int csa2_topk(const csa2_topk_args* a, void* ws, size_t ws_bytes, void* stream) {
@@ -230,10 +229,10 @@ int csa2_topk(const csa2_topk_args* a, void* ws, size_t ws_bytes, void* stream) 
   TopkWs w = carve_topk(ws, Q, a->n_cand, sp, c);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = launch_score_maxima(a->scores, Q, a->n_cand, a->n_entries, a->cand_blocks, a->n_blocks, a->n_valid,
-                                     sp, w.gmax, w.ctrl, s);
+                                     sp, w.gmax, s);
   if (e != hipSuccess) return CSA2_ERR_HIP;
   e = launch_select(a->scores, Q, a->n_cand, a->n_entries, a->cand_blocks, a->n_blocks, a->n_valid, a->k, sp, w.gmax,
-                    w.ctrl, w.cand, a->idx, a->top_scores, s);
+                    w.counts, w.cand, a->idx, a->top_scores, s);
   return hip_status(e);
 }
 
@@ -246,17 +245,14 @@ int csa2_sparse_attn(const csa2_attn_args* a, void* ws, size_t ws_bytes, void* s
   if (st) return st;
   AttnPlan ap = plan_attn(Q, a->k_sel + a->n_swa);
   hipStream_t s = (hipStream_t)stream;
-  unsigned* ticket = nullptr;
   float* partial = nullptr;
   if (ap.n_splits > 1) {
     Carve c(ws);
-    ticket = c.take<unsigned>((size_t)Q);
     partial = c.take<float>(attn_partial_bytes(Q, ap) / sizeof(float));
-    if (launch_zero_u32(ticket, Q, s) != hipSuccess) return CSA2_ERR_HIP;
   }
   AttnLaunch L{Q, a->n_entries, a->cache_q_stride, a->main_cache, a->idx, a->k_sel, a->q, a->swa, a->swa_q_stride,
                a->n_swa, a->softmax_scale, a->out, a->lse};
-  return hip_status(launch_attn(L, ap, partial, ticket, s));
+  return hip_status(launch_attn(L, ap, partial, s));
 }
 
 int csa2_decode(const csa2_decode_args* a, void* ws, size_t ws_bytes, void* stream) {
@@ -286,21 +282,21 @@ int csa2_decode(const csa2_decode_args* a, void* ws, size_t ws_bytes, void* stre
   auto mark = [&](int i) {
     return a->stage_events[i] ? hipEventRecord((hipEvent_t)a->stage_events[i], s) : hipSuccess;
   };
-  // 1. scores + sub-chunk maxima; also zeroes the three control rows
+  // 1. scores + sub-chunk maxima
   hipError_t e = mark(0);
-  if (e == hipSuccess) e = launch_index_score(L, sp, w.scores, w.tk.gmax, w.tk.ctrl, s);
+  if (e == hipSuccess) e = launch_index_score(L, sp, w.scores, w.tk.gmax, s);
   if (e == hipSuccess) e = mark(1);
   if (e != hipSuccess) return CSA2_ERR_HIP;
-  // 2. threshold, compaction, exact top-k
+  // 2. threshold + compaction, exact top-k
   e = launch_select(w.scores, Q, n_cand, a->index.n_entries, a->index.cand_blocks, a->index.n_blocks,
-                    a->index.n_valid, a->k, sp, w.tk.gmax, w.tk.ctrl, w.tk.cand, w.idx, nullptr, s);
+                    a->index.n_valid, a->k, sp, w.tk.gmax, w.tk.counts, w.tk.cand, w.idx, nullptr, s);
   if (e == hipSuccess) e = mark(2);
   if (e != hipSuccess) return CSA2_ERR_HIP;
-  // 3. attention over the selection + window; tickets = control row 2
+  // 3. attention over the selection + window
   AttnPlan ap = plan_attn(Q, a->k + a->n_swa);
   AttnLaunch A{Q,    a->index.n_entries, a->index.cache_q_stride, a->main_cache, w.idx,  a->k,  a->q,
                a->swa, a->swa_q_stride,  a->n_swa,                a->softmax_scale, a->out, a->lse};
-  e = launch_attn(A, ap, w.partial, w.tk.ctrl + 2 * (size_t)Q, s);
+  e = launch_attn(A, ap, w.partial, s);
   if (e == hipSuccess) e = mark(3);
   return hip_status(e);
 }

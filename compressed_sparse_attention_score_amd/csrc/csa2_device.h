@@ -137,19 +137,4 @@ __device__ __forceinline__ unsigned umax_xor16(unsigned x) {
   return r[0] > r[1] ? r[0] : r[1];
 }
 
-// Block-wide helpers over `nwaves` waves via LDS.
-template <int NT>
-__device__ __forceinline__ unsigned block_sum_u32(unsigned v, unsigned* red) {
-  constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  unsigned t = 0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) t += red[i];
-  return t;
-}
-
 }  // namespace csa2

@@ -47,19 +47,20 @@ hipError_t launch_dequant(int kind, const uint8_t* codes, const uint8_t* scales,
                           hipStream_t s);
 
 // Scores [Q][n_cand] and, if gmax != NULL, the maximum selection key of each
-// sub-chunk [Q][plan.n_groups]; zeroes ctrl[0 .. 2*Q) when ctrl != NULL.
+// sub-chunk [Q][plan.n_groups].
 hipError_t launch_index_score(const IndexLaunch& a, const ScorePlan& plan, float* scores, unsigned* gmax,
-                              unsigned* ctrl, hipStream_t s);
+                              hipStream_t s);
 
-// Sub-chunk maxima straight from a score array (standalone top-k); zeroes ctrl.
+// Sub-chunk maxima straight from a score array (standalone top-k).
 hipError_t launch_score_maxima(const float* scores, int Q, int64_t n_cand, int64_t n_entries,
                                const int32_t* cand_blocks, int n_blocks, const int32_t* n_valid,
-                               const ScorePlan& plan, unsigned* gmax, unsigned* ctrl, hipStream_t s);
+                               const ScorePlan& plan, unsigned* gmax, hipStream_t s);
 
-// Threshold + compaction + (last workgroup per query) exact final selection.
+// Threshold + compaction kernel, then the exact selection kernel.
+// counts: [Q][plan_select(n_cand).n_chunks]; cand: [Q][n_cand] composites.
 hipError_t launch_select(const float* scores, int Q, int64_t n_cand, int64_t n_entries, const int32_t* cand_blocks,
                          int n_blocks, const int32_t* n_valid, int k, const ScorePlan& sp, const unsigned* gmax,
-                         unsigned* ctrl, unsigned long long* cand, int32_t* idx, float* top_scores, hipStream_t s);
+                         unsigned* counts, unsigned long long* cand, int32_t* idx, float* top_scores, hipStream_t s);
 
 struct AttnLaunch {
   int Q;
@@ -76,9 +77,9 @@ struct AttnLaunch {
   float* lse;
 };
 
-// ws: partials (plan.n_splits > 1); ctrl: Q tickets, zero on entry.
-hipError_t launch_attn(const AttnLaunch& a, const AttnPlan& plan, float* partial, unsigned* ctrl, hipStream_t s);
-hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t s);
+// partial: workspace for the per-split records (plan.n_splits > 1); the merge
+// runs as a second kernel.
+hipError_t launch_attn(const AttnLaunch& a, const AttnPlan& plan, float* partial, hipStream_t s);
 
 size_t attn_partial_bytes(int Q, const AttnPlan& plan);
 

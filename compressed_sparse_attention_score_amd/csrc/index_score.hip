@@ -21,7 +21,8 @@
 namespace csa2 {
 
 namespace {
-constexpr int kUnroll = 4;  // 16-entry groups in flight per wave
+constexpr int kUnroll = 4;  // 16-entry groups per load batch (two batches in flight per wave)
+constexpr int kMaxWaveSpan = 512;  // entries per wave (the plan picks 64..512)
 
 struct ScoreArgs {
   const uint8_t* key_codes;
@@ -35,7 +36,6 @@ struct ScoreArgs {
   int n_blocks, Q, wave_span, group;
   float* scores;
   unsigned* gmax;
-  unsigned* ctrl;
 };
 }  // namespace
 
@@ -54,13 +54,15 @@ __device__ __forceinline__ int64_t cand_entry(const ScoreArgs& a, int q, int64_t
   return (e >= 0 && e < limit) ? e : -1;
 }
 
-template <bool POOL>
+template <bool POOL, int UNROLL = kUnroll>
 __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
   const int q = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, kb = lane >> 4;
-
-  if (a.ctrl && blockIdx.x == 0 && threadIdx.x < 3) a.ctrl[(int64_t)threadIdx.x * a.Q + q] = 0u;
+  // Scores and sub-chunk maxima are staged in LDS and written once per wave
+  // after the loop, so the loop's only vector-memory operations are loads.
+  __shared__ float s_score[4][kMaxWaveSpan];
+  __shared__ unsigned s_gmax[4][kMaxWaveSpan / 16];
 
   // A operands: query heads r16 and 16+r16, scale block kb.
   const uint8_t* iqc = a.iq_codes + (int64_t)q * kIHeads * 64;
@@ -87,43 +89,53 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
   const int64_t w1p = min(w0p + a.wave_span, a.n_cand);
   unsigned gm = 0u;
 
-  for (int64_t g0 = w0p; g0 < w1p; g0 += 16 * kUnroll) {
-    v4u bc[kUnroll];
-    int bs[kUnroll];
-    bool ok[kUnroll];
+  // Key loads run one batch of UNROLL groups ahead of the matrix cores (two
+  // statically indexed buffers, alternated by a 2x unrolled loop). Loads are
+  // unconditional so that the compiler keeps the second batch in flight:
+  // lanes without a valid candidate read row 0 of their cache and are masked
+  // at compute time.
+  if (limit <= 0) {  // no valid candidate in this query's list
+    for (int64_t p = w0p + lane; p < w1p; p += 64) out[p] = -__builtin_inff();
+    if (a.gmax && lane == 0)
+      for (int64_t g = w0p / a.group; g * a.group < w1p; ++g) a.gmax[(int64_t)q * a.n_groups + g] = 0u;
+    return;
+  }
+  v4u bcA[UNROLL], bcB[UNROLL];
+  unsigned bsA[UNROLL], bsB[UNROLL];
+  bool okA[UNROLL], okB[UNROLL];
+  auto issue = [&](v4u* bc, unsigned* bs, bool* ok, int64_t g0) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < UNROLL; ++u) {
       const int64_t p = g0 + 16 * u + r16;
       const int64_t e = (p < w1p) ? cand_entry<POOL>(a, q, p, limit) : -1;
       ok[u] = e >= 0;
-      bc[u] = v4u{0u, 0u, 0u, 0u};
-      bs[u] = 127;
-      if (ok[u]) {
-        const int64_t row = base_row + e;
-        bc[u] = __builtin_nontemporal_load((const v4u*)(a.key_codes + row * 64 + kb * 16));
-        bs[u] = (int)((__builtin_nontemporal_load((const unsigned*)(a.key_scales + row * 4)) >> (8 * kb)) & 0xFFu);
-      }
+      const int64_t row = base_row + (e >= 0 ? e : 0);
+      bc[u] = __builtin_nontemporal_load((const v4u*)(a.key_codes + row * 64 + kb * 16));
+      bs[u] = __builtin_nontemporal_load((const unsigned*)(a.key_scales + row * 4));
     }
+  };
+  auto compute = [&](const v4u* bc, const unsigned* bs, const bool* ok, int64_t g0) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < UNROLL; ++u) {
       const int64_t gp = g0 + 16 * u;
       if (gp >= w1p) break;
-      v8i B = {(int)bc[u][0], (int)bc[u][1], (int)bc[u][2], (int)bc[u][3], 0, 0, 0, 0};
+      const v4u c = ok[u] ? bc[u] : v4u{0u, 0u, 0u, 0u};
+      const int sb = ok[u] ? (int)((bs[u] >> (8 * kb)) & 0xFFu) : 127;
+      v8i B = {(int)c[0], (int)c[1], (int)c[2], (int)c[3], 0, 0, 0, 0};
       v4f c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
-      c0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A0, B, c0, 4, 4, 0, sa0, 0, bs[u]);
-      c1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1, B, c1, 4, 4, 0, sa1, 0, bs[u]);
-      float s = 0.f;
+      c0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A0, B, c0, 4, 4, 0, sa0, 0, sb);
+      c1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1, B, c1, 4, 4, 0, sa1, 0, sb);
+      float sc = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s = fmaf(w0[r], fmaxf(c0[r], 0.f), s);
+      for (int r = 0; r < 4; ++r) sc = fmaf(w0[r], fmaxf(c0[r], 0.f), sc);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s = fmaf(w1[r], fmaxf(c1[r], 0.f), s);
-      s = add_xor16(s);
-      s = add_xor32(s);
+      for (int r = 0; r < 4; ++r) sc = fmaf(w1[r], fmaxf(c1[r], 0.f), sc);
+      sc = add_xor16(sc);
+      sc = add_xor32(sc);
       // every lane now holds the score of entry r16 of this group
-      const int64_t p = gp + r16;
-      if (kb == 0 && p < w1p) out[p] = ok[u] ? s : -__builtin_inff();
+      if (kb == 0) s_score[wave][gp - w0p + r16] = ok[u] ? sc : -__builtin_inff();
       if (a.gmax) {
-        gm = max(gm, ok[u] ? score_key(s) : 0u);
+        gm = max(gm, ok[u] ? score_key(sc) : 0u);
         const int64_t gend = gp + 16;
         if ((gend & (a.group - 1)) == 0 || gend >= w1p) {
           unsigned v = gm;
@@ -131,11 +143,27 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
           v = max(v, (unsigned)__shfl_xor((int)v, 2, 64));
           v = max(v, (unsigned)__shfl_xor((int)v, 4, 64));
           v = max(v, (unsigned)__shfl_xor((int)v, 8, 64));
-          if (lane == 0) a.gmax[(int64_t)q * a.n_groups + gp / a.group] = v;
+          if (lane == 0) s_gmax[wave][(gp - w0p) / a.group] = v;
           gm = 0u;
         }
       }
     }
+  };
+  constexpr int64_t kStep = 16 * UNROLL;
+  issue(bcA, bsA, okA, w0p);
+  for (int64_t g0 = w0p; g0 < w1p; g0 += 2 * kStep) {
+    if (g0 + kStep < w1p) issue(bcB, bsB, okB, g0 + kStep);
+    compute(bcA, bsA, okA, g0);
+    if (g0 + kStep >= w1p) break;
+    if (g0 + 2 * kStep < w1p) issue(bcA, bsA, okA, g0 + 2 * kStep);
+    compute(bcB, bsB, okB, g0 + kStep);
+  }
+  // flush this wave's staged scores and maxima (wave-private LDS rows)
+  const int span = (int)(w1p - w0p);
+  for (int i = lane; i < span; i += 64) out[w0p + i] = s_score[wave][i];
+  if (a.gmax) {
+    const int ng = (span + a.group - 1) / a.group;
+    for (int i = lane; i < ng; i += 64) a.gmax[(int64_t)q * a.n_groups + w0p / a.group + i] = s_gmax[wave][i];
   }
 }
 
@@ -144,11 +172,9 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
 __global__ __launch_bounds__(256) void k_score_maxima(const float* __restrict__ scores, int Q, int64_t n_cand,
                                                       int64_t n_entries, const int32_t* __restrict__ cand_blocks,
                                                       int n_blocks, const int32_t* __restrict__ n_valid, int group,
-                                                      int64_t n_groups, unsigned* __restrict__ gmax,
-                                                      unsigned* __restrict__ ctrl) {
+                                                      int64_t n_groups, unsigned* __restrict__ gmax) {
   const int q = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (ctrl && blockIdx.x == 0 && threadIdx.x < 3) ctrl[(int64_t)threadIdx.x * Q + q] = 0u;
   const int64_t gi = (int64_t)blockIdx.x * 4 + wave;
   if (gi >= n_groups) return;
   int64_t limit = n_entries;
@@ -188,7 +214,7 @@ ScorePlan plan_score(int64_t n_cand, int Q, int k) {
 }
 
 hipError_t launch_index_score(const IndexLaunch& L, const ScorePlan& plan, float* scores, unsigned* gmax,
-                              unsigned* ctrl, hipStream_t s) {
+                              hipStream_t s) {
   if (L.Q <= 0) return hipSuccess;
   ScoreArgs a;
   a.key_codes = L.key_codes;
@@ -208,11 +234,7 @@ hipError_t launch_index_score(const IndexLaunch& L, const ScorePlan& plan, float
   a.group = plan.group;
   a.scores = scores;
   a.gmax = gmax;
-  a.ctrl = ctrl;
-  if (L.n_cand <= 0) {
-    if (ctrl) return launch_zero_u32(ctrl, 3 * (int64_t)L.Q, s);
-    return hipSuccess;
-  }
+  if (L.n_cand <= 0) return hipSuccess;
   dim3 grid((unsigned)plan.n_wg, (unsigned)L.Q);
   if (L.cand_blocks)
     k_index_score<true><<<grid, 256, 0, s>>>(a);
@@ -223,12 +245,11 @@ hipError_t launch_index_score(const IndexLaunch& L, const ScorePlan& plan, float
 
 hipError_t launch_score_maxima(const float* scores, int Q, int64_t n_cand, int64_t n_entries,
                                const int32_t* cand_blocks, int n_blocks, const int32_t* n_valid,
-                               const ScorePlan& plan, unsigned* gmax, unsigned* ctrl, hipStream_t s) {
-  if (Q <= 0) return hipSuccess;
-  if (n_cand <= 0) return launch_zero_u32(ctrl, 3 * (int64_t)Q, s);
+                               const ScorePlan& plan, unsigned* gmax, hipStream_t s) {
+  if (Q <= 0 || n_cand <= 0) return hipSuccess;
   dim3 grid((unsigned)((plan.n_groups + 3) / 4), (unsigned)Q);
   k_score_maxima<<<grid, 256, 0, s>>>(scores, Q, n_cand, n_entries, cand_blocks, n_blocks, n_valid, plan.group,
-                                      plan.n_groups, gmax, ctrl);
+                                      plan.n_groups, gmax);
   return hipGetLastError();
 }
 

@@ -2,23 +2,27 @@
 // look": main sparse selection of 512 entries; "An infra-oriented diagram of
 // the DeepSeek-V4.1-Flash architecture", indexer bullet: top-512).
 //
-// Order: score descending, entry id ascending (-0 == +0, NaN lowest). Each
-// candidate is a 64-bit composite (order-preserving score key << 32 | ~id), so
-// the exact top-k is simply the k largest composites, which are unique.
+// Ranking: score descending, entry id ascending (-0 == +0, NaN lowest). Each
+// candidate is a 64-bit composite (order-preserving score key << 32 | ~id),
+// so the exact top-k is the set of the k largest composites, which are
+// unique. The set is returned in ascending entry id.
 //
-// Three steps, no host round trip and no full sort:
+// No sort is needed:
 //  1. The scoring pass records the largest key of every sub-chunk of the
 //     candidate list (>= 2k sub-chunks when the list is long enough).
 //  2. theta = the k-th largest of those sub-chunk maxima is a lower bound on
 //     the k-th largest score: k distinct sub-chunks each hold an element
-//     >= theta. Every selection workgroup recomputes theta for its query,
-//     then appends the composites of its chunk with key >= theta to a
-//     per-query candidate list (typically ~k(1 + small) entries in all).
-//  3. The last workgroup of each query (atomic ticket) radix-selects the k
-//     largest composites of that list and bitonic-sorts them.
+//     >= theta. Each compaction workgroup finds theta by radix select and
+//     writes its chunk's composites with key >= theta, in position order
+//     (block prefix sum), to a fixed region of the candidate list.
+//  3. One workgroup per query gathers the regions in chunk order, finds the
+//     k-th largest composite T by radix select and writes every candidate
+//     >= T in list order, which is ascending entry id.
 // With fewer than k non-empty sub-chunks theta falls back to "every valid
-// candidate", so the result is exact for any input; degenerate inputs (huge
-// tie sets) only make the list longer.
+// candidate", so the result is exact for any input; heavy ties only make the
+// candidate list longer. Steps 2 and 3 are separate kernels: handing the list
+// over at a kernel boundary is cheaper on this multi-XCD part than an
+// in-kernel hand-off between workgroups.
 #include "csa2_device.h"
 #include "csa2_internal.h"
 
@@ -26,205 +30,290 @@ namespace csa2 {
 
 namespace {
 constexpr int NT = 256;
-constexpr int kRadixBits = 11;
-constexpr int kBins = 1 << kRadixBits;  // 2048
-constexpr int kChunk = 4096;            // scores per selection workgroup
-constexpr int kLdsCand = 4096;          // composites kept in LDS for the final select
-constexpr int kSortMax = 1024;          // CSA2_MAX_K
+constexpr int kChunk = 4096;  // scores per compaction workgroup (16 per thread)
+constexpr int kPer = kChunk / NT;
+constexpr int kRegCand = 16;  // candidates per thread held in registers by the final pass
+constexpr int kRadixBits = 8;
+constexpr int kBins = 1 << kRadixBits;
 
 struct SelShared {
   unsigned hist[kBins];
-  unsigned red[8];
+  unsigned wsum[NT / 64];
   unsigned res[4];
-  unsigned long long buf[kLdsCand];
-  unsigned long long sortbuf[kSortMax];
-  unsigned n_buf;
-  unsigned base;
-  unsigned is_last;
+  unsigned long long cand[NT * kRegCand];
 };
 }  // namespace
 
-// k-th largest of the non-zero values src[0..n) (values may repeat), by MSB-first
-// radix passes of 11 bits with an LDS histogram. Returns 0 when fewer than k
-// non-zero values exist. If the bucket holding the k-th value is taken whole,
-// the returned threshold T has that bucket's lower bits cleared: exactly the
-// values >= T are then "the k largest" (or a superset when values repeat).
-// All NT threads must call it.
+// Inclusive prefix sum of x over the workgroup (thread order); *total gets the
+// sum of all. Uses wsum (NT/64 entries); contains barriers.
+__device__ __forceinline__ unsigned block_incl_scan(unsigned x, unsigned* wsum, unsigned* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned y = (unsigned)__shfl_up((int)x, off, 64);
+    if (lane >= off) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) wsum[wv] = x;
+  __syncthreads();
+  unsigned before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const unsigned s = wsum[w];
+    before += (w < wv) ? s : 0u;
+    all += s;
+  }
+  *total = all;
+  return x + before;
+}
+
+// One radix pass: pick the digit (bits shift..shift+7) of the k-th largest
+// value given the histogram in sh.hist. Updates prefix/remaining; returns
+// false if the histogram holds fewer than `remaining` values and true when
+// the chosen bucket is taken whole (no further pass needed) via *done.
 template <typename T>
-__device__ T radix_kth_largest(const T* src, int64_t n, unsigned k, SelShared& sh) {
-  constexpr int W = (int)(sizeof(T) * 8);
+__device__ __forceinline__ bool radix_pick(SelShared& sh, int shift, T& prefix, unsigned& remaining, bool* done) {
   const int tid = threadIdx.x;
+  // thread t looks at bin 255 - t: the inclusive scan is a suffix count
+  const unsigned h = sh.hist[kBins - 1 - tid];
+  unsigned total;
+  const unsigned incl = block_incl_scan(h, sh.wsum, &total);
+  if (incl - h < remaining && remaining <= incl) {
+    sh.res[0] = (unsigned)(kBins - 1 - tid);
+    sh.res[1] = incl - h;
+    sh.res[2] = h;
+  }
+  __syncthreads();
+  if (total < remaining) return false;
+  const unsigned d = sh.res[0], above = sh.res[1], cnt = sh.res[2];
+  prefix |= ((T)d) << shift;
+  remaining -= above;
+  *done = (cnt == remaining);
+  __syncthreads();
+  return true;
+}
+
+// k-th largest of the non-zero values held PER per thread (values may
+// repeat), by MSB-first radix passes of 8 bits over an LDS histogram.
+// Returns 0 when fewer than k non-zero values exist. When the bucket holding
+// the k-th value is taken whole the remaining low bits are left at zero, so
+// the values >= the result are exactly the k largest (a superset when values
+// repeat). All NT threads must call it.
+template <typename T, int PER>
+__device__ T radix_kth_regs(const T (&v)[PER], unsigned k, SelShared& sh) {
+  constexpr int W = (int)(sizeof(T) * 8);
   T prefix = 0;
   unsigned remaining = k;
-  int hi = W;  // bits >= hi are fixed in prefix
-  while (hi > 0) {
-    const int bits = (hi >= kRadixBits) ? kRadixBits : hi;
-    const int shift = hi - bits;
-    const unsigned mask = (1u << bits) - 1u;
-    for (int i = tid; i < kBins; i += NT) sh.hist[i] = 0u;
+  for (int hi = W; hi > 0; hi -= kRadixBits) {
+    const int shift = hi - kRadixBits;
+    sh.hist[threadIdx.x] = 0u;
     __syncthreads();
-    for (int64_t i = tid; i < n; i += NT) {
-      T v = src[i];
-      if (v == 0) continue;
-      if (hi < W && (v >> hi) != (prefix >> hi)) continue;
-      atomicAdd(&sh.hist[(unsigned)(v >> shift) & mask], 1u);
-    }
-    __syncthreads();
-    // suffix sums: thread t owns bins [t*8, t*8+8)
-    constexpr int PER = kBins / NT;
-    unsigned local = 0;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) local += sh.hist[tid * PER + j];
-    // inclusive suffix scan over threads (higher thread ids = larger digits)
-    const int lane = tid & 63, wv = tid >> 6;
-    unsigned x = local;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      unsigned y = (unsigned)__shfl_down((int)x, off, 64);
-      if (lane + off < 64) x += y;
-    }
-    if (lane == 0) sh.red[wv] = x;
-    __syncthreads();
-    unsigned higher_waves = 0;
-    for (int w2 = wv + 1; w2 < NT / 64; ++w2) higher_waves += sh.red[w2];
-    const unsigned incl = x + higher_waves;  // sum over bins >= t*PER
-    const unsigned above = incl - local;     // sum over bins >= (t+1)*PER
-    if (tid == 0) {
-      unsigned total = 0;
-      for (int w2 = 0; w2 < NT / 64; ++w2) total += sh.red[w2];
-      sh.res[3] = total;
-    }
-    if (above < remaining && remaining <= incl) {
-      unsigned acc = above;
-      for (int j = PER - 1; j >= 0; --j) {
-        unsigned h = sh.hist[tid * PER + j];
-        if (acc + h >= remaining) {
-          sh.res[0] = (unsigned)(tid * PER + j);
-          sh.res[1] = acc;
-          sh.res[2] = h;
-          break;
-        }
-        acc += h;
-      }
+    for (int j = 0; j < PER; ++j) {
+      const T x = v[j];
+      if (x == 0) continue;
+      if (hi < W && (x >> hi) != (prefix >> hi)) continue;
+      atomicAdd(&sh.hist[(unsigned)(x >> shift) & (kBins - 1)], 1u);
     }
     __syncthreads();
-    if (sh.res[3] < remaining) {  // fewer than k values in total (first pass only)
-      __syncthreads();
-      return (T)0;
-    }
-    const unsigned d = sh.res[0], acc = sh.res[1], h = sh.res[2];
-    __syncthreads();
-    prefix |= ((T)d) << shift;
-    remaining -= acc;
-    hi = shift;
-    if (h == remaining) break;  // the whole bucket is taken
+    bool done = false;
+    if (!radix_pick<T>(sh, shift, prefix, remaining, &done)) return (T)0;
+    if (done) break;
   }
   return prefix;
 }
 
-// Selection workgroup: grid (n_chunks, Q).
-__global__ __launch_bounds__(NT) void k_select(const float* __restrict__ scores, int Q, int64_t n_cand,
-                                               int64_t n_entries, const int32_t* __restrict__ cand_blocks,
-                                               int n_blocks, const int32_t* __restrict__ n_valid, int k, int chunk,
-                                               int n_chunks, const unsigned* __restrict__ gmax, int64_t n_groups,
-                                               unsigned* __restrict__ ctrl, unsigned long long* __restrict__ cand,
-                                               int32_t* __restrict__ idx, float* __restrict__ top_scores) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  SelShared& sh = *reinterpret_cast<SelShared*>(smem);
+// Same selection over values streamed from memory (lists too long for
+// registers); zeros are ignored.
+template <typename T>
+__device__ T radix_kth_stream(const T* src, int64_t n, unsigned k, SelShared& sh) {
+  constexpr int W = (int)(sizeof(T) * 8);
+  T prefix = 0;
+  unsigned remaining = k;
+  for (int hi = W; hi > 0; hi -= kRadixBits) {
+    const int shift = hi - kRadixBits;
+    sh.hist[threadIdx.x] = 0u;
+    __syncthreads();
+    for (int64_t i = threadIdx.x; i < n; i += NT) {
+      const T x = src[i];
+      if (x == 0) continue;
+      if (hi < W && (x >> hi) != (prefix >> hi)) continue;
+      atomicAdd(&sh.hist[(unsigned)(x >> shift) & (kBins - 1)], 1u);
+    }
+    __syncthreads();
+    bool done = false;
+    if (!radix_pick<T>(sh, shift, prefix, remaining, &done)) return (T)0;
+    if (done) break;
+  }
+  return prefix;
+}
+
+// Threshold + compaction: grid (n_chunks, Q). Writes cand[q][c0 .. c0+cnt) in
+// position order and counts[q][chunk] = cnt.
+__global__ __launch_bounds__(NT) void k_select_compact(const float* __restrict__ scores, int64_t n_cand,
+                                                       int64_t n_entries, const int32_t* __restrict__ cand_blocks,
+                                                       int n_blocks, const int32_t* __restrict__ n_valid, int k,
+                                                       const unsigned* __restrict__ gmax, int64_t n_groups,
+                                                       int n_chunks, unsigned* __restrict__ counts,
+                                                       unsigned long long* __restrict__ cand) {
+  __shared__ SelShared sh;
   const int q = blockIdx.y, tid = threadIdx.x;
-  unsigned* qcount = ctrl;
-  unsigned* ticket = ctrl + Q;
   int64_t limit = n_entries;
   if (n_valid) limit = min(limit, (int64_t)n_valid[q]);
 
-  // ---- 1. theta from the sub-chunk maxima
-  unsigned theta = 1u;
-  if (n_groups >= k) theta = radix_kth_largest<unsigned>(gmax + (int64_t)q * n_groups, n_groups, (unsigned)k, sh);
-  if (theta < 1u) theta = 1u;
-
-  // ---- 2. compact this chunk's candidates with key >= theta
-  if (tid == 0) sh.n_buf = 0u;
-  __syncthreads();
-  const int64_t c0 = (int64_t)blockIdx.x * chunk, c1 = min(c0 + chunk, n_cand);
+  // this thread's 16 consecutive positions (loads issued before the threshold work)
+  const int64_t c0 = (int64_t)blockIdx.x * kChunk;
+  const int64_t p0 = c0 + (int64_t)tid * kPer;
   const float* srow = scores + (int64_t)q * n_cand;
-  for (int64_t p = c0 + tid; p < c1; p += NT) {
+  float sc[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) sc[j] = (p0 + j < n_cand) ? srow[p0 + j] : 0.f;
+  int64_t ent[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int64_t p = p0 + j;
     int64_t e = p;
     if (cand_blocks) {
-      int32_t b = cand_blocks[(int64_t)q * n_blocks + (p >> 3)];
+      const int32_t b = (p < n_cand) ? cand_blocks[(int64_t)q * n_blocks + (p >> 3)] : -1;
       e = (b < 0) ? -1 : 8 * (int64_t)b + (p & 7);
     }
-    if (e < 0 || e >= limit) continue;
-    unsigned key = score_key(srow[p]);
-    if (key >= theta) {
-      unsigned pos = atomicAdd(&sh.n_buf, 1u);
-      sh.buf[pos] = ((unsigned long long)key << 32) | (unsigned long long)(~(unsigned)e);
-    }
+    ent[j] = (p < n_cand && e >= 0 && e < limit) ? e : -1;
   }
-  __syncthreads();
-  const unsigned nb = sh.n_buf;
-  if (tid == 0) sh.base = nb ? atomicAdd(&qcount[q], nb) : 0u;
-  __syncthreads();
-  unsigned long long* qc = cand + (int64_t)q * n_cand;
-  for (unsigned i = tid; i < nb; i += NT) qc[sh.base + i] = sh.buf[i];
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) sh.is_last = (atomicAdd(&ticket[q], 1u) == (unsigned)(n_chunks - 1)) ? 1u : 0u;
-  __syncthreads();
-  if (!sh.is_last) return;
 
-  // ---- 3. last workgroup of query q: exact top-k of the candidate list
-  __threadfence();
-  const unsigned m = atomicAdd(&qcount[q], 0u);
-  const unsigned long long* src = qc;
-  if (m <= (unsigned)kLdsCand) {
-    for (unsigned i = tid; i < m; i += NT) sh.buf[i] = qc[i];
-    __syncthreads();
-    src = sh.buf;
-  }
-  unsigned long long T = 0ull;
-  if (m > (unsigned)k) T = radix_kth_largest<unsigned long long>(src, m, (unsigned)k, sh);
-  if (tid == 0) sh.n_buf = 0u;
-  __syncthreads();
-  for (unsigned i = tid; i < m; i += NT) {
-    unsigned long long v = src[i];
-    if (v >= T) {
-      unsigned pos = atomicAdd(&sh.n_buf, 1u);
-      if (pos < (unsigned)kSortMax) sh.sortbuf[pos] = v;
-    }
-  }
-  __syncthreads();
-  const unsigned cnt = min(sh.n_buf, (unsigned)k);
-  int P = 1;
-  while (P < (int)cnt) P <<= 1;
-  for (int i = tid; i < P; i += NT)
-    if (i >= (int)cnt) sh.sortbuf[i] = 0ull;
-  __syncthreads();
-  // bitonic sort, descending
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = tid; t < P / 2; t += NT) {
-        int i = 2 * t - (t & (stride - 1));
-        int j = i + stride;
-        bool desc = ((i & size) == 0);
-        unsigned long long x = sh.sortbuf[i], y = sh.sortbuf[j];
-        if ((x < y) == desc) {
-          sh.sortbuf[i] = y;
-          sh.sortbuf[j] = x;
-        }
+  // ---- theta = k-th largest sub-chunk maximum
+  unsigned theta = 1u;
+  if (n_groups >= k) {
+    const unsigned* gq = gmax + (int64_t)q * n_groups;
+    unsigned t;
+    if (n_groups <= (int64_t)NT * 16) {
+      unsigned g[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int64_t i = (int64_t)j * NT + tid;
+        g[j] = (i < n_groups) ? gq[i] : 0u;
       }
-      __syncthreads();
+      t = radix_kth_regs<unsigned, 16>(g, (unsigned)k, sh);
+    } else {
+      t = radix_kth_stream<unsigned>(gq, n_groups, (unsigned)k, sh);
     }
+    theta = t > 1u ? t : 1u;
   }
-  for (int j = tid; j < k; j += NT) {
-    int32_t id = -1;
-    float sc = -__builtin_inff();
-    if (j < (int)cnt) {
-      unsigned long long v = sh.sortbuf[j];
-      id = (int32_t)(~(unsigned)(v & 0xFFFFFFFFull));
-      sc = key_score((unsigned)(v >> 32));
+
+  // ---- keep key >= theta, in position order
+  unsigned long long comp[kPer];
+  unsigned cnt = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const unsigned key = score_key(sc[j]);
+    const bool keep = ent[j] >= 0 && key >= theta;
+    comp[j] = keep ? (((unsigned long long)key << 32) | (unsigned long long)(~(unsigned)ent[j])) : 0ull;
+    cnt += keep ? 1u : 0u;
+  }
+  unsigned total;
+  const unsigned incl = block_incl_scan(cnt, sh.wsum, &total);
+  unsigned pos = incl - cnt;
+  unsigned long long* dst = cand + (int64_t)q * n_cand + c0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (comp[j]) dst[pos++] = comp[j];
+  if (tid == 0) counts[(int64_t)q * n_chunks + blockIdx.x] = total;
+}
+
+// Exact top-k of each query's candidate list: grid (Q). Output in list order.
+__global__ __launch_bounds__(NT) void k_select_final(const unsigned* __restrict__ counts, int n_chunks,
+                                                     int64_t n_cand, int k, const unsigned long long* __restrict__ cand,
+                                                     int32_t* __restrict__ idx, float* __restrict__ top_scores) {
+  __shared__ SelShared sh;
+  const int q = blockIdx.x, tid = threadIdx.x;
+  const unsigned* cq = counts + (int64_t)q * n_chunks;
+  const unsigned long long* lq = cand + (int64_t)q * n_cand;
+  int32_t* iq = idx + (int64_t)q * k;
+  float* tq = top_scores ? top_scores + (int64_t)q * k : nullptr;
+
+  // total candidates
+  unsigned m = 0;
+  for (int c0 = 0; c0 < n_chunks; c0 += NT) {
+    const unsigned x = (c0 + tid < n_chunks) ? cq[c0 + tid] : 0u;
+    unsigned tot;
+    block_incl_scan(x, sh.wsum, &tot);
+    m += tot;
+  }
+  unsigned written = 0;
+  if (m <= (unsigned)(NT * kRegCand) && n_chunks <= NT) {
+    // gather the regions in chunk order into LDS: thread c copies chunk c
+    const unsigned cnt_c = (tid < n_chunks) ? cq[tid] : 0u;
+    unsigned tot;
+    const unsigned off = block_incl_scan(cnt_c, sh.wsum, &tot) - cnt_c;
+    for (unsigned i = 0; i < cnt_c; ++i) sh.cand[off + i] = lq[(int64_t)tid * kChunk + i];
+    __syncthreads();
+    unsigned long long v[kRegCand];
+#pragma unroll
+    for (int j = 0; j < kRegCand; ++j) {
+      const unsigned e = tid * kRegCand + j;
+      v[j] = (e < m) ? sh.cand[e] : 0ull;
     }
-    idx[(int64_t)q * k + j] = id;
-    if (top_scores) top_scores[(int64_t)q * k + j] = sc;
+    const unsigned long long T =
+        (m > (unsigned)k) ? radix_kth_regs<unsigned long long, kRegCand>(v, (unsigned)k, sh) : 0ull;
+    unsigned c = 0;
+#pragma unroll
+    for (int j = 0; j < kRegCand; ++j) c += (v[j] != 0ull && v[j] >= T) ? 1u : 0u;
+    unsigned all;
+    unsigned pos = block_incl_scan(c, sh.wsum, &all) - c;
+#pragma unroll
+    for (int j = 0; j < kRegCand; ++j) {
+      if (v[j] != 0ull && v[j] >= T && pos < (unsigned)k) {
+        iq[pos] = (int32_t)(~(unsigned)(v[j] & 0xFFFFFFFFull));
+        if (tq) tq[pos] = key_score((unsigned)(v[j] >> 32));
+        ++pos;
+      }
+    }
+    written = min(all, (unsigned)k);
+  } else {
+    // long lists (heavy ties or huge candidate sets): stream the chunk regions
+    unsigned long long T = 0ull;
+    if (m > (unsigned)k) {
+      unsigned long long prefix = 0;
+      unsigned remaining = (unsigned)k;
+      for (int hi = 64; hi > 0; hi -= kRadixBits) {
+        const int shift = hi - kRadixBits;
+        sh.hist[tid] = 0u;
+        __syncthreads();
+        for (int c = 0; c < n_chunks; ++c) {
+          const unsigned n_c = cq[c];
+          for (unsigned i = tid; i < n_c; i += NT) {
+            const unsigned long long x = lq[(int64_t)c * kChunk + i];
+            if (hi < 64 && (x >> hi) != (prefix >> hi)) continue;
+            atomicAdd(&sh.hist[(unsigned)(x >> shift) & (kBins - 1)], 1u);
+          }
+        }
+        __syncthreads();
+        bool done = false;
+        radix_pick<unsigned long long>(sh, shift, prefix, remaining, &done);
+        if (done) break;
+      }
+      T = prefix;
+    }
+    // ordered write: chunk by chunk, NT elements at a time
+    for (int c = 0; c < n_chunks; ++c) {
+      const unsigned n_c = cq[c];
+      for (unsigned i0 = 0; i0 < n_c; i0 += NT) {
+        const unsigned i = i0 + tid;
+        const unsigned long long x = (i < n_c) ? lq[(int64_t)c * kChunk + i] : 0ull;
+        const unsigned sel = (x != 0ull && x >= T) ? 1u : 0u;
+        unsigned tot;
+        const unsigned pos = written + block_incl_scan(sel, sh.wsum, &tot) - sel;
+        if (sel && pos < (unsigned)k) {
+          iq[pos] = (int32_t)(~(unsigned)(x & 0xFFFFFFFFull));
+          if (tq) tq[pos] = key_score((unsigned)(x >> 32));
+        }
+        written += tot;
+      }
+    }
+    written = min(written, (unsigned)k);
+  }
+  for (int j = (int)written + tid; j < k; j += NT) {
+    iq[j] = -1;
+    if (tq) tq[j] = -__builtin_inff();
   }
 }
 
@@ -238,23 +327,14 @@ SelectPlan plan_select(int64_t n_cand) {
 
 hipError_t launch_select(const float* scores, int Q, int64_t n_cand, int64_t n_entries, const int32_t* cand_blocks,
                          int n_blocks, const int32_t* n_valid, int k, const ScorePlan& sp, const unsigned* gmax,
-                         unsigned* ctrl, unsigned long long* cand, int32_t* idx, float* top_scores, hipStream_t s) {
+                         unsigned* counts, unsigned long long* cand, int32_t* idx, float* top_scores, hipStream_t s) {
   if (Q <= 0) return hipSuccess;
   SelectPlan pl = plan_select(n_cand);
-  dim3 grid((unsigned)pl.n_chunks, (unsigned)Q);
-  k_select<<<grid, NT, sizeof(SelShared), s>>>(scores, Q, n_cand, n_entries, cand_blocks, n_blocks, n_valid, k,
-                                               pl.chunk, pl.n_chunks, gmax, sp.n_groups, ctrl, cand, idx, top_scores);
-  return hipGetLastError();
-}
-
-__global__ void k_zero_u32(unsigned* p, int64_t n) {
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = 0u;
-}
-
-hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  k_zero_u32<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(p, n);
+  k_select_compact<<<dim3((unsigned)pl.n_chunks, (unsigned)Q), NT, 0, s>>>(
+      scores, n_cand, n_entries, cand_blocks, n_blocks, n_valid, k, gmax, sp.n_groups, pl.n_chunks, counts, cand);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_select_final<<<(unsigned)Q, NT, 0, s>>>(counts, pl.n_chunks, n_cand, k, cand, idx, top_scores);
   return hipGetLastError();
 }
 

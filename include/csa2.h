@@ -135,11 +135,14 @@ typedef struct csa2_topk_args {
 } csa2_topk_args;
 
 /* csa2_topk — per-query top-k of the candidate scores ("DeepSeek V4.1 Flash"
- * guide, "A closer look": main sparse selection of 512 entries). Output order
- * is (score descending, entry id ascending); equal scores go to the lower id,
- * -0 equals +0, NaN ranks below every number. When fewer than k candidates are
- * valid the tail is -1. Needs a workspace of csa2_workspace_size(CSA2_WS_TOPK,
- * args) bytes, 256-B aligned, contents ignored on entry. */
+ * guide, "A closer look": main sparse selection of 512 entries). The k best
+ * candidates by (score descending, entry id ascending) are kept: equal scores
+ * go to the lower id, -0 equals +0, NaN ranks below every number. The kept set
+ * is written in ascending entry id (the selection fixes a set, not an order);
+ * top_scores[q][j] is the score of idx[q][j]. When fewer than k candidates are
+ * valid the tail is -1 / -inf. Needs a workspace of
+ * csa2_workspace_size(CSA2_WS_TOPK, args) bytes, 256-B aligned, contents
+ * ignored on entry. */
 CSA2_API int csa2_topk(const csa2_topk_args* args, void* workspace, size_t ws_bytes, void* stream);
 
 /* --------------------------------------------------------- sparse attn */
