@@ -7,17 +7,28 @@ synthetic input already resident in HBM. Steps rotate over device replicas of
 the batch so that consecutive steps cannot be served from the 256 MB
 memory-side cache.
 
-Prints one JSON line: queries/s (value), entries scored/s, per-stage times
-from HIP events recorded by the library on its stream, the roofline of the
-dominant kernel (indexer scoring, HBM-bound: 68 B per scored entry) and the
-CPU oracle timed on the host as a baseline.
+Phases (all on one stream):
+  1. warm-up, then K timed decode steps bracketed by synchronisation and two
+     HIP events (no other event inside the timed region);
+  2. per-stage times: up to 50 more steps with the library's stage events;
+  3. isolated kernel timing for the roofline: K back-to-back launches of
+     csa2_index_score (the scan kernel) and of csa2_sparse_attn, each
+     bracketed by two HIP events on the launch stream;
+  4. the CPU oracle on the host cores over a bounded sample (>= --cpu-seconds).
+
+Prints one JSON line. `python bench.py --pmc-summary DIR` instead summarises
+the counter CSVs of `rocprofv3 --pmc ... --output-format csv -d DIR` runs of
+this script (with --copy-calibration) into per-launch HBM bytes, and
+`--trace-summary DIR` the kernel-trace CSVs of a `--kernel-trace` run.
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import ctypes
+import glob
+import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -28,12 +39,21 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0
-FP4_PEAK_TFLOPS = 10100.0
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+FP4_PEAK_TFLOPS = 10100.0    # MI355X dense MXFP4 MFMA, published
 METRIC = "CSA2 decode queries/s + indexer entries scored/s; % HBM / FP4-MFMA roofline"
-IQ_BYTES = 32 * 64 + 32 * 4 + 32 * 4  # indexer query codes + scales + head weights
-FIXED_BYTES = IQ_BYTES + 65536 + 131072 + 512 * 288 + 65536  # + q, SWA, selected latents, output
+IQ_BYTES = 32 * 64 + 32 * 4 + 32 * 4   # indexer query codes + E8M0 scales + head weights
+ENTRY_BYTES_INDEX = 68                 # 64 B codes + 4 B scales per scored entry
+ENTRY_BYTES_MAIN = 288
+FLOP_PER_PAIR = 2 * 32 * 128
+SCORE_KERNEL = "k_index_score"
+SCORE_SOURCES = ("index_score.hip", "csa2_device.h")
+CSRC = os.path.join(ROOT, "compressed_sparse_attention_score_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_index_score_hbm_traffic.md")
+COPY_MIB = 512
 
+
+# ------------------------------------------------------------------ helpers
 
 class HipEvents:
     """hipEvent_t handles via the HIP runtime (created once, reused)."""
@@ -44,11 +64,15 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.ev = []
         for _ in range(n):
             h = ctypes.c_void_p()
             assert self.hip.hipEventCreate(ctypes.byref(h)) == 0
             self.ev.append(h.value)
+
+    def record(self, i, stream):
+        assert self.hip.hipEventRecord(ctypes.c_void_p(self.ev[i]), ctypes.c_void_p(stream.cuda_stream)) == 0
 
     def ms(self, a, b):
         out = ctypes.c_float()
@@ -74,28 +98,188 @@ def replicate(db, R):
     return reps
 
 
-def cpu_baseline(wl, gpu_out=None):
+def work_of(wl):
+    """Algorithmic bytes / FLOP of one batch (inputs read once, outputs written once)."""
+    Q = wl.Q
+    if wl.n_valid is not None:
+        per_q = np.minimum(wl.n_valid.astype(np.int64), wl.n_entries)
+    else:
+        per_q = np.full(Q, wl.n_cand, np.int64)
+    pairs = int(per_q.sum())
+    block_ids = 4 * wl.n_blocks if wl.cand_blocks is not None else 0
+    # keys: a shared prefill cache is read once, independent decode caches once per query
+    if wl.cache_q_stride == 0:
+        key_bytes = ENTRY_BYTES_INDEX * int(per_q.max(initial=0))
+    else:
+        key_bytes = ENTRY_BYTES_INDEX * pairs
+    score_bytes = key_bytes + Q * (IQ_BYTES + block_ids)
+    k_sel = np.minimum(per_q, wl.k)
+    swa_rows = (Q - 1) * wl.swa_q_stride + wl.n_swa if Q else 0
+    swa_rows = min(swa_rows, Q * wl.n_swa)
+    attn_bytes = Q * 65536 * 2 + ENTRY_BYTES_MAIN * int(k_sel.sum()) + 1024 * swa_rows
+    attn_flops = int(2 * 2 * 64 * 512 * (k_sel + wl.n_swa).sum())
+    return dict(pairs=pairs, score_bytes=score_bytes, score_flops=pairs * FLOP_PER_PAIR, attn_bytes=attn_bytes,
+                attn_flops=attn_flops, step_bytes=score_bytes + attn_bytes)
+
+
+def source_digest(names=SCORE_SOURCES):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload_name):
+    """HBM bytes per launch of the scan kernel from the committed counter
+    summary, or None if absent or taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    digest = source_digest()
+    for line in open(TRAFFIC_FILE):
+        # machine-readable lines: "traffic: <digest> <bytes_per_launch> <workload name>"
+        if line.startswith("traffic: "):
+            parts = line[len("traffic: "):].strip().split(" ", 2)
+            if len(parts) == 3 and parts[0] == digest and parts[2] == workload_name:
+                return float(parts[1])
+    return None
+
+
+def cpu_baseline(wl, seconds):
+    """The oracle as it stands, timed over a bounded sample of the workload:
+    whole batches (or, when one batch is too long, strided query subsets) until
+    `seconds` of wall time have passed."""
     import oracle
+    import synth
+    view = synth.compact_pool_view(wl) if (wl.cand_blocks is not None and not wl.extra.get("dense_rows", True)) \
+        else wl
     threads = oracle.get_threads()
+    per_call = wl.Q
+    if wl.n_valid is not None and wl.Q > 2 * threads:   # prefill: strided subsets of `threads` queries
+        per_call = threads
+    done, calls = 0, 0
     t0 = time.perf_counter()
-    ref = oracle.decode(wl)
-    dt = time.perf_counter() - t0
-    return ref, dict(value=wl.Q / dt, unit="queries/s", cores=min(threads, wl.Q), kind="oracle",
-                     sample=f"one full batch of the same workload ({wl.Q} queries x {wl.n_cand} candidates), "
-                            f"fp64 CPU oracle, {dt:.2f} s wall")
+    first = None
+    while True:
+        if per_call == wl.Q:
+            qs = None
+        else:
+            stride = wl.Q // per_call
+            qs = [(calls + stride * j) % wl.Q for j in range(per_call)]
+        ref = oracle.decode(view, queries=qs)
+        if first is None:
+            first = (qs, ref)
+        done += per_call
+        calls += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds or calls >= 100000:
+            break
+    what = "the whole batch" if per_call == wl.Q else f"strided subsets of {per_call} queries"
+    return first, dict(value=round(done / dt, 3), unit="queries/s", cores=int(min(threads, per_call)), kind="oracle",
+                       sample=f"{calls} oracle decode call(s) on {what} of this workload ({done} queries, "
+                              f"{wl.n_cand} candidates each), fp64, {dt:.1f} s wall")
 
 
-def parity_summary(wl, ref, out_bf16, idx):
-    """Band-rule ids + attention tolerance of the first timed batch (reported)."""
+def parity_summary(wl, first, out_bf16, idx):
+    """Band-rule ids + attention tolerance of the first timed batch on the
+    queries the CPU baseline computed (reported, not asserted)."""
+    import synth
     sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_util import QueryView, check_attn, check_topk_band
+    qs, ref = first
+    sel = np.arange(wl.Q) if qs is None else np.asarray(qs)
     try:
-        from gpu_util import check_attn, check_topk_band
-        check_topk_band(idx, ref["scores"], ref["idx"], wl, wl.k, "bench")
-        rel = check_attn(out_bf16, ref["out_f32"], "bench")
-        return dict(ok=True, attn_max_err_rel=rel)
+        if wl.cand_blocks is not None and not wl.extra.get("dense_rows", True):
+            comp = synth.compact_pool_view(wl)
+            gidx = np.stack([np.searchsorted(synth.pool_ids(wl, i), idx[i]) for i in sel]).astype(np.int32)
+            check_topk_band(gidx, ref["scores"], ref["idx"], QueryView(comp, sel), wl.k, "bench")
+        else:
+            check_topk_band(idx[sel], ref["scores"], ref["idx"], QueryView(wl, sel), wl.k, "bench")
+        rel = check_attn(out_bf16[sel], ref["out_f32"], "bench")
+        return dict(ok=True, queries_checked=int(len(sel)), attn_max_err_rel=round(float(rel), 6))
     except AssertionError as e:
         return dict(ok=False, error=str(e)[:300])
 
+
+# ------------------------------------------------------- counter summaries
+
+def pmc_summary(root):
+    """Per-kernel mean counter values (KiB per dispatch for FETCH_SIZE /
+    WRITE_SIZE) over every counter_collection CSV under `root`."""
+    acc = {}
+    for path in glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True):
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                name = row.get("Kernel_Name", "")
+                cn, cv = row.get("Counter_Name"), row.get("Counter_Value")
+                did = row.get("Dispatch_Id")
+                if cn is None or cv is None:
+                    continue
+                d = acc.setdefault(name, {}).setdefault(cn, {})
+                d[did] = d.get(did, 0.0) + float(cv)
+    out = {}
+    for name, counters in acc.items():
+        out[name] = {cn: (sum(v.values()) / len(v), len(v)) for cn, v in counters.items()}
+    return out
+
+
+def print_pmc_summary(root):
+    s = pmc_summary(root)
+    copy_bytes = COPY_MIB << 20
+    fetch_f = write_f = None
+    for name, cs in s.items():
+        if "neg" in name.lower():   # the calibration kernel: reads and writes COPY_MIB MiB
+            if "FETCH_SIZE" in cs:
+                fetch_f = cs["FETCH_SIZE"][0] * 1024 / copy_bytes
+            if "WRITE_SIZE" in cs:
+                write_f = cs["WRITE_SIZE"][0] * 1024 / copy_bytes
+    print(f"calibration kernel (elementwise negation, {COPY_MIB} MiB in + {COPY_MIB} MiB out): "
+          f"FETCH_SIZE factor {fetch_f}, WRITE_SIZE factor {write_f}")
+    print(f"{'kernel':70s} {'counter':12s} {'mean KiB/dispatch':>18s} {'dispatches':>10s} {'calibrated MB':>14s}")
+    for name, cs in sorted(s.items()):
+        for cn, (v, n) in sorted(cs.items()):
+            f = fetch_f if cn == "FETCH_SIZE" else write_f if cn == "WRITE_SIZE" else None
+            cal = f"{v * 1024 / f / 1e6:14.3f}" if f else f"{'':14s}"
+            print(f"{name[:70]:70s} {cn:12s} {v:18.1f} {n:10d} {cal}")
+    print(f"kernel source digest ({', '.join(SCORE_SOURCES)}): {source_digest()}")
+
+
+def print_trace_summary(root):
+    """Per-kernel durations from `rocprofv3 --kernel-trace --output-format csv`
+    (as in its kernel_stats file), plus the scan kernel split into launches
+    inside decode steps and the isolated back-to-back launches bench.py times."""
+    rows = []
+    for path in glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"],
+                             r["Grid_Size_X"], r["Grid_Size_Y"], r["Workgroup_Size_X"], r["LDS_Block_Size"],
+                             r["VGPR_Count"], r["Accum_VGPR_Count"], r["Scratch_Size"]))
+    rows.sort()
+    stats, meta = {}, {}
+    for st, en, name, *m in rows:
+        stats.setdefault(name, []).append((en - st) / 1e3)
+        meta.setdefault(name, m)
+    print(f"{'kernel':72s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}")
+    for name, v in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
+        print(f"{name[:72]:72s} {len(v):6d} {sum(v) / len(v):9.2f} {min(v):9.2f} {max(v):9.2f}")
+    print("launch shapes (grid threads x, y; workgroup; LDS B; VGPR; AGPR; scratch):")
+    for name, m in meta.items():
+        if "csa2" in name:
+            print(f"  {name[:60]:60s} grid {m[0]}x{m[1]} wg {m[2]} lds {m[3]} vgpr {m[4]} agpr {m[5]} scratch {m[6]}")
+    lib = [r for r in rows if "csa2" in r[2]]
+    iso, dec = [], []
+    for i, (st, en, name, *_) in enumerate(lib):
+        if SCORE_KERNEL not in name:
+            continue
+        nb = [lib[j][2] for j in (i - 1, i + 1) if 0 <= j < len(lib)]
+        (iso if all(SCORE_KERNEL in n for n in nb) else dec).append((en - st) / 1e3)
+    for label, v in (("inside decode steps", dec), ("isolated back-to-back", iso)):
+        if v:
+            print(f"{SCORE_KERNEL} {label}: {len(v)} launches, avg {sum(v) / len(v):.2f} us")
+
+
+# -------------------------------------------------------------------- main
 
 def main():
     ap = argparse.ArgumentParser()
@@ -105,10 +289,22 @@ def main():
     ap.add_argument("--config", type=int, default=1, help="workload shape 0..4 (default 1: batch 16 x 65,536)")
     ap.add_argument("--replicas", type=int, default=0, help="device copies rotated per step (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum wall time of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help=f"also run an elementwise {COPY_MIB} MiB negation (counter calibration)")
+    ap.add_argument("--pmc-summary", metavar="DIR", help="summarise rocprofv3 counter CSVs under DIR and exit")
+    ap.add_argument("--trace-summary", metavar="DIR", help="summarise rocprofv3 kernel-trace CSVs under DIR and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        print_pmc_summary(args.pmc_summary)
+        return
+    if args.trace_summary:
+        print_trace_summary(args.trace_summary)
+        return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported on this single-GPU build "
-              "(the decode batch shards by sequence with no exchange; see the design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported. Decode batches and prefill "
+              "chunks shard across GPUs by sequence / query rows with no exchange, so the one-GPU figure is the "
+              "per-GPU share.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -122,65 +318,110 @@ def main():
     wl = synth.make_config(args.config, dense_rows=False)
     gen_s = time.perf_counter() - t_gen
     db = to_device(wl)
-    Q, n_cand = wl.Q, wl.n_cand
-    step_bytes = Q * (FIXED_BYTES + 68 * n_cand + (4 * n_cand // 8 if wl.cand_blocks is not None else 0))
-    score_bytes = Q * (68 * n_cand + IQ_BYTES + (4 * n_cand // 8 if wl.cand_blocks is not None else 0))
-    if wl.n_valid is not None:  # causal prefill: only visible entries are scored
-        pairs = int(np.minimum(wl.n_valid, wl.n_entries).astype(np.int64).sum())
-    else:
-        pairs = Q * n_cand
+    Q = wl.Q
+    work = work_of(wl)
     resident = sum(t.numel() * t.element_size() for t in (db.main_cache, db.key_codes, db.key_scales))
-    R = args.replicas or int(min(8, max(1, math.ceil(768e6 / max(1, resident)))))
+    R = args.replicas or int(min(8, max(1, -(-768_000_000 // max(1, resident)))))
     reps = replicate(db, R)
-
-    out, lse, idx = db.new_outputs()
-    probe = db.decode_args(out, lse, idx)
-    ws = torch.empty(max(1, csa.csa2_workspace_size(csa.CSA2_WS_DECODE, probe)), dtype=torch.uint8, device="cuda")
-    K, W = args.steps, args.warmup
-    # Stage events are recorded on every EVERY-th timed step only: an event
-    # between two kernels costs a few microseconds of idle time.
-    EVERY = 10
-    sampled = list(range(0, K, EVERY))
-    ev = HipEvents(4 * len(sampled) + 2)
     stream = torch.cuda.current_stream()
 
+    out, lse, idx = db.new_outputs()
+    ws = torch.empty(max(1, csa.csa2_workspace_size(csa.CSA2_WS_DECODE, db.decode_args(out, lse, idx))),
+                     dtype=torch.uint8, device="cuda")
+    K, W = args.steps, args.warmup
+    S = min(K, 50)
+    ev = HipEvents(2 + 4 * S + 4)
+
+    # ---- phase 1: timed decode steps
+    dec_args = [reps[i % R].decode_args(out, lse, idx) for i in range(R)]
     for i in range(W):
-        csa.csa2_decode(reps[i % R].decode_args(out, lse, idx), ws, stream)
-    torch.cuda.synchronize()
-    # first batch outputs (replica 0) for the parity report
-    csa.csa2_decode(reps[0].decode_args(out, lse, idx), ws, stream)
+        csa.csa2_decode(dec_args[i % R], ws, stream)
+    csa.csa2_decode(dec_args[0], ws, stream)   # replica 0's outputs for the parity report
     torch.cuda.synchronize()
     first_out = out.cpu().numpy().view(np.uint16).copy()
     first_idx = idx.cpu().numpy().copy()
-
-    timed_args = []
-    for i in range(K):
-        if i % EVERY == 0:
-            j = i // EVERY
-            timed_args.append(reps[i % R].decode_args(out, lse, idx, stage_events=tuple(ev.ev[4 * j:4 * j + 4])))
-        else:
-            timed_args.append(reps[i % R].decode_args(out, lse, idx))
-    start_ev, end_ev = len(ev.ev) - 2, len(ev.ev) - 1
-    hip_record = ev.hip.hipEventRecord
-    hip_record.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    hip_record(ctypes.c_void_p(ev.ev[start_ev]), ctypes.c_void_p(stream.cuda_stream))
+    ev.record(0, stream)
     for i in range(K):
-        csa.csa2_decode(timed_args[i], ws, stream)
-    hip_record(ctypes.c_void_p(ev.ev[end_ev]), ctypes.c_void_p(stream.cuda_stream))
+        csa.csa2_decode(dec_args[i % R], ws, stream)
+    ev.record(1, stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    gpu_elapsed_ms = ev.ms(start_ev, end_ev)
+    gpu_ms = ev.ms(0, 1)
 
-    st = np.array([[ev.ms(4 * j, 4 * j + 1), ev.ms(4 * j + 1, 4 * j + 2), ev.ms(4 * j + 2, 4 * j + 3)]
-                   for j in range(len(sampled))])
+    # ---- phase 2: per-stage times (events between kernels cost a few us each)
+    st_args = [reps[i % R].decode_args(out, lse, idx, stage_events=tuple(ev.ev[2 + 4 * i:6 + 4 * i]))
+               for i in range(S)]
+    for i in range(S):
+        csa.csa2_decode(st_args[i], ws, stream)
+    torch.cuda.synchronize()
+    st = np.array([[ev.ms(2 + 4 * i + j, 3 + 4 * i + j) for j in range(3)] for i in range(S)])
+    stage_ms = st.mean(axis=0)
+
+    # ---- phase 3: isolated kernels
+    e0 = 2 + 4 * S
+    scores = torch.empty((Q, max(1, wl.n_cand)), dtype=torch.float32, device="cuda")
+    sc_args = [reps[i % R].index_args() for i in range(R)]
+    for i in range(3):
+        csa.csa2_index_score(sc_args[i % R], scores, stream)
+    torch.cuda.synchronize()
+    ev.record(e0, stream)
+    for i in range(K):
+        csa.csa2_index_score(sc_args[i % R], scores, stream)
+    ev.record(e0 + 1, stream)
+    torch.cuda.synchronize()
+    score_ms = ev.ms(e0, e0 + 1) / K
+    at_out = torch.empty_like(out)
+    at_lse = torch.empty_like(lse)
+    at_args = [reps[i % R].attn_args(idx, at_out, at_lse) for i in range(R)]
+    at_ws = torch.empty(max(1, csa.csa2_workspace_size(csa.CSA2_WS_ATTN, at_args[0])), dtype=torch.uint8,
+                        device="cuda")
+    for i in range(3):
+        csa.csa2_sparse_attn(at_args[i % R], at_ws, stream)
+    torch.cuda.synchronize()
+    ev.record(e0 + 2, stream)
+    for i in range(K):
+        csa.csa2_sparse_attn(at_args[i % R], at_ws, stream)
+    ev.record(e0 + 3, stream)
+    torch.cuda.synchronize()
+    attn_ms = ev.ms(e0 + 2, e0 + 3) / K
     ev.close()
-    score_ms, select_ms, attn_ms = st.mean(axis=0)
+    if args.copy_calibration:
+        src = torch.ones(COPY_MIB << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     ms_per_step = 1e3 * elapsed / K
     value = Q * K / elapsed
-    achieved = score_bytes / (score_ms * 1e-3) / 1e9
-
+    prefill = wl.n_valid is not None
+    name = synth.CONFIG_NAMES[args.config]
+    score_gbs = work["score_bytes"] / (score_ms * 1e-3) / 1e9
+    score_tfs = work["score_flops"] / (score_ms * 1e-3) / 1e12
+    attn_gbs = work["attn_bytes"] / (attn_ms * 1e-3) / 1e9
+    kernels = {
+        "index_score": {"kernels": [SCORE_KERNEL], "us_per_launch": round(1e3 * score_ms, 3),
+                        "algorithmic_bytes": work["score_bytes"], "GB_s": round(score_gbs, 1),
+                        "hbm_frac": round(score_gbs / HBM_PEAK_GBS, 4), "TFLOP_s": round(score_tfs, 2),
+                        "fp4_mfma_frac": round(score_tfs / FP4_PEAK_TFLOPS, 4)},
+        "sparse_attn": {"kernels": ["k_sparse_attn", "k_attn_combine"], "us_per_launch": round(1e3 * attn_ms, 3),
+                        "algorithmic_bytes": work["attn_bytes"], "GB_s": round(attn_gbs, 1),
+                        "hbm_frac": round(attn_gbs / HBM_PEAK_GBS, 4)},
+    }
+    traffic = recorded_traffic(name)
+    if prefill:
+        roof = {"bound": "mfma", "achieved": round(score_tfs, 2), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(score_tfs / FP4_PEAK_TFLOPS, 4), "traffic": traffic, "kernel": SCORE_KERNEL,
+                "algorithmic_flops_per_launch": work["score_flops"], "launch_us": round(1e3 * score_ms, 3)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(score_gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": SCORE_KERNEL,
+                "algorithmic_bytes_per_launch": work["score_bytes"], "launch_us": round(1e3 * score_ms, 3)}
+    if attn_ms > score_ms and not prefill:
+        roof["note"] = "the attention stage took longer than the scan in this run; see kernels.sparse_attn"
     res = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -194,29 +435,20 @@ def main():
         "vs_baseline": None,
         "dtype": "fp4(mx)+bf16",
         "data": "synthetic (seeded N(0,1) latents/keys/queries quantised to FP4 per the pages' formats)",
-        "config": {"workload": synth.CONFIG_NAMES[args.config], "config_index": args.config, "queries": Q,
-                   "candidates_per_query": n_cand, "top_k": wl.k, "swa_rows": wl.n_swa, "replicas": R},
-        "entries_scored_per_s": round(pairs * K / elapsed, 1),
-        "gpu_ms_per_step": round(gpu_elapsed_ms / K, 5),
-        "stage_us": {"index_score": round(1e3 * score_ms, 2), "select": round(1e3 * select_ms, 2),
-                     "attention": round(1e3 * attn_ms, 2), "sampled_steps": len(sampled)},
-        "path_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "roofline": {"kernel": "k_index_score", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "algorithmic_bytes_per_launch": score_bytes},
+        "config": {"workload": name, "config_index": args.config, "queries": Q, "candidates_per_query": wl.n_cand,
+                   "top_k": wl.k, "swa_rows": wl.n_swa, "replicas": R},
+        "entries_scored_per_s": round(work["pairs"] * K / elapsed, 1),
+        "gpu_ms_per_step": round(gpu_ms / K, 5),
+        "stage_us": {"index_score": round(1e3 * stage_ms[0], 2), "select": round(1e3 * stage_ms[1], 2),
+                     "attention": round(1e3 * stage_ms[2], 2), "steps": S},
+        "path_hbm_frac": round(work["step_bytes"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": roof,
+        "kernels": kernels,
     }
-    if args.config == 3:
-        tflops = pairs * 8192 / (score_ms * 1e-3) / 1e12
-        res["roofline"] = {"kernel": "k_index_score", "bound": "mfma", "achieved": round(tflops, 2),
-                           "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / FP4_PEAK_TFLOPS, 4),
-                           "traffic": None, "algorithmic_flops_per_launch": pairs * 8192}
     if not args.no_cpu_baseline:
-        if wl.extra.get("dense_rows", True) and args.config != 3:
-            ref, cb = cpu_baseline(wl)
-            res["cpu_baseline"] = cb
-            res["parity"] = parity_summary(wl, ref, first_out, first_idx)
-        else:
-            res["cpu_baseline"] = None
+        first, cb = cpu_baseline(wl, args.cpu_seconds)
+        res["cpu_baseline"] = cb
+        res["parity"] = parity_summary(wl, first, first_out, first_idx)
     res["gen_s"] = round(gen_s, 2)
     print(json.dumps(res), flush=True)
 

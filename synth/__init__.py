@@ -282,3 +282,20 @@ def make_config(i: int, seed: int = 0, dense_rows: Optional[bool] = None) -> Wor
     if c["kind"] == "reindex_decode":
         return reindex_decode(c["Q"], c["N"], c["n_blocks"], seed, dense_rows=bool(dense_rows), name=f"config{i}")
     return prefill(c["T"], c["n_cache"], c["t0"], seed, name=f"config{i}")
+
+
+def compact_pool_view(wl: Workload) -> Workload:
+    """A Reindex workload built with dense_rows=False holds only the pool rows
+    (query-major, blocks in ascending id). This view renumbers query i's pool
+    as entries 0..8*n_blocks-1 of its own cache, so a host consumer that wants
+    dense rows can run on it; entry j of the view is pool_ids(wl, i)[j]."""
+    assert wl.cand_blocks is not None and not wl.extra.get("dense_rows", True)
+    nb = wl.n_blocks
+    return Workload(wl.name + "-compact", wl.Q, 8 * nb, 8 * nb, wl.main_cache, wl.key_codes, wl.key_scales,
+                    wl.iq_codes, wl.iq_scales, wl.w, wl.q, wl.swa, wl.swa_q_stride, wl.n_swa,
+                    cand_blocks=np.tile(np.arange(nb, dtype=np.int32), (wl.Q, 1)), k=wl.k, scale=wl.scale)
+
+
+def pool_ids(wl: Workload, i: int) -> np.ndarray:
+    """Global entry ids of query i's candidate pool, ascending."""
+    return (8 * wl.cand_blocks[i][:, None].astype(np.int64) + np.arange(8)[None, :]).reshape(-1)

@@ -130,6 +130,15 @@ def check_topk_band(gpu_idx: np.ndarray, ref_scores: np.ndarray, ref_idx: np.nda
             assert abs(se - tau) <= band, f"{what} q{qi}: entry {e} score {se} outside band of tau {tau}"
 
 
+class QueryView:
+    """The workload fields the band check reads, restricted to queries qs."""
+
+    def __init__(self, wl, qs):
+        self.n_entries = wl.n_entries
+        self.cand_blocks = None if wl.cand_blocks is None else wl.cand_blocks[qs]
+        self.n_valid = None if wl.n_valid is None else wl.n_valid[qs]
+
+
 def check_attn(gpu_bf16: np.ndarray, ref_f32: np.ndarray, what=""):
     g = bf16_np_to_f64(gpu_bf16)
     r = ref_f32.astype(np.float64)
@@ -147,4 +156,4 @@ def check_lse(gpu: np.ndarray, ref: np.ndarray, what=""):
 
 
 __all__ = ["announce", "to_device", "gpu_scores", "gpu_topk", "gpu_attn", "gpu_decode", "check_scores",
-           "check_topk_band", "check_attn", "check_lse", "oracle", "bf16_np_to_f64", "valid_entries"]
+           "check_topk_band", "QueryView", "check_attn", "check_lse", "oracle", "bf16_np_to_f64", "valid_entries"]

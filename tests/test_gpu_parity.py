@@ -199,7 +199,7 @@ def _check_decode(wl, queries=None, what=""):
     ob, glse, gidx = gpu_decode(db)
     ref = oracle.decode(wl, queries=queries)
     qs = list(range(wl.Q)) if queries is None else list(queries)
-    check_topk_band(gidx[qs], ref["scores"], ref["idx"], _sub(wl, qs), wl.k, what)
+    check_topk_band(gidx[qs], ref["scores"], ref["idx"], QueryView(wl, qs), wl.k, what)
     # attention with the GPU's own selection isolates the attention step
     _, of_own, lse_own = oracle.sparse_attn(wl, gidx[qs], queries=qs)
     check_attn(ob[qs], of_own, what + " (own ids)")
@@ -207,16 +207,6 @@ def _check_decode(wl, queries=None, what=""):
     # end to end against the oracle's selection (differences only from band swaps)
     check_attn(ob[qs], ref["out_f32"], what + " (oracle ids)")
     return gidx
-
-
-def _sub(wl, qs):
-    class V:  # the fields check_topk_band reads, restricted to qs
-        pass
-    v = V()
-    v.n_entries = wl.n_entries
-    v.cand_blocks = None if wl.cand_blocks is None else wl.cand_blocks[qs]
-    v.n_valid = None if wl.n_valid is None else wl.n_valid[qs]
-    return v
 
 
 def test_decode_full_small():
@@ -269,15 +259,12 @@ def test_config2_full_pool():
     db = to_device(wl)
     ob, glse, gidx = gpu_decode(db)
     # compact view: query i's pool becomes entries 0..16383 of its own cache
-    Q, nb = wl.Q, wl.n_blocks
-    comp = synth.Workload("c2c", Q, 8 * nb, 8 * nb, wl.main_cache, wl.key_codes, wl.key_scales, wl.iq_codes,
-                          wl.iq_scales, wl.w, wl.q, wl.swa, wl.swa_q_stride, wl.n_swa,
-                          cand_blocks=np.tile(np.arange(nb, dtype=np.int32), (Q, 1)))
+    comp = synth.compact_pool_view(wl)
     ref = oracle.decode(comp)
-    pools = [(8 * wl.cand_blocks[i][:, None].astype(np.int64) + np.arange(8)[None, :]).reshape(-1) for i in range(Q)]
+    pools = [synth.pool_ids(wl, i) for i in range(wl.Q)]
     # map the GPU's global ids back to compact ids
-    comp_gidx = np.stack([np.searchsorted(pools[i], gidx[i]) for i in range(Q)]).astype(np.int32)
-    for i in range(Q):
+    comp_gidx = np.stack([np.searchsorted(pools[i], gidx[i]) for i in range(wl.Q)]).astype(np.int32)
+    for i in range(wl.Q):
         assert np.array_equal(pools[i][comp_gidx[i]], gidx[i]), "GPU selected an entry outside the pool"
     check_topk_band(comp_gidx, ref["scores"], ref["idx"], comp, wl.k, "config2")
     _, of_own, _ = oracle.sparse_attn(comp, comp_gidx)
