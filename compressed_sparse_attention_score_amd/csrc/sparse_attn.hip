@@ -22,7 +22,9 @@
 //    with the scale folded into log2 units). The running max is a reference
 //    that only moves when a head's tile max exceeds it by more than 2^8, so
 //    the accumulators are rescaled a handful of times per query instead of
-//    every tile (p <= 256 is exact enough in bf16 and safe in fp32).
+//    every tile (p <= 256 is exact enough in bf16 and safe in fp32). The
+//    hardware exp2 is used as is: terms below 2^-126 of the reference do not
+//    matter to the sum.
 //  * Small batches split the slot list over workgroups; each writes
 //    (reference max, sum, unnormalised O) and a second kernel, one workgroup
 //    per (query, 16 heads), merges them in split order. Handing the partials
@@ -265,7 +267,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(AttnArgs a) {
     const bool move = mt > m_ref + kRescaleSlack;  // also true when m_ref = -inf and mt is finite
     if (__any(move)) {
       const float m_new = move ? mt : m_ref;
-      const float alpha = (m_ref == -__builtin_inff()) ? 0.f : exp2f(m_ref - m_new);
+      const float alpha = (m_ref == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
       if (move) l_run *= alpha;
 #pragma unroll
       for (int ct = 0; ct < 32; ++ct) o[ct] = move ? o[ct] * alpha : o[ct];
@@ -275,7 +277,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(AttnArgs a) {
     const bool live = m_ref != -__builtin_inff();
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      p[i] = live ? exp2f(x[i] - m_ref) : 0.f;
+      p[i] = live ? __builtin_amdgcn_exp2f(x[i] - m_ref) : 0.f;
       ps += p[i];
     }
     ps = add_xor16(ps);
@@ -349,7 +351,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
     for (int sp = 0; sp < n_splits; ++sp) {
       const float* ps = base + sp * kPartialFloats;
       const float ms = ps[h];
-      const float f = (ms == -__builtin_inff()) ? 0.f : exp2f(ms - M);
+      const float f = (ms == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
       L += ps[64 + h] * f;
       const v4f* src = (const v4f*)(ps + 128 + (int64_t)h * kDim + c0);
       const v4f x0 = src[0], x1 = src[1];

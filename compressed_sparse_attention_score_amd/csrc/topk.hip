@@ -40,7 +40,7 @@ struct SelShared {
   unsigned hist[kBins];
   unsigned wsum[NT / 64];
   unsigned res[4];
-  unsigned long long cand[NT * kRegCand];
+  unsigned off[NT + 1];  // exclusive offsets of the chunk regions in the joined list
 };
 }  // namespace
 
@@ -240,18 +240,36 @@ __global__ __launch_bounds__(NT) void k_select_final(const unsigned* __restrict_
   }
   unsigned written = 0;
   if (m <= (unsigned)(NT * kRegCand) && n_chunks <= NT) {
-    // gather the regions in chunk order into LDS: thread c copies chunk c
+    // The joined list is the chunk regions in chunk order; thread t takes its
+    // elements t*kRegCand .. +kRegCand-1, locating their chunk through the
+    // offset table (one binary search, then a forward walk).
     const unsigned cnt_c = (tid < n_chunks) ? cq[tid] : 0u;
     unsigned tot;
-    const unsigned off = block_incl_scan(cnt_c, sh.wsum, &tot) - cnt_c;
-    for (unsigned i = 0; i < cnt_c; ++i) sh.cand[off + i] = lq[(int64_t)tid * kChunk + i];
+    const unsigned incl = block_incl_scan(cnt_c, sh.wsum, &tot);
+    if (tid < n_chunks) sh.off[tid] = incl - cnt_c;
+    if (tid == 0) sh.off[n_chunks] = tot;
     __syncthreads();
+    const unsigned e0 = (unsigned)tid * kRegCand;
+    int ch = 0;
+    if (e0 < m) {
+      int lo = 0, hi = n_chunks - 1;  // largest c with off[c] <= e0
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (sh.off[mid] <= e0) lo = mid; else hi = mid - 1;
+      }
+      ch = lo;
+    }
     unsigned long long v[kRegCand];
 #pragma unroll
     for (int j = 0; j < kRegCand; ++j) {
-      const unsigned e = tid * kRegCand + j;
-      v[j] = (e < m) ? sh.cand[e] : 0ull;
+      const unsigned e = e0 + j;
+      v[j] = 0ull;
+      if (e < m) {
+        while (e >= sh.off[ch + 1]) ++ch;  // e < m = off[n_chunks] bounds the walk
+        v[j] = lq[(int64_t)ch * kChunk + (e - sh.off[ch])];
+      }
     }
+    __syncthreads();  // offsets read before the radix passes reuse shared state
     const unsigned long long T =
         (m > (unsigned)k) ? radix_kth_regs<unsigned long long, kRegCand>(v, (unsigned)k, sh) : 0ull;
     unsigned c = 0;

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import synth
-from gpu_util import (announce, bf16_np_to_f64, check_attn, check_lse, check_scores, check_topk_band, gpu_attn,
+from gpu_util import (QueryView, announce, bf16_np_to_f64, check_attn, check_lse, check_scores, check_topk_band, gpu_attn,
                       gpu_decode, gpu_scores, gpu_topk, oracle, to_device)
 
 pytestmark = pytest.mark.gpu
