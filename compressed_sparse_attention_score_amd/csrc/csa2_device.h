@@ -110,7 +110,22 @@ __device__ __forceinline__ float key_score(unsigned k) {
   return __uint_as_float(u);
 }
 
+// max(x, 0) on the bit pattern: every value with the sign bit set (-0
+// included) becomes +0, the rest pass unchanged. Equal to fmaxf(x, 0) for
+// every non-NaN x, in one integer max and without NaN canonicalisation.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // ---- cross-lane helpers (wave64) -------------------------------------------
+// Maximum over the 16 lanes of a row (lanes 16r..16r+15), left in every lane
+// of the row: DPP row rotations by 8 and 4, then quad permutations.
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false)));  // row_ror:8
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xF, 0xF, false)));  // row_ror:4
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false)));   // [2,3,0,1]
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false)));   // [1,0,3,2]
+  return x;
+}
+
 // x + x[lane ^ 32] and x + x[lane ^ 16] with gfx950 lane swaps (no LDS).
 __device__ __forceinline__ float add_xor32(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -167,6 +167,151 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
   }
 }
 
+// Many queries over one shared cache (a prefill chunk): the contraction is
+// dense, so queries are tiled instead of streaming the keys once per query.
+// MFMA rows are (query, head) pairs, 4 queries x 4 heads; the eight MFMAs of
+// one 16-entry key block cover 32 heads of 4 queries, and the output layout
+// (lane l holds rows 4*(l/16)..+3 of column l%16) leaves each lane with heads
+// 4hb..4hb+3 of query l/16 for entry l%16. So ReLU and the weighted head sum
+// stay inside the lane, with no cross-lane step. Each wave keeps 8 queries'
+// operands and weights in registers and walks an entry range; the range index
+// runs fastest in the grid, so with a multiple of 8 ranges each XCD's L2
+// serves 1/8 of the key cache.
+namespace {
+constexpr int kQSets = 2;  // 4-query sets per wave
+constexpr int kTileUnroll = 4;  // 16-entry steps per load batch
+}  // namespace
+
+template <bool GMAX, int QSETS = kQSets, int TU = kTileUnroll>
+__global__ __launch_bounds__(256) void k_index_score_qtile(ScoreArgs a, int range) {
+  constexpr int kQPerWave = 4 * QSETS;
+  constexpr int kQPerWg = 4 * kQPerWave;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, kb = lane >> 4;
+  const int q0 = blockIdx.y * kQPerWg + wave * kQPerWave;
+  const int64_t e_begin = (int64_t)blockIdx.x * range;
+  const int64_t e_end = min(e_begin + range, a.n_cand);
+  if (q0 >= a.Q || e_begin >= e_end) return;
+
+  // A operands: set s, head block hb -> row r16 = query q0+4s+r16/4, head 4hb+r16%4
+  v8i A[QSETS][8];
+  int sA[QSETS][8];
+#pragma unroll
+  for (int s = 0; s < QSETS; ++s) {
+    const int qa = q0 + 4 * s + (r16 >> 2);
+#pragma unroll
+    for (int hb = 0; hb < 8; ++hb) {
+      const int h = 4 * hb + (r16 & 3);
+      v4u c = v4u{0u, 0u, 0u, 0u};
+      int sc = 127;
+      if (qa < a.Q) {
+        c = *(const v4u*)(a.iq_codes + ((int64_t)qa * kIHeads + h) * 64 + kb * 16);
+        sc = a.iq_scales[((int64_t)qa * kIHeads + h) * 4 + kb];
+      }
+      A[s][hb] = v8i{(int)c[0], (int)c[1], (int)c[2], (int)c[3], 0, 0, 0, 0};
+      sA[s][hb] = sc;
+    }
+  }
+  // this lane's output rows: query q0+4s+kb, heads 4hb+r. Positions inside
+  // the range are 32-bit offsets from e_begin; the output row of set s is a
+  // wave-uniform base plus kb*n_cand.
+  const int span = (int)(e_end - e_begin);
+  float wt[QSETS][32];
+  int lim[QSETS];
+  bool qok[QSETS];
+  float* obase[QSETS];
+#pragma unroll
+  for (int s = 0; s < QSETS; ++s) {
+    const int qo = q0 + 4 * s + kb;
+    qok[s] = qo < a.Q;
+#pragma unroll
+    for (int h = 0; h < 32; ++h) wt[s][h] = qok[s] ? a.w[(int64_t)qo * kIHeads + h] : 0.f;
+    int64_t l = a.n_entries;
+    if (a.n_valid && qok[s]) l = min(l, (int64_t)a.n_valid[qo]);
+    lim[s] = (int)max((int64_t)0, min(l - e_begin, (int64_t)span));
+    obase[s] = a.scores + (int64_t)(q0 + 4 * s) * a.n_cand + e_begin;
+  }
+  const unsigned orow_off = (unsigned)kb * (unsigned)a.n_cand + (unsigned)r16;
+  // running maximum score of the current sub-chunk (invalid entries as -inf;
+  // a NaN score can only lower it, which keeps the selection bound valid)
+  const float ninf = -__builtin_inff();
+  float gm[QSETS];
+#pragma unroll
+  for (int s = 0; s < QSETS; ++s) gm[s] = ninf;
+  const int steps_per_group = a.group >> 4;
+  int step_in_group = 0;
+  int64_t gidx = e_begin / a.group;
+
+  v4u bcA[TU], bcB[TU];
+  unsigned bsA[TU], bsB[TU];
+  auto issue = [&](v4u* bc, unsigned* bs, int off0) {
+#pragma unroll
+    for (int u = 0; u < TU; ++u) {
+      const int64_t e = e_begin + min(off0 + 16 * u + r16, span - 1);  // rows past the range are not stored
+      bc[u] = *(const v4u*)(a.key_codes + e * 64 + kb * 16);
+      bs[u] = *(const unsigned*)(a.key_scales + e * 4);
+    }
+  };
+  auto compute = [&](const v4u* bc, const unsigned* bs, int off0) {
+#pragma unroll
+    for (int u = 0; u < TU; ++u) {
+      const int off = off0 + 16 * u;
+      if (off >= span) break;
+      const v8i B = {(int)bc[u][0], (int)bc[u][1], (int)bc[u][2], (int)bc[u][3], 0, 0, 0, 0};
+      const int sb = (int)((bs[u] >> (8 * kb)) & 0xFFu);
+      const int p = off + r16;
+      const bool in_range = p < span;
+      // the query sets interleaved: independent MFMAs in flight
+      float acc[QSETS];
+#pragma unroll
+      for (int s = 0; s < QSETS; ++s) acc[s] = 0.f;
+#pragma unroll
+      for (int hb = 0; hb < 8; ++hb) {
+        v4f c[QSETS];
+#pragma unroll
+        for (int s = 0; s < QSETS; ++s) {
+          c[s] = v4f{0.f, 0.f, 0.f, 0.f};
+          c[s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[s][hb], B, c[s], 4, 4, 0, sA[s][hb], 0, sb);
+        }
+#pragma unroll
+        for (int s = 0; s < QSETS; ++s)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[s] = fmaf(wt[s][4 * hb + r], relu_bits(c[s][r]), acc[s]);
+      }
+#pragma unroll
+      for (int s = 0; s < QSETS; ++s) {
+        const float sv = (p < lim[s]) ? acc[s] : ninf;
+        // scores stream out past L2 (the selection pass reads them much later)
+        if (qok[s] && in_range) __builtin_nontemporal_store(sv, obase[s] + orow_off + (unsigned)off);
+        if (GMAX) gm[s] = fmaxf(gm[s], sv);  // lim <= span, so sv is -inf outside the range
+      }
+      if (GMAX) {
+        ++step_in_group;
+        if (step_in_group == steps_per_group || off + 16 >= span) {
+#pragma unroll
+          for (int s = 0; s < QSETS; ++s) {
+            const float m = row16_max(gm[s]);
+            if (r16 == 0 && qok[s])
+              a.gmax[(int64_t)(q0 + 4 * s + kb) * a.n_groups + gidx] = (m == ninf) ? 0u : score_key(m);
+            gm[s] = ninf;
+          }
+          step_in_group = 0;
+          ++gidx;
+        }
+      }
+    }
+  };
+  constexpr int kStep = 16 * TU;
+  issue(bcA, bsA, 0);
+  for (int g0 = 0; g0 < span; g0 += 2 * kStep) {
+    if (g0 + kStep < span) issue(bcB, bsB, g0 + kStep);
+    compute(bcA, bsA, g0);
+    if (g0 + kStep >= span) break;
+    if (g0 + 2 * kStep < span) issue(bcA, bsA, g0 + 2 * kStep);
+    compute(bcB, bsB, g0 + kStep);
+  }
+}
+
 // Sub-chunk maximum keys computed from an existing score array (standalone
 // top-k). One wave per sub-chunk.
 __global__ __launch_bounds__(256) void k_score_maxima(const float* __restrict__ scores, int Q, int64_t n_cand,
@@ -213,6 +358,12 @@ ScorePlan plan_score(int64_t n_cand, int Q, int k) {
   return p;
 }
 
+// The query-tiled kernel applies when all queries share one cache (prefill).
+static bool use_query_tiles(const IndexLaunch& L) {
+  // 32-bit in-range offsets: 4*n_cand must stay below 2^32
+  return L.cache_q_stride == 0 && L.cand_blocks == nullptr && L.Q >= 16 * kQSets && L.n_cand < (1ll << 28);
+}
+
 hipError_t launch_index_score(const IndexLaunch& L, const ScorePlan& plan, float* scores, unsigned* gmax,
                               hipStream_t s) {
   if (L.Q <= 0) return hipSuccess;
@@ -235,6 +386,21 @@ hipError_t launch_index_score(const IndexLaunch& L, const ScorePlan& plan, float
   a.scores = scores;
   a.gmax = gmax;
   if (L.n_cand <= 0) return hipSuccess;
+  if (use_query_tiles(L)) {
+    const int qb = (L.Q + 16 * kQSets - 1) / (16 * kQSets);
+    const int64_t align = plan.group > 64 ? plan.group : 64;
+    int64_t want = (2048 + qb - 1) / qb;
+    want = (want + 7) / 8 * 8;
+    int64_t range = (L.n_cand + want - 1) / want;
+    range = (range + align - 1) / align * align;
+    const int64_t n_ranges = (L.n_cand + range - 1) / range;
+    const dim3 grid((unsigned)n_ranges, (unsigned)qb);
+    if (gmax)
+      k_index_score_qtile<true><<<grid, 256, 0, s>>>(a, (int)range);
+    else
+      k_index_score_qtile<false><<<grid, 256, 0, s>>>(a, (int)range);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)plan.n_wg, (unsigned)L.Q);
   if (L.cand_blocks)
     k_index_score<true><<<grid, 256, 0, s>>>(a);

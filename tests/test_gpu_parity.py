@@ -97,6 +97,18 @@ def test_index_score_causal_prefill():
     check_scores(got, ref, dots, wl.w, "causal")
 
 
+@pytest.mark.parametrize("T,n,t0", [(32, 2048, 4096), (70, 5003, 9900), (33, 777, 0), (97, 20000, 39000)])
+def test_index_score_prefill_query_tiles(T, n, t0):
+    """Many queries over one shared cache: the query-tiled kernel. Ragged query
+    counts (partial waves), ragged entry counts, causal limits from 0 up to
+    past the cache end."""
+    wl = synth.prefill(T, n, t0, seed=40 + T)
+    announce(f"prefill scores T={T} n={n} t0={t0}")
+    ref, dots = oracle.index_score(wl, want_dots=True)
+    got = gpu_scores(to_device(wl))
+    check_scores(got, ref, dots, wl.w, f"prefill tiles T={T}")
+
+
 # ------------------------------------------------------------------- top-k
 
 def _assert_topk_exact(scores, k, n_entries, cand_blocks=None, n_valid=None, what=""):
@@ -223,6 +235,13 @@ def test_decode_reindex_small_poisoned():
 
 def test_decode_prefill_small():
     _check_decode(synth.prefill(50, 2048, 3000, seed=23), what="prefill small")
+
+
+@pytest.mark.parametrize("T,n,t0", [(70, 5003, 9900), (64, 40000, 79000)])
+def test_decode_prefill_query_tiles(T, n, t0):
+    """Decode over a query-tiled prefill: the selection uses the sub-chunk
+    maxima recorded by the tiled scoring kernel."""
+    _check_decode(synth.prefill(T, n, t0, seed=50 + T), what=f"prefill tiles T={T}")
 
 
 def test_decode_fewer_than_k_entries():
