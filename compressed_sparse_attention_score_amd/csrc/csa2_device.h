@@ -46,6 +46,10 @@ __device__ __forceinline__ float e4m3_to_f32(unsigned b) {
   return (b & 0x80u) ? -mag : mag;
 }
 
+// The same decode by the gfx950 fp8 convert (OCP E4M3FN), one instruction.
+// Equal to e4m3_to_f32 for every byte (NaN codes give a NaN).
+__device__ __forceinline__ float e4m3_to_f32_hw(unsigned b) { return __builtin_amdgcn_cvt_f32_fp8((int)b, 0); }
+
 // E8M0 byte -> fp32 2^(b-127); b == 0 is the subnormal 2^-127, 0xFF is NaN.
 __device__ __forceinline__ float e8m0_to_f32(unsigned b) {
   b &= 0xFFu;

@@ -5,26 +5,36 @@
 // heads, serving as both key and value; each layer attends over the 128-token
 // window plus the 512 selected entries.
 //
-// Mapping (one workgroup = one query x one split of the joint slot list,
-// 4 waves, wave w owns heads 16w..16w+15):
+// Mapping (one workgroup of 8 waves = one query x one split of the joint slot
+// list):
 //  * Tiles of 32 joint slots are gathered and dequantised ONCE into LDS as
-//    bf16 (exact), in two layouts: Kt[slot][channel] feeds S^T = K q^T, and
-//    a blocked V^T (16 channels x 4 slots per 128-byte block, chunks rotated
-//    by the writer's lane so stores and loads are bank-conflict free) feeds
-//    O^T = V^T P^T. One tile serves as K and V; MFMA operand fragments are
-//    loaded from LDS four ahead of their use.
-//  * q stays in registers (16 fragments per lane). S^T comes out with one
-//    head per lane column, so the online-softmax max/sum over the tile's
-//    entries is 8 in-lane values plus two lane swaps, and the P^T fragments
-//    are already in the B-operand layout of the PV product (the k-slot order
-//    of the PV MFMA is permuted to match, and V^T is read in that order).
-//  * O^T accumulates in 32 fp32 4-vectors per lane; softmax in fp32 (exp2
-//    with the scale folded into log2 units). The running max is a reference
-//    that only moves when a head's tile max exceeds it by more than 2^8, so
-//    the accumulators are rescaled a handful of times per query instead of
-//    every tile (p <= 256 is exact enough in bf16 and safe in fp32). The
-//    hardware exp2 is used as is: terms below 2^-126 of the reference do not
-//    matter to the sum.
+//    bf16 (exact), in two layouts: Kt[slot][channel] (16-byte chunks XOR-
+//    swizzled by slot) feeds S^T = K q^T, and a blocked V^T (16 channels x 4
+//    slots per 128-byte block, chunks rotated by the writer's lane) feeds
+//    O^T = V^T P^T. Reads of both are bank-conflict free.
+//  * Wave (hh, cc) owns heads 32hh..32hh+31 and channels 128cc..128cc+127
+//    for the matrix products: every LDS fragment it reads feeds two MFMAs
+//    (two 16-head blocks), and q for its heads and channels stays in
+//    registers. Each wave forms S^T over its channel quarter; the softmax is
+//    then done once per (slot, head): wave w owns heads 8w..8w+7 over all 32
+//    slots of the tile (4 values per lane), adds the four partial sums from
+//    LDS, and writes P^T (bf16, laid out as the PV B operand) and the
+//    per-head rescale factor back to LDS for the product waves.
+//  * Per tile t, three barrier-separated phases: (1) S^T of tile t and
+//    O^T += V^T P^T of tile t-1 back to back on the matrix cores; (2) the
+//    softmax of tile t, and tile t+1 dequantised into LDS (V^T
+//    double-buffered, K single-buffered) with the latents of tile t+2
+//    requested; (3) P^T of tile t picked up and O^T rescaled if a head's
+//    reference moved.
+//  * The PV product's k-slot order is permuted (slots 4g..4g+3 and
+//    16+4g..16+4g+3 for lane group g) so that S^T fragments, P^T fragments
+//    and V^T reads line up without shuffles.
+//  * Softmax in fp32 with exp2 (the scale folded into log2 units). The
+//    running max is a reference that only moves when a head's tile max
+//    exceeds it by more than 2^8, so the accumulators are rescaled a handful
+//    of times per query instead of every tile (p <= 256 is exact enough in
+//    bf16 and safe in fp32). The hardware exp2 is used as is: terms below
+//    2^-126 of the reference do not matter to the sum.
 //  * Small batches split the slot list over workgroups; each writes
 //    (reference max, sum, unnormalised O) and a second kernel, one workgroup
 //    per (query, 16 heads), merges them in split order. Handing the partials
@@ -37,7 +47,7 @@ namespace csa2 {
 
 namespace {
 constexpr int TILE = 32;
-constexpr int KT_LD = kDim + 8;  // bf16 per Kt row (16-byte pad)
+constexpr int NT = 512;  // threads per workgroup
 constexpr float kRescaleSlack = 8.f;  // log2 units
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -58,279 +68,346 @@ struct AttnArgs {
 // Per-split partial record: m[64], l[64], O[64][512] (fp32, O unnormalised).
 constexpr int64_t kPartialFloats = 64 + 64 + 64 * 512;
 constexpr int kMaxSplits = 64;
+
+struct AttnShared {
+  uint16_t kt[TILE * kDim];         // [slot][channel], 16-byte chunks swizzled
+  uint16_t vb[2][TILE * kDim];      // blocked V^T, double-buffered
+  v4f sx[8][4][64];                 // partial S^T per wave: [wave][2*sb+hb][lane]
+  uint2 pl[kHeads][TILE / 4];       // P^T as bf16: [head][slot quad] = 4 slots
+  float alpha[kHeads];              // per-head rescale of O for this tile (1 = none)
+  float fin_m[kHeads], fin_l[kHeads];
+  unsigned ok[2][TILE / 4];         // slot validity bytes per tile (double-buffered)
+};
 }  // namespace
 
-__device__ __forceinline__ void finalize_head(const AttnArgs& a, int q, int head, int g, const v4f* o, float m,
-                                              float l) {
-  const float inv = (l > 0.f) ? 1.f / l : 0.f;
-  uint16_t* orow = a.out + ((int64_t)q * kHeads + head) * kDim;
-#pragma unroll
-  for (int ct = 0; ct < 32; ++ct) {
-    const int ch = ct * 16 + 4 * g;
-    __bf16 b0 = (__bf16)(o[ct][0] * inv), b1 = (__bf16)(o[ct][1] * inv);
-    __bf16 b2 = (__bf16)(o[ct][2] * inv), b3 = (__bf16)(o[ct][3] * inv);
-    uint2 pk;
-    pk.x = (unsigned)__builtin_bit_cast(uint16_t, b0) | ((unsigned)__builtin_bit_cast(uint16_t, b1) << 16);
-    pk.y = (unsigned)__builtin_bit_cast(uint16_t, b2) | ((unsigned)__builtin_bit_cast(uint16_t, b3) << 16);
-    *(uint2*)(orow + ch) = pk;
-  }
-  if (a.lse && g == 0) a.lse[(int64_t)q * kHeads + head] = (l > 0.f) ? (m + __log2f(l)) * kLn2 : -__builtin_inff();
-}
-
-// One staged slot of 16 channels: FP4 codes (8 bytes) + E4M3 scale byte of a
-// selected latent (kind 1), a window row to be read at decode time (kind 2),
-// or nothing (kind 0).
+// One staged slot of 8 channels: 4 bytes of FP4 codes + the E4M3 scale byte
+// of a selected latent (kind 1), 8 bf16 of a window row (kind 2), or nothing.
 struct RawSlot {
-  uint2 c;
-  unsigned sc;
-  int kind;
+  v4u a;
+  unsigned sc;  // bits 7:0 scale byte, bits 9:8 kind
 };
 
-// Selected ids of the 4 slots (4eg..4eg+3) of tile t; -1 marks a non-latent slot.
+// Selected ids of the 4 slots (4eg..4eg+3) of tile t; -1 marks a non-latent
+// slot. Tiles wholly inside the selected part read their ids unconditionally
+// (a per-slot branch around a load makes the compiler wait for it).
 __device__ __forceinline__ void load_ids(const AttnArgs& a, int q, int t, int eg, int* e) {
+  const int s0 = t * TILE + 4 * eg;
+  if (t * TILE + TILE <= a.k_sel) {
+    const int32_t* ip = a.idx + (int64_t)q * a.k_sel + s0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int slot = t * TILE + 4 * eg + i;
-    e[i] = (slot < a.k_sel) ? a.idx[(int64_t)q * a.k_sel + slot] : -1;
+    for (int i = 0; i < 4; ++i) e[i] = ip[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e[i] = (s0 + i < a.k_sel) ? a.idx[(int64_t)q * a.k_sel + s0 + i] : -1;
   }
 }
 
-__device__ __forceinline__ void issue_raw(const AttnArgs& a, int q, int t, int eg, int cg, const int* e,
+// Channels 8c8..8c8+7 of the 4 slots of tile t. A tile holds only selected
+// latents or only window rows unless k_sel is not a multiple of the tile:
+// those two cases issue every load unconditionally (invalid slots read row 0
+// of the query's cache or window and are flagged empty), so all loads of the
+// tile stay in flight together; a mixed tile takes the per-slot path.
+__device__ __forceinline__ void issue_raw(const AttnArgs& a, int q, int t, int eg, int c8, const int* e,
                                           RawSlot* r) {
+  const int s0 = t * TILE;
+  if (s0 + TILE <= a.k_sel && a.n_entries > 0) {
+    const uint8_t* base = a.main_cache + (int64_t)q * a.cache_q_stride * kMainBytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = e[i] >= 0 && (int64_t)e[i] < a.n_entries;
+      const uint8_t* ent = base + (int64_t)(ok ? e[i] : 0) * kMainBytes;
+      r[i].a = v4u{*(const unsigned*)(ent + c8 * 4), 0u, 0u, 0u};
+      r[i].sc = (unsigned)ent[256 + (c8 >> 1)] | (ok ? (1u << 8) : 0u);
+    }
+    return;
+  }
+  if (s0 >= a.k_sel) {  // window rows only (this tile exists, so n_swa >= 1)
+    const uint16_t* base = a.swa + (int64_t)q * a.swa_q_stride * kDim + c8 * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int slot = s0 + 4 * eg + i;
+      const bool ok = slot < a.nj;
+      r[i].a = *(const v4u*)(base + (int64_t)(ok ? slot - a.k_sel : 0) * kDim);
+      r[i].sc = ok ? (2u << 8) : 0u;
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int slot = t * TILE + 4 * eg + i;
-    r[i].kind = 0;
-    r[i].c = uint2{0u, 0u};
+    const int slot = s0 + 4 * eg + i;
+    r[i].a = v4u{0u, 0u, 0u, 0u};
     r[i].sc = 0u;
     if (slot < a.k_sel) {
       if (e[i] >= 0 && (int64_t)e[i] < a.n_entries) {
         const uint8_t* ent = a.main_cache + ((int64_t)q * a.cache_q_stride + e[i]) * kMainBytes;
-        r[i].c = *(const uint2*)(ent + cg * 8);
-        r[i].sc = ent[256 + cg];
-        r[i].kind = 1;
+        r[i].a = v4u{*(const unsigned*)(ent + c8 * 4), 0u, 0u, 0u};
+        r[i].sc = ent[256 + (c8 >> 1)] | (1u << 8);
       }
     } else if (slot < a.nj) {
-      r[i].kind = 2;
+      r[i].a = *(const v4u*)(a.swa + ((int64_t)q * a.swa_q_stride + (slot - a.k_sel)) * kDim + c8 * 8);
+      r[i].sc = 2u << 8;
     }
   }
 }
 
-__device__ __forceinline__ void decode_raw(const AttnArgs& a, int q, int t, int eg, int cg, int i, const RawSlot& r,
-                                           unsigned* kw, bool& ok) {
-  ok = r.kind != 0;
+// kw[j] = channels 8c8+2j (bits 15:0) and 8c8+2j+1 (bits 31:16) as bf16.
+// Branch-free: a latent is decoded, a window row passed through, an empty
+// slot gives zeros (its loaded bytes may be anything, NaN included).
+__device__ __forceinline__ void decode_raw(const RawSlot& r, unsigned* kw) {
+  float f[8];
+  decode_e2m1x8_scaled(r.a[0], e4m3_to_f32_hw(r.sc & 0xFFu), f);
+  const unsigned kind = r.sc >> 8;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) kw[j] = 0u;
-  if (r.kind == 1) {
-    const float sc = e4m3_to_f32(r.sc);
-    float f[8];
-    decode_e2m1x8_scaled(r.c.x, sc, f);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) kw[j] = pack_bf16x2_exact(f[2 * j], f[2 * j + 1]);
-    decode_e2m1x8_scaled(r.c.y, sc, f);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) kw[4 + j] = pack_bf16x2_exact(f[2 * j], f[2 * j + 1]);
-  } else if (r.kind == 2) {
-    // window rows are already bf16 pairs
-    const int slot = t * TILE + 4 * eg + i;
-    const uint16_t* row = a.swa + ((int64_t)q * a.swa_q_stride + (slot - a.k_sel)) * kDim + cg * 16;
-    const v4u r0 = *(const v4u*)row, r1 = *(const v4u*)(row + 8);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      kw[j] = r0[j];
-      kw[4 + j] = r1[j];
-    }
+  for (int j = 0; j < 4; ++j) {
+    const unsigned dec = pack_bf16x2_exact(f[2 * j], f[2 * j + 1]);
+    kw[j] = (kind == 1u) ? dec : (kind == 2u) ? r.a[j] : 0u;
   }
 }
 
-// V^T block of (channel group cg, slot group sg): 16 channels x 4 slots, chunk
-// c (channel c of the group, 4 slots = 8 bytes) stored at chunk (c + rot) & 15
-// where rot = (cg*8 + sg) & 15 is the writer lane's index mod 16.
+// Validity bytes of the 4 staged slots (byte i = slot 4eg+i holds data).
+__device__ __forceinline__ unsigned raw_ok(const RawSlot* r) {
+  unsigned okb = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) okb |= ((r[i].sc >> 8) != 0u ? 1u : 0u) << (8 * i);
+  return okb;
+}
+
+// Element offset of channel chunk `chunk` (8 channels, 16 bytes) of Kt row
+// `slot`; chunks are XOR-swizzled by the row so that a store of one row by 64
+// lanes and a fragment read of 16 rows at one chunk both touch 16 distinct
+// 16-byte bank groups.
+__device__ __forceinline__ int kt_offset(int slot, int chunk) { return slot * kDim + ((chunk ^ (slot & 15)) << 3); }
+
+// V^T block of (channel group cg, slot group sg): 16 channels x 4 slots, 128
+// bytes. Block order within a channel group alternates with cg's parity and
+// chunk c (channel c of the group, 4 slots = 8 bytes) sits at (c + cg) & 15:
+// a fragment read (16 channels of 4 consecutive slot groups) covers 512
+// contiguous bytes, and a store of one slot group by 64 lanes (32 channel
+// groups) spreads over every bank twice.
 __device__ __forceinline__ int vb_offset(int cg, int sg, int c) {
-  return ((cg * 8 + sg) * 16 + ((c + ((cg * 8 + sg) & 15)) & 15)) * 4;
+  return ((cg * 8 + (sg ^ (cg & 1))) * 16 + ((c + cg) & 15)) * 4;
 }
 
-__global__ __launch_bounds__(256, 1) void k_sparse_attn(AttnArgs a) {
+// Store this thread's 4 dequantised slots (8 channels each) as tile data:
+// Kt rows, V^T buffer vbuf, validity flags okbuf.
+__device__ __forceinline__ void store_tile(AttnShared& sh, int vbuf, int eg, int c8, const unsigned (*kw)[4],
+                                           unsigned okb) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *(v4u*)(sh.kt + kt_offset(4 * eg + i, c8)) = v4u{kw[i][0], kw[i][1], kw[i][2], kw[i][3]};
+  const int cg = c8 >> 1, cbase = (c8 & 1) * 8;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // channel cbase+2j: low halves; channel cbase+2j+1: high halves; slots 4eg..4eg+3
+    uint2 lo, hi;
+    lo.x = __builtin_amdgcn_perm(kw[1][j], kw[0][j], 0x05040100u);
+    lo.y = __builtin_amdgcn_perm(kw[3][j], kw[2][j], 0x05040100u);
+    hi.x = __builtin_amdgcn_perm(kw[1][j], kw[0][j], 0x07060302u);
+    hi.y = __builtin_amdgcn_perm(kw[3][j], kw[2][j], 0x07060302u);
+    *(uint2*)(sh.vb[vbuf] + vb_offset(cg, eg, cbase + 2 * j)) = lo;
+    *(uint2*)(sh.vb[vbuf] + vb_offset(cg, eg, cbase + 2 * j + 1)) = hi;
+  }
+  if (c8 == 0) sh.ok[vbuf][eg] = okb;  // one lane per slot group
+}
+
+__global__ __launch_bounds__(NT, 1) void k_sparse_attn(AttnArgs a) {
   const int q = blockIdx.y, split = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
-  const int head = 16 * wave + r16;
+  const int hh = wave & 1, cc = wave >> 1;
 
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[TILE * KT_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vb[TILE * kDim];
-  __shared__ unsigned char slot_ok[TILE];
+  __shared__ AttnShared sh;
 
-  // q fragments: head, channels kk*32 + 8g .. +7
-  v8bf qf[16];
-  {
-    const uint16_t* qrow = a.q + ((int64_t)q * kHeads + head) * kDim + 8 * g;
+  // q fragments: head 32hh + 16hb + r16, channels 128cc + 32ks + 8g .. +7
+  v8bf qf[2][4];
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      v4u raw = *(const v4u*)(qrow + kk * 32);
-      qf[kk] = __builtin_bit_cast(v8bf, raw);
-    }
+  for (int hb = 0; hb < 2; ++hb) {
+    const uint16_t* qrow = a.q + ((int64_t)q * kHeads + 32 * hh + 16 * hb + r16) * kDim + 128 * cc + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[hb][ks] = __builtin_bit_cast(v8bf, *(const v4u*)(qrow + ks * 32));
   }
-  v4f o[32];
+  // O^T accumulators: channels 128cc + 16cb + 4g + r, head 32hh + 16hb + r16
+  v4f o[8][2];
 #pragma unroll
-  for (int ct = 0; ct < 32; ++ct) o[ct] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) o[cb][hb] = v4f{0.f, 0.f, 0.f, 0.f};
+  v8bf pb[2];  // P^T of the last softmaxed tile, B-operand layout
+
+  // softmax ownership: head sh_head = 8*wave + (lane & 7), slots 4*quad..+3
+  const int quad = lane >> 3;
+  const int sh_head = 8 * wave + (lane & 7);
+  const int s_hh = sh_head >> 5, s_hb = (sh_head >> 4) & 1, s_r16 = sh_head & 15;
+  const int s_sb = quad >> 2, s_g = quad & 3;
   float m_ref = -__builtin_inff(), l_run = 0.f;
 
   const int t0 = split * a.tiles_per_split;
   const int t1 = min(t0 + a.tiles_per_split, a.n_tiles);
-  const int eg = tid & 7, cg = tid >> 3;  // staging: slots 4eg..4eg+3, channels 16cg..16cg+15
+  const int eg = wave, c8 = lane;  // staging: slots 4eg..4eg+3, channels 8c8..8c8+7
 
-  // Software pipeline: while tile t is multiplied, the FP4 latents of tile
-  // t+1 and the selected ids of tile t+2 are in flight.
-  int e_nxt[4];
+  auto pv_product = [&](int vbuf) {
+    const uint16_t* vb = sh.vb[vbuf];
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+      const int cg = 8 * cc + cb;
+      const uint2 lo = *(const uint2*)(vb + vb_offset(cg, g, r16));
+      const uint2 hi = *(const uint2*)(vb + vb_offset(cg, 4 + g, r16));
+      const v8bf vf = __builtin_bit_cast(v8bf, v4u{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) o[cb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[hb], o[cb][hb], 0, 0, 0);
+    }
+  };
+
   RawSlot raw[4];
+  int e_nxt[4];
   if (t0 < t1) {
     int e0[4];
     load_ids(a, q, t0, eg, e0);
-    issue_raw(a, q, t0, eg, cg, e0, raw);
-    if (t0 + 1 < t1) load_ids(a, q, t0 + 1, eg, e_nxt);
+    issue_raw(a, q, t0, eg, c8, e0, raw);
+    unsigned kw[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) decode_raw(raw[i], kw[i]);
+    store_tile(sh, 0, eg, c8, kw, raw_ok(raw));
+    if (t0 + 1 < t1) {
+      load_ids(a, q, t0 + 1, eg, e0);
+      issue_raw(a, q, t0 + 1, eg, c8, e0, raw);
+    }
+    if (t0 + 2 < t1) load_ids(a, q, t0 + 2, eg, e_nxt);
   }
 
   for (int t = t0; t < t1; ++t) {
-    // ---- this thread's 4 slots x 16 channels as bf16 pairs
-    // kw[i][j] = channels 16cg+2j (bits 15:0) and 16cg+2j+1 (bits 31:16) of slot 4eg+i
-    unsigned kw[4][8];
-    bool okf[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) decode_raw(a, q, t, eg, cg, i, raw[i], kw[i], okf[i]);
-    __syncthreads();  // previous tile's LDS reads are complete
-    if (cg == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) slot_ok[4 * eg + i] = okf[i] ? 1 : 0;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v4u* kp = (v4u*)(Kt + (4 * eg + i) * KT_LD + cg * 16);
-      kp[0] = v4u{kw[i][0], kw[i][1], kw[i][2], kw[i][3]};
-      kp[1] = v4u{kw[i][4], kw[i][5], kw[i][6], kw[i][7]};
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      // channel 2j: low halves; channel 2j+1: high halves; slots 4eg..4eg+3
-      uint2 lo, hi;
-      lo.x = __builtin_amdgcn_perm(kw[1][j], kw[0][j], 0x05040100u);
-      lo.y = __builtin_amdgcn_perm(kw[3][j], kw[2][j], 0x05040100u);
-      hi.x = __builtin_amdgcn_perm(kw[1][j], kw[0][j], 0x07060302u);
-      hi.y = __builtin_amdgcn_perm(kw[3][j], kw[2][j], 0x07060302u);
-      *(uint2*)(Vb + vb_offset(cg, eg, 2 * j)) = lo;
-      *(uint2*)(Vb + vb_offset(cg, eg, 2 * j + 1)) = hi;
-    }
-    // ---- prefetch the next tile's latents and the ids after it
-    if (t + 1 < t1) {
-      issue_raw(a, q, t + 1, eg, cg, e_nxt, raw);
-      if (t + 2 < t1) load_ids(a, q, t + 2, eg, e_nxt);
-    }
-    __syncthreads();
+    const int b = (t - t0) & 1;
+    __syncthreads();  // tile t is in Kt and vb[b]; sx is free
 
-    // ---- S^T[entry][head] for entries et*16 + 4g + r
-    v4f s[2];
+    // ---- phase 1: S^T(t) over this wave's channel quarter; O^T += V^T(t-1) P^T(t-1)
+    {
+      v4f s[2][2];
 #pragma unroll
-    for (int et = 0; et < 2; ++et) {
-      s[et] = v4f{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* kr = Kt + (et * 16 + r16) * KT_LD + 8 * g;
-      v4u fr[4], nx[4];
+      for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) fr[j] = *(const v4u*)(kr + j * 32);
+        for (int hb = 0; hb < 2; ++hb) s[sb][hb] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        if (kb < 3) {
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) nx[j] = *(const v4u*)(kr + (4 * (kb + 1) + j) * 32);
+        for (int sb = 0; sb < 2; ++sb) {
+          const v8bf kf =
+              __builtin_bit_cast(v8bf, *(const v4u*)(sh.kt + kt_offset(16 * sb + r16, 16 * cc + 4 * ks + g)));
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb)
+            s[sb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[hb][ks], s[sb][hb], 0, 0, 0);
         }
+      if (t > t0) pv_product(b ^ 1);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          s[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, fr[j]), qf[4 * kb + j], s[et],
-                                                          0, 0, 0);
-        if (kb < 3) {
+      for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) fr[j] = nx[j];
-        }
-      }
+        for (int hb = 0; hb < 2; ++hb) sh.sx[wave][2 * sb + hb][lane] = s[sb][hb];
     }
-    // ---- online softmax in log2 units with a lazily moved reference max
-    float x[8];
-    float mt = -__builtin_inff();
+    __syncthreads();  // partial sums written; Kt and vb[b^1] are no longer read
+
+    // ---- phase 2: softmax of this lane's head over slots 4quad..4quad+3
+    {
+      v4f tot = sh.sx[s_hh][2 * s_sb + s_hb][16 * s_g + s_r16];
 #pragma unroll
-    for (int et = 0; et < 2; ++et)
+      for (int c = 1; c < 4; ++c) tot += sh.sx[s_hh + 2 * c][2 * s_sb + s_hb][16 * s_g + s_r16];
+      const unsigned okw = sh.ok[b][quad];
+      float x[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = ((okw >> (8 * r)) & 1u) ? tot[r] * a.scale_log2 : -__builtin_inff();
+      float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      mt = fmaxf(mt, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mt), 0x128, 0xF, 0xF, false)));  // lane ^ 8
+      mt = max_xor16(mt);
+      mt = max_xor32(mt);
+      float al = 1.f;
+      if (mt > m_ref + kRescaleSlack) {  // also true when m_ref = -inf and mt is finite
+        al = (m_ref == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(m_ref - mt);
+        l_run *= al;
+        m_ref = mt;
+      }
+      const bool live = m_ref != -__builtin_inff();
+      float p[4], ps = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int e = et * 16 + 4 * g + r;
-        x[et * 4 + r] = slot_ok[e] ? s[et][r] * a.scale_log2 : -__builtin_inff();
-        mt = fmaxf(mt, x[et * 4 + r]);
+        p[r] = live ? __builtin_amdgcn_exp2f(x[r] - m_ref) : 0.f;
+        ps += p[r];
       }
-    mt = max_xor16(mt);
-    mt = max_xor32(mt);
-    const bool move = mt > m_ref + kRescaleSlack;  // also true when m_ref = -inf and mt is finite
-    if (__any(move)) {
-      const float m_new = move ? mt : m_ref;
-      const float alpha = (m_ref == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-      if (move) l_run *= alpha;
-#pragma unroll
-      for (int ct = 0; ct < 32; ++ct) o[ct] = move ? o[ct] * alpha : o[ct];
-      m_ref = m_new;
+      ps += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(ps), 0x128, 0xF, 0xF, false));
+      ps = add_xor16(ps);
+      ps = add_xor32(ps);
+      l_run += ps;
+      uint2 pk;
+      pk.x = (unsigned)__builtin_bit_cast(uint16_t, (__bf16)p[0]) |
+             ((unsigned)__builtin_bit_cast(uint16_t, (__bf16)p[1]) << 16);
+      pk.y = (unsigned)__builtin_bit_cast(uint16_t, (__bf16)p[2]) |
+             ((unsigned)__builtin_bit_cast(uint16_t, (__bf16)p[3]) << 16);
+      sh.pl[sh_head][quad] = pk;
+      if (quad == 0) sh.alpha[sh_head] = al;
     }
-    float p[8], ps = 0.f;
-    const bool live = m_ref != -__builtin_inff();
+    // ---- tile t+1 to LDS, latents of tile t+2 and ids of tile t+3 requested
+    if (t + 1 < t1) {
+      unsigned kw[4][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = live ? __builtin_amdgcn_exp2f(x[i] - m_ref) : 0.f;
-      ps += p[i];
+      for (int i = 0; i < 4; ++i) decode_raw(raw[i], kw[i]);
+      store_tile(sh, b ^ 1, eg, c8, kw, raw_ok(raw));
     }
-    ps = add_xor16(ps);
-    ps = add_xor32(ps);
-    l_run += ps;
-    v8bf pb;
+    if (t + 2 < t1) {
+      issue_raw(a, q, t + 2, eg, c8, e_nxt, raw);
+      if (t + 3 < t1) load_ids(a, q, t + 3, eg, e_nxt);
+    }
+    __syncthreads();  // P^T and the rescale factors of tile t are written
+
+    // ---- phase 3: pick up P^T(t); rescale O^T where a reference moved
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pb[i] = (__bf16)p[i];
-    // ---- O^T[channel][head] += V^T P^T; this lane's k-slots: slots 4g..4g+3, 16+4g..16+4g+3
-    {
-      v4u fr[4], nx[4];
-      // lane-constant parts of vb_offset(ct, sg, r16): the rotation only
-      // depends on ct's parity, the rest is ct * 512 elements
-      const uint16_t* vlo[2] = {Vb + vb_offset(0, g, r16), Vb + vb_offset(1, g, r16) - 512};
-      const uint16_t* vhi[2] = {Vb + vb_offset(0, 4 + g, r16), Vb + vb_offset(1, 4 + g, r16) - 512};
-      auto vfrag = [&](int ct) {
-        const uint2 lo = *(const uint2*)(vlo[ct & 1] + ct * 512);
-        const uint2 hi = *(const uint2*)(vhi[ct & 1] + ct * 512);
-        return v4u{lo.x, lo.y, hi.x, hi.y};
-      };
+    for (int hb = 0; hb < 2; ++hb) {
+      const int head = 32 * hh + 16 * hb + r16;
+      const uint2 lo = sh.pl[head][g], hi = sh.pl[head][4 + g];
+      pb[hb] = __builtin_bit_cast(v8bf, v4u{lo.x, lo.y, hi.x, hi.y});
+      const float al = sh.alpha[head];
+      if (__any(al != 1.f)) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) fr[j] = vfrag(j);
+        for (int cb = 0; cb < 8; ++cb) o[cb][hb] *= al;
+      }
+    }
+  }
+  // O^T += V^T P^T of the last tile (its V^T buffer is no longer written)
+  if (t0 < t1) pv_product((t1 - 1 - t0) & 1);
+  if (quad == 0) {
+    sh.fin_m[sh_head] = m_ref;
+    sh.fin_l[sh_head] = l_run;
+  }
+  __syncthreads();
+
+  // ---- epilogue: this wave's heads x channel quarter
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const int head = 32 * hh + 16 * hb + r16;
+    const float mh = sh.fin_m[head], lh = sh.fin_l[head];
+    if (a.n_splits == 1) {
+      const float inv = (lh > 0.f) ? 1.f / lh : 0.f;
+      uint16_t* orow = a.out + ((int64_t)q * kHeads + head) * kDim + 128 * cc;
 #pragma unroll
       for (int cb = 0; cb < 8; ++cb) {
-        if (cb < 7) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) nx[j] = vfrag(4 * (cb + 1) + j);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          o[4 * cb + j] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, fr[j]), pb, o[4 * cb + j], 0, 0, 0);
-        if (cb < 7) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) fr[j] = nx[j];
-        }
+        const int ch = cb * 16 + 4 * g;
+        __bf16 b0 = (__bf16)(o[cb][hb][0] * inv), b1 = (__bf16)(o[cb][hb][1] * inv);
+        __bf16 b2 = (__bf16)(o[cb][hb][2] * inv), b3 = (__bf16)(o[cb][hb][3] * inv);
+        uint2 pk;
+        pk.x = (unsigned)__builtin_bit_cast(uint16_t, b0) | ((unsigned)__builtin_bit_cast(uint16_t, b1) << 16);
+        pk.y = (unsigned)__builtin_bit_cast(uint16_t, b2) | ((unsigned)__builtin_bit_cast(uint16_t, b3) << 16);
+        *(uint2*)(orow + ch) = pk;
       }
+      if (a.lse && cc == 0 && g == 0)
+        a.lse[(int64_t)q * kHeads + head] = (lh > 0.f) ? (mh + __log2f(lh)) * kLn2 : -__builtin_inff();
+    } else {
+      // this split's partial record, merged by k_attn_combine
+      float* part = a.partial + ((int64_t)q * a.n_splits + split) * kPartialFloats;
+      if (cc == 0 && g == 0) {
+        part[head] = mh;
+        part[64 + head] = lh;
+      }
+      float* po = part + 128 + (int64_t)head * kDim + 128 * cc;
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) *(v4f*)(po + cb * 16 + 4 * g) = o[cb][hb];
     }
   }
-
-  if (a.n_splits == 1) {
-    finalize_head(a, q, head, g, o, m_ref, l_run);
-    return;
-  }
-  // ---- write this split's partial (merged by k_attn_combine)
-  float* part = a.partial + ((int64_t)q * a.n_splits + split) * kPartialFloats;
-  if (g == 0) {
-    part[head] = m_ref;
-    part[64 + head] = l_run;
-  }
-  float* po = part + 128 + (int64_t)head * kDim;
-#pragma unroll
-  for (int ct = 0; ct < 32; ++ct) *(v4f*)(po + ct * 16 + 4 * g) = o[ct];
 }
 
 // Merge the splits of one query: out = sum_s O_s 2^(m_s - M) /
@@ -418,7 +495,7 @@ hipError_t launch_attn(const AttnLaunch& L, const AttnPlan& plan, float* partial
   a.n_splits = plan.n_splits;
   a.scale_log2 = L.scale * kLog2e;
   dim3 grid((unsigned)plan.n_splits, (unsigned)L.Q);
-  k_sparse_attn<<<grid, 256, 0, s>>>(a);
+  k_sparse_attn<<<grid, NT, 0, s>>>(a);
   if (plan.n_splits > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
