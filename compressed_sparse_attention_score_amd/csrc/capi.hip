@@ -3,6 +3,8 @@
 #include "../../include/csa2.h"
 #include "csa2_internal.h"
 
+static_assert(CSA2_MAX_K == csa2::kMaxSelected, "on-chip selected-id capacity must match the ABI limit");
+
 #include <limits.h>
 #include <stdint.h>
 

@@ -9,6 +9,10 @@
 
 namespace csa2 {
 
+// Largest number of selected entries per query the kernels hold on chip
+// (equal to CSA2_MAX_K; checked where the public header is included).
+constexpr int kMaxSelected = 1024;
+
 struct IndexLaunch {
   int Q;
   int64_t n_entries, cache_q_stride, n_cand;

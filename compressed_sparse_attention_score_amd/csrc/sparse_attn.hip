@@ -67,7 +67,7 @@ struct AttnArgs {
 
 // Per-split partial record: m[64], l[64], O[64][512] (fp32, O unnormalised).
 constexpr int64_t kPartialFloats = 64 + 64 + 64 * 512;
-constexpr int kMaxSplits = 64;
+constexpr int kMaxSplits = 32;
 
 struct AttnShared {
   uint16_t kt[TILE * kDim];         // [slot][channel], 16-byte chunks swizzled
@@ -77,47 +77,33 @@ struct AttnShared {
   float alpha[kHeads];              // per-head rescale of O for this tile (1 = none)
   float fin_m[kHeads], fin_l[kHeads];
   unsigned ok[2][TILE / 4];         // slot validity bytes per tile (double-buffered)
+  int32_t ids[kMaxSelected];        // this split's selected ids, from slot t0*TILE on
 };
 }  // namespace
 
-// One staged slot of 8 channels: 4 bytes of FP4 codes + the E4M3 scale byte
-// of a selected latent (kind 1), 8 bf16 of a window row (kind 2), or nothing.
-struct RawSlot {
-  v4u a;
-  unsigned sc;  // bits 7:0 scale byte, bits 9:8 kind
-};
+// The staged raw data of one slot for this lane's 8 channels: a selected
+// latent keeps its 4 code bytes in x and its E4M3 scale byte in y with bit 8
+// set when the id is valid; a window row keeps its 8 bf16 in x..w. Which of
+// the two a slot is follows from its index.
+typedef v4u RawSlot;
 
-// Selected ids of the 4 slots (4eg..4eg+3) of tile t; -1 marks a non-latent
-// slot. Tiles wholly inside the selected part read their ids unconditionally
-// (a per-slot branch around a load makes the compiler wait for it).
-__device__ __forceinline__ void load_ids(const AttnArgs& a, int q, int t, int eg, int* e) {
-  const int s0 = t * TILE + 4 * eg;
-  if (t * TILE + TILE <= a.k_sel) {
-    const int32_t* ip = a.idx + (int64_t)q * a.k_sel + s0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) e[i] = ip[i];
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) e[i] = (s0 + i < a.k_sel) ? a.idx[(int64_t)q * a.k_sel + s0 + i] : -1;
-  }
-}
-
-// Channels 8c8..8c8+7 of the 4 slots of tile t. A tile holds only selected
-// latents or only window rows unless k_sel is not a multiple of the tile:
-// those two cases issue every load unconditionally (invalid slots read row 0
-// of the query's cache or window and are flagged empty), so all loads of the
-// tile stay in flight together; a mixed tile takes the per-slot path.
-__device__ __forceinline__ void issue_raw(const AttnArgs& a, int q, int t, int eg, int c8, const int* e,
-                                          RawSlot* r) {
+// Channels 8c8..8c8+7 of the 4 slots of tile t (slot group eg), ids from LDS.
+// A tile holds only selected latents or only window rows unless k_sel is not
+// a multiple of the tile: those two cases issue every load unconditionally
+// (invalid slots read row 0 of the query's cache or window and are flagged),
+// so all loads stay in flight together; a mixed tile takes a per-slot path.
+__device__ __forceinline__ void issue_raw(const AttnArgs& a, const AttnShared& sh, int q, int t, int t0, int eg,
+                                          int c8, RawSlot* r) {
   const int s0 = t * TILE;
+  const int32_t* ids = sh.ids + (s0 - t0 * TILE) + 4 * eg;
   if (s0 + TILE <= a.k_sel && a.n_entries > 0) {
     const uint8_t* base = a.main_cache + (int64_t)q * a.cache_q_stride * kMainBytes;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool ok = e[i] >= 0 && (int64_t)e[i] < a.n_entries;
-      const uint8_t* ent = base + (int64_t)(ok ? e[i] : 0) * kMainBytes;
-      r[i].a = v4u{*(const unsigned*)(ent + c8 * 4), 0u, 0u, 0u};
-      r[i].sc = (unsigned)ent[256 + (c8 >> 1)] | (ok ? (1u << 8) : 0u);
+      const int e = ids[i];
+      const bool ok = e >= 0 && (int64_t)e < a.n_entries;
+      const uint8_t* ent = base + (int64_t)(ok ? e : 0) * kMainBytes;
+      r[i] = v4u{*(const unsigned*)(ent + c8 * 4), (unsigned)ent[256 + (c8 >> 1)] | (ok ? 0x100u : 0u), 0u, 0u};
     }
     return;
   }
@@ -126,50 +112,48 @@ __device__ __forceinline__ void issue_raw(const AttnArgs& a, int q, int t, int e
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int slot = s0 + 4 * eg + i;
-      const bool ok = slot < a.nj;
-      r[i].a = *(const v4u*)(base + (int64_t)(ok ? slot - a.k_sel : 0) * kDim);
-      r[i].sc = ok ? (2u << 8) : 0u;
+      r[i] = *(const v4u*)(base + (int64_t)(slot < a.nj ? slot - a.k_sel : 0) * kDim);
     }
     return;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int slot = s0 + 4 * eg + i;
-    r[i].a = v4u{0u, 0u, 0u, 0u};
-    r[i].sc = 0u;
+    r[i] = v4u{0u, 0u, 0u, 0u};
     if (slot < a.k_sel) {
-      if (e[i] >= 0 && (int64_t)e[i] < a.n_entries) {
-        const uint8_t* ent = a.main_cache + ((int64_t)q * a.cache_q_stride + e[i]) * kMainBytes;
-        r[i].a = v4u{*(const unsigned*)(ent + c8 * 4), 0u, 0u, 0u};
-        r[i].sc = ent[256 + (c8 >> 1)] | (1u << 8);
+      const int e = ids[i];
+      if (e >= 0 && (int64_t)e < a.n_entries) {
+        const uint8_t* ent = a.main_cache + ((int64_t)q * a.cache_q_stride + e) * kMainBytes;
+        r[i] = v4u{*(const unsigned*)(ent + c8 * 4), (unsigned)ent[256 + (c8 >> 1)] | 0x100u, 0u, 0u};
       }
     } else if (slot < a.nj) {
-      r[i].a = *(const v4u*)(a.swa + ((int64_t)q * a.swa_q_stride + (slot - a.k_sel)) * kDim + c8 * 8);
-      r[i].sc = 2u << 8;
+      r[i] = *(const v4u*)(a.swa + ((int64_t)q * a.swa_q_stride + (slot - a.k_sel)) * kDim + c8 * 8);
     }
   }
 }
 
-// kw[j] = channels 8c8+2j (bits 15:0) and 8c8+2j+1 (bits 31:16) as bf16.
-// Branch-free: a latent is decoded, a window row passed through, an empty
-// slot gives zeros (its loaded bytes may be anything, NaN included).
-__device__ __forceinline__ void decode_raw(const RawSlot& r, unsigned* kw) {
-  float f[8];
-  decode_e2m1x8_scaled(r.a[0], e4m3_to_f32_hw(r.sc & 0xFFu), f);
-  const unsigned kind = r.sc >> 8;
+// kw[i][j] = channels 8c8+2j (bits 15:0) and 8c8+2j+1 (bits 31:16) of slot
+// 4eg+i of tile t as bf16. Branch-free per slot: a latent is decoded, a
+// window row passed through, an empty slot gives zeros (its loaded bytes may
+// be anything, NaN included). *okb gets the validity byte of each slot.
+__device__ __forceinline__ void decode_tile(const AttnArgs& a, int t, int eg, const RawSlot* r, unsigned (*kw)[4],
+                                            unsigned* okb) {
+  unsigned ob = 0u;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const unsigned dec = pack_bf16x2_exact(f[2 * j], f[2 * j + 1]);
-    kw[j] = (kind == 1u) ? dec : (kind == 2u) ? r.a[j] : 0u;
+  for (int i = 0; i < 4; ++i) {
+    const int slot = t * TILE + 4 * eg + i;
+    const bool latent = slot < a.k_sel, window = !latent && slot < a.nj;
+    const bool lat_ok = latent && (r[i][1] & 0x100u);
+    float f[8];
+    decode_e2m1x8_scaled(r[i][0], e4m3_to_f32_hw(r[i][1] & 0xFFu), f);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const unsigned dec = pack_bf16x2_exact(f[2 * j], f[2 * j + 1]);
+      kw[i][j] = lat_ok ? dec : window ? r[i][j] : 0u;
+    }
+    ob |= ((lat_ok || window) ? 1u : 0u) << (8 * i);
   }
-}
-
-// Validity bytes of the 4 staged slots (byte i = slot 4eg+i holds data).
-__device__ __forceinline__ unsigned raw_ok(const RawSlot* r) {
-  unsigned okb = 0u;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) okb |= ((r[i].sc >> 8) != 0u ? 1u : 0u) << (8 * i);
-  return okb;
+  *okb = ob;
 }
 
 // Element offset of channel chunk `chunk` (8 channels, 16 bytes) of Kt row
@@ -258,26 +242,31 @@ __global__ __launch_bounds__(NT, 1) void k_sparse_attn(AttnArgs a) {
     }
   };
 
-  RawSlot raw[4];
-  int e_nxt[4];
+  // The split's selected ids, read once into LDS.
+  {
+    const int sbeg = t0 * TILE, send = min(t1 * TILE, a.k_sel);
+    for (int sl = sbeg + tid; sl < send; sl += NT) sh.ids[sl - sbeg] = a.idx[(int64_t)q * a.k_sel + sl];
+  }
+  __syncthreads();
+
+  // Pipeline: tile t is multiplied from LDS while tile t+1 (raw data already
+  // in registers) is dequantised into the other buffer and the latents of
+  // tile t+2 are in flight; the two raw buffers alternate by a 2x unrolled
+  // loop so no loaded register is copied before it is consumed.
+  RawSlot rawA[4], rawB[4];
   if (t0 < t1) {
-    int e0[4];
-    load_ids(a, q, t0, eg, e0);
-    issue_raw(a, q, t0, eg, c8, e0, raw);
-    unsigned kw[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) decode_raw(raw[i], kw[i]);
-    store_tile(sh, 0, eg, c8, kw, raw_ok(raw));
-    if (t0 + 1 < t1) {
-      load_ids(a, q, t0 + 1, eg, e0);
-      issue_raw(a, q, t0 + 1, eg, c8, e0, raw);
-    }
-    if (t0 + 2 < t1) load_ids(a, q, t0 + 2, eg, e_nxt);
+    issue_raw(a, sh, q, t0, t0, eg, c8, rawA);
+    unsigned kw[4][4], okb;
+    decode_tile(a, t0, eg, rawA, kw, &okb);
+    store_tile(sh, 0, eg, c8, kw, okb);
+    if (t0 + 1 < t1) issue_raw(a, sh, q, t0 + 1, t0, eg, c8, rawA);
   }
 
-  for (int t = t0; t < t1; ++t) {
+  // One tile: nxt holds the raw data of tile t+1, fut receives tile t+2's.
+  auto step = [&](int t, RawSlot* nxt, RawSlot* fut) {
     const int b = (t - t0) & 1;
-    __syncthreads();  // tile t is in Kt and vb[b]; sx is free
+    __syncthreads();  // tile t is in Kt and vb[b]; sx, pl and alpha are free
+    if (t + 2 < t1) issue_raw(a, sh, q, t + 2, t0, eg, c8, fut);
 
     // ---- phase 1: S^T(t) over this wave's channel quarter; O^T += V^T(t-1) P^T(t-1)
     {
@@ -342,16 +331,11 @@ __global__ __launch_bounds__(NT, 1) void k_sparse_attn(AttnArgs a) {
       sh.pl[sh_head][quad] = pk;
       if (quad == 0) sh.alpha[sh_head] = al;
     }
-    // ---- tile t+1 to LDS, latents of tile t+2 and ids of tile t+3 requested
+    // ---- tile t+1 to LDS
     if (t + 1 < t1) {
-      unsigned kw[4][4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) decode_raw(raw[i], kw[i]);
-      store_tile(sh, b ^ 1, eg, c8, kw, raw_ok(raw));
-    }
-    if (t + 2 < t1) {
-      issue_raw(a, q, t + 2, eg, c8, e_nxt, raw);
-      if (t + 3 < t1) load_ids(a, q, t + 3, eg, e_nxt);
+      unsigned kw[4][4], okb;
+      decode_tile(a, t + 1, eg, nxt, kw, &okb);
+      store_tile(sh, b ^ 1, eg, c8, kw, okb);
     }
     __syncthreads();  // P^T and the rescale factors of tile t are written
 
@@ -367,6 +351,10 @@ __global__ __launch_bounds__(NT, 1) void k_sparse_attn(AttnArgs a) {
         for (int cb = 0; cb < 8; ++cb) o[cb][hb] *= al;
       }
     }
+  };
+  for (int t = t0; t < t1; t += 2) {
+    step(t, rawA, rawB);
+    if (t + 1 < t1) step(t + 1, rawB, rawA);
   }
   // O^T += V^T P^T of the last tile (its V^T buffer is no longer written)
   if (t0 < t1) pv_product((t1 - 1 - t0) & 1);
@@ -412,30 +400,55 @@ __global__ __launch_bounds__(NT, 1) void k_sparse_attn(AttnArgs a) {
 
 // Merge the splits of one query: out = sum_s O_s 2^(m_s - M) /
 // sum_s l_s 2^(m_s - M), in split order. grid (16, Q), 256 threads:
-// thread -> head blockIdx.x*4 + tid/64, channels (tid%64)*8 .. +7.
+// thread -> head blockIdx.x*4 + tid/64, channels (tid%64)*8 .. +7. Every
+// split's (m, l) and each batch of 8 splits' O rows are requested together
+// (clamped indices, zero weight past the last split), so the merge costs a
+// few memory round trips however many splits there are.
 __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ partial, int n_splits,
                                                       uint16_t* __restrict__ out, float* __restrict__ lse) {
   const int q = blockIdx.y, tid = threadIdx.x;
   const int h = blockIdx.x * 4 + (tid >> 6), c0 = (tid & 63) * 8;
   const float* base = partial + (int64_t)q * n_splits * kPartialFloats;
+  float ms[kMaxSplits], ls[kMaxSplits];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp) {
+    const int ss = min(sp, n_splits - 1);
+    ms[sp] = base[ss * kPartialFloats + h];
+    ls[sp] = base[ss * kPartialFloats + 64 + h];
+  }
   float M = -__builtin_inff();
-  for (int sp = 0; sp < n_splits; ++sp) M = fmaxf(M, base[sp * kPartialFloats + h]);
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp) M = (sp < n_splits) ? fmaxf(M, ms[sp]) : M;
   float L = 0.f;
   float acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = 0.f;
   if (M != -__builtin_inff()) {
-    for (int sp = 0; sp < n_splits; ++sp) {
-      const float* ps = base + sp * kPartialFloats;
-      const float ms = ps[h];
-      const float f = (ms == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-      L += ps[64 + h] * f;
-      const v4f* src = (const v4f*)(ps + 128 + (int64_t)h * kDim + c0);
-      const v4f x0 = src[0], x1 = src[1];
+    float f[kMaxSplits];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        acc[c] += x0[c] * f;
-        acc[4 + c] += x1[c] * f;
+    for (int sp = 0; sp < kMaxSplits; ++sp) {
+      f[sp] = (sp < n_splits && ms[sp] != -__builtin_inff()) ? __builtin_amdgcn_exp2f(ms[sp] - M) : 0.f;
+      L += ls[sp] * f[sp];
+    }
+    for (int s0 = 0; s0 < n_splits; s0 += 8) {
+      v4f x0[8], x1[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int ss = min(s0 + u, n_splits - 1);
+        const v4f* src = (const v4f*)(base + ss * kPartialFloats + 128 + (int64_t)h * kDim + c0);
+        x0[u] = src[0];
+        x1[u] = src[1];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        float fu = 0.f;
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplits; ++sp) fu = (sp == s0 + u) ? f[sp] : fu;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          acc[c] += x0[u][c] * fu;
+          acc[4 + c] += x1[u][c] * fu;
+        }
       }
     }
   }
@@ -452,14 +465,15 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
 }
 
 AttnPlan plan_attn(int Q, int nj) {
-  // Aim for one workgroup per CU, with at least 4 tiles per split so the
-  // software pipeline has work to overlap and the merge reads few partials.
+  // As many splits as keep every workgroup of the launch resident at once
+  // (one per CU), with at least 2 tiles per split so the gather of the next
+  // tile overlaps the current one; at most kMaxSplits splits.
   AttnPlan p;
   p.n_tiles = (nj + TILE - 1) / TILE;
   if (p.n_tiles < 1) p.n_tiles = 1;
-  const int want = (Q > 0) ? (256 + Q - 1) / Q : 1;
-  int tps = (p.n_tiles + want - 1) / want;
-  if (tps < 4) tps = 4;
+  const int want = (Q > 0) ? 256 / Q : 1;
+  int tps = (want > 0) ? (p.n_tiles + want - 1) / want : p.n_tiles;
+  if (tps < 2) tps = 2;
   p.tiles_per_split = tps;
   p.n_splits = (p.n_tiles + tps - 1) / tps;
   if (p.n_splits > kMaxSplits) {
