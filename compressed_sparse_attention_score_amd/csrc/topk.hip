@@ -67,6 +67,7 @@ __device__ __forceinline__ unsigned block_incl_scan(unsigned x, unsigned* wsum, 
   return x + before;
 }
 
+
 // One radix pass: pick the digit (bits shift..shift+7) of the k-th largest
 // value given the histogram in sh.hist. Updates prefix/remaining; returns
 // false if the histogram holds fewer than `remaining` values and true when
@@ -335,6 +336,252 @@ __global__ __launch_bounds__(NT) void k_select_final(const unsigned* __restrict_
   }
 }
 
+// ---------------------------------------------------------------------------
+// One workgroup per query (lists up to kQMaxCand candidates). Same method as
+// the two kernels above, in one launch: theta from the sub-chunk maxima,
+// compaction of the candidates >= theta in position order (ascending entry
+// id: pools list their blocks in ascending order), then the exact k-th
+// composite among the survivors and the ordered write.
+namespace {
+constexpr int NQ = 1024;            // threads
+constexpr int kQPer = 16;           // consecutive positions per thread per pass
+constexpr int kQCap = 8192;         // survivors held in LDS (8 per thread)
+constexpr int64_t kQMaxCand = 1 << 18;
+
+struct QSelShared {
+  unsigned hist[kBins];
+  unsigned wsum[NQ / 64];
+  unsigned res[4];
+  unsigned long long cand[kQCap];
+};
+
+// Inclusive prefix sum over the NQ threads; *total = sum of all. Barriers inside.
+__device__ __forceinline__ unsigned q_scan(unsigned x, QSelShared& sh, unsigned* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned y = (unsigned)__shfl_up((int)x, off, 64);
+    if (lane >= off) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) sh.wsum[wv] = x;
+  __syncthreads();
+  unsigned before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NQ / 64; ++w) {
+    const unsigned v = sh.wsum[w];
+    before += (w < wv) ? v : 0u;
+    all += v;
+  }
+  *total = all;
+  return x + before;
+}
+
+// Digit of the k-th largest from the histogram (threads 0..255 scan the bins
+// from the top). Returns false if fewer than `remaining` values are counted.
+template <typename T>
+__device__ __forceinline__ bool q_pick(QSelShared& sh, int shift, T& prefix, unsigned& remaining, bool* done) {
+  const int tid = threadIdx.x;
+  const unsigned h = (tid < kBins) ? sh.hist[kBins - 1 - tid] : 0u;
+  unsigned total;
+  const unsigned incl = q_scan(h, sh, &total);
+  if (tid < kBins && incl - h < remaining && remaining <= incl) {
+    sh.res[0] = (unsigned)(kBins - 1 - tid);
+    sh.res[1] = incl - h;
+    sh.res[2] = h;
+  }
+  __syncthreads();
+  if (total < remaining) return false;
+  const unsigned d = sh.res[0], above = sh.res[1], cnt = sh.res[2];
+  prefix |= ((T)d) << shift;
+  remaining -= above;
+  *done = (cnt == remaining);
+  __syncthreads();
+  return true;
+}
+
+// k-th largest non-zero value (see radix_kth_regs), NQ threads, PER values each.
+template <typename T, int PER>
+__device__ T q_kth_regs(const T (&v)[PER], unsigned k, QSelShared& sh) {
+  constexpr int W = (int)(sizeof(T) * 8);
+  T prefix = 0;
+  unsigned remaining = k;
+  for (int hi = W; hi > 0; hi -= kRadixBits) {
+    const int shift = hi - kRadixBits;
+    if (threadIdx.x < kBins) sh.hist[threadIdx.x] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const T x = v[j];
+      if (x == 0) continue;
+      if (hi < W && (x >> hi) != (prefix >> hi)) continue;
+      atomicAdd(&sh.hist[(unsigned)(x >> shift) & (kBins - 1)], 1u);
+    }
+    __syncthreads();
+    bool done = false;
+    if (!q_pick<T>(sh, shift, prefix, remaining, &done)) return (T)0;
+    if (done) break;
+  }
+  return prefix;
+}
+
+// Same over values in memory (global or LDS), zeros ignored.
+template <typename T>
+__device__ T q_kth_stream(const T* src, int64_t n, unsigned k, QSelShared& sh) {
+  constexpr int W = (int)(sizeof(T) * 8);
+  T prefix = 0;
+  unsigned remaining = k;
+  for (int hi = W; hi > 0; hi -= kRadixBits) {
+    const int shift = hi - kRadixBits;
+    if (threadIdx.x < kBins) sh.hist[threadIdx.x] = 0u;
+    __syncthreads();
+    for (int64_t i = threadIdx.x; i < n; i += NQ) {
+      const T x = src[i];
+      if (x == 0) continue;
+      if (hi < W && (x >> hi) != (prefix >> hi)) continue;
+      atomicAdd(&sh.hist[(unsigned)(x >> shift) & (kBins - 1)], 1u);
+    }
+    __syncthreads();
+    bool done = false;
+    if (!q_pick<T>(sh, shift, prefix, remaining, &done)) return (T)0;
+    if (done) break;
+  }
+  return prefix;
+}
+}  // namespace
+
+__global__ __launch_bounds__(NQ) void k_select_query(const float* __restrict__ scores, int64_t n_cand,
+                                                     int64_t n_entries, const int32_t* __restrict__ cand_blocks,
+                                                     int n_blocks, const int32_t* __restrict__ n_valid, int k,
+                                                     const unsigned* __restrict__ gmax, int64_t n_groups,
+                                                     unsigned long long* __restrict__ gcand, int32_t* __restrict__ idx,
+                                                     float* __restrict__ top_scores) {
+  __shared__ QSelShared sh;
+  const int q = blockIdx.x, tid = threadIdx.x;
+  int64_t limit = n_entries;
+  if (n_valid) limit = min(limit, (int64_t)n_valid[q]);
+  int32_t* iq = idx + (int64_t)q * k;
+  float* tq = top_scores ? top_scores + (int64_t)q * k : nullptr;
+  const float* srow = scores + (int64_t)q * n_cand;
+  unsigned long long* gq = gcand + (int64_t)q * n_cand;
+
+  // ---- theta = k-th largest sub-chunk maximum (1 = keep every valid candidate)
+  unsigned theta = 1u;
+  if (gmax && n_groups >= k) {
+    const unsigned* gm = gmax + (int64_t)q * n_groups;
+    unsigned t;
+    if (n_groups <= 4 * NQ) {
+      unsigned g[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t i = (int64_t)j * NQ + tid;
+        g[j] = (i < n_groups) ? gm[i] : 0u;
+      }
+      t = q_kth_regs<unsigned, 4>(g, (unsigned)k, sh);
+    } else {
+      t = q_kth_stream<unsigned>(gm, n_groups, (unsigned)k, sh);
+    }
+    theta = t > 1u ? t : 1u;
+  }
+
+  // ---- keep key >= theta, in position order: thread t takes positions
+  // p0 + 16t .. +15 of each pass of NQ*16 positions
+  unsigned m = 0;  // survivors so far (block-uniform)
+  for (int64_t p0 = 0; p0 < n_cand; p0 += (int64_t)NQ * kQPer) {
+    const int64_t pb = p0 + (int64_t)tid * kQPer;
+    float sc[kQPer];
+    if (pb + kQPer <= n_cand && (n_cand & 3) == 0) {  // rows start 16-byte aligned
+#pragma unroll
+      for (int j = 0; j < kQPer; j += 4) {
+        const v4f v = *(const v4f*)(srow + pb + j);
+        sc[j] = v[0]; sc[j + 1] = v[1]; sc[j + 2] = v[2]; sc[j + 3] = v[3];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kQPer; ++j) sc[j] = (pb + j < n_cand) ? srow[pb + j] : 0.f;
+    }
+    int32_t blk[kQPer / 8];
+#pragma unroll
+    for (int j = 0; j < kQPer / 8; ++j)
+      blk[j] = (cand_blocks && pb + 8 * j < n_cand) ? cand_blocks[(int64_t)q * n_blocks + ((pb >> 3) + j)] : 0;
+    unsigned long long comp[kQPer];
+    unsigned cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kQPer; ++j) {
+      const int64_t p = pb + j;
+      int64_t e = p;
+      if (cand_blocks) e = (blk[j >> 3] < 0) ? -1 : 8 * (int64_t)blk[j >> 3] + (p & 7);
+      const bool valid = p < n_cand && e >= 0 && e < limit;
+      const unsigned key = score_key(sc[j]);
+      const bool keep = valid && key >= theta;
+      comp[j] = keep ? (((unsigned long long)key << 32) | (unsigned long long)(~(unsigned)e)) : 0ull;
+      cnt += keep ? 1u : 0u;
+    }
+    unsigned total;
+    unsigned pos = m + q_scan(cnt, sh, &total) - cnt;
+#pragma unroll
+    for (int j = 0; j < kQPer; ++j) {
+      if (comp[j]) {
+        if (pos < (unsigned)kQCap) sh.cand[pos] = comp[j];
+        else gq[pos] = comp[j];
+        ++pos;
+      }
+    }
+    m += total;
+  }
+  __syncthreads();
+
+  unsigned written = 0;
+  if (m <= (unsigned)kQCap) {
+    // ---- survivors in LDS: thread t holds list elements 8t..8t+7
+    constexpr int PER = kQCap / NQ;
+    unsigned long long v[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const unsigned e = (unsigned)tid * PER + j;
+      v[j] = (e < m) ? sh.cand[e] : 0ull;
+    }
+    const unsigned long long T = (m > (unsigned)k) ? q_kth_regs<unsigned long long, PER>(v, (unsigned)k, sh) : 0ull;
+    unsigned c = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) c += (v[j] != 0ull && v[j] >= T) ? 1u : 0u;
+    unsigned all;
+    unsigned pos = q_scan(c, sh, &all) - c;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (v[j] != 0ull && v[j] >= T && pos < (unsigned)k) {
+        iq[pos] = (int32_t)(~(unsigned)(v[j] & 0xFFFFFFFFull));
+        if (tq) tq[pos] = key_score((unsigned)(v[j] >> 32));
+        ++pos;
+      }
+    }
+    written = min(all, (unsigned)k);
+  } else {
+    // ---- long survivor lists (heavy ties): move the LDS part to global and
+    // select from there
+    for (int i = tid; i < kQCap; i += NQ) gq[i] = sh.cand[i];
+    __syncthreads();
+    const unsigned long long T = q_kth_stream<unsigned long long>(gq, m, (unsigned)k, sh);
+    for (unsigned i0 = 0; i0 < m; i0 += NQ) {
+      const unsigned i = i0 + tid;
+      const unsigned long long x = (i < m) ? gq[i] : 0ull;
+      const unsigned sel = (x != 0ull && x >= T) ? 1u : 0u;
+      unsigned tot;
+      const unsigned pos = written + q_scan(sel, sh, &tot) - sel;
+      if (sel && pos < (unsigned)k) {
+        iq[pos] = (int32_t)(~(unsigned)(x & 0xFFFFFFFFull));
+        if (tq) tq[pos] = key_score((unsigned)(x >> 32));
+      }
+      written += tot;
+    }
+    written = min(written, (unsigned)k);
+  }
+  for (int j = (int)written + tid; j < k; j += NQ) {
+    iq[j] = -1;
+    if (tq) tq[j] = -__builtin_inff();
+  }
+}
+
 SelectPlan plan_select(int64_t n_cand) {
   SelectPlan p;
   p.chunk = kChunk;
@@ -347,6 +594,12 @@ hipError_t launch_select(const float* scores, int Q, int64_t n_cand, int64_t n_e
                          int n_blocks, const int32_t* n_valid, int k, const ScorePlan& sp, const unsigned* gmax,
                          unsigned* counts, unsigned long long* cand, int32_t* idx, float* top_scores, hipStream_t s) {
   if (Q <= 0) return hipSuccess;
+  // one workgroup per query when that fills the chip or the lists are short
+  if (n_cand <= kQMaxCand && (Q >= 64 || n_cand <= 16384)) {
+    k_select_query<<<(unsigned)Q, NQ, 0, s>>>(scores, n_cand, n_entries, cand_blocks, n_blocks, n_valid, k, gmax,
+                                             sp.n_groups, cand, idx, top_scores);
+    return hipGetLastError();
+  }
   SelectPlan pl = plan_select(n_cand);
   k_select_compact<<<dim3((unsigned)pl.n_chunks, (unsigned)Q), NT, 0, s>>>(
       scores, n_cand, n_entries, cand_blocks, n_blocks, n_valid, k, gmax, sp.n_groups, pl.n_chunks, counts, cand);
