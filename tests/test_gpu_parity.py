@@ -128,14 +128,31 @@ def test_topk_exact_random(n, k):
     _assert_topk_exact(s, k, n, what=f"n{n} k{k}")
 
 
-def test_topk_ties_nan_negzero():
+@pytest.mark.parametrize("n", [20000, 16000])
+def test_topk_ties_nan_negzero(n):
+    """n=20000 with 4 queries takes the chunk-parallel selection, n=16000 the
+    one-workgroup-per-query kernel; the all-equal row keeps every candidate,
+    more than that kernel holds in LDS."""
     rng = np.random.default_rng(1)
-    s = np.round(rng.standard_normal((4, 20000)) * 3).astype(np.float32)  # heavy ties
+    s = np.round(rng.standard_normal((4, n)) * 3).astype(np.float32)  # heavy ties
     s[1, ::7] = -0.0
     s[1, 1::7] = 0.0
     s[2, :300] = np.nan
     s[3, :] = 2.5  # all equal: the whole list is one tie set
-    _assert_topk_exact(s, 512, 20000, what="ties")
+    _assert_topk_exact(s, 512, n, what=f"ties n{n}")
+
+
+def test_topk_many_queries_long_lists():
+    """64 queries of 30,000 candidates: one workgroup per query with several
+    compaction passes; some rows tie heavily."""
+    rng = np.random.default_rng(5)
+    s = rng.standard_normal((64, 30000)).astype(np.float32)
+    s[3] = np.round(s[3] * 2)
+    s[7, :] = -1.0
+    nv = np.full(64, 30000, np.int32)
+    nv[5] = 100
+    nv[9] = 0
+    _assert_topk_exact(s, 512, 30000, n_valid=nv, what="many queries")
 
 
 def test_topk_pool_and_causal():
