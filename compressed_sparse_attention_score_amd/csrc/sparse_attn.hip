@@ -65,8 +65,10 @@ struct AttnArgs {
   float scale_log2;
 };
 
-// Per-split partial record: m[64], l[64], O[64][512] (fp32, O unnormalised).
-constexpr int64_t kPartialFloats = 64 + 64 + 64 * 512;
+// Per-split partial record: fp32 m[64], fp32 l[64], then O[64][512] as bf16
+// normalised by the split's own l (an average of V rows, so of the output's
+// magnitude; one bf16 rounding). Sized in floats.
+constexpr int64_t kPartialFloats = 64 + 64 + 64 * 512 / 2;
 constexpr int kMaxSplits = 32;
 
 struct AttnShared {
@@ -364,42 +366,42 @@ __global__ __launch_bounds__(NT, 1) void k_sparse_attn(AttnArgs a) {
   }
   __syncthreads();
 
-  // ---- epilogue: this wave's heads x channel quarter
+  // ---- epilogue: this wave's heads x channel quarter, O / l as bf16, into
+  // the output (one split) or this split's partial record
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
     const int head = 32 * hh + 16 * hb + r16;
     const float mh = sh.fin_m[head], lh = sh.fin_l[head];
+    const float inv = (lh > 0.f) ? 1.f / lh : 0.f;
+    uint16_t* orow;
     if (a.n_splits == 1) {
-      const float inv = (lh > 0.f) ? 1.f / lh : 0.f;
-      uint16_t* orow = a.out + ((int64_t)q * kHeads + head) * kDim + 128 * cc;
-#pragma unroll
-      for (int cb = 0; cb < 8; ++cb) {
-        const int ch = cb * 16 + 4 * g;
-        __bf16 b0 = (__bf16)(o[cb][hb][0] * inv), b1 = (__bf16)(o[cb][hb][1] * inv);
-        __bf16 b2 = (__bf16)(o[cb][hb][2] * inv), b3 = (__bf16)(o[cb][hb][3] * inv);
-        uint2 pk;
-        pk.x = (unsigned)__builtin_bit_cast(uint16_t, b0) | ((unsigned)__builtin_bit_cast(uint16_t, b1) << 16);
-        pk.y = (unsigned)__builtin_bit_cast(uint16_t, b2) | ((unsigned)__builtin_bit_cast(uint16_t, b3) << 16);
-        *(uint2*)(orow + ch) = pk;
-      }
+      orow = a.out + ((int64_t)q * kHeads + head) * kDim + 128 * cc;
       if (a.lse && cc == 0 && g == 0)
         a.lse[(int64_t)q * kHeads + head] = (lh > 0.f) ? (mh + __log2f(lh)) * kLn2 : -__builtin_inff();
     } else {
-      // this split's partial record, merged by k_attn_combine
       float* part = a.partial + ((int64_t)q * a.n_splits + split) * kPartialFloats;
       if (cc == 0 && g == 0) {
         part[head] = mh;
         part[64 + head] = lh;
       }
-      float* po = part + 128 + (int64_t)head * kDim + 128 * cc;
+      orow = (uint16_t*)(part + 128) + (int64_t)head * kDim + 128 * cc;
+    }
 #pragma unroll
-      for (int cb = 0; cb < 8; ++cb) *(v4f*)(po + cb * 16 + 4 * g) = o[cb][hb];
+    for (int cb = 0; cb < 8; ++cb) {
+      const int ch = cb * 16 + 4 * g;
+      __bf16 b0 = (__bf16)(o[cb][hb][0] * inv), b1 = (__bf16)(o[cb][hb][1] * inv);
+      __bf16 b2 = (__bf16)(o[cb][hb][2] * inv), b3 = (__bf16)(o[cb][hb][3] * inv);
+      uint2 pk;
+      pk.x = (unsigned)__builtin_bit_cast(uint16_t, b0) | ((unsigned)__builtin_bit_cast(uint16_t, b1) << 16);
+      pk.y = (unsigned)__builtin_bit_cast(uint16_t, b2) | ((unsigned)__builtin_bit_cast(uint16_t, b3) << 16);
+      *(uint2*)(orow + ch) = pk;
     }
   }
 }
 
-// Merge the splits of one query: out = sum_s O_s 2^(m_s - M) /
-// sum_s l_s 2^(m_s - M), in split order. grid (16, Q), 256 threads:
+// Merge the splits of one query: with O_s stored as O_s / l_s,
+// out = sum_s (O_s / l_s) l_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), in split
+// order. grid (16, Q), 256 threads:
 // thread -> head blockIdx.x*4 + tid/64, channels (tid%64)*8 .. +7. Every
 // split's (m, l) and each batch of 8 splits' O rows are requested together
 // (clamped indices, zero weight past the last split), so the merge costs a
@@ -424,20 +426,18 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = 0.f;
   if (M != -__builtin_inff()) {
-    float f[kMaxSplits];
+    float f[kMaxSplits];  // weight of split s: l_s 2^(m_s - M)
 #pragma unroll
     for (int sp = 0; sp < kMaxSplits; ++sp) {
-      f[sp] = (sp < n_splits && ms[sp] != -__builtin_inff()) ? __builtin_amdgcn_exp2f(ms[sp] - M) : 0.f;
-      L += ls[sp] * f[sp];
+      f[sp] = (sp < n_splits && ms[sp] != -__builtin_inff()) ? ls[sp] * __builtin_amdgcn_exp2f(ms[sp] - M) : 0.f;
+      L += f[sp];
     }
     for (int s0 = 0; s0 < n_splits; s0 += 8) {
-      v4f x0[8], x1[8];
+      v4u x[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int ss = min(s0 + u, n_splits - 1);
-        const v4f* src = (const v4f*)(base + ss * kPartialFloats + 128 + (int64_t)h * kDim + c0);
-        x0[u] = src[0];
-        x1[u] = src[1];
+        x[u] = *(const v4u*)((const uint16_t*)(base + ss * kPartialFloats + 128) + (int64_t)h * kDim + c0);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -446,8 +446,8 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
         for (int sp = 0; sp < kMaxSplits; ++sp) fu = (sp == s0 + u) ? f[sp] : fu;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          acc[c] += x0[u][c] * fu;
-          acc[4 + c] += x1[u][c] * fu;
+          acc[2 * c] += __uint_as_float(x[u][c] << 16) * fu;
+          acc[2 * c + 1] += __uint_as_float(x[u][c] & 0xFFFF0000u) * fu;
         }
       }
     }
