@@ -465,6 +465,26 @@ __global__ __launch_bounds__(NQ) void k_select_query(const float* __restrict__ s
   const float* srow = scores + (int64_t)q * n_cand;
   unsigned long long* gq = gcand + (int64_t)q * n_cand;
 
+  // Positions are taken in passes of NQ*kQPer; thread t owns positions
+  // 16t..16t+15 of each pass. Full passes (rows 16-byte aligned) load with
+  // aligned vectors and no per-thread conditions, the next pass's scores
+  // in flight while this one is compacted; a ragged last pass is guarded.
+  constexpr int64_t kStep = (int64_t)NQ * kQPer;
+  const int64_t n_full = ((n_cand & 3) == 0) ? n_cand / kStep : 0;
+  auto load_full = [&](float* sc, int32_t* blk, int64_t p0) {
+    const int64_t pb = p0 + (int64_t)tid * kQPer;
+#pragma unroll
+    for (int j = 0; j < kQPer; j += 4) {
+      const v4f v = *(const v4f*)(srow + pb + j);
+      sc[j] = v[0]; sc[j + 1] = v[1]; sc[j + 2] = v[2]; sc[j + 3] = v[3];
+    }
+#pragma unroll
+    for (int j = 0; j < kQPer / 8; ++j) blk[j] = cand_blocks ? cand_blocks[(int64_t)q * n_blocks + ((pb >> 3) + j)] : 0;
+  };
+  float scA[kQPer], scB[kQPer];
+  int32_t bkA[kQPer / 8], bkB[kQPer / 8];
+  if (n_full > 0) load_full(scA, bkA, 0);  // in flight during the threshold search
+
   // ---- theta = k-th largest sub-chunk maximum (1 = keep every valid candidate)
   unsigned theta = 1u;
   if (gmax && n_groups >= k) {
@@ -484,26 +504,10 @@ __global__ __launch_bounds__(NQ) void k_select_query(const float* __restrict__ s
     theta = t > 1u ? t : 1u;
   }
 
-  // ---- keep key >= theta, in position order: thread t takes positions
-  // p0 + 16t .. +15 of each pass of NQ*16 positions
+  // ---- keep key >= theta, in position order
   unsigned m = 0;  // survivors so far (block-uniform)
-  for (int64_t p0 = 0; p0 < n_cand; p0 += (int64_t)NQ * kQPer) {
+  auto process = [&](const float* sc, const int32_t* blk, int64_t p0) {
     const int64_t pb = p0 + (int64_t)tid * kQPer;
-    float sc[kQPer];
-    if (pb + kQPer <= n_cand && (n_cand & 3) == 0) {  // rows start 16-byte aligned
-#pragma unroll
-      for (int j = 0; j < kQPer; j += 4) {
-        const v4f v = *(const v4f*)(srow + pb + j);
-        sc[j] = v[0]; sc[j + 1] = v[1]; sc[j + 2] = v[2]; sc[j + 3] = v[3];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < kQPer; ++j) sc[j] = (pb + j < n_cand) ? srow[pb + j] : 0.f;
-    }
-    int32_t blk[kQPer / 8];
-#pragma unroll
-    for (int j = 0; j < kQPer / 8; ++j)
-      blk[j] = (cand_blocks && pb + 8 * j < n_cand) ? cand_blocks[(int64_t)q * n_blocks + ((pb >> 3) + j)] : 0;
     unsigned long long comp[kQPer];
     unsigned cnt = 0;
 #pragma unroll
@@ -528,6 +532,22 @@ __global__ __launch_bounds__(NQ) void k_select_query(const float* __restrict__ s
       }
     }
     m += total;
+  };
+  for (int64_t i = 0; i < n_full; i += 2) {
+    if (i + 1 < n_full) load_full(scB, bkB, (i + 1) * kStep);
+    process(scA, bkA, i * kStep);
+    if (i + 1 >= n_full) break;
+    if (i + 2 < n_full) load_full(scA, bkA, (i + 2) * kStep);
+    process(scB, bkB, (i + 1) * kStep);
+  }
+  for (int64_t p0 = n_full * kStep; p0 < n_cand; p0 += kStep) {  // ragged or unaligned passes
+    const int64_t pb = p0 + (int64_t)tid * kQPer;
+#pragma unroll
+    for (int j = 0; j < kQPer; ++j) scA[j] = (pb + j < n_cand) ? srow[pb + j] : 0.f;
+#pragma unroll
+    for (int j = 0; j < kQPer / 8; ++j)
+      bkA[j] = (cand_blocks && pb + 8 * j < n_cand) ? cand_blocks[(int64_t)q * n_blocks + ((pb >> 3) + j)] : 0;
+    process(scA, bkA, p0);
   }
   __syncthreads();
 
@@ -595,6 +615,7 @@ hipError_t launch_select(const float* scores, int Q, int64_t n_cand, int64_t n_e
                          unsigned* counts, unsigned long long* cand, int32_t* idx, float* top_scores, hipStream_t s) {
   if (Q <= 0) return hipSuccess;
   // one workgroup per query when that fills the chip or the lists are short
+  // (a single CU compacts ~20 vector ops per candidate)
   if (n_cand <= kQMaxCand && (Q >= 64 || n_cand <= 16384)) {
     k_select_query<<<(unsigned)Q, NQ, 0, s>>>(scores, n_cand, n_entries, cand_blocks, n_blocks, n_valid, k, gmax,
                                              sp.n_groups, cand, idx, top_scores);
