@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
   const int64_t w0p = ((int64_t)blockIdx.x * 4 + wave) * a.wave_span;
   if (w0p >= a.n_cand) return;
   const int64_t w1p = min(w0p + a.wave_span, a.n_cand);
-  unsigned gm = 0u;
+  float gm = -__builtin_inff();
 
   // Key loads run one batch of UNROLL groups ahead of the matrix cores (two
   // statically indexed buffers, alternated by a 2x unrolled loop). Loads are
@@ -127,24 +127,24 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
       c1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1, B, c1, 4, 4, 0, sa1, 0, sb);
       float sc = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sc = fmaf(w0[r], fmaxf(c0[r], 0.f), sc);
+      for (int r = 0; r < 4; ++r) sc = fmaf(w0[r], relu_bits(c0[r]), sc);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sc = fmaf(w1[r], fmaxf(c1[r], 0.f), sc);
+      for (int r = 0; r < 4; ++r) sc = fmaf(w1[r], relu_bits(c1[r]), sc);
       sc = add_xor16(sc);
       sc = add_xor32(sc);
       // every lane now holds the score of entry r16 of this group
-      if (kb == 0) s_score[wave][gp - w0p + r16] = ok[u] ? sc : -__builtin_inff();
+      const float sv = ok[u] ? sc : -__builtin_inff();
+      if (kb == 0) s_score[wave][gp - w0p + r16] = sv;
       if (a.gmax) {
-        gm = max(gm, ok[u] ? score_key(sc) : 0u);
+        // running maximum as a float (invalid entries are -inf; a NaN score
+        // can only lower it, which keeps the selection bound valid); the
+        // order key is formed once per sub-chunk
+        gm = fmaxf(gm, sv);
         const int64_t gend = gp + 16;
         if ((gend & (a.group - 1)) == 0 || gend >= w1p) {
-          unsigned v = gm;
-          v = max(v, (unsigned)__shfl_xor((int)v, 1, 64));
-          v = max(v, (unsigned)__shfl_xor((int)v, 2, 64));
-          v = max(v, (unsigned)__shfl_xor((int)v, 4, 64));
-          v = max(v, (unsigned)__shfl_xor((int)v, 8, 64));
-          if (lane == 0) s_gmax[wave][(gp - w0p) / a.group] = v;
-          gm = 0u;
+          const float v = row16_max(gm);
+          if (lane == 0) s_gmax[wave][(gp - w0p) / a.group] = (v == -__builtin_inff()) ? 0u : score_key(v);
+          gm = -__builtin_inff();
         }
       }
     }
