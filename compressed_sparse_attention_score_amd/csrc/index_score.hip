@@ -174,7 +174,11 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
 // (lane l holds rows 4*(l/16)..+3 of column l%16) leaves each lane with heads
 // 4hb..4hb+3 of query l/16 for entry l%16. So ReLU and the weighted head sum
 // stay inside the lane, with no cross-lane step. Each wave keeps 8 queries'
-// operands and weights in registers and walks an entry range; the range index
+// operands and weights in registers; the workgroup walks an entry range in
+// batches of 64 keys that all four waves share: each batch is loaded once,
+// cooperatively, one batch ahead into registers and then into a
+// double-buffered LDS stage (one barrier per batch), and every wave reads its
+// B fragments from LDS (64 lanes read one contiguous 1 KiB). The range index
 // runs fastest in the grid, so with a multiple of 8 ranges each XCD's L2
 // serves 1/8 of the key cache.
 namespace {
@@ -182,8 +186,10 @@ constexpr int kQSets = 2;  // 4-query sets per wave
 constexpr int kTileUnroll = 4;  // 16-entry steps per load batch
 }  // namespace
 
-template <bool GMAX, int QSETS = kQSets, int TU = kTileUnroll>
+template <bool GMAX, int QSETS = kQSets, int BB = kTileUnroll>
 __global__ __launch_bounds__(256) void k_index_score_qtile(ScoreArgs a, int range) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][BB * 16 * 64];
+  __shared__ unsigned s_scl[2][BB * 16];
   constexpr int kQPerWave = 4 * QSETS;
   constexpr int kQPerWg = 4 * kQPerWave;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -191,7 +197,9 @@ __global__ __launch_bounds__(256) void k_index_score_qtile(ScoreArgs a, int rang
   const int q0 = blockIdx.y * kQPerWg + wave * kQPerWave;
   const int64_t e_begin = (int64_t)blockIdx.x * range;
   const int64_t e_end = min(e_begin + range, a.n_cand);
-  if (q0 >= a.Q || e_begin >= e_end) return;
+  // Every wave takes part in the batch loads and barriers below, also one
+  // whose queries are past Q (its operands are zero and it stores nothing).
+  if (e_begin >= e_end) return;
 
   // A operands: set s, head block hb -> row r16 = query q0+4s+r16/4, head 4hb+r16%4
   v8i A[QSETS][8];
@@ -242,23 +250,39 @@ __global__ __launch_bounds__(256) void k_index_score_qtile(ScoreArgs a, int rang
   int step_in_group = 0;
   int64_t gidx = e_begin / a.group;
 
-  v4u bcA[TU], bcB[TU];
-  unsigned bsA[TU], bsB[TU];
-  auto issue = [&](v4u* bc, unsigned* bs, int off0) {
+  // cooperative batch loads: batch = BB*16 entries; thread t loads code chunks
+  // t and t+256 (16 B each: entry c/4, quarter c%4) and, t < BB*16, one scale dword
+  constexpr int kEnt = BB * 16;
+  constexpr int kChunks = kEnt * 4;
+  v4u pf[kChunks / 256];
+  unsigned pfs = 0u;
+  const int tid = threadIdx.x;
+  auto gload = [&](int off0) {
 #pragma unroll
-    for (int u = 0; u < TU; ++u) {
-      const int64_t e = e_begin + min(off0 + 16 * u + r16, span - 1);  // rows past the range are not stored
-      bc[u] = *(const v4u*)(a.key_codes + e * 64 + kb * 16);
-      bs[u] = *(const unsigned*)(a.key_scales + e * 4);
+    for (int i = 0; i < kChunks / 256; ++i) {
+      const int c = tid + 256 * i;
+      const int64_t e = e_begin + min(off0 + (c >> 2), span - 1);
+      pf[i] = *(const v4u*)(a.key_codes + e * 64 + (c & 3) * 16);
+    }
+    if (tid < kEnt) {
+      const int64_t e = e_begin + min(off0 + tid, span - 1);
+      pfs = *(const unsigned*)(a.key_scales + e * 4);
     }
   };
-  auto compute = [&](const v4u* bc, const unsigned* bs, int off0) {
+  auto lstore = [&](int st) {
 #pragma unroll
-    for (int u = 0; u < TU; ++u) {
+    for (int i = 0; i < kChunks / 256; ++i) *(v4u*)(&s_codes[st][(tid + 256 * i) * 16]) = pf[i];
+    if (tid < kEnt) s_scl[st][tid] = pfs;
+  };
+  auto compute = [&](int st, int off0) {
+#pragma unroll
+    for (int u = 0; u < BB; ++u) {
       const int off = off0 + 16 * u;
       if (off >= span) break;
-      const v8i B = {(int)bc[u][0], (int)bc[u][1], (int)bc[u][2], (int)bc[u][3], 0, 0, 0, 0};
-      const int sb = (int)((bs[u] >> (8 * kb)) & 0xFFu);
+      const v4u bc = *(const v4u*)(&s_codes[st][(16 * u + r16) * 64 + kb * 16]);
+      const unsigned bs = s_scl[st][16 * u + r16];
+      const v8i B = {(int)bc[0], (int)bc[1], (int)bc[2], (int)bc[3], 0, 0, 0, 0};
+      const int sb = (int)((bs >> (8 * kb)) & 0xFFu);
       const int p = off + r16;
       const bool in_range = p < span;
       // the query sets interleaved: independent MFMAs in flight
@@ -301,14 +325,17 @@ __global__ __launch_bounds__(256) void k_index_score_qtile(ScoreArgs a, int rang
       }
     }
   };
-  constexpr int kStep = 16 * TU;
-  issue(bcA, bsA, 0);
-  for (int g0 = 0; g0 < span; g0 += 2 * kStep) {
-    if (g0 + kStep < span) issue(bcB, bsB, g0 + kStep);
-    compute(bcA, bsA, g0);
-    if (g0 + kStep >= span) break;
-    if (g0 + 2 * kStep < span) issue(bcA, bsA, g0 + 2 * kStep);
-    compute(bcB, bsB, g0 + kStep);
+  constexpr int kStep = 16 * BB;
+  gload(0);
+  lstore(0);
+  if (kStep < span) gload(kStep);
+  int st = 0;
+  for (int g0 = 0; g0 < span; g0 += kStep) {
+    __syncthreads();  // stage st holds this batch; stage st^1 is free
+    if (g0 + kStep < span) lstore(st ^ 1);
+    if (g0 + 2 * kStep < span) gload(g0 + 2 * kStep);
+    compute(st, g0);
+    st ^= 1;
   }
 }
 
