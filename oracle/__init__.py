@@ -43,6 +43,8 @@ def _bind(L):
     L.orc_sparse_attn.argtypes = [i32, i64, i64, vp, vp, i32, vp, vp, i64, i32, dbl, vp, vp, vp, vp]
     L.orc_decode.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp, i64, i32, dbl, vp, vp,
                              vp, vp, vp]
+    L.orc_quantize_main.argtypes = [vp, i64, vp]
+    L.orc_quantize_index.argtypes = [vp, i64, vp, vp]
     L.orc_set_threads.argtypes = [i32]
     L.orc_get_threads.restype = i32
     return L
@@ -109,6 +111,23 @@ def dequant_index(codes: np.ndarray, scales: np.ndarray, L=None):
     b = np.empty((n, 128), np.uint16)
     (L or lib()).orc_dequant_index(_p(codes), _p(scales), n, _p(f), _p(b))
     return f, b
+
+
+def quantize_main(x: np.ndarray, L=None) -> np.ndarray:
+    """fp32 latents [n][512] -> main entries [n][288] (uint8)."""
+    x = np.ascontiguousarray(x, np.float32).reshape(-1, 512)
+    out = np.empty((x.shape[0], 288), np.uint8)
+    (L or lib()).orc_quantize_main(_p(x), x.shape[0], _p(out))
+    return out
+
+
+def quantize_index(x: np.ndarray, L=None):
+    """fp32 indexer keys [n][128] -> (codes [n][64], E8M0 scales [n][4])."""
+    x = np.ascontiguousarray(x, np.float32).reshape(-1, 128)
+    codes = np.empty((x.shape[0], 64), np.uint8)
+    scales = np.empty((x.shape[0], 4), np.uint8)
+    (L or lib()).orc_quantize_index(_p(x), x.shape[0], _p(codes), _p(scales))
+    return codes, scales
 
 
 def _i32(a):

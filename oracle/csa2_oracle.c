@@ -30,6 +30,14 @@
  *      latent is both key and value; RoPE is outside this path.
  *   R8 selected ids outside [0, n_entries) (the -1 padding) are skipped; an
  *      empty joint set gives a zero output and lse = -inf.
+ *   R9 writing a new entry (fp32 in): a main block's E4M3 scale is the
+ *      E4M3FN value nearest to amax/6 (ties to the even code, saturating at
+ *      448); an indexer block's E8M0 scale is 2^e for the smallest e in
+ *      [-127, 127] with 6 * 2^e >= amax (e = 0 for an all-zero block); each
+ *      element takes the E2M1 magnitude nearest to |x| / scale (ties to the
+ *      even code, saturating at 6) and the sign bit of x; a block whose scale
+ *      is zero (main) or whose amax is zero (indexer) gets all-zero codes.
+ *      NaN counts as a zero magnitude, +-inf as the largest one.
  */
 #include <math.h>
 #include <stdint.h>
@@ -125,6 +133,105 @@ ORC_API void orc_dequant_index(const uint8_t* codes, const uint8_t* scales, int6
     for (int c = 0; c < 128; ++c) {
       if (out_f32) out_f32[(size_t)i * 128 + c] = (float)v[c];
       if (out_bf16) out_bf16[(size_t)i * 128 + c] = f64_to_bf16(v[c]);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------ O7 --- */
+/* Cache write: quantise new fp32 entries into the two stored formats
+ * ([ATLAS] "The KV cache" and Full-layer cache bullet give the formats; the
+ * rounding rule is reading R9). Brute force: every candidate code is tried
+ * and the nearest kept, so the result is the definition itself. */
+
+static int e2m1_is_better(double d, unsigned m, double best_d, unsigned best_m) {
+  return d < best_d || (d == best_d && (m & 1u) == 0 && (best_m & 1u) == 1);
+}
+
+/* Nearest E2M1 magnitude code (0..7) to |x| / s, s > 0; compared as
+ * |x| against s * value so that no quotient is rounded. Magnitudes above the
+ * largest value 6 are first brought down to it (saturation). */
+static unsigned e2m1_nearest_mag(double ax, double s) {
+  if (isnan(ax)) return 0;
+  if (ax > 6.0 * s) ax = 6.0 * s;
+  unsigned best = 0;
+  double best_d = INFINITY;
+  for (unsigned m = 0; m < 8; ++m) {
+    double d = fabs(ax - s * orc_e2m1(m));
+    if (e2m1_is_better(d, m, best_d, best)) { best = m; best_d = d; }
+  }
+  return best;
+}
+
+/* Nearest finite non-negative E4M3FN code (0..0x7E) to amax / 6, after
+ * bringing amax / 6 down to the largest finite value 448 (saturation). */
+static unsigned e4m3_scale_code(double amax) {
+  if (amax > 6.0 * 448.0) amax = 6.0 * 448.0;
+  unsigned best = 0;
+  double best_d = INFINITY;
+  for (unsigned c = 0; c <= 0x7E; ++c) {
+    double d = fabs(amax - 6.0 * orc_e4m3(c));
+    if (e2m1_is_better(d, c, best_d, best)) { best = c; best_d = d; }
+  }
+  return best;
+}
+
+static double abs_or_zero(float x) { return isnan(x) ? 0.0 : fabs((double)x); }
+
+static void put_code(uint8_t* codes, int ch, float x, unsigned mag) { /* R1 */
+  unsigned code = mag | (signbit(x) ? 8u : 0u);
+  codes[ch >> 1] |= (uint8_t)(code << ((ch & 1) ? 4 : 0));
+}
+
+/* n main latents [n][512] fp32 -> n entries of 288 bytes. */
+ORC_API void orc_quantize_main(const float* x, int64_t n, uint8_t* entries) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    const float* xi = x + (size_t)i * 512;
+    uint8_t* out = entries + (size_t)i * 288;
+    memset(out, 0, 288);
+    for (int g = 0; g < 32; ++g) {
+      double amax = 0.0;
+      for (int c = 0; c < 16; ++c) {
+        double a = abs_or_zero(xi[16 * g + c]);
+        if (a > amax) amax = a;
+      }
+      unsigned sc = e4m3_scale_code(amax);
+      out[256 + g] = (uint8_t)sc;
+      double s = orc_e4m3(sc);
+      if (s == 0.0) continue;
+      for (int c = 0; c < 16; ++c) {
+        int ch = 16 * g + c;
+        put_code(out, ch, xi[ch], e2m1_nearest_mag(fabs((double)xi[ch]), s));
+      }
+    }
+  }
+}
+
+/* n indexer keys [n][128] fp32 -> codes [n][64] and E8M0 scales [n][4]. */
+ORC_API void orc_quantize_index(const float* x, int64_t n, uint8_t* codes, uint8_t* scales) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    const float* xi = x + (size_t)i * 128;
+    uint8_t* co = codes + (size_t)i * 64;
+    memset(co, 0, 64);
+    for (int g = 0; g < 4; ++g) {
+      double amax = 0.0;
+      for (int c = 0; c < 32; ++c) {
+        double a = abs_or_zero(xi[32 * g + c]);
+        if (a > amax) amax = a;
+      }
+      int e = 0;
+      if (amax > 0.0) {
+        e = -127;
+        while (e < 127 && 6.0 * ldexp(1.0, e) < amax) ++e;
+      }
+      scales[(size_t)i * 4 + g] = (uint8_t)(e + 127);
+      if (amax == 0.0) continue;
+      double s = ldexp(1.0, e);
+      for (int c = 0; c < 32; ++c) {
+        int ch = 32 * g + c;
+        put_code(co, ch, xi[ch], e2m1_nearest_mag(fabs((double)xi[ch]), s));
+      }
     }
   }
 }

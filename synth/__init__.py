@@ -66,6 +66,7 @@ def lib():
         L.syn_bf16_normal.argtypes = [u64, i32, u64, i64, i64, vp]
         L.syn_pool_blocks.argtypes = [u64, u64, i64, i64, vp]
         L.syn_bf16_rows.argtypes = [u64, i32, u64, i64, i64, i32, vp]
+        L.syn_f32_rows.argtypes = [u64, i32, u64, i64, i64, i32, vp]
         _lib = L
     return _lib
 
@@ -125,6 +126,15 @@ def bf16_normal(seed: int, tid: int, seq: int, first: int, n: int) -> np.ndarray
 def bf16_rows(seed: int, tid: int, seq: int, first_row: int, n_rows: int, width: int) -> np.ndarray:
     out = np.empty((n_rows, width), np.uint16)
     lib().syn_bf16_rows(seed, tid, seq, first_row, n_rows, width, _p(out))
+    return out
+
+
+def f32_rows(seed: int, tid: int, seq: int, first_row: int, n_rows: int, width: int) -> np.ndarray:
+    """fp32 N(0,1) rows; on streams TID_MAIN / TID_IKEY (width 512 / 128) these
+    are the unquantised sources of the stored entries ``first_row ...``."""
+    assert width % 2 == 0
+    out = np.empty((n_rows, width), np.float32)
+    lib().syn_f32_rows(seed, tid, seq, first_row, n_rows, width, _p(out))
     return out
 
 

@@ -240,6 +240,23 @@ static uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+/* fp32 N(0,1) rows: rows [first_row, first_row + n_rows) of width `width`
+ * (even) of stream (tid, seq), row r using elements r*width + c. On the
+ * main-latent and indexer-key streams these are the unquantised values the
+ * stored cache entries were made from, rounded to fp32. */
+SYN_API void syn_f32_rows(uint64_t seed, int tid, uint64_t seq, int64_t first_row, int64_t n_rows, int width,
+                          float* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    double x[1024];
+    for (int c0 = 0; c0 < width; c0 += 1024) {
+      int n = width - c0 < 1024 ? width - c0 : 1024;
+      ctr_normals(seed, (uint64_t)tid, seq, (uint64_t)(first_row + r) * (uint64_t)width + (uint64_t)c0, n, x);
+      for (int c = 0; c < n; ++c) out[(size_t)r * (size_t)width + (size_t)(c0 + c)] = (float)x[c];
+    }
+  }
+}
+
 /* bf16 N(0,1) values: element `first + i` of stream (tid, seq). */
 SYN_API void syn_bf16_normal(uint64_t seed, int tid, uint64_t seq, int64_t first, int64_t n, uint16_t* out) {
 #pragma omp parallel for schedule(static)

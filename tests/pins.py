@@ -357,5 +357,116 @@ def check_decode_composition(L, seed=17):
         assert list(idx[i]) == _ref_topk(ref[i].astype(np.float32), range(wl.n_entries), 512)
 
 
+# ------------------------------------------------------------- cache write ---
+
+_E2M1_MIDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+# Nearest E2M1 codes (OCP MX: round to nearest, ties to even) at the midpoints
+# of the value table, and just below / just above them.
+_AT_MID = [0, 2, 2, 4, 4, 6, 6]
+_BELOW_MID = [0, 1, 2, 3, 4, 5, 6]
+_ABOVE_MID = [1, 2, 3, 4, 5, 6, 7]
+
+
+def _lib_e4m3_encode(v: np.ndarray) -> np.ndarray:
+    """torch's float32 -> float8_e4m3fn conversion (RNE), as code bytes."""
+    t = torch.from_numpy(np.ascontiguousarray(v, np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def check_quantize(L, seed=21):
+    # (1) quantising the fp32-rounded sources reproduces the generator's stored
+    # entries (an independent implementation of the same rule, from fp64)
+    xm = synth.f32_rows(seed, synth.TID_MAIN, 0, 0, 600, 512)
+    ent = synth.main_latents(seed, 0, 0, 600)
+    assert np.array_equal(oracle.quantize_main(xm, L), ent)
+    xk = synth.f32_rows(seed, synth.TID_IKEY, 0, 0, 600, 128)
+    kc, ks = synth.index_keys(seed, 0, 0, 600)
+    c, sc = oracle.quantize_index(xk, L)
+    assert np.array_equal(c, kc) and np.array_equal(sc, ks)
+    # (2) re-quantising dequantised entries gives them back: byte for byte for
+    # main entries (their largest code is always 6); by value for indexer keys,
+    # whose ceil-log2 scale drops by one where a block's largest code is <= 3
+    assert np.array_equal(oracle.quantize_main(ref_dequant_main(ent).astype(np.float32), L), ent)
+    d = ref_dequant_index(kc, ks)
+    c, sc = oracle.quantize_index(d.astype(np.float32), L)
+    assert np.array_equal(ref_dequant_index(c, sc), d)
+    top = np.abs(d).reshape(-1, 4, 32).max(axis=2) > 3 * lib_e8m0(ks)
+    assert top.any() and (~top).any() and np.array_equal(sc[top], ks[top])
+    assert np.array_equal(sc[~top].astype(int), ks[~top].astype(int) - 1)
+    # (3) the element error is at most half the local E2M1 spacing of x / s
+    q = oracle.quantize_main(xm, L)
+    s = np.repeat(lib_e4m3(q[:, 256:]), 16, axis=1)
+    y = np.abs(xm.astype(np.float64)) / s
+    err = np.abs(np.abs(ref_dequant_main(q)) / s - y)
+    half = np.where(y <= 2, 0.25, np.where(y <= 4, 0.5, 1.0))
+    assert np.all((err <= half) | (y >= 6))
+
+    # (4) main scales: every finite E4M3 code, its midpoints, saturation, and
+    # torch's own conversion of amax / 6 on random magnitudes
+    vals = lib_e4m3(np.arange(0x7F, dtype=np.uint8))
+    amax = [6 * vals, 6 * (vals[:-1] + vals[1:]) / 2, np.array([6 * 448 * 1.01, 6 * 480.0, 1e30, np.inf])]
+    want = [np.arange(0x7F), [c if c % 2 == 0 else c + 1 for c in range(0x7E)], [0x7E] * 4]
+    rng = np.random.default_rng(seed)
+    r = np.exp2(rng.uniform(-12, 11, 4000)).astype(np.float32)
+    amax.append(r)
+    want.append(_lib_e4m3_encode((r.astype(np.float64) / 6).astype(np.float32)))
+    a = np.concatenate(amax).astype(np.float32)
+    w = np.concatenate([np.asarray(v, np.int64) for v in want])
+    pad = (-len(a)) % 32
+    a = np.concatenate([a, np.zeros(pad, np.float32)])
+    w = np.concatenate([w, np.zeros(pad, np.int64)])
+    x = np.zeros((len(a) // 32, 512), np.float32)
+    x.reshape(-1, 32, 16)[:, :, 5] = -a.reshape(-1, 32)  # amax is a magnitude
+    got = oracle.quantize_main(x, L)[:, 256:].reshape(-1)
+    assert np.array_equal(got.astype(np.int64), w), np.nonzero(got.astype(np.int64) != w)
+
+    # (5) element codes at a scale of exactly 1 (amax 6): ties, neighbours, signs
+    row = np.zeros((3, 512), np.float32)
+    tie = [6.0, *_E2M1_MIDS, *(-_E2M1_MIDS), -0.0]
+    row[0, :16] = tie
+    row[1, :16] = [6.0, *np.nextafter(_E2M1_MIDS.astype(np.float32), np.float32(0)), 0, 0, 0, 0, 0, 0, 0, np.nan]
+    row[2, :16] = [6.0, *np.nextafter(_E2M1_MIDS.astype(np.float32), np.float32(np.inf)), *([0.0] * 7), 6.3]
+    # a block whose scale rounds to zero, and one saturated at 448
+    row[0, 16:32] = [-1e-4, 2e-4, -3e-4, *([0.0] * 13)]
+    row[0, 32:48] = [6000.0, 2700.0, 2000.0, -6000.0, *([0.0] * 12)]
+    row[0, 48:64] = [np.inf, 448.0, 224.0, *([0.0] * 13)]
+    q = oracle.quantize_main(row, L)
+    codes = nibbles(q[:, :256])
+    assert list(q[:, 256]) == [0x38, 0x38, 0x38]
+    assert list(codes[0, :16]) == [7, *_AT_MID, *(8 | np.array(_AT_MID)), 8]
+    assert list(codes[1, :16]) == [7, *_BELOW_MID, *([0] * 7), 0]
+    assert list(codes[2, :16]) == [7, *_ABOVE_MID, *([0] * 7), 7]
+    assert q[0, 257] == 0 and not codes[0, 16:32].any()
+    assert q[0, 258] == 0x7E and list(codes[0, 32:36]) == [7, 7, 6, 15]
+    assert q[0, 259] == 0x7E and list(codes[0, 48:51]) == [7, 2, 1]
+
+    # (6) indexer scales: exact powers of two, the next float up, clamps, zero
+    es = np.arange(-127, 126)  # 6 * 2^126 is beyond the fp32 range
+    a = np.concatenate([6 * np.exp2(es), np.nextafter((6 * np.exp2(es[:-1])).astype(np.float32), np.float32(np.inf)),
+                        [1e-45, 0.0, 3e38]]).astype(np.float32)
+    w = np.concatenate([es + 127, es[:-1] + 128, [0, 127, 253]])
+    r = np.exp2(rng.uniform(-60, 60, 3000)).astype(np.float32)
+    a = np.concatenate([a, r])
+    # smallest e with 6 * 2^e >= amax, from Python's exact frexp
+    w = np.concatenate([w, [(lambda m, e: e + 127 - (m == 0.5))(*math.frexp(float(v) / 6.0)) for v in r]])
+    pad = (-len(a)) % 4
+    a = np.concatenate([a, np.zeros(pad, np.float32)])
+    w = np.concatenate([w, np.full(pad, 127)])
+    x = np.zeros((len(a) // 4, 128), np.float32)
+    x.reshape(-1, 4, 32)[:, :, 31] = a.reshape(-1, 4)
+    _, sc = oracle.quantize_index(x, L)
+    assert np.array_equal(sc.reshape(-1).astype(np.int64), w)
+    # element codes at scale 2^0 (amax 6), and at 2^-3 (amax 0.75)
+    x = np.zeros((2, 128), np.float32)
+    x[0, :16] = tie
+    x[1, :8] = [0.75, *(_E2M1_MIDS / 8)]
+    x[1, 64:80] = [-0.0] * 16  # all-zero block: scale 2^0, codes 0
+    c, sc = oracle.quantize_index(x, L)
+    cc = nibbles(c)
+    assert list(sc[0]) == [127, 127, 127, 127] and list(sc[1]) == [124, 127, 127, 127]
+    assert list(cc[0, :16]) == [7, *_AT_MID, *(8 | np.array(_AT_MID)), 8]
+    assert list(cc[1, :8]) == [7, *_AT_MID] and not cc[1, 64:80].any()
+
+
 ALL_CHECKS = [check_format_tables, check_layout, check_dequant, check_index_scores, check_candidate_sets,
-              check_topk, check_attention, check_decode_composition]
+              check_topk, check_attention, check_decode_composition, check_quantize]

@@ -33,6 +33,17 @@ MUTANTS = [
     ("swa_row_stride", "swa + (size_t)((int64_t)qi * swa_q_stride + r) * 512", "swa + (size_t)((int64_t)qi * swa_q_stride) * 512"),
     ("wrong_head_query", "q_bf16[((size_t)qi * 64 + h) * 512 + c]", "q_bf16[((size_t)qi * 64 + (h ^ 1)) * 512 + c]"),
     ("lse_missing_max", "(float)(mx + log(z))", "(float)(log(z))"),
+    ("quant_ties_to_odd", "(m & 1u) == 0 && (best_m & 1u) == 1", "(m & 1u) == 1 && (best_m & 1u) == 0"),
+    ("quant_scale_over_4", "double d = fabs(amax - 6.0 * orc_e4m3(c));", "double d = fabs(amax - 4.0 * orc_e4m3(c));"),
+    ("quant_no_e4m3_saturation", "if (amax > 6.0 * 448.0) amax = 6.0 * 448.0;", ""),
+    ("quant_mx_floor_at_powers", "6.0 * ldexp(1.0, e) < amax", "6.0 * ldexp(1.0, e) <= amax"),
+    ("quant_mx_scale_over_4", "6.0 * ldexp(1.0, e) < amax", "4.0 * ldexp(1.0, e) < amax"),
+    ("quant_sign_of_zero", "signbit(x) ? 8u : 0u", "(x < 0.0f) ? 8u : 0u"),
+    ("quant_nibble_order", "codes[ch >> 1] |= (uint8_t)(code << ((ch & 1) ? 4 : 0));",
+     "codes[ch >> 1] |= (uint8_t)(code << ((ch & 1) ? 0 : 4));"),
+    ("quant_zero_scale_codes", "if (s == 0.0) continue;", ""),
+    ("quant_amax_one_channel", "double a = abs_or_zero(xi[16 * g + c]);", "double a = abs_or_zero(xi[16 * g]);"),
+    ("quant_mx_zero_block", "if (amax > 0.0) {\n        e = -127;", "if (amax >= 0.0) {\n        e = -127;"),
 ]
 
 
