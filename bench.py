@@ -51,6 +51,7 @@ SCORE_SOURCES = ("index_score.hip", "csa2_device.h")
 CSRC = os.path.join(ROOT, "compressed_sparse_attention_score_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_index_score_hbm_traffic.md")
 COPY_MIB = 512
+CACHE_WRITE_ROWS = 131072           # new entries quantised per cache-write launch (a long prefill chunk)
 
 
 # ------------------------------------------------------------------ helpers
@@ -330,7 +331,7 @@ def main():
                      dtype=torch.uint8, device="cuda")
     K, W = args.steps, args.warmup
     S = min(K, 50)
-    ev = HipEvents(2 + 4 * S + 4)
+    ev = HipEvents(2 + 4 * S + 8)
 
     # ---- phase 1: timed decode steps
     dec_args = [reps[i % R].decode_args(out, lse, idx) for i in range(R)]
@@ -386,6 +387,28 @@ def main():
     ev.record(e0 + 3, stream)
     torch.cuda.synchronize()
     attn_ms = ev.ms(e0 + 2, e0 + 3) / K
+    # ---- phase 4: cache write of a long prefill chunk's new entries (not part
+    # of the step): fp32 rows -> FP4 main entries and indexer keys
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4242)
+    xm = torch.randn((CACHE_WRITE_ROWS, 512), generator=gen, device="cuda")
+    xk = torch.randn((CACHE_WRITE_ROWS, 128), generator=gen, device="cuda")
+    qm = torch.empty((CACHE_WRITE_ROWS, 288), dtype=torch.uint8, device="cuda")
+    qc = torch.empty((CACHE_WRITE_ROWS, 64), dtype=torch.uint8, device="cuda")
+    qs = torch.empty((CACHE_WRITE_ROWS, 4), dtype=torch.uint8, device="cuda")
+    qargs = [(0, xm, qm, None), (1, xk, qc, qs)]
+    q_ms = []
+    for j, (kind, xin, co, so) in enumerate(qargs):
+        for _ in range(3):
+            csa.csa2_quantize(kind, xin, csa.CSA2_IN_F32, CACHE_WRITE_ROWS, None, CACHE_WRITE_ROWS, co, so, stream)
+        torch.cuda.synchronize()
+        ev.record(e0 + 4 + 2 * j, stream)
+        for _ in range(K):
+            csa.csa2_quantize(kind, xin, csa.CSA2_IN_F32, CACHE_WRITE_ROWS, None, CACHE_WRITE_ROWS, co, so, stream)
+        ev.record(e0 + 5 + 2 * j, stream)
+        torch.cuda.synchronize()
+        q_ms.append(ev.ms(e0 + 4 + 2 * j, e0 + 5 + 2 * j) / K)
+    del xm, xk, qm, qc, qs
     ev.close()
     if args.copy_calibration:
         src = torch.ones(COPY_MIB << 18, dtype=torch.float32, device="cuda")
@@ -411,6 +434,13 @@ def main():
                         "algorithmic_bytes": work["attn_bytes"], "GB_s": round(attn_gbs, 1),
                         "hbm_frac": round(attn_gbs / HBM_PEAK_GBS, 4)},
     }
+    for kname, kind, ms_ in (("quantize_main", "k_quantize_main", q_ms[0]), ("quantize_index", "k_quantize_index",
+                                                                             q_ms[1])):
+        per_row = (512 * 4 + ENTRY_BYTES_MAIN) if kname == "quantize_main" else (128 * 4 + ENTRY_BYTES_INDEX)
+        qb = CACHE_WRITE_ROWS * per_row
+        kernels[kname] = {"kernels": [kind], "rows": CACHE_WRITE_ROWS, "us_per_launch": round(1e3 * ms_, 3),
+                          "algorithmic_bytes": qb, "GB_s": round(qb / (ms_ * 1e-3) / 1e9, 1),
+                          "hbm_frac": round(qb / (ms_ * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     traffic = recorded_traffic(name)
     if prefill:
         roof = {"bound": "mfma", "achieved": round(score_tfs, 2), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",

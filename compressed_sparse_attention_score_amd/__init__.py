@@ -19,8 +19,9 @@ LIB_PATH = os.path.join(_PKG, "libcsa2.so")
 CSA2_OK, CSA2_ERR_NULL, CSA2_ERR_SHAPE, CSA2_ERR_ALIGN, CSA2_ERR_WORKSPACE, CSA2_ERR_HIP, CSA2_ERR_ARG = range(7)
 CSA2_KIND_MAIN, CSA2_KIND_INDEX = 0, 1
 CSA2_OUT_F32, CSA2_OUT_BF16 = 0, 1
+CSA2_IN_F32, CSA2_IN_BF16 = 0, 1
 CSA2_WS_TOPK, CSA2_WS_ATTN, CSA2_WS_DECODE = 0, 1, 2
-EXPORTED = ("csa2_dequant", "csa2_index_score", "csa2_topk", "csa2_sparse_attn", "csa2_decode",
+EXPORTED = ("csa2_dequant", "csa2_quantize", "csa2_index_score", "csa2_topk", "csa2_sparse_attn", "csa2_decode",
             "csa2_workspace_size", "csa2_status_string", "csa2_version")
 
 _vp, _i32, _i64, _sz, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
@@ -56,6 +57,7 @@ def _load():
                           "(run __graft_entry__.build() or compressed_sparse_attention_score_amd/_build.py)")
     L = ctypes.CDLL(LIB_PATH)
     L.csa2_dequant.argtypes = [ctypes.c_int, _vp, _vp, _i64, ctypes.c_int, _vp, _vp]
+    L.csa2_quantize.argtypes = [ctypes.c_int, _vp, ctypes.c_int, _i64, _vp, _i64, _vp, _vp, _vp]
     L.csa2_index_score.argtypes = [ctypes.POINTER(IndexArgs), _vp, _vp]
     L.csa2_topk.argtypes = [ctypes.POINTER(TopkArgs), _vp, _sz, _vp]
     L.csa2_sparse_attn.argtypes = [ctypes.POINTER(AttnArgs), _vp, _sz, _vp]
@@ -65,7 +67,7 @@ def _load():
     L.csa2_status_string.argtypes = [ctypes.c_int]
     L.csa2_status_string.restype = ctypes.c_char_p
     L.csa2_version.restype = ctypes.c_int
-    for name in ("csa2_dequant", "csa2_index_score", "csa2_topk", "csa2_sparse_attn", "csa2_decode"):
+    for name in ("csa2_dequant", "csa2_quantize", "csa2_index_score", "csa2_topk", "csa2_sparse_attn", "csa2_decode"):
         getattr(L, name).restype = ctypes.c_int
     return L
 
@@ -121,6 +123,12 @@ def _alloc_ws(nbytes: int, device) -> torch.Tensor | None:
 def csa2_dequant(kind: int, codes, scales, n_entries: int, out_dtype: int, out, stream=None) -> None:
     _check("csa2_dequant", lib.csa2_dequant(kind, _ptr(codes), _ptr(scales), n_entries, out_dtype, _ptr(out),
                                             _stream(stream)))
+
+
+def csa2_quantize(kind: int, x, in_dtype: int, n_entries: int, dst_rows, n_cache_rows: int, codes, scales=None,
+                  stream=None) -> None:
+    _check("csa2_quantize", lib.csa2_quantize(kind, _ptr(x), in_dtype, n_entries, _ptr(dst_rows), n_cache_rows,
+                                              _ptr(codes), _ptr(scales), _stream(stream)))
 
 
 def index_args(Q, n_entries, cache_q_stride, key_codes, key_scales, iq_codes, iq_scales, head_weights,

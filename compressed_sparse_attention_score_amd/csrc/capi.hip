@@ -206,6 +206,21 @@ int csa2_dequant(int kind, const void* codes, const void* scales, int64_t n_entr
                                    out_dtype == CSA2_OUT_BF16, out, (hipStream_t)stream));
 }
 
+int csa2_quantize(int kind, const void* x, int in_dtype, int64_t n_entries, const int64_t* dst_rows,
+                  int64_t n_cache_rows, void* codes, void* scales, void* stream) {
+  if (kind != CSA2_KIND_MAIN && kind != CSA2_KIND_INDEX) return CSA2_ERR_ARG;
+  if (in_dtype != CSA2_IN_F32 && in_dtype != CSA2_IN_BF16) return CSA2_ERR_ARG;
+  if (n_entries < 0 || n_entries > kMaxI32 || n_cache_rows < 0) return CSA2_ERR_SHAPE;
+  if (!dst_rows && n_cache_rows < n_entries) return CSA2_ERR_SHAPE;
+  if (n_entries == 0) return CSA2_OK;
+  if (!x || !codes || (kind == CSA2_KIND_INDEX && !scales)) return CSA2_ERR_NULL;
+  if (!aligned(x, in_dtype == CSA2_IN_F32 ? 16 : 8) || !aligned(codes, 16) || !aligned(scales, 4) ||
+      !aligned(dst_rows, 8))
+    return CSA2_ERR_ALIGN;
+  return hip_status(launch_quantize(kind, x, in_dtype == CSA2_IN_BF16, n_entries, dst_rows, n_cache_rows,
+                                    (uint8_t*)codes, (uint8_t*)scales, (hipStream_t)stream));
+}
+
 int csa2_index_score(const csa2_index_args* a, float* scores, void* stream) {
   int64_t n_cand = 0;
   int st = check_index(a, &n_cand);

@@ -50,6 +50,12 @@ AttnPlan plan_attn(int Q, int nj);
 hipError_t launch_dequant(int kind, const uint8_t* codes, const uint8_t* scales, int64_t n, int out_bf16, void* out,
                           hipStream_t s);
 
+// Quantise n fp32 (or bf16) rows into main entries (kind 0, cache [rows][288])
+// or indexer keys (kind 1, codes [rows][64] + scales [rows][4]); row i goes to
+// cache row rows[i] (i when rows == NULL), skipped outside [0, n_rows).
+hipError_t launch_quantize(int kind, const void* x, int in_bf16, int64_t n, const int64_t* rows, int64_t n_rows,
+                           uint8_t* codes, uint8_t* scales, hipStream_t s);
+
 // Scores [Q][n_cand] and, if gmax != NULL, the maximum selection key of each
 // sub-chunk [Q][plan.n_groups].
 hipError_t launch_index_score(const IndexLaunch& a, const ScorePlan& plan, float* scores, unsigned* gmax,

@@ -90,6 +90,36 @@ enum { CSA2_OUT_F32 = 0, CSA2_OUT_BF16 = 1 };
 CSA2_API int csa2_dequant(int kind, const void* codes, const void* scales, int64_t n_entries, int out_dtype, void* out,
                  void* stream);
 
+/* ------------------------------------------------------------ quantize */
+enum { CSA2_IN_F32 = 0, CSA2_IN_BF16 = 1 };
+
+/* csa2_quantize — write new cache entries: encode real rows into the stored
+ * formats that csa2_dequant decodes ("An infra-oriented diagram ...",
+ * Full-layer cache bullet and "The KV cache" fix the formats; the pages do not
+ * give the rounding, which is fixed here as follows).
+ *   main scale (per 16 channels): the E4M3FN value nearest to amax/6, ties to
+ *     the even code, saturating at 448;
+ *   index scale (per 32 channels): E8M0 2^e with e the smallest integer in
+ *     [-127, 127] such that 6 * 2^e >= amax (byte 127, i.e. 2^0, when the
+ *     block is all zero);
+ *   element: the E2M1 magnitude nearest to |x| / scale, ties to the even code,
+ *     saturating at 6, with the sign bit of x; every code of a block is 0 when
+ *     its main scale is 0 or its index block is all zero.
+ * NaN inputs count as zero magnitudes (keeping their sign bit), +-inf as the
+ * largest. All decisions are exact (no rounded quotient takes part), so the
+ * result is the nearest code, not an approximation of it.
+ *   kind       CSA2_KIND_MAIN:  x = [n][512]; codes = main cache [n_cache_rows][288];
+ *                               scales ignored.
+ *              CSA2_KIND_INDEX: x = [n][128]; codes = [n_cache_rows][64],
+ *                               scales = [n_cache_rows][4].
+ *   in_dtype   CSA2_IN_F32 (float, 16-B aligned) or CSA2_IN_BF16 (bf16 bits, 8-B aligned).
+ *   dst_rows   [n] int64 cache row of each input row (8-B aligned), or NULL for
+ *              row i -> cache row i (then n_cache_rows >= n). Rows outside
+ *              [0, n_cache_rows) are skipped; duplicate rows race.
+ *   Alignment: codes 16 B, scales 4 B. n_entries >= 0 (0 = no-op). */
+CSA2_API int csa2_quantize(int kind, const void* x, int in_dtype, int64_t n_entries, const int64_t* dst_rows,
+                           int64_t n_cache_rows, void* codes, void* scales, void* stream);
+
 /* --------------------------------------------------------- index score */
 typedef struct csa2_index_args {
   size_t struct_size;

@@ -81,6 +81,17 @@ def test_validation_rejects_before_launch():
     assert L.csa2_dequant(0, A + 8, None, 10, 0, A, None) == csa.CSA2_ERR_ALIGN
     assert L.csa2_dequant(0, A, None, -1, 0, A, None) == csa.CSA2_ERR_SHAPE
     assert L.csa2_dequant(0, None, None, 0, 0, None, None) == csa.CSA2_OK  # empty: no-op
+    # quantize
+    assert L.csa2_quantize(2, A, 0, 10, None, 10, A, A, None) == csa.CSA2_ERR_ARG
+    assert L.csa2_quantize(0, A, 3, 10, None, 10, A, A, None) == csa.CSA2_ERR_ARG
+    assert L.csa2_quantize(0, A, 0, 10, None, 9, A, None, None) == csa.CSA2_ERR_SHAPE  # cache too small
+    assert L.csa2_quantize(0, A, 0, -1, None, 10, A, None, None) == csa.CSA2_ERR_SHAPE
+    assert L.csa2_quantize(1, A, 0, 10, None, 10, A, None, None) == csa.CSA2_ERR_NULL
+    assert L.csa2_quantize(0, None, 0, 10, None, 10, A, None, None) == csa.CSA2_ERR_NULL
+    assert L.csa2_quantize(0, A + 8, 0, 10, None, 10, A, None, None) == csa.CSA2_ERR_ALIGN  # fp32 needs 16 B
+    assert L.csa2_quantize(0, A + 4, 1, 10, None, 10, A, None, None) == csa.CSA2_ERR_ALIGN  # bf16 needs 8 B
+    assert L.csa2_quantize(0, A, 0, 10, A + 4, 3, A, None, None) == csa.CSA2_ERR_ALIGN
+    assert L.csa2_quantize(0, None, 0, 0, None, 0, None, None, None) == csa.CSA2_OK  # empty: no-op
     # index score
     ia = csa.IndexArgs(ctypes.sizeof(csa.IndexArgs), 2, 100, 100, A, A, A, A, A, None, 0, None)
     bad = csa.IndexArgs.from_buffer_copy(ia)

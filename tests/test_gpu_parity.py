@@ -69,6 +69,147 @@ def test_dequant_index_bitexact():
     assert np.array_equal(b[~bn], b_ref[~bn])
 
 
+# ---------------------------------------------------------------- quantize
+
+_MIDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)
+
+
+def _quant_inputs(width, n, seed):
+    """Seeded fp32 rows of the cache-entry streams plus rows of edge values:
+    scales from subnormal to overflow, NaN, +-inf, -0, all-zero blocks, exact
+    E2M1 ties at every E4M3 scale and their neighbouring floats."""
+    tid = synth.TID_MAIN if width == 512 else synth.TID_IKEY
+    base = synth.f32_rows(seed, tid, 0, 0, n, width)
+    rng = np.random.default_rng(seed)
+    extra = []
+    for sc in (1e-44, 1e-40, 1e-30, 1e-6, 1e4, 1e20, 1e37):
+        with np.errstate(over="ignore"):
+            extra.append((base[:8].astype(np.float64) * sc).astype(np.float32))
+    sp = base[:16].copy()
+    flat = sp.reshape(-1)
+    flat[rng.integers(0, flat.size, 40)] = np.nan
+    flat[rng.integers(0, flat.size, 10)] = np.inf
+    flat[rng.integers(0, flat.size, 10)] = -np.inf
+    flat[rng.integers(0, flat.size, 60)] = -0.0
+    sp[3] = 0.0
+    sp[4] = -0.0
+    extra.append(sp)
+    ties = []
+    scales = [oracle.e4m3(c) for c in range(1, 0x7F)] if width == 512 else [2.0 ** e for e in range(-127, 120, 2)]
+    g = 16 if width == 512 else 32
+    for s in scales:
+        r = np.zeros(width, np.float32)
+        for b in range(width // g):
+            r[g * b] = 6 * s
+            r[g * b + 1:g * b + 8] = s * _MIDS
+            r[g * b + 8:g * b + 15] = -s * _MIDS
+        ties.append(r)
+    t = np.array(ties, np.float32)
+    extra += [t, np.nextafter(t, np.float32(np.inf)), np.nextafter(t, np.float32(-np.inf))]
+    return np.ascontiguousarray(np.concatenate([base, *extra]))
+
+
+def _quantize_gpu(kind, x, bf16=False, dst_rows=None, n_cache_rows=None, fill=0xA5):
+    n = x.shape[0]
+    rows = n if n_cache_rows is None else n_cache_rows
+    # bf16 inputs are rounded on the host so that the oracle sees the very bits
+    # the kernel reads (device and host conversions may differ in NaN signs)
+    xt = (torch.from_numpy(x).to(torch.bfloat16) if bf16 else torch.from_numpy(x)).cuda()
+    codes = torch.full((rows, 288 if kind == 0 else 64), fill, dtype=torch.uint8, device="cuda")
+    scales = torch.full((rows, 4), fill, dtype=torch.uint8, device="cuda") if kind == 1 else None
+    dr = None if dst_rows is None else torch.from_numpy(np.ascontiguousarray(dst_rows, np.int64)).cuda()
+    csa.csa2_quantize(kind, xt, 1 if bf16 else 0, n, dr, rows, codes, scales)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), (None if scales is None else scales.cpu().numpy())
+
+
+def _bf16_round(x):
+    return torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_quantize_main_bitexact(bf16):
+    x = _quant_inputs(512, 1001, seed=31)
+    got, _ = _quantize_gpu(0, x, bf16)
+    ref = oracle.quantize_main(_bf16_round(x) if bf16 else x)
+    bad = np.nonzero((got != ref).any(axis=1))[0]
+    assert bad.size == 0, f"rows {bad[:10]} differ, e.g. got {got[bad[0]][:8]} want {ref[bad[0]][:8]}"
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+def test_quantize_index_bitexact(bf16):
+    x = _quant_inputs(128, 999, seed=33)
+    got_c, got_s = _quantize_gpu(1, x, bf16)
+    ref_c, ref_s = oracle.quantize_index(_bf16_round(x) if bf16 else x)
+    assert np.array_equal(got_s, ref_s), np.nonzero((got_s != ref_s).any(axis=1))[0][:10]
+    assert np.array_equal(got_c, ref_c), np.nonzero((got_c != ref_c).any(axis=1))[0][:10]
+
+
+def test_quantize_reproduces_generated_cache():
+    """fp32 sources of seeded cache entries give back the stored entries."""
+    x = synth.f32_rows(5, synth.TID_MAIN, 0, 0, 3000, 512)
+    got, _ = _quantize_gpu(0, x)
+    assert np.array_equal(got, synth.main_latents(5, 0, 0, 3000))
+    x = synth.f32_rows(5, synth.TID_IKEY, 0, 0, 3000, 128)
+    c, s = _quantize_gpu(1, x)
+    kc, ks = synth.index_keys(5, 0, 0, 3000)
+    assert np.array_equal(c, kc) and np.array_equal(s, ks)
+
+
+@pytest.mark.parametrize("kind", [0, 1], ids=["main", "index"])
+def test_quantize_scatter_rows(kind):
+    """Rows go to dst_rows; -1 and out-of-range rows are skipped and the rest
+    of the cache is untouched."""
+    width = 512 if kind == 0 else 128
+    n, cap = 700, 2000
+    x = synth.f32_rows(9, synth.TID_MAIN if kind == 0 else synth.TID_IKEY, 1, 0, n, width)
+    rng = np.random.default_rng(9)
+    dst = rng.permutation(cap)[:n].astype(np.int64)
+    dst[::50] = -1
+    dst[7::50] = cap + 5
+    got_c, got_s = _quantize_gpu(kind, x, dst_rows=dst, n_cache_rows=cap)
+    if kind == 0:
+        ref_c, ref_s = oracle.quantize_main(x), None
+    else:
+        ref_c, ref_s = oracle.quantize_index(x)
+    ok = (dst >= 0) & (dst < cap)
+    assert np.array_equal(got_c[dst[ok]], ref_c[ok])
+    if kind == 1:
+        assert np.array_equal(got_s[dst[ok]], ref_s[ok])
+    untouched = np.setdiff1d(np.arange(cap), dst[ok])
+    assert (got_c[untouched] == 0xA5).all()
+    if kind == 1:
+        assert (got_s[untouched] == 0xA5).all()
+
+
+def test_quantize_full_size_sampled():
+    """131072 new main entries and indexer keys in one launch each (the size of
+    a long prefill chunk's cache write); sampled rows against the oracle."""
+    n = 131072
+    xm = synth.f32_rows(41, synth.TID_MAIN, 0, 0, n, 512)
+    got, _ = _quantize_gpu(0, xm)
+    rows = np.random.default_rng(41).choice(n, 1500, replace=False)
+    rows[-1] = n - 1
+    assert np.array_equal(got[rows], oracle.quantize_main(xm[rows]))
+    xk = synth.f32_rows(41, synth.TID_IKEY, 0, 0, n, 128)
+    c, s = _quantize_gpu(1, xk)
+    rc, rs = oracle.quantize_index(xk[rows])
+    assert np.array_equal(c[rows], rc) and np.array_equal(s[rows], rs)
+
+
+def test_quantize_empty_and_errors():
+    x = torch.zeros((4, 512), dtype=torch.float32, device="cuda")
+    c = torch.zeros((4, 288), dtype=torch.uint8, device="cuda")
+    csa.csa2_quantize(0, x, 0, 0, None, 0, c)  # n = 0: no-op
+    with pytest.raises(csa.Csa2Error):
+        csa.csa2_quantize(2, x, 0, 4, None, 4, c)  # bad kind
+    with pytest.raises(csa.Csa2Error):
+        csa.csa2_quantize(0, x, 0, 4, None, 3, c)  # cache smaller than n without dst_rows
+    with pytest.raises(csa.Csa2Error):
+        csa.csa2_quantize(1, x, 0, 4, None, 4, c, None)  # index keys need scales
+    assert (c.cpu() == 0).all()
+
+
 # ------------------------------------------------------------ index scores
 
 @pytest.mark.parametrize("Q,N", [(3, 5000), (1, 17), (2, 16), (1, 4096 + 37)])
