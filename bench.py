@@ -434,8 +434,8 @@ def main():
                         "algorithmic_bytes": work["attn_bytes"], "GB_s": round(attn_gbs, 1),
                         "hbm_frac": round(attn_gbs / HBM_PEAK_GBS, 4)},
     }
-    for kname, kind, ms_ in (("quantize_main", "k_quantize_main", q_ms[0]), ("quantize_index", "k_quantize_index",
-                                                                             q_ms[1])):
+    for kname, kind, ms_ in (("quantize_main", "k_quantize<f32, main>", q_ms[0]),
+                             ("quantize_index", "k_quantize<f32, index>", q_ms[1])):
         per_row = (512 * 4 + ENTRY_BYTES_MAIN) if kname == "quantize_main" else (128 * 4 + ENTRY_BYTES_INDEX)
         qb = CACHE_WRITE_ROWS * per_row
         kernels[kname] = {"kernels": [kind], "rows": CACHE_WRITE_ROWS, "us_per_launch": round(1e3 * ms_, 3),

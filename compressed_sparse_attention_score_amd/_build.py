@@ -24,8 +24,10 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-fvisibility=h
 
 
 # Per-file extra flags. The scoring kernels consume every MFMA result at once
-# in vector code, so the MFMAs write VGPRs directly instead of AGPRs.
-FILE_FLAGS = {"index_score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# in vector code, so the MFMAs write VGPRs directly instead of AGPRs. The
+# quantiser's rounding decisions rest on exact products and sums, so no
+# multiply-add may be fused there.
+FILE_FLAGS = {"index_score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "quantize.hip": ["-ffp-contract=off"]}
 
 
 def sources():

@@ -18,15 +18,19 @@
 // or 3 * (two adjacent E4M3 values) have at most 7 significant bits, so no
 // quotient is ever rounded and the result is the exact nearest code.
 //
-// Thread layout: one thread per 4 consecutive channels (one 16-B fp32 load or
-// one 8-B bf16 load), so a wave reads 1 KiB (fp32) of contiguous input. A
-// main scale group is a quad of lanes, an index scale block 8 lanes; the block
-// maximum is combined with DPP lane moves. Each lane stores its two code bytes
-// and the first lane of a group stores the scale byte.
+// Thread layout: each lane encodes 16 consecutive channels (a main scale
+// group, or half of an indexer scale block), so the scale and its thresholds
+// are worked out once per 16 values; waves stream tiles of 64 such groups
+// through LDS so that the HBM reads stay fully coalesced (see k_quantize).
 #include "csa2_device.h"
 #include "csa2_internal.h"
 
 namespace csa2 {
+
+// Workgroup cap of a quantiser launch. One tile per wave measured fastest (a
+// 131072-row write fills 16384 workgroups); only larger writes loop.
+constexpr int64_t kQuantGroups = 65536;
+
 namespace {
 
 // |x| as ordered bits, NaN -> 0 (so that integer max is the float max).
@@ -35,165 +39,238 @@ __device__ __forceinline__ unsigned mag_bits(float x) {
   return u > 0x7F800000u ? 0u : u;
 }
 
-template <int CTRL>
-__device__ __forceinline__ unsigned umax_dpp(unsigned x) {
-  return max(x, (unsigned)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, false));
+// Largest magnitude of a block, NaNs counting as zero. The plain integer max
+// of the magnitude bits is a NaN pattern only when the block holds a NaN;
+// only then is the block scanned again without them.
+template <int G>
+__device__ __forceinline__ float block_amax(const float (&f)[G]) {
+  unsigned m = 0;
+#pragma unroll
+  for (int i = 0; i < G; ++i) m = max(m, __float_as_uint(f[i]) & 0x7FFFFFFFu);
+  if (m > 0x7F800000u) {
+    m = 0;
+#pragma unroll
+    for (int i = 0; i < G; ++i) m = max(m, mag_bits(f[i]));
+  }
+  return __uint_as_float(m);
 }
 
-// Maximum over lanes 4i..4i+3 (quad_perm [1,0,3,2] then [2,3,0,1]).
-__device__ __forceinline__ unsigned quad_umax(unsigned x) { return umax_dpp<0x4E>(umax_dpp<0xB1>(x)); }
-
-// Maximum over lanes 8i..8i+7: quad maximum, then the mirrored quad of the
-// same half-row (row_half_mirror maps lane j of a half-row to lane 7-j).
-__device__ __forceinline__ unsigned oct_umax(unsigned x) { return umax_dpp<0x141>(quad_umax(x)); }
-
-// Non-negative E4M3FN code -> value (codes 0..0x7E; subnormals step 2^-9).
-__device__ __forceinline__ float e4m3_pos_value(unsigned c) {
-  return (c < 8u) ? (float)c * 0x1p-9f : __uint_as_float(((c >> 3) + 120u) << 23 | (c & 7u) << 20);
+// Non-negative E4M3FN code -> value, codes 0..0x7E: c * 2^-9 below 8, else
+// bits (c << 20) + (120 << 23) (exponent field c >> 3, mantissa c & 7).
+__device__ __forceinline__ float e4m3_pos_value(int c) {
+  float sub = (float)c * 0x1p-9f;
+  float nrm = __uint_as_float(((unsigned)c << 20) + 0x3C000000u);
+  return c < 8 ? sub : nrm;
 }
 
-// E4M3 code of the scale for a main block with maximum magnitude a (a >= 0,
-// not NaN): nearest to a/6, ties to even, saturating at 448 (code 0x7E).
+// Largest float below t when `odd`, else t: comparing y > result is y >= t
+// for an odd lower code (a tie rounds up to the even neighbour) and y > t for
+// an even one. t is a positive float (inf gives FLT_MAX).
+__device__ __forceinline__ float tie_nudge(float t, bool odd) {
+  return __uint_as_float(__float_as_uint(t) - (odd ? 1u : 0u));
+}
+
+// E4M3 code of the scale of a main block with largest magnitude a (a >= 0,
+// not NaN): nearest to a/6, ties to the even code, saturating at 448 (0x7E).
+// The floor code c of an approximate a/6 is off by at most one (the quotient
+// is within a few ulp and the E4M3 grid is 2^-3 relative, 2^-9 absolute
+// below 2^-6), so the answer lies in [c-1, c+2]: counting the exact
+// midpoints 6 * (val(k) + val(k+1)) / 2 that a passes from lo = c-1 gives it.
+// 3 * (val(k) + val(k+1)) has at most 7 significant bits, so is exact.
 __device__ __forceinline__ unsigned e4m3_scale_code(float a) {
-  if (a >= 2688.0f) return 0x7Eu;  // 6 * 448 and above (including inf)
-  // Floor code of an approximate a/6, then corrected by exact comparisons.
   float v = a * (1.0f / 6.0f);
-  unsigned vb = __float_as_uint(v);
-  int c;
-  if (v < 0x1p-6f) {
-    c = (int)(v * 512.0f);
-    c = c > 8 ? 8 : c;
-  } else {
-    c = (int)(((vb >> 23) - 120u) << 3 | ((vb >> 20) & 7u));
-    c = c > 0x7E ? 0x7E : c;
-  }
-  // v is within a few ulp of a/6 and the E4M3 grid is 2^-3 relative (2^-9
-  // absolute below 2^-6), so the floor code is off by at most one.
-  if (c > 0 && 6.0f * e4m3_pos_value((unsigned)c) > a) --c;
-  if (c < 0x7E && 6.0f * e4m3_pos_value((unsigned)c + 1u) <= a) ++c;
-  if (c < 0x7E) {
-    float mid6 = 3.0f * (e4m3_pos_value((unsigned)c) + e4m3_pos_value((unsigned)c + 1u));
-    if (a > mid6 || (a == mid6 && (c & 1))) ++c;
-  }
-  return (unsigned)c;
+  int cn = (int)(__float_as_uint(v) >> 20) - 960;  // v >= 2^-6 (inf: large)
+  int cs = (int)(v * 512.0f);                      // v < 2^-6
+  int c = v < 0x1p-6f ? cs : cn;
+  int lo = min(max(c - 1, 0), 0x7B);
+  float w0 = 3.0f * e4m3_pos_value(lo), w1 = 3.0f * e4m3_pos_value(lo + 1);
+  float w2 = 3.0f * e4m3_pos_value(lo + 2), w3 = 3.0f * e4m3_pos_value(lo + 3);
+  bool odd = lo & 1;
+  unsigned r = (unsigned)lo;
+  r += a > tie_nudge(w0 + w1, odd) ? 1u : 0u;
+  r += a > tie_nudge(w1 + w2, !odd) ? 1u : 0u;
+  r += a > tie_nudge(w2 + w3, odd) ? 1u : 0u;
+  return r;
 }
 
-// Exponent e of the E8M0 scale for an index block with maximum magnitude a:
-// the smallest e in [-127, 127] with a * 2^-e <= 6 (0 when a == 0).
+// Exponent e of the E8M0 scale of an index block with largest magnitude a:
+// the smallest e in [-127, 127] with a * 2^-e <= 6 (0 when a == 0). The
+// estimate from the bits of an approximate a/6 is off by at most one; two
+// exact tests on a * 2^-e (a power-of-two scaling, exact here) settle it.
 __device__ __forceinline__ int e8m0_scale_exp(float a) {
-  if (a == 0.0f) return 0;
-  float v = a * (1.0f / 6.0f);
-  // ceil(log2(v)) from the bits of the approximate quotient (subnormal v: the
-  // clamp below takes over), then exact corrections on a * 2^-e.
-  unsigned vb = __float_as_uint(v);
-  int e = (int)(vb >> 23) - 127 + ((vb & 0x7FFFFFu) != 0u);
-  e = e < -127 ? -127 : (e > 127 ? 127 : e);
-  if (e < 127 && __builtin_amdgcn_ldexpf(a, -e) > 6.0f) ++e;
-  if (e > -127 && __builtin_amdgcn_ldexpf(a, -(e - 1)) <= 6.0f) --e;
-  return e;
+  unsigned vb = __float_as_uint(a * (1.0f / 6.0f));
+  int e = (int)(vb >> 23) - 127 + ((vb & 0x7FFFFFu) != 0u ? 1 : 0);
+  e = min(max(e, -127), 127);
+  e += (e < 127 && __builtin_amdgcn_ldexpf(a, -e) > 6.0f) ? 1 : 0;
+  e -= (e > -127 && __builtin_amdgcn_ldexpf(a, 1 - e) <= 6.0f) ? 1 : 0;
+  return a == 0.0f ? 0 : e;
 }
 
-// E2M1 magnitude code of y against thresholds t[0..6] (the midpoints of the
-// E2M1 values scaled to y's units; the odd ones lowered by one ulp so that a
-// tie there rounds up to the even code): the count of thresholds below y.
-// NaN gives 0, anything above the last threshold 7.
+// E2M1 thresholds: the midpoints between consecutive E2M1 magnitudes
+// (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5) in the block's units, nudged for the
+// tie rule. An element's magnitude code is the number of thresholds below
+// |x| (NaN: 0; beyond the last: 7, the saturated code).
 struct Thresholds {
   float t[7];
 };
 
-__device__ __forceinline__ Thresholds make_thresholds(float s) {
+// Main blocks: scale s is an E4M3 value (>= 2^-9, <= 448); s * midpoint has
+// at most 7 significant bits and is a normal float, hence exact.
+__device__ __forceinline__ Thresholds thresholds_e4m3(float s) {
+  const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+  Thresholds r;
+#pragma unroll
+  for (int k = 0; k < 7; ++k) r.t[k] = tie_nudge(s * mids[k], k & 1);
+  return r;
+}
+
+// Index blocks: scale 2^e. midpoint * 2^e is exact (subnormal included) or
+// overflows to inf, which only happens for e = 127 (an inf in the block):
+// there the even thresholds are brought down to FLT_MAX and the nudged odd
+// ones are FLT_MAX already, so inf still passes every threshold while no
+// finite value passes one beyond the float range.
+__device__ __forceinline__ Thresholds thresholds_e8m0(int e) {
   const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
   Thresholds r;
 #pragma unroll
   for (int k = 0; k < 7; ++k) {
-    float t = s * mids[k];  // exact: <= 4 significant bits times <= 3
-    r.t[k] = (k & 1) ? __uint_as_float(__float_as_uint(t) - 1u) : t;
+    float t = __builtin_amdgcn_ldexpf(mids[k], e);
+    r.t[k] = (k & 1) ? tie_nudge(t, true) : fminf(t, 0x1.fffffep127f);
   }
   return r;
 }
 
-__device__ __forceinline__ unsigned e2m1_code(float x, const Thresholds& th) {
-  float y = fabsf(x);
-  unsigned c = 0;
+// E2M1 magnitude code of y: the number of thresholds below y, found by a
+// three-level binary search over the sorted thresholds (is it above t3? then
+// above t5 or t1? then above the one threshold left between the two codes).
+__device__ __forceinline__ unsigned e2m1_mag(float y, const Thresholds& th) {
+  bool b2 = y > th.t[3];
+  bool b1 = y > (b2 ? th.t[5] : th.t[1]);
+  float lo = b1 ? th.t[2] : th.t[0];
+  float hi = b1 ? th.t[6] : th.t[4];
+  bool b0 = y > (b2 ? hi : lo);
+  return (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
+}
+
+// Eight E2M1 codes in one word: nibble i (bits 4i..4i+3) is channel i, i.e.
+// byte j holds channel 2j in its low nibble and 2j+1 in its high one. Each
+// code is the magnitude code with the sign bit of x on bit 3.
+__device__ __forceinline__ unsigned encode8(const float* f, const Thresholds& th) {
+  unsigned w = 0;
 #pragma unroll
-  for (int k = 0; k < 7; ++k) c += (y > th.t[k]) ? 1u : 0u;
-  return c | ((__float_as_uint(x) >> 28) & 8u);
+  for (int i = 0; i < 8; ++i) {
+    unsigned sgn = (__float_as_uint(f[i]) >> (28 - 4 * i)) & (8u << (4 * i));
+    w |= (e2m1_mag(fabsf(f[i]), th) << (4 * i)) | sgn;
+  }
+  return w;
 }
 
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
-// Channels 4t..4t+3 of the input as fp32 (bf16 widens exactly).
-template <bool BF16>
-__device__ __forceinline__ v4f load4(const void* x, int64_t t) {
-  if (BF16) {
-    v2u h = __builtin_nontemporal_load((const v2u*)x + t);
-    return v4f{__uint_as_float(h.x << 16), __uint_as_float(h.x & 0xFFFF0000u), __uint_as_float(h.y << 16),
-               __uint_as_float(h.y & 0xFFFF0000u)};
-  } else {
-    return __builtin_nontemporal_load((const v4f*)x + t);
-  }
+// Largest of a and the value of the neighbouring lane (lane ^ 1), for
+// non-negative floats compared as bits (quad_perm [1,0,3,2]).
+__device__ __forceinline__ float pair_max(float a) {
+  unsigned u = __float_as_uint(a);
+  return __uint_as_float(max(u, (unsigned)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, false)));
 }
 
-// Destination row of entry e, or -1 when it is out of range.
-__device__ __forceinline__ int64_t dst_row(const int64_t* rows, int64_t e, int64_t n_rows) {
-  int64_t r = rows ? rows[e] : e;
-  return (r >= 0 && r < n_rows) ? r : -1;
-}
-
-// Main latents: thread t covers channels 4q..4q+3 of entry t/128 (q = t%128).
-template <bool BF16>
-__global__ __launch_bounds__(256) void k_quantize_main(const void* __restrict__ x, int64_t n,
-                                                       const int64_t* __restrict__ rows, int64_t n_rows,
-                                                       uint8_t* __restrict__ cache) {
-  int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  // Every lane of a group runs the DPP steps; a grid tail of whole groups
-  // (n * 128 is a multiple of 64) never splits a wave's active quads.
-  if (t >= n * 128) return;
-  v4f v = load4<BF16>(x, t);
-  unsigned m = max(max(mag_bits(v.x), mag_bits(v.y)), max(mag_bits(v.z), mag_bits(v.w)));
-  float a = __uint_as_float(quad_umax(m));
-  unsigned sc = e4m3_scale_code(a);
-  unsigned codes = 0;
-  if (sc != 0u) {
-    Thresholds th = make_thresholds(e4m3_pos_value(sc));
-    codes = e2m1_code(v.x, th) | e2m1_code(v.y, th) << 4 | e2m1_code(v.z, th) << 8 | e2m1_code(v.w, th) << 12;
+// One kernel for both formats and input types. The unit of work is a
+// half-block of 16 channels: a main scale group, or half of an indexer scale
+// block (the two halves are neighbouring lanes and share their maximum).
+//
+// Each wave streams tiles of 64 consecutive half-blocks (4 KiB of fp32, 2 KiB
+// of bf16): the tile is read with coalesced 16-B loads (lane l takes chunks
+// l, l+64, ...), written to a wave-private, padded LDS area and read back so
+// that lane l holds half-block l; reading 64 B per lane straight from HBM
+// instead would touch every cache line four times per load instruction and
+// cost a third of the bandwidth. The next tile's loads are issued before the
+// current one is encoded.
+template <bool BF16, bool INDEX>
+__global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, int64_t n,
+                                                  const int64_t* __restrict__ rows, int64_t n_rows,
+                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  constexpr int C = BF16 ? 2 : 4;  // 16-B chunks per half-block
+  constexpr int S = C + 1;         // padded stride: lanes read distinct LDS banks
+  constexpr int SHIFT = INDEX ? 3 : 5;  // half-blocks per entry: 8 (index), 32 (main)
+  __shared__ v4u lds[4][64 * S];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t nhb = n << SHIFT, nchunk = nhb * C;
+  const int64_t ntile = (nhb + 63) >> 6, wstride = (int64_t)gridDim.x * 4;
+  int64_t tile = (int64_t)blockIdx.x * 4 + w;
+  if (tile >= ntile) return;
+  const v4u* src = (const v4u*)x;
+  v4u reg[C];
+  int64_t row_next;
+  // Loads of tile t; indexes past the end are clamped to the last chunk (their
+  // half-blocks are never stored), so no load sits behind a branch. The
+  // destination row is loaded first and checked only at the store, so that
+  // nothing waits on these loads before the tile is needed.
+  auto fetch = [&](int64_t t) {
+    const int64_t e = min(t * 64 + lane, nhb - 1) >> SHIFT;
+    row_next = rows ? rows[e] : e;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      int64_t c = min(t * 64 * C + lane + 64 * j, nchunk - 1);
+      reg[j] = __builtin_nontemporal_load(src + c);
+    }
+  };
+  fetch(tile);
+  for (;;) {
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      int c = lane + 64 * j;
+      lds[w][(c / C) * S + (c % C)] = reg[j];
+    }
+    const int64_t row = row_next;
+    __builtin_amdgcn_wave_barrier();
+    const int64_t next = tile + wstride;
+    if (next < ntile) fetch(next);
+    float f[16];
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      v4u v = lds[w][lane * S + i];
+      if (BF16) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f[8 * i + 2 * j] = __uint_as_float(v[j] << 16);
+          f[8 * i + 2 * j + 1] = __uint_as_float(v[j] & 0xFFFF0000u);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f[4 * i + j] = __uint_as_float(v[j]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    const int64_t hb = tile * 64 + lane;
+    const int h = (int)(hb & ((1 << SHIFT) - 1));
+    if (INDEX) {
+      float a = pair_max(block_amax(f));  // both lanes of the pair run this
+      int ex = e8m0_scale_exp(a);
+      v2u cw = {0u, 0u};
+      if (a != 0.0f) {
+        Thresholds th = thresholds_e8m0(ex);
+        cw = v2u{encode8(f, th), encode8(f + 8, th)};
+      }
+      if (hb < nhb && row >= 0 && row < n_rows) {
+        *(v2u*)(codes + row * 64 + 8 * h) = cw;
+        if ((h & 1) == 0) scales[row * 4 + (h >> 1)] = (uint8_t)(ex + 127);
+      }
+    } else {
+      unsigned sc = e4m3_scale_code(block_amax(f));
+      v2u cw = {0u, 0u};
+      if (sc != 0u) {
+        Thresholds th = thresholds_e4m3(e4m3_pos_value((int)sc));
+        cw = v2u{encode8(f, th), encode8(f + 8, th)};
+      }
+      if (hb < nhb && row >= 0 && row < n_rows) {
+        uint8_t* ent = codes + row * kMainBytes;
+        *(v2u*)(ent + 8 * h) = cw;
+        ent[256 + h] = (uint8_t)sc;
+      }
+    }
+    if (next >= ntile) break;
+    tile = next;
   }
-  int64_t e = t >> 7;
-  int q = (int)(t & 127);
-  int64_t r = dst_row(rows, e, n_rows);
-  if (r < 0) return;
-  uint8_t* ent = cache + r * kMainBytes;
-  *(uint16_t*)(ent + 2 * q) = (uint16_t)codes;
-  if ((q & 3) == 0) ent[256 + (q >> 2)] = (uint8_t)sc;
-}
-
-// Indexer keys: thread t covers channels 4q..4q+3 of key t/32 (q = t%32).
-template <bool BF16>
-__global__ __launch_bounds__(256) void k_quantize_index(const void* __restrict__ x, int64_t n,
-                                                        const int64_t* __restrict__ rows, int64_t n_rows,
-                                                        uint8_t* __restrict__ codes_out,
-                                                        uint8_t* __restrict__ scales_out) {
-  int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= n * 32) return;  // n * 32 is a multiple of 8: groups stay whole
-  v4f v = load4<BF16>(x, t);
-  unsigned m = max(max(mag_bits(v.x), mag_bits(v.y)), max(mag_bits(v.z), mag_bits(v.w)));
-  float a = __uint_as_float(oct_umax(m));
-  int ex = e8m0_scale_exp(a);
-  unsigned codes = 0;
-  if (a != 0.0f) {
-    // Compare |x| * 2^-e (exact: the result is <= 6 or the block saturates)
-    // with the unit-scale thresholds.
-    Thresholds th = make_thresholds(1.0f);
-    codes = e2m1_code(__builtin_amdgcn_ldexpf(v.x, -ex), th) | e2m1_code(__builtin_amdgcn_ldexpf(v.y, -ex), th) << 4 |
-            e2m1_code(__builtin_amdgcn_ldexpf(v.z, -ex), th) << 8 |
-            e2m1_code(__builtin_amdgcn_ldexpf(v.w, -ex), th) << 12;
-  }
-  int64_t e = t >> 5;
-  int q = (int)(t & 31);
-  int64_t r = dst_row(rows, e, n_rows);
-  if (r < 0) return;
-  *(uint16_t*)(codes_out + r * 64 + 2 * q) = (uint16_t)codes;
-  if ((q & 7) == 0) scales_out[r * 4 + (q >> 3)] = (uint8_t)(ex + 127);
 }
 
 }  // namespace
@@ -201,18 +278,21 @@ __global__ __launch_bounds__(256) void k_quantize_index(const void* __restrict__
 hipError_t launch_quantize(int kind, const void* x, int in_bf16, int64_t n, const int64_t* rows, int64_t n_rows,
                            uint8_t* codes, uint8_t* scales, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  int64_t threads = n * (kind == 0 ? 128 : 32);
-  dim3 grid((unsigned)((threads + 255) / 256));
+  const int64_t nhb = n * (kind == 0 ? 32 : 8), ntile = (nhb + 63) / 64;
+  // Four waves per workgroup, one tile per wave at a time; large writes cap
+  // the grid at kQuantGroups workgroups and loop.
+  const int64_t groups = (ntile + 3) / 4;
+  dim3 grid((unsigned)(groups < kQuantGroups ? groups : kQuantGroups));
   if (kind == 0) {
     if (in_bf16)
-      k_quantize_main<true><<<grid, 256, 0, s>>>(x, n, rows, n_rows, codes);
+      k_quantize<true, false><<<grid, 256, 0, s>>>(x, n, rows, n_rows, codes, scales);
     else
-      k_quantize_main<false><<<grid, 256, 0, s>>>(x, n, rows, n_rows, codes);
+      k_quantize<false, false><<<grid, 256, 0, s>>>(x, n, rows, n_rows, codes, scales);
   } else {
     if (in_bf16)
-      k_quantize_index<true><<<grid, 256, 0, s>>>(x, n, rows, n_rows, codes, scales);
+      k_quantize<true, true><<<grid, 256, 0, s>>>(x, n, rows, n_rows, codes, scales);
     else
-      k_quantize_index<false><<<grid, 256, 0, s>>>(x, n, rows, n_rows, codes, scales);
+      k_quantize<false, true><<<grid, 256, 0, s>>>(x, n, rows, n_rows, codes, scales);
   }
   return hipGetLastError();
 }
