@@ -30,14 +30,16 @@
  *      latent is both key and value; RoPE is outside this path.
  *   R8 selected ids outside [0, n_entries) (the -1 padding) are skipped; an
  *      empty joint set gives a zero output and lse = -inf.
- *   R9 writing a new entry (fp32 in): a main block's E4M3 scale is the
- *      E4M3FN value nearest to amax/6 (ties to the even code, saturating at
- *      448); an indexer block's E8M0 scale is 2^e for the smallest e in
- *      [-127, 127] with 6 * 2^e >= amax (e = 0 for an all-zero block); each
- *      element takes the E2M1 magnitude nearest to |x| / scale (ties to the
- *      even code, saturating at 6) and the sign bit of x; a block whose scale
- *      is zero (main) or whose amax is zero (indexer) gets all-zero codes.
- *      NaN counts as a zero magnitude, +-inf as the largest one.
+ *   R13 writing a new entry (fp32 in): a main block's E4M3 scale is the
+ *       E4M3FN value nearest to amax/6 (ties to the even code, saturating at
+ *       448); an indexer block's E8M0 scale is 2^e for the smallest e in
+ *       [-127, 127] with 6 * 2^e >= amax (e = 0 for an all-zero block); each
+ *       element takes the E2M1 magnitude nearest to |x| / scale (ties to the
+ *       even code, saturating at 6) and the sign bit of x; a block whose scale
+ *       is zero (main) or whose amax is zero (indexer) gets all-zero codes.
+ *       NaN counts as a zero magnitude, +-inf as the largest one.
+ *   (R9-R12 concern the workload and its generator; they are listed with the
+ *   design notes.)
  */
 #include <math.h>
 #include <stdint.h>
@@ -140,7 +142,7 @@ ORC_API void orc_dequant_index(const uint8_t* codes, const uint8_t* scales, int6
 /* ------------------------------------------------------------------ O7 --- */
 /* Cache write: quantise new fp32 entries into the two stored formats
  * ([ATLAS] "The KV cache" and Full-layer cache bullet give the formats; the
- * rounding rule is reading R9). Brute force: every candidate code is tried
+ * rounding rule is reading R13). Brute force: every candidate code is tried
  * and the nearest kept, so the result is the definition itself. */
 
 static int e2m1_is_better(double d, unsigned m, double best_d, unsigned best_m) {
