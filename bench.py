@@ -26,6 +26,7 @@ from __future__ import annotations
 import argparse
 import csv
 import ctypes
+import dataclasses
 import glob
 import hashlib
 import json
@@ -88,8 +89,6 @@ class HipEvents:
 
 
 def replicate(db, R):
-    import dataclasses
-
     import torch
     reps = [db]
     for _ in range(R - 1):
@@ -119,8 +118,10 @@ def work_of(wl):
     swa_rows = min(swa_rows, Q * wl.n_swa)
     attn_bytes = Q * 65536 * 2 + ENTRY_BYTES_MAIN * int(k_sel.sum()) + 1024 * swa_rows
     attn_flops = int(2 * 2 * 64 * 512 * (k_sel + wl.n_swa).sum())
+    # FP8 window rows (528 B) and the (cos, sin) table instead of bf16 rows
+    attn_fp8_bytes = attn_bytes - (1024 - 528) * swa_rows + Q * 32 * 2 * 4
     return dict(pairs=pairs, score_bytes=score_bytes, score_flops=pairs * FLOP_PER_PAIR, attn_bytes=attn_bytes,
-                attn_flops=attn_flops, step_bytes=score_bytes + attn_bytes)
+                attn_flops=attn_flops, step_bytes=score_bytes + attn_bytes, attn_fp8_bytes=attn_fp8_bytes)
 
 
 def source_digest(names=SCORE_SOURCES):
@@ -331,7 +332,7 @@ def main():
                      dtype=torch.uint8, device="cuda")
     K, W = args.steps, args.warmup
     S = min(K, 50)
-    ev = HipEvents(2 + 4 * S + 8)
+    ev = HipEvents(2 + 4 * S + 10)
 
     # ---- phase 1: timed decode steps
     dec_args = [reps[i % R].decode_args(out, lse, idx) for i in range(R)]
@@ -387,6 +388,27 @@ def main():
     ev.record(e0 + 3, stream)
     torch.cuda.synchronize()
     attn_ms = ev.ms(e0 + 2, e0 + 3) / K
+    # the same attention with the pages' FP8 window rows (528 B each) and the
+    # RoPE un-rotation epilogue (rows from the same seeded streams)
+    if wl.extra.get("shared_swa"):
+        rows8 = synth.fp8_rows(0, synth.TID_SWA, 0, 0, wl.swa.shape[0])
+    else:
+        rows8 = np.concatenate([synth.fp8_rows(0, synth.TID_SWA, i, 0, wl.n_swa) for i in range(Q)])
+    pos = wl.extra["t0"] + np.arange(Q) if "t0" in wl.extra else wl.n_entries + 7 * np.arange(Q)
+    swa8 = torch.from_numpy(np.ascontiguousarray(rows8)).cuda()
+    rope_t = torch.from_numpy(synth.rope_table(pos)).cuda()
+    a8_args = [dataclasses.replace(reps[i % R], swa=swa8, swa_format=csa.CSA2_SWA_FP8, rope=rope_t)
+               .attn_args(idx, at_out, at_lse) for i in range(R)]
+    for i in range(3):
+        csa.csa2_sparse_attn(a8_args[i % R], at_ws, stream)
+    torch.cuda.synchronize()
+    ev.record(e0 + 4, stream)
+    for i in range(K):
+        csa.csa2_sparse_attn(a8_args[i % R], at_ws, stream)
+    ev.record(e0 + 5, stream)
+    torch.cuda.synchronize()
+    attn8_ms = ev.ms(e0 + 4, e0 + 5) / K
+    del swa8, rope_t
     # ---- phase 4: cache write of a long prefill chunk's new entries (not part
     # of the step): fp32 rows -> FP4 main entries and indexer keys
     gen = torch.Generator(device="cuda")
@@ -402,12 +424,12 @@ def main():
         for _ in range(3):
             csa.csa2_quantize(kind, xin, csa.CSA2_IN_F32, CACHE_WRITE_ROWS, None, CACHE_WRITE_ROWS, co, so, stream)
         torch.cuda.synchronize()
-        ev.record(e0 + 4 + 2 * j, stream)
+        ev.record(e0 + 6 + 2 * j, stream)
         for _ in range(K):
             csa.csa2_quantize(kind, xin, csa.CSA2_IN_F32, CACHE_WRITE_ROWS, None, CACHE_WRITE_ROWS, co, so, stream)
-        ev.record(e0 + 5 + 2 * j, stream)
+        ev.record(e0 + 7 + 2 * j, stream)
         torch.cuda.synchronize()
-        q_ms.append(ev.ms(e0 + 4 + 2 * j, e0 + 5 + 2 * j) / K)
+        q_ms.append(ev.ms(e0 + 6 + 2 * j, e0 + 7 + 2 * j) / K)
     del xm, xk, qm, qc, qs
     ev.close()
     if args.copy_calibration:
@@ -433,6 +455,10 @@ def main():
         "sparse_attn": {"kernels": ["k_sparse_attn", "k_attn_combine"], "us_per_launch": round(1e3 * attn_ms, 3),
                         "algorithmic_bytes": work["attn_bytes"], "GB_s": round(attn_gbs, 1),
                         "hbm_frac": round(attn_gbs / HBM_PEAK_GBS, 4)},
+        "sparse_attn_fp8_window_rope": {
+            "kernels": ["k_sparse_attn<fp8 window>", "k_attn_combine"], "us_per_launch": round(1e3 * attn8_ms, 3),
+            "algorithmic_bytes": work["attn_fp8_bytes"],
+            "GB_s": round(work["attn_fp8_bytes"] / (attn8_ms * 1e-3) / 1e9, 1)},
     }
     for kname, kind, ms_ in (("quantize_main", "k_quantize<f32, main>", q_ms[0]),
                              ("quantize_index", "k_quantize<f32, index>", q_ms[1])):

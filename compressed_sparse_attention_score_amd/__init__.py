@@ -20,6 +20,7 @@ CSA2_OK, CSA2_ERR_NULL, CSA2_ERR_SHAPE, CSA2_ERR_ALIGN, CSA2_ERR_WORKSPACE, CSA2
 CSA2_KIND_MAIN, CSA2_KIND_INDEX = 0, 1
 CSA2_OUT_F32, CSA2_OUT_BF16 = 0, 1
 CSA2_IN_F32, CSA2_IN_BF16 = 0, 1
+CSA2_SWA_BF16, CSA2_SWA_FP8 = 0, 1
 CSA2_WS_TOPK, CSA2_WS_ATTN, CSA2_WS_DECODE = 0, 1, 2
 EXPORTED = ("csa2_dequant", "csa2_quantize", "csa2_index_score", "csa2_topk", "csa2_sparse_attn", "csa2_decode",
             "csa2_workspace_size", "csa2_status_string", "csa2_version")
@@ -42,13 +43,15 @@ class TopkArgs(ctypes.Structure):
 class AttnArgs(ctypes.Structure):
     _fields_ = [("struct_size", _sz), ("n_queries", _i32), ("n_entries", _i64), ("cache_q_stride", _i64),
                 ("main_cache", _vp), ("idx", _vp), ("k_sel", _i32), ("q", _vp), ("swa", _vp),
-                ("swa_q_stride", _i64), ("n_swa", _i32), ("softmax_scale", _f32), ("out", _vp), ("lse", _vp)]
+                ("swa_q_stride", _i64), ("n_swa", _i32), ("softmax_scale", _f32), ("out", _vp), ("lse", _vp),
+                ("swa_format", _i32), ("rope_cos_sin", _vp)]
 
 
 class DecodeArgs(ctypes.Structure):
     _fields_ = [("struct_size", _sz), ("index", IndexArgs), ("k", _i32), ("main_cache", _vp), ("q", _vp),
                 ("swa", _vp), ("swa_q_stride", _i64), ("n_swa", _i32), ("softmax_scale", _f32), ("out", _vp),
-                ("lse", _vp), ("idx_out", _vp), ("stage_events", _vp * 4)]
+                ("lse", _vp), ("idx_out", _vp), ("stage_events", _vp * 4), ("swa_format", _i32),
+                ("rope_cos_sin", _vp)]
 
 
 def _load():
@@ -164,10 +167,11 @@ def csa2_topk(args: TopkArgs, workspace=None, stream=None, device="cuda") -> Non
 
 
 def attn_args(Q, n_entries, cache_q_stride, main_cache, idx, q, swa, swa_q_stride, n_swa, softmax_scale, out,
-              lse=None) -> AttnArgs:
+              lse=None, swa_format=CSA2_SWA_BF16, rope_cos_sin=None) -> AttnArgs:
     k_sel = 0 if idx is None else int(idx.shape[-1])
     return AttnArgs(ctypes.sizeof(AttnArgs), Q, n_entries, cache_q_stride, _ptr(main_cache), _ptr(idx), k_sel, _ptr(q),
-                    _ptr(swa), swa_q_stride, n_swa, softmax_scale, _ptr(out), _ptr(lse))
+                    _ptr(swa), swa_q_stride, n_swa, softmax_scale, _ptr(out), _ptr(lse), swa_format,
+                    _ptr(rope_cos_sin))
 
 
 def csa2_sparse_attn(args: AttnArgs, workspace=None, stream=None, device="cuda") -> None:
@@ -178,10 +182,10 @@ def csa2_sparse_attn(args: AttnArgs, workspace=None, stream=None, device="cuda")
 
 
 def decode_args(index: IndexArgs, k, main_cache, q, swa, swa_q_stride, n_swa, softmax_scale, out, lse=None,
-                idx_out=None, stage_events=None) -> DecodeArgs:
+                idx_out=None, stage_events=None, swa_format=CSA2_SWA_BF16, rope_cos_sin=None) -> DecodeArgs:
     ev = (_vp * 4)(*(stage_events or (None, None, None, None)))
     return DecodeArgs(ctypes.sizeof(DecodeArgs), index, k, _ptr(main_cache), _ptr(q), _ptr(swa), swa_q_stride, n_swa,
-                      softmax_scale, _ptr(out), _ptr(lse), _ptr(idx_out), ev)
+                      softmax_scale, _ptr(out), _ptr(lse), _ptr(idx_out), ev, swa_format, _ptr(rope_cos_sin))
 
 
 def csa2_decode(args: DecodeArgs, workspace=None, stream=None, device="cuda") -> None:

@@ -22,13 +22,15 @@ class DeviceBatch:
     iq_scales: torch.Tensor     # uint8 [Q][32][4]
     w: torch.Tensor             # float32 [Q][32]
     q: torch.Tensor             # int16 (bf16 bits) [Q][64][512]
-    swa: torch.Tensor           # int16 (bf16 bits) [rows][512]
+    swa: torch.Tensor           # int16 (bf16 bits) [rows][512], or uint8 [rows][528] FP8 rows
     swa_q_stride: int
     n_swa: int
     k: int = 512
     scale: float = 512 ** -0.5
     cand_blocks: Optional[torch.Tensor] = None  # int32 [Q][n_blocks]
     n_valid: Optional[torch.Tensor] = None      # int32 [Q]
+    swa_format: int = 0                         # CSA2_SWA_BF16 / CSA2_SWA_FP8
+    rope: Optional[torch.Tensor] = None         # float32 [Q][32][2] (cos, sin)
 
     @property
     def n_cand(self) -> int:
@@ -40,11 +42,12 @@ class DeviceBatch:
 
     def attn_args(self, idx, out, lse=None, n_swa=None):
         return attn_args(self.Q, self.n_entries, self.cache_q_stride, self.main_cache, idx, self.q, self.swa,
-                         self.swa_q_stride, self.n_swa if n_swa is None else n_swa, self.scale, out, lse)
+                         self.swa_q_stride, self.n_swa if n_swa is None else n_swa, self.scale, out, lse,
+                         self.swa_format, self.rope)
 
     def decode_args(self, out, lse=None, idx_out=None, stage_events=None):
         return decode_args(self.index_args(), self.k, self.main_cache, self.q, self.swa, self.swa_q_stride, self.n_swa,
-                           self.scale, out, lse, idx_out, stage_events)
+                           self.scale, out, lse, idx_out, stage_events, self.swa_format, self.rope)
 
     def new_outputs(self):
         dev = self.q.device

@@ -73,8 +73,10 @@ int check_topk(const csa2_topk_args* a) {
 }
 
 int check_attn_fields(int Q, int64_t n_entries, int64_t cache_q_stride, const uint8_t* main_cache,
-                      const int32_t* idx, int k_sel, const uint16_t* q, const uint16_t* swa, int64_t swa_q_stride,
-                      int n_swa, const uint16_t* out, const float* lse, bool idx_internal) {
+                      const int32_t* idx, int k_sel, const uint16_t* q, const void* swa, int64_t swa_q_stride,
+                      int n_swa, const uint16_t* out, const float* lse, int swa_format, const float* rope,
+                      bool idx_internal) {
+  if (swa_format != CSA2_SWA_BF16 && swa_format != CSA2_SWA_FP8) return CSA2_ERR_ARG;
   if (Q < 0 || Q > kMaxQ) return CSA2_ERR_SHAPE;
   if (n_entries < 0 || n_entries > kMaxI32 || cache_q_stride < 0) return CSA2_ERR_SHAPE;
   if (k_sel < 0 || k_sel > CSA2_MAX_K) return CSA2_ERR_SHAPE;
@@ -84,7 +86,7 @@ int check_attn_fields(int Q, int64_t n_entries, int64_t cache_q_stride, const ui
   if (k_sel > 0 && ((!idx && !idx_internal) || (n_entries > 0 && !main_cache))) return CSA2_ERR_NULL;
   if (n_swa > 0 && !swa) return CSA2_ERR_NULL;
   if (!aligned(main_cache, 16) || !aligned(q, 16) || !aligned(swa, 16) || !aligned(out, 16) || !aligned(idx, 4) ||
-      !aligned(lse, 4))
+      !aligned(lse, 4) || !aligned(rope, 8))
     return CSA2_ERR_ALIGN;
   return CSA2_OK;
 }
@@ -93,7 +95,7 @@ int check_attn(const csa2_attn_args* a) {
   if (!a) return CSA2_ERR_NULL;
   if (a->struct_size != sizeof(csa2_attn_args)) return CSA2_ERR_ARG;
   return check_attn_fields(a->n_queries, a->n_entries, a->cache_q_stride, a->main_cache, a->idx, a->k_sel, a->q,
-                           a->swa, a->swa_q_stride, a->n_swa, a->out, a->lse, false);
+                           a->swa, a->swa_q_stride, a->n_swa, a->out, a->lse, a->swa_format, a->rope_cos_sin, false);
 }
 
 int check_decode(const csa2_decode_args* a, int64_t* n_cand) {
@@ -103,7 +105,8 @@ int check_decode(const csa2_decode_args* a, int64_t* n_cand) {
   if (st) return st;
   if (a->k < 1 || a->k > CSA2_MAX_K) return CSA2_ERR_SHAPE;
   st = check_attn_fields(a->index.n_queries, a->index.n_entries, a->index.cache_q_stride, a->main_cache, a->idx_out,
-                         a->k, a->q, a->swa, a->swa_q_stride, a->n_swa, a->out, a->lse, true);
+                         a->k, a->q, a->swa, a->swa_q_stride, a->n_swa, a->out, a->lse, a->swa_format,
+                         a->rope_cos_sin, true);
   if (st) return st;
   if (!aligned(a->idx_out, 4)) return CSA2_ERR_ALIGN;
   return CSA2_OK;
@@ -267,8 +270,10 @@ int csa2_sparse_attn(const csa2_attn_args* a, void* ws, size_t ws_bytes, void* s
     Carve c(ws);
     partial = c.take<float>(attn_partial_bytes(Q, ap) / sizeof(float));
   }
-  AttnLaunch L{Q, a->n_entries, a->cache_q_stride, a->main_cache, a->idx, a->k_sel, a->q, a->swa, a->swa_q_stride,
-               a->n_swa, a->softmax_scale, a->out, a->lse};
+  AttnLaunch L{Q,        a->n_entries,     a->cache_q_stride, a->main_cache,
+               a->idx,   a->k_sel,         a->q,              a->swa,
+               a->swa_q_stride, a->n_swa,  a->softmax_scale,  a->out,
+               a->lse,   a->swa_format == CSA2_SWA_FP8, a->rope_cos_sin};
   return hip_status(launch_attn(L, ap, partial, s));
 }
 
@@ -311,8 +316,10 @@ int csa2_decode(const csa2_decode_args* a, void* ws, size_t ws_bytes, void* stre
   if (e != hipSuccess) return CSA2_ERR_HIP;
   // 3. attention over the selection + window
   AttnPlan ap = plan_attn(Q, a->k + a->n_swa);
-  AttnLaunch A{Q,    a->index.n_entries, a->index.cache_q_stride, a->main_cache, w.idx,  a->k,  a->q,
-               a->swa, a->swa_q_stride,  a->n_swa,                a->softmax_scale, a->out, a->lse};
+  AttnLaunch A{Q,      a->index.n_entries, a->index.cache_q_stride, a->main_cache,
+               w.idx,  a->k,               a->q,                    a->swa,
+               a->swa_q_stride, a->n_swa, a->softmax_scale,        a->out,
+               a->lse, a->swa_format == CSA2_SWA_FP8, a->rope_cos_sin};
   e = launch_attn(A, ap, w.partial, s);
   if (e == hipSuccess) e = mark(3);
   return hip_status(e);

@@ -79,12 +79,14 @@ struct AttnLaunch {
   const int32_t* idx;
   int k_sel;
   const uint16_t* q;
-  const uint16_t* swa;
+  const void* swa;  // bf16 rows [..][512], or FP8 rows [..][528] when swa_fp8
   int64_t swa_q_stride;
   int n_swa;
   float scale;
   uint16_t* out;
   float* lse;
+  int swa_fp8;
+  const float* rope;  // [Q][32][2] (cos, sin) or nullptr
 };
 
 // partial: workspace for the per-split records (plan.n_splits > 1); the merge

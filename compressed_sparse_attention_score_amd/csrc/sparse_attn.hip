@@ -40,6 +40,10 @@
 //    per (query, 16 heads), merges them in split order. Handing the partials
 //    over at a kernel boundary is cheaper on this multi-XCD part than any
 //    in-kernel hand-off between workgroups.
+//  * Window rows are bf16, or FP8 (MXFP8: 512 E4M3 codes + 16 E8M0 scales,
+//    528 bytes, the pages' window entry size) decoded to bf16 at staging like
+//    the latents. With a RoPE table, the 64 rotary channels of the output are
+//    rotated back by each query's angles in the epilogue that writes it.
 #include "csa2_device.h"
 #include "csa2_internal.h"
 
@@ -52,11 +56,16 @@ constexpr float kRescaleSlack = 8.f;  // log2 units
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+constexpr int kSwa8Bytes = 528;  // FP8 window row: 512 E4M3 codes + 16 E8M0 scales
+constexpr int kRopeFirst = 448;  // first rotary channel; pairs (448+2i, 449+2i), i < 32
+
 struct AttnArgs {
   const uint8_t* main_cache;
   const int32_t* idx;
   const uint16_t* q;
-  const uint16_t* swa;
+  const uint16_t* swa;   // bf16 window rows
+  const uint8_t* swa8;   // FP8 window rows
+  const float* rope;     // [Q][32][2] (cos, sin) or nullptr
   uint16_t* out;
   float* lse;
   float* partial;
@@ -85,15 +94,24 @@ struct AttnShared {
 
 // The staged raw data of one slot for this lane's 8 channels: a selected
 // latent keeps its 4 code bytes in x and its E4M3 scale byte in y with bit 8
-// set when the id is valid; a window row keeps its 8 bf16 in x..w. Which of
-// the two a slot is follows from its index.
+// set when the id is valid; a bf16 window row keeps its 8 bf16 in x..w; an
+// FP8 window row keeps its 8 E4M3 codes in x, y and its E8M0 scale byte in z.
+// Which of these a slot is follows from its index and the window format.
 typedef v4u RawSlot;
+
+// This lane's 8 channels of FP8 window row `row` (codes 8c8..8c8+7, scale of
+// their 32-channel block).
+__device__ __forceinline__ RawSlot load_swa8(const uint8_t* rowp, int c8) {
+  const uint2 c = *(const uint2*)(rowp + 8 * c8);
+  return v4u{c.x, c.y, (unsigned)rowp[512 + (c8 >> 2)], 0u};
+}
 
 // Channels 8c8..8c8+7 of the 4 slots of tile t (slot group eg), ids from LDS.
 // A tile holds only selected latents or only window rows unless k_sel is not
 // a multiple of the tile: those two cases issue every load unconditionally
 // (invalid slots read row 0 of the query's cache or window and are flagged),
 // so all loads stay in flight together; a mixed tile takes a per-slot path.
+template <bool SWA8>
 __device__ __forceinline__ void issue_raw(const AttnArgs& a, const AttnShared& sh, int q, int t, int t0, int eg,
                                           int c8, RawSlot* r) {
   const int s0 = t * TILE;
@@ -110,11 +128,20 @@ __device__ __forceinline__ void issue_raw(const AttnArgs& a, const AttnShared& s
     return;
   }
   if (s0 >= a.k_sel) {  // window rows only (this tile exists, so n_swa >= 1)
-    const uint16_t* base = a.swa + (int64_t)q * a.swa_q_stride * kDim + c8 * 8;
+    if (SWA8) {
+      const uint8_t* base = a.swa8 + (int64_t)q * a.swa_q_stride * kSwa8Bytes;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int slot = s0 + 4 * eg + i;
-      r[i] = *(const v4u*)(base + (int64_t)(slot < a.nj ? slot - a.k_sel : 0) * kDim);
+      for (int i = 0; i < 4; ++i) {
+        const int slot = s0 + 4 * eg + i;
+        r[i] = load_swa8(base + (int64_t)(slot < a.nj ? slot - a.k_sel : 0) * kSwa8Bytes, c8);
+      }
+    } else {
+      const uint16_t* base = a.swa + (int64_t)q * a.swa_q_stride * kDim + c8 * 8;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int slot = s0 + 4 * eg + i;
+        r[i] = *(const v4u*)(base + (int64_t)(slot < a.nj ? slot - a.k_sel : 0) * kDim);
+      }
     }
     return;
   }
@@ -129,30 +156,58 @@ __device__ __forceinline__ void issue_raw(const AttnArgs& a, const AttnShared& s
         r[i] = v4u{*(const unsigned*)(ent + c8 * 4), (unsigned)ent[256 + (c8 >> 1)] | 0x100u, 0u, 0u};
       }
     } else if (slot < a.nj) {
-      r[i] = *(const v4u*)(a.swa + ((int64_t)q * a.swa_q_stride + (slot - a.k_sel)) * kDim + c8 * 8);
+      const int64_t row = (int64_t)q * a.swa_q_stride + (slot - a.k_sel);
+      if (SWA8)
+        r[i] = load_swa8(a.swa8 + row * kSwa8Bytes, c8);
+      else
+        r[i] = *(const v4u*)(a.swa + row * kDim + c8 * 8);
     }
   }
 }
 
+// Window row of a slot as 4 bf16 pairs: passed through (bf16) or decoded
+// (FP8: E4M3 times a power of two, exact in bf16 inside its normal range).
+template <bool SWA8>
+__device__ __forceinline__ void window_pairs(const RawSlot& r, unsigned* win) {
+  if (SWA8) {
+    const float ws = e8m0_to_f32(r[2]);
+    const v2f v[4] = {__builtin_amdgcn_cvt_pk_f32_fp8((int)r[0], false), __builtin_amdgcn_cvt_pk_f32_fp8((int)r[0], true),
+                      __builtin_amdgcn_cvt_pk_f32_fp8((int)r[1], false), __builtin_amdgcn_cvt_pk_f32_fp8((int)r[1], true)};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) win[j] = pack_bf16x2_exact(v[j].x * ws, v[j].y * ws);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) win[j] = r[j];
+  }
+}
+
 // kw[i][j] = channels 8c8+2j (bits 15:0) and 8c8+2j+1 (bits 31:16) of slot
-// 4eg+i of tile t as bf16. Branch-free per slot: a latent is decoded, a
-// window row passed through, an empty slot gives zeros (its loaded bytes may
-// be anything, NaN included). *okb gets the validity byte of each slot.
+// 4eg+i of tile t as bf16: a latent decoded, a window row passed through or
+// decoded, an empty slot zeros (its loaded bytes may be anything, NaN
+// included). A tile of latents only or of window rows only (all but at most
+// one tile per query) decodes only its own kind; the test is uniform over the
+// workgroup. *okb gets the validity byte of each slot.
+template <bool SWA8>
 __device__ __forceinline__ void decode_tile(const AttnArgs& a, int t, int eg, const RawSlot* r, unsigned (*kw)[4],
                                             unsigned* okb) {
+  const int s0 = t * TILE;
+  const bool all_lat = s0 + TILE <= a.k_sel, all_win = s0 >= a.k_sel;
   unsigned ob = 0u;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int slot = t * TILE + 4 * eg + i;
+    const int slot = s0 + 4 * eg + i;
     const bool latent = slot < a.k_sel, window = !latent && slot < a.nj;
     const bool lat_ok = latent && (r[i][1] & 0x100u);
-    float f[8];
-    decode_e2m1x8_scaled(r[i][0], e4m3_to_f32_hw(r[i][1] & 0xFFu), f);
+    unsigned dec[4] = {0u, 0u, 0u, 0u}, win[4] = {0u, 0u, 0u, 0u};
+    if (!all_win) {
+      float f[8];
+      decode_e2m1x8_scaled(r[i][0], e4m3_to_f32_hw(r[i][1] & 0xFFu), f);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const unsigned dec = pack_bf16x2_exact(f[2 * j], f[2 * j + 1]);
-      kw[i][j] = lat_ok ? dec : window ? r[i][j] : 0u;
+      for (int j = 0; j < 4; ++j) dec[j] = pack_bf16x2_exact(f[2 * j], f[2 * j + 1]);
     }
+    if (!all_lat) window_pairs<SWA8>(r[i], win);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kw[i][j] = lat_ok ? dec[j] : window ? win[j] : 0u;
     ob |= ((lat_ok || window) ? 1u : 0u) << (8 * i);
   }
   *okb = ob;
@@ -196,6 +251,15 @@ __device__ __forceinline__ void store_tile(AttnShared& sh, int vbuf, int eg, int
   if (c8 == 0) sh.ok[vbuf][eg] = okb;  // one lane per slot group
 }
 
+// Channels (a, b) of one rotary pair rotated back by the angle whose cosine
+// and sine are cs: (a c + b s, b c - a s).
+__device__ __forceinline__ void unrotate(float& x, float& y, float2 cs) {
+  const float a = x, b = y;
+  x = a * cs.x + b * cs.y;
+  y = b * cs.x - a * cs.y;
+}
+
+template <bool SWA8>
 __global__ __launch_bounds__(NT, 1) void k_sparse_attn(AttnArgs a) {
   const int q = blockIdx.y, split = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -257,18 +321,18 @@ __global__ __launch_bounds__(NT, 1) void k_sparse_attn(AttnArgs a) {
   // loop so no loaded register is copied before it is consumed.
   RawSlot rawA[4], rawB[4];
   if (t0 < t1) {
-    issue_raw(a, sh, q, t0, t0, eg, c8, rawA);
+    issue_raw<SWA8>(a, sh, q, t0, t0, eg, c8, rawA);
     unsigned kw[4][4], okb;
-    decode_tile(a, t0, eg, rawA, kw, &okb);
+    decode_tile<SWA8>(a, t0, eg, rawA, kw, &okb);
     store_tile(sh, 0, eg, c8, kw, okb);
-    if (t0 + 1 < t1) issue_raw(a, sh, q, t0 + 1, t0, eg, c8, rawA);
+    if (t0 + 1 < t1) issue_raw<SWA8>(a, sh, q, t0 + 1, t0, eg, c8, rawA);
   }
 
   // One tile: nxt holds the raw data of tile t+1, fut receives tile t+2's.
   auto step = [&](int t, RawSlot* nxt, RawSlot* fut) {
     const int b = (t - t0) & 1;
     __syncthreads();  // tile t is in Kt and vb[b]; sx, pl and alpha are free
-    if (t + 2 < t1) issue_raw(a, sh, q, t + 2, t0, eg, c8, fut);
+    if (t + 2 < t1) issue_raw<SWA8>(a, sh, q, t + 2, t0, eg, c8, fut);
 
     // ---- phase 1: S^T(t) over this wave's channel quarter; O^T += V^T(t-1) P^T(t-1)
     {
@@ -336,7 +400,7 @@ __global__ __launch_bounds__(NT, 1) void k_sparse_attn(AttnArgs a) {
     // ---- tile t+1 to LDS
     if (t + 1 < t1) {
       unsigned kw[4][4], okb;
-      decode_tile(a, t + 1, eg, nxt, kw, &okb);
+      decode_tile<SWA8>(a, t + 1, eg, nxt, kw, &okb);
       store_tile(sh, b ^ 1, eg, c8, kw, okb);
     }
     __syncthreads();  // P^T and the rescale factors of tile t are written
@@ -367,7 +431,9 @@ __global__ __launch_bounds__(NT, 1) void k_sparse_attn(AttnArgs a) {
   __syncthreads();
 
   // ---- epilogue: this wave's heads x channel quarter, O / l as bf16, into
-  // the output (one split) or this split's partial record
+  // the output (one split, rotary channels rotated back when a table is
+  // given) or this split's partial record (rotated after the merge)
+  const float* rope = (a.n_splits == 1 && a.rope && cc == 3) ? a.rope + (int64_t)q * 64 : nullptr;
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
     const int head = 32 * hh + 16 * hb + r16;
@@ -389,8 +455,12 @@ __global__ __launch_bounds__(NT, 1) void k_sparse_attn(AttnArgs a) {
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) {
       const int ch = cb * 16 + 4 * g;
-      __bf16 b0 = (__bf16)(o[cb][hb][0] * inv), b1 = (__bf16)(o[cb][hb][1] * inv);
-      __bf16 b2 = (__bf16)(o[cb][hb][2] * inv), b3 = (__bf16)(o[cb][hb][3] * inv);
+      float v0 = o[cb][hb][0] * inv, v1 = o[cb][hb][1] * inv, v2 = o[cb][hb][2] * inv, v3 = o[cb][hb][3] * inv;
+      if (cb >= 4 && rope) {  // channels 384 + ch >= 448: pairs (384 + ch - 448) / 2 and +1
+        unrotate(v0, v1, *(const float2*)(rope + (ch - 64)));  // the table is 8-B aligned
+        unrotate(v2, v3, *(const float2*)(rope + (ch - 62)));
+      }
+      __bf16 b0 = (__bf16)v0, b1 = (__bf16)v1, b2 = (__bf16)v2, b3 = (__bf16)v3;
       uint2 pk;
       pk.x = (unsigned)__builtin_bit_cast(uint16_t, b0) | ((unsigned)__builtin_bit_cast(uint16_t, b1) << 16);
       pk.y = (unsigned)__builtin_bit_cast(uint16_t, b2) | ((unsigned)__builtin_bit_cast(uint16_t, b3) << 16);
@@ -407,7 +477,8 @@ __global__ __launch_bounds__(NT, 1) void k_sparse_attn(AttnArgs a) {
 // (clamped indices, zero weight past the last split), so the merge costs a
 // few memory round trips however many splits there are.
 __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ partial, int n_splits,
-                                                      uint16_t* __restrict__ out, float* __restrict__ lse) {
+                                                      const float* __restrict__ rope, uint16_t* __restrict__ out,
+                                                      float* __restrict__ lse) {
   const int q = blockIdx.y, tid = threadIdx.x;
   const int h = blockIdx.x * 4 + (tid >> 6), c0 = (tid & 63) * 8;
   const float* base = partial + (int64_t)q * n_splits * kPartialFloats;
@@ -453,10 +524,17 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
     }
   }
   const float inv = (L > 0.f) ? 1.f / L : 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] *= inv;
+  if (rope && c0 >= kRopeFirst) {  // pairs (c0 - 448) / 2 .. +3
+    const float* cs = rope + (int64_t)q * 64 + (c0 - kRopeFirst);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) unrotate(acc[2 * j], acc[2 * j + 1], *(const float2*)(cs + 2 * j));
+  }
   v4u pk;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    __bf16 lo = (__bf16)(acc[2 * j] * inv), hi = (__bf16)(acc[2 * j + 1] * inv);
+    __bf16 lo = (__bf16)acc[2 * j], hi = (__bf16)acc[2 * j + 1];
     pk[j] = (unsigned)__builtin_bit_cast(uint16_t, lo) | ((unsigned)__builtin_bit_cast(uint16_t, hi) << 16);
   }
   *(v4u*)(out + ((int64_t)q * kHeads + h) * kDim + c0) = pk;
@@ -494,7 +572,9 @@ hipError_t launch_attn(const AttnLaunch& L, const AttnPlan& plan, float* partial
   a.main_cache = L.main_cache;
   a.idx = L.idx;
   a.q = L.q;
-  a.swa = L.swa;
+  a.swa = (const uint16_t*)L.swa;
+  a.swa8 = (const uint8_t*)L.swa;
+  a.rope = L.rope;
   a.out = L.out;
   a.lse = L.lse;
   a.partial = partial;
@@ -509,11 +589,14 @@ hipError_t launch_attn(const AttnLaunch& L, const AttnPlan& plan, float* partial
   a.n_splits = plan.n_splits;
   a.scale_log2 = L.scale * kLog2e;
   dim3 grid((unsigned)plan.n_splits, (unsigned)L.Q);
-  k_sparse_attn<<<grid, NT, 0, s>>>(a);
+  if (L.swa_fp8)
+    k_sparse_attn<true><<<grid, NT, 0, s>>>(a);
+  else
+    k_sparse_attn<false><<<grid, NT, 0, s>>>(a);
   if (plan.n_splits > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    k_attn_combine<<<dim3(16, (unsigned)L.Q), 256, 0, s>>>(partial, plan.n_splits, L.out, L.lse);
+    k_attn_combine<<<dim3(16, (unsigned)L.Q), 256, 0, s>>>(partial, plan.n_splits, L.rope, L.out, L.lse);
   }
   return hipGetLastError();
 }

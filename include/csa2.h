@@ -72,6 +72,8 @@ enum {
 #define CSA2_POOL_BLOCK 8          /* Reindex pools are built from blocks of 8   */
 #define CSA2_MAX_K 1024            /* largest supported top-k                    */
 #define CSA2_MAX_SWA 128           /* sliding-window rows per query              */
+#define CSA2_SWA_FP8_ROW_BYTES 528 /* 512 E4M3 codes + 16 E8M0 scales            */
+#define CSA2_ROPE_PAIRS 32         /* RoPE covers channels 448..511 in 32 pairs  */
 
 /* ------------------------------------------------------------- dequant */
 enum { CSA2_KIND_MAIN = 0, CSA2_KIND_INDEX = 1 };
@@ -185,23 +187,40 @@ typedef struct csa2_attn_args {
   const int32_t* idx;         /* [Q][k_sel] selected ids; ids outside [0,N) skipped */
   int32_t k_sel;              /* 0 <= k_sel <= CSA2_MAX_K                        */
   const uint16_t* q;          /* [Q][64][512] bf16, 16-B aligned                 */
-  const uint16_t* swa;        /* bf16 rows [..][512], 16-B aligned (NULL iff n_swa == 0) */
+  const void* swa;            /* window rows, 16-B aligned (NULL iff n_swa == 0): bf16 [..][512]
+                                 or FP8 [..][528], as swa_format says          */
   int64_t swa_q_stride;       /* query i's window = rows i*swa_q_stride + 0..n_swa-1 */
   int32_t n_swa;              /* 0 <= n_swa <= 128                               */
   float softmax_scale;        /* e.g. 1/sqrt(512)                                */
   uint16_t* out;              /* out [Q][64][512] bf16, 16-B aligned             */
   float* lse;                 /* out [Q][64] natural-log sum-exp of scaled logits, or NULL */
+  int32_t swa_format;         /* CSA2_SWA_BF16 or CSA2_SWA_FP8                   */
+  const float* rope_cos_sin;  /* [Q][32][2] (cos, sin) of each query's RoPE angles, 8-B
+                                 aligned, or NULL: no un-rotation of the output */
 } csa2_attn_args;
+
+/* Window row formats. The pages give the window cache as 128 entries of 528
+ * FP8 bytes ("An infra-oriented diagram ...", "The KV cache") without its
+ * scale layout; CSA2_SWA_FP8 reads it as OCP MXFP8: bytes 0..511 are E4M3FN
+ * codes of channels 0..511, bytes 512..527 are E8M0 scales, scale b for
+ * channels 32b..32b+31; value = E4M3(code) * 2^(scale - 127). */
+enum { CSA2_SWA_BF16 = 0, CSA2_SWA_FP8 = 1 };
 
 /* csa2_sparse_attn — attention of 64 query heads over one shared k = v latent
  * per entry ("An infra-oriented diagram ...", KV-latent bullet), for the joint
  * set J = selected entries (in idx order) followed by the n_swa window rows
  * (role bullet: the 128-token window plus 512 selected entries):
  *     o_h = sum_{j in J} softmax_j(scale * q_h . x_j) x_j
- * with x_j the dequantised latent (exact in bf16) or the bf16 SWA row. bf16
- * matrix-core products, fp32 accumulation and softmax, bf16 output. An empty
- * J gives zeros and lse = -inf. Also the whole path of a Reuse layer (given
- * ids) and of an SWA-only layer (k_sel = 0). Workspace:
+ * with x_j the dequantised latent (exact in bf16) or the window row (bf16, or
+ * FP8 decoded exactly to bf16 while the scaled value stays in bf16's normal
+ * range). bf16 matrix-core products, fp32 accumulation and softmax, bf16
+ * output. An empty J gives zeros and lse = -inf. Also the whole path of a
+ * Reuse layer (given ids) and of an SWA-only layer (k_sel = 0).
+ * RoPE un-rotation (KV-latent bullet: RoPE touches 64 of the 512 dims and is
+ * un-rotated on the attention output): with rope_cos_sin set, channels
+ * 448 + 2i and 449 + 2i of every head's normalised output (a, b) become
+ * (a c + b s, b c - a s) with (c, s) = rope_cos_sin[q][i], i < 32, before
+ * the bf16 rounding; lse is unchanged. Workspace:
  * csa2_workspace_size(CSA2_WS_ATTN, args) bytes, 256-B aligned. */
 CSA2_API int csa2_sparse_attn(const csa2_attn_args* args, void* workspace, size_t ws_bytes, void* stream);
 
@@ -212,7 +231,7 @@ typedef struct csa2_decode_args {
   int32_t k;                  /* top-k, 1..CSA2_MAX_K                            */
   const uint8_t* main_cache;  /* [rows][288], same row indexing as the keys      */
   const uint16_t* q;          /* [Q][64][512] bf16                               */
-  const uint16_t* swa;        /* bf16 window rows                                */
+  const void* swa;            /* window rows, format swa_format                  */
   int64_t swa_q_stride;
   int32_t n_swa;
   float softmax_scale;
@@ -222,6 +241,8 @@ typedef struct csa2_decode_args {
   void* stage_events[4];      /* optional hipEvent_t (as void*) recorded on the stream
                                  before scoring [0], after scoring [1], after
                                  selection [2] and after attention [3]; NULL = skip */
+  int32_t swa_format;         /* CSA2_SWA_BF16 or CSA2_SWA_FP8                   */
+  const float* rope_cos_sin;  /* [Q][32][2] or NULL, as in csa2_attn_args        */
 } csa2_decode_args;
 
 /* csa2_decode — the whole path for one batch: csa2_index_score ->

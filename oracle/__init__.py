@@ -40,9 +40,10 @@ def _bind(L):
     L.orc_dequant_index.argtypes = [vp, vp, i64, vp, vp]
     L.orc_index_score.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp]
     L.orc_topk.argtypes = [vp, i32, i64, vp, i64, vp, i32, i32, vp, vp]
-    L.orc_sparse_attn.argtypes = [i32, i64, i64, vp, vp, i32, vp, vp, i64, i32, dbl, vp, vp, vp, vp]
+    L.orc_sparse_attn.argtypes = [i32, i64, i64, vp, vp, i32, vp, vp, i64, i32, dbl, vp, vp, vp, vp, i32, vp]
     L.orc_decode.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp, i64, i32, dbl, vp, vp,
-                             vp, vp, vp]
+                             vp, vp, vp, i32, vp]
+    L.orc_dequant_swa_fp8.argtypes = [vp, i64, vp]
     L.orc_quantize_main.argtypes = [vp, i64, vp]
     L.orc_quantize_index.argtypes = [vp, i64, vp, vp]
     L.orc_set_threads.argtypes = [i32]
@@ -130,6 +131,18 @@ def quantize_index(x: np.ndarray, L=None):
     return codes, scales
 
 
+def dequant_swa_fp8(rows: np.ndarray, L=None) -> np.ndarray:
+    """FP8 window rows [n][528] -> exact values [n][512] (fp64)."""
+    rows = np.ascontiguousarray(rows, np.uint8).reshape(-1, 528)
+    out = np.empty((rows.shape[0], 512), np.float64)
+    (L or lib()).orc_dequant_swa_fp8(_p(rows), rows.shape[0], _p(out))
+    return out
+
+
+def _f32(a):
+    return None if a is None else np.ascontiguousarray(a, np.float32)
+
+
 def _i32(a):
     return None if a is None else np.ascontiguousarray(a, np.int32)
 
@@ -180,7 +193,7 @@ def sparse_attn(wl, idx: np.ndarray, want_probs: bool = False, L=None, queries=N
     probs = np.empty((Q, 64, k_sel + n_swa), np.float64) if want_probs else None
     (L or lib()).orc_sparse_attn(Q, wl.n_entries, wl_q["stride"], _p(wl_q["main_cache"]), _p(idx), k_sel,
                                  _p(wl_q["q"]), _p(wl_q["swa"]), wl_q["swa_q_stride"], n_swa, float(wl.scale), _p(ob),
-                                 _p(of), _p(lse), _p(probs))
+                                 _p(of), _p(lse), _p(probs), int(wl.swa_format), _p(wl_q["rope"]))
     return (ob, of, lse, probs) if want_probs else (ob, of, lse)
 
 
@@ -197,7 +210,7 @@ def decode(wl, L=None, queries=None):
                             _p(wl_q["iq_codes"]), _p(wl_q["iq_scales"]), _p(wl_q["w"]), _p(wl_q["cand_blocks"]),
                             wl.n_blocks, _p(wl_q["n_valid"]), k, _p(wl_q["main_cache"]), _p(wl_q["q"]),
                             _p(wl_q["swa"]), wl_q["swa_q_stride"], wl.n_swa, float(wl.scale), _p(ob), _p(of), _p(lse),
-                            _p(idx), _p(sc))
+                            _p(idx), _p(sc), int(wl.swa_format), _p(wl_q["rope"]))
     return dict(out_bf16=ob, out_f32=of, lse=lse, idx=idx, scores=sc)
 
 
@@ -208,7 +221,7 @@ def _subset(wl, queries):
         return dict(Q=wl.Q, stride=wl.cache_q_stride, key_codes=wl.key_codes, key_scales=wl.key_scales,
                     main_cache=wl.main_cache, iq_codes=wl.iq_codes, iq_scales=wl.iq_scales, w=wl.w, q=wl.q,
                     swa=wl.swa, swa_q_stride=wl.swa_q_stride, cand_blocks=_i32(wl.cand_blocks),
-                    n_valid=_i32(wl.n_valid))
+                    n_valid=_i32(wl.n_valid), rope=_f32(wl.rope))
     qs = list(queries)
     N, S = wl.n_entries, wl.cache_q_stride
     if S == 0:
@@ -231,4 +244,5 @@ def _subset(wl, queries):
                 w=np.ascontiguousarray(wl.w[qs]), q=np.ascontiguousarray(wl.q[qs]), swa=swa,
                 swa_q_stride=swa_stride,
                 cand_blocks=None if wl.cand_blocks is None else np.ascontiguousarray(wl.cand_blocks[qs], np.int32),
-                n_valid=None if wl.n_valid is None else np.ascontiguousarray(wl.n_valid[qs], np.int32))
+                n_valid=None if wl.n_valid is None else np.ascontiguousarray(wl.n_valid[qs], np.int32),
+                rope=None if wl.rope is None else np.ascontiguousarray(wl.rope[qs], np.float32))

@@ -38,6 +38,12 @@
  *       even code, saturating at 6) and the sign bit of x; a block whose scale
  *       is zero (main) or whose amax is zero (indexer) gets all-zero codes.
  *       NaN counts as a zero magnitude, +-inf as the largest one.
+ *   R14 a window row in FP8 (528 bytes, [ATLAS] "The KV cache") is OCP
+ *       MXFP8: 512 E4M3FN codes, then 16 E8M0 scales, one per 32 channels.
+ *   R15 RoPE un-rotation of the output ([ATLAS] KV-latent bullet): the rotary
+ *       channels are 448..511 in adjacent pairs (448+2i, 449+2i); a caller
+ *       table gives each query's (cos, sin) per pair; the pair (a, b) of the
+ *       normalised output becomes (a c + b s, b c - a s).
  *   (R9-R12 concern the workload and its generator; they are listed with the
  *   design notes.)
  */
@@ -342,6 +348,15 @@ ORC_API void orc_topk(const float* scores, int Q, int64_t n_cand, const int32_t*
   }
 }
 
+/* FP8 window row (R14): value = E4M3(code_c) * E8M0(scale_{c/32}). */
+static void swa_fp8_row_f64(const uint8_t* row, double* out512) {
+  for (int c = 0; c < 512; ++c) out512[c] = orc_e4m3(row[c]) * orc_e8m0(row[512 + c / 32]);
+}
+
+ORC_API void orc_dequant_swa_fp8(const uint8_t* rows, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) swa_fp8_row_f64(rows + (size_t)i * 528, out + (size_t)i * 512);
+}
+
 /* ------------------------------------------------------------------ O5 --- */
 /* Sparse attention, [ATLAS] role bullet (every non-SWA-only layer attends
  * over the 128-token window plus 512 selected entries) and KV-latent bullet
@@ -351,11 +366,13 @@ ORC_API void orc_topk(const float* scores, int Q, int64_t n_cand, const int32_t*
  * o_h = sum_j p_hj V_j, all in fp64. Outputs: bf16 (RNE) and/or fp32 of the
  * fp64 result, and optional lse_h = m_h + log(sum_j exp(l_hj - m_h)).
  * probs_out (optional, for tests): [Q][64][k_sel + n_swa] softmax weights in
- * joint-list order, with skipped slots left at 0. */
+ * joint-list order, with skipped slots left at 0. Window rows are bf16
+ * [..][512], or FP8 [..][528] (R14) when swa_fp8; rope_cs ([Q][32][2] or
+ * NULL) rotates the output's rotary pairs back (R15) before the rounding. */
 ORC_API void orc_sparse_attn(int Q, int64_t n_entries, int64_t cache_q_stride, const uint8_t* main_cache,
-                             const int32_t* idx, int k_sel, const uint16_t* q_bf16, const uint16_t* swa,
+                             const int32_t* idx, int k_sel, const uint16_t* q_bf16, const void* swa,
                              int64_t swa_q_stride, int n_swa, double scale, uint16_t* out_bf16, float* out_f32,
-                             float* lse, double* probs_out) {
+                             float* lse, double* probs_out, int swa_fp8, const float* rope_cs) {
 #pragma omp parallel for schedule(dynamic, 1)
   for (int qi = 0; qi < Q; ++qi) {
     int jmax = k_sel + n_swa;
@@ -369,8 +386,12 @@ ORC_API void orc_sparse_attn(int Q, int64_t n_entries, int64_t cache_q_stride, c
       slot[nj++] = j;
     }
     for (int r = 0; r < n_swa; ++r) {
-      const uint16_t* row = swa + (size_t)((int64_t)qi * swa_q_stride + r) * 512;
-      for (int c = 0; c < 512; ++c) kv[(size_t)nj * 512 + c] = bf16_to_f64(row[c]);
+      if (swa_fp8) {
+        swa_fp8_row_f64((const uint8_t*)swa + (size_t)((int64_t)qi * swa_q_stride + r) * 528, kv + (size_t)nj * 512);
+      } else {
+        const uint16_t* row = (const uint16_t*)swa + (size_t)((int64_t)qi * swa_q_stride + r) * 512;
+        for (int c = 0; c < 512; ++c) kv[(size_t)nj * 512 + c] = bf16_to_f64(row[c]);
+      }
       slot[nj++] = k_sel + r;
     }
     double* lg = (double*)malloc(sizeof(double) * (size_t)(nj > 0 ? nj : 1));
@@ -394,6 +415,14 @@ ORC_API void orc_sparse_attn(int Q, int64_t n_entries, int64_t cache_q_stride, c
         if (probs_out) probs_out[((size_t)qi * 64 + h) * jmax + slot[j]] = p;
         for (int c = 0; c < 512; ++c) o[c] += p * kv[(size_t)j * 512 + c];
       }
+      if (rope_cs) { /* R15 */
+        for (int i = 0; i < 32; ++i) {
+          double cs = rope_cs[((size_t)qi * 32 + i) * 2], sn = rope_cs[((size_t)qi * 32 + i) * 2 + 1];
+          double a = o[448 + 2 * i], b = o[449 + 2 * i];
+          o[448 + 2 * i] = a * cs + b * sn;
+          o[449 + 2 * i] = b * cs - a * sn;
+        }
+      }
       for (int c = 0; c < 512; ++c) {
         size_t at = ((size_t)qi * 64 + h) * 512 + c;
         if (out_bf16) out_bf16[at] = f64_to_bf16(o[c]);
@@ -413,9 +442,9 @@ ORC_API void orc_sparse_attn(int Q, int64_t n_entries, int64_t cache_q_stride, c
 ORC_API void orc_decode(int Q, int64_t n_entries, int64_t cache_q_stride, const uint8_t* key_codes,
                         const uint8_t* key_scales, const uint8_t* iq_codes, const uint8_t* iq_scales,
                         const float* w, const int32_t* cand_blocks, int n_blocks, const int32_t* n_valid, int k,
-                        const uint8_t* main_cache, const uint16_t* q_bf16, const uint16_t* swa,
+                        const uint8_t* main_cache, const uint16_t* q_bf16, const void* swa,
                         int64_t swa_q_stride, int n_swa, double scale, uint16_t* out_bf16, float* out_f32,
-                        float* lse, int32_t* idx_out, float* scores_out) {
+                        float* lse, int32_t* idx_out, float* scores_out, int swa_fp8, const float* rope_cs) {
   int64_t n_cand = cand_blocks ? 8 * (int64_t)n_blocks : n_entries;
   float* sc = scores_out ? scores_out : (float*)malloc(sizeof(float) * (size_t)Q * (size_t)(n_cand > 0 ? n_cand : 1));
   int32_t* id = idx_out ? idx_out : (int32_t*)malloc(sizeof(int32_t) * (size_t)Q * (size_t)(k > 0 ? k : 1));
@@ -423,7 +452,7 @@ ORC_API void orc_decode(int Q, int64_t n_entries, int64_t cache_q_stride, const 
                   n_valid, sc, NULL);
   orc_topk(sc, Q, n_cand, n_valid, n_entries, cand_blocks, n_blocks, k, id, NULL);
   orc_sparse_attn(Q, n_entries, cache_q_stride, main_cache, id, k, q_bf16, swa, swa_q_stride, n_swa, scale, out_bf16,
-                  out_f32, lse, NULL);
+                  out_f32, lse, NULL, swa_fp8, rope_cs);
   if (!scores_out) free(sc);
   if (!idx_out) free(id);
 }

@@ -32,6 +32,7 @@ N_HEADS = 64
 HEAD_DIM = 512
 TOPK = 512
 N_SWA = 128
+SWA_FP8_BYTES = 528
 BLOCK = 8
 
 
@@ -67,6 +68,7 @@ def lib():
         L.syn_pool_blocks.argtypes = [u64, u64, i64, i64, vp]
         L.syn_bf16_rows.argtypes = [u64, i32, u64, i64, i64, i32, vp]
         L.syn_f32_rows.argtypes = [u64, i32, u64, i64, i64, i32, vp]
+        L.syn_fp8_rows.argtypes = [u64, i32, u64, i64, i64, vp]
         _lib = L
     return _lib
 
@@ -138,6 +140,25 @@ def f32_rows(seed: int, tid: int, seq: int, first_row: int, n_rows: int, width: 
     return out
 
 
+def fp8_rows(seed: int, tid: int, seq: int, first_row: int, n_rows: int) -> np.ndarray:
+    """MXFP8 window rows [n_rows][528] of stream (tid, seq): the same N(0,1)
+    elements as ``bf16_rows(..., width=512)``, quantised to E4M3 codes with an
+    E8M0 scale per 32 channels."""
+    out = np.empty((n_rows, SWA_FP8_BYTES), np.uint8)
+    lib().syn_fp8_rows(seed, tid, seq, first_row, n_rows, _p(out))
+    return out
+
+
+def rope_table(positions, base: float = 10000.0) -> np.ndarray:
+    """(cos, sin) [len(positions)][32][2] fp32 of standard RoPE angles
+    position * base^(-2i/64) over the 32 rotary pairs (input data for the
+    attention epilogue's un-rotation; the model's own table may differ)."""
+    pos = np.asarray(positions, np.float64)[:, None]
+    inv_freq = base ** (-np.arange(0, 64, 2, dtype=np.float64) / 64.0)
+    ang = pos * inv_freq[None, :]
+    return np.ascontiguousarray(np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32))
+
+
 def pool_blocks(seed: int, seq: int, n_pick: int, n_total: int) -> np.ndarray:
     out = np.empty((n_pick,), np.int32)
     lib().syn_pool_blocks(seed, seq, n_pick, n_total, _p(out))
@@ -158,8 +179,10 @@ class Workload:
       main_cache  uint8 [rows][288]     key_codes uint8 [rows][64]   key_scales uint8 [rows][4]
       iq_codes    uint8 [Q][32][64]     iq_scales uint8 [Q][32][4]   w float32 [Q][32]
       q           uint16(bf16) [Q][64][512]
-      swa         uint16(bf16) [swa_rows][512]; query i's window starts at row i*swa_q_stride
+      swa         uint16(bf16) [swa_rows][512], or uint8 [swa_rows][528] FP8 rows when
+                  swa_format == 1; query i's window starts at row i*swa_q_stride
       cand_blocks int32 [Q][n_blocks] or None   n_valid int32 [Q] or None
+      rope        float32 [Q][32][2] (cos, sin) or None
     Query i's cache occupies rows [i*cache_q_stride, i*cache_q_stride + n_entries).
     Entries listed in ``sparse_rows`` (if not None) are the only ones holding data;
     all other rows are poison.
@@ -184,6 +207,8 @@ class Workload:
     k: int = TOPK
     scale: float = 1.0 / np.sqrt(512.0)
     extra: dict = field(default_factory=dict)
+    swa_format: int = 0
+    rope: Optional[np.ndarray] = None
 
     @property
     def n_blocks(self) -> int:
@@ -194,16 +219,41 @@ class Workload:
         return self.n_blocks * BLOCK if self.cand_blocks is not None else self.n_entries
 
 
-def _queries(seed, Q, swa_rows_per_query, shared_swa_rows=None):
+def _swa_rows(seed, seq, n_rows, fp8):
+    return fp8_rows(seed, TID_SWA, seq, 0, n_rows) if fp8 else bf16_rows(seed, TID_SWA, seq, 0, n_rows, HEAD_DIM)
+
+
+def _queries(seed, Q, swa_rows_per_query, shared_swa_rows=None, swa_fp8=False):
     iq_codes, iq_scales = index_queries(seed, 0, Q)
     w = head_weights(seed, 0, Q)
     q = np.stack([bf16_rows(seed, TID_Q, i, 0, N_HEADS, HEAD_DIM) for i in range(Q)])
     if shared_swa_rows is None:
-        swa = np.stack([bf16_rows(seed, TID_SWA, i, 0, swa_rows_per_query, HEAD_DIM) for i in range(Q)])
-        swa = swa.reshape(Q * swa_rows_per_query, HEAD_DIM)
+        swa = np.stack([_swa_rows(seed, i, swa_rows_per_query, swa_fp8) for i in range(Q)])
+        swa = swa.reshape(Q * swa_rows_per_query, -1)
     else:
-        swa = bf16_rows(seed, TID_SWA, 0, 0, shared_swa_rows, HEAD_DIM)
-    return iq_codes, iq_scales, w, q, swa
+        swa = _swa_rows(seed, 0, shared_swa_rows, swa_fp8)
+    return iq_codes, iq_scales, w, q, np.ascontiguousarray(swa)
+
+
+def with_window_options(wl: Workload, positions=None, swa_fp8: bool = False, rope: bool = False) -> Workload:
+    """Attach the optional window format and RoPE table to a built workload:
+    ``swa_fp8`` regenerates its window rows as FP8 from the same streams
+    (row layout unchanged), ``rope`` adds the (cos, sin) table of ``positions``
+    (default: entry count + 7 i for decode queries)."""
+    seed = wl.extra.get("seed", 0)
+    if swa_fp8:
+        if wl.extra.get("shared_swa"):
+            wl.swa = _swa_rows(seed, 0, wl.swa.shape[0], True)
+        else:
+            per = wl.swa.shape[0] // max(wl.Q, 1)
+            wl.swa = np.ascontiguousarray(np.concatenate([_swa_rows(seed, i, per, True) for i in range(wl.Q)])
+                                          if wl.Q else np.zeros((0, SWA_FP8_BYTES), np.uint8))
+        wl.swa_format = 1
+    if rope:
+        if positions is None:
+            positions = (wl.extra["t0"] + np.arange(wl.Q)) if "t0" in wl.extra else wl.n_entries + 7 * np.arange(wl.Q)
+        wl.rope = rope_table(positions)
+    return wl
 
 
 def full_decode(Q: int, N: int, seed: int = 0, n_swa: int = N_SWA, name: str = "full_decode") -> Workload:
@@ -211,8 +261,10 @@ def full_decode(Q: int, N: int, seed: int = 0, n_swa: int = N_SWA, name: str = "
     main = np.concatenate([main_latents(seed, i, 0, N) for i in range(Q)]) if N else np.zeros((0, MAIN_BYTES), np.uint8)
     kc, ks = zip(*[index_keys(seed, i, 0, N) for i in range(Q)]) if N else ((np.zeros((0, 64), np.uint8),), (np.zeros((0, 4), np.uint8),))
     iq_codes, iq_scales, w, q, swa = _queries(seed, Q, n_swa)
-    return Workload(name, Q, N, N, main, np.concatenate(kc), np.concatenate(ks), iq_codes, iq_scales, w, q,
-                    swa, n_swa, n_swa)
+    wl = Workload(name, Q, N, N, main, np.concatenate(kc), np.concatenate(ks), iq_codes, iq_scales, w, q,
+                  swa, n_swa, n_swa)
+    wl.extra["seed"] = seed
+    return wl
 
 
 def reindex_decode(Q: int, N: int, n_blocks: int, seed: int = 0, dense_rows: bool = True,
@@ -249,6 +301,7 @@ def reindex_decode(Q: int, N: int, n_blocks: int, seed: int = 0, dense_rows: boo
                       cand_blocks=blocks.astype(np.int32))
     wl.extra["pool_rows"] = pool_rows
     wl.extra["dense_rows"] = dense_rows
+    wl.extra["seed"] = seed
     return wl
 
 
@@ -264,6 +317,8 @@ def prefill(T: int, n_cache: int, t0: int, seed: int = 0, m: int = 2, name: str 
     n_valid = np.minimum(n_valid, n_cache).astype(np.int32)
     wl = Workload(name, T, n_cache, 0, main, kc, ks, iq_codes, iq_scales, w, q, swa, 1, N_SWA, n_valid=n_valid)
     wl.extra["t0"] = t0
+    wl.extra["seed"] = seed
+    wl.extra["shared_swa"] = True
     return wl
 
 

@@ -240,6 +240,36 @@ static uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+/* FP8 window rows (512 channels, 528 bytes each): rows [first_row, +n_rows)
+ * of stream (tid, seq), row r using elements r*512 + c, quantised as OCP
+ * MXFP8: per 32 channels an E8M0 scale 2^e with e the smallest integer in
+ * [-127, 127] such that 448 * 2^e >= amax (0 for an all-zero block), codes
+ * E4M3FN(x / 2^e) rounded to nearest even, saturating at 448. Layout: 512
+ * codes (byte c = channel c), then the 16 scale bytes. */
+SYN_API void syn_fp8_rows(uint64_t seed, int tid, uint64_t seq, int64_t first_row, int64_t n_rows, uint8_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    double x[512];
+    ctr_normals(seed, (uint64_t)tid, seq, (uint64_t)(first_row + r) * 512u, 512, x);
+    uint8_t* o = out + (size_t)r * 528;
+    for (int b = 0; b < 16; ++b) {
+      double amax = 0.0;
+      for (int c = 0; c < 32; ++c) amax = fmax(amax, fabs(x[32 * b + c]));
+      int e = 0;
+      if (amax > 0.0) {
+        e = -127;
+        while (e < 127 && 448.0 * ldexp(1.0, e) < amax) ++e;
+      }
+      o[512 + b] = (uint8_t)(e + 127);
+      for (int c = 0; c < 32; ++c) {
+        double v = ldexp(x[32 * b + c], -e);
+        unsigned code = enc_e4m3_pos(fabs(v));
+        o[32 * b + c] = (uint8_t)(code | (v < 0.0 ? 0x80u : 0u));
+      }
+    }
+  }
+}
+
 /* fp32 N(0,1) rows: rows [first_row, first_row + n_rows) of width `width`
  * (even) of stream (tid, seq), row r using elements r*width + c. On the
  * main-latent and indexer-key streams these are the unquantised values the

@@ -33,7 +33,8 @@ def to_device(wl, device="cuda") -> DeviceBatch:
     return DeviceBatch(
         Q=wl.Q, n_entries=wl.n_entries, cache_q_stride=wl.cache_q_stride, main_cache=main, key_codes=kc,
         key_scales=ks, iq_codes=_t(wl.iq_codes, device), iq_scales=_t(wl.iq_scales, device), w=_t(wl.w, device),
-        q=_t(wl.q, device, torch.int16), swa=_t(wl.swa, device, torch.int16), swa_q_stride=wl.swa_q_stride,
-        n_swa=wl.n_swa, k=wl.k, scale=float(wl.scale),
+        q=_t(wl.q, device, torch.int16), swa=_t(wl.swa, device, None if wl.swa_format else torch.int16),
+        swa_q_stride=wl.swa_q_stride, n_swa=wl.n_swa, k=wl.k, scale=float(wl.scale),
         cand_blocks=None if wl.cand_blocks is None else _t(wl.cand_blocks.astype(np.int32), device),
-        n_valid=None if wl.n_valid is None else _t(wl.n_valid.astype(np.int32), device))
+        n_valid=None if wl.n_valid is None else _t(wl.n_valid.astype(np.int32), device),
+        swa_format=int(wl.swa_format), rope=None if wl.rope is None else _t(wl.rope.astype(np.float32), device))

@@ -14,6 +14,7 @@ disagrees with:
 """
 from __future__ import annotations
 
+import copy
 import math
 import os
 
@@ -468,5 +469,67 @@ def check_quantize(L, seed=21):
     assert list(cc[1, :8]) == [7, *_AT_MID] and not cc[1, 64:80].any()
 
 
+# ------------------------------------------------- window format and RoPE ---
+
+def _with(wl, **kw):
+    w2 = copy.copy(wl)
+    w2.extra = dict(wl.extra)
+    for k, v in kw.items():
+        setattr(w2, k, v)
+    return w2
+
+
+def check_window_options(L, seed=23):
+    # (1) FP8 window rows (R14): codes through torch's float8_e4m3fn, scales
+    # through float8_e8m0fnu, scale b for channels 32b..32b+31
+    rows = synth.fp8_rows(seed, synth.TID_SWA, 0, 0, 40)
+    sweep = np.zeros((2, 528), np.uint8)
+    sweep[0, :512] = np.arange(512) % 256
+    sweep[0, 512:] = np.arange(112, 128)
+    sweep[1, :512] = (np.arange(512) * 7) % 256
+    sweep[1, 512:] = np.arange(120, 136)
+    for r in (rows, sweep):
+        ref = lib_e4m3(r[:, :512]) * np.repeat(lib_e8m0(r[:, 512:]), 32, axis=1)
+        got = oracle.dequant_swa_fp8(r, L)
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(got), nan) and np.array_equal(got[~nan], ref[~nan])
+
+    # (2) attention over FP8 rows equals attention over the same values as bf16 rows
+    wl = synth.full_decode(3, 600, seed=seed)
+    idx = np.stack([np.random.default_rng(seed + i).choice(600, 512, replace=False) for i in range(3)]).astype(np.int32)
+    wl8 = synth.with_window_options(_with(wl), swa_fp8=True)
+    vals = lib_e4m3(wl8.swa[:, :512]) * np.repeat(lib_e8m0(wl8.swa[:, 512:]), 32, axis=1)
+    vb = torch.from_numpy(vals.astype(np.float32)).to(torch.bfloat16)
+    assert np.array_equal(vb.to(torch.float64).numpy(), vals)  # exact in bf16
+    wlb = _with(wl, swa=np.ascontiguousarray(vb.view(torch.int16).numpy().view(np.uint16)), swa_format=0)
+    a8, b8 = oracle.sparse_attn(wl8, idx, L=L), oracle.sparse_attn(wlb, idx, L=L)
+    for x, y in zip(a8, b8):
+        assert np.array_equal(x.view(np.uint32) if x.dtype == np.float32 else x,
+                              y.view(np.uint32) if y.dtype == np.float32 else y)
+
+    # (3) RoPE un-rotation (R15) of the rotary pairs (448 + 2i, 449 + 2i)
+    plain = oracle.sparse_attn(wl, idx, L=L)
+    ident = np.zeros((3, 32, 2), np.float32)
+    ident[:, :, 0] = 1.0
+    got = oracle.sparse_attn(_with(wl, rope=ident), idx, L=L)
+    assert np.array_equal(got[0], plain[0]) and np.array_equal(got[1], plain[1])
+    quarter = np.zeros((3, 32, 2), np.float32)
+    quarter[:, :, 1] = 1.0  # cos 0, sin 1: (a, b) -> (b, -a)
+    got = oracle.sparse_attn(_with(wl, rope=quarter), idx, L=L)[1]
+    pf = plain[1]
+    assert np.array_equal(got[:, :, :448], pf[:, :, :448])
+    assert np.array_equal(got[:, :, 448::2], pf[:, :, 449::2])
+    assert np.array_equal(got[:, :, 449::2], -pf[:, :, 448::2])
+    tab = synth.rope_table(600 + 7 * np.arange(3))
+    un = oracle.sparse_attn(_with(wl, rope=tab), idx, L=L)
+    assert np.array_equal(un[2], plain[2])  # lse unchanged
+    a, b = un[1][:, :, 448::2].astype(np.float64), un[1][:, :, 449::2].astype(np.float64)
+    c, sn = tab[:, None, :, 0].astype(np.float64), tab[:, None, :, 1].astype(np.float64)
+    fa, fb = a * c - b * sn, a * sn + b * c  # forward rotation by the same angles
+    tol = 1e-6 * np.abs(pf).max()
+    assert np.abs(fa - pf[:, :, 448::2]).max() <= tol and np.abs(fb - pf[:, :, 449::2]).max() <= tol
+    assert np.array_equal(un[1][:, :, :448], pf[:, :, :448])
+
+
 ALL_CHECKS = [check_format_tables, check_layout, check_dequant, check_index_scores, check_candidate_sets,
-              check_topk, check_attention, check_decode_composition, check_quantize]
+              check_topk, check_attention, check_decode_composition, check_quantize, check_window_options]

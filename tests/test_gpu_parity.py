@@ -362,6 +362,35 @@ def test_sparse_attn_edge_cases():
     assert np.all(ob == 0) and np.all(np.isneginf(glse))
 
 
+@pytest.mark.parametrize("Q,fp8,rope", [(1, True, True), (3, True, False), (2, False, True), (40, True, True),
+                                         (700, True, True)])
+def test_sparse_attn_fp8_window_and_rope(Q, fp8, rope):
+    """FP8 (MXFP8, 528-B) window rows and the RoPE un-rotation epilogue, in
+    the split (small Q, merged by the combine kernel) and unsplit layouts."""
+    wl = synth.with_window_options(synth.full_decode(Q, 600, seed=50 + Q), swa_fp8=fp8, rope=rope)
+    rng = np.random.default_rng(Q)
+    idx = np.stack([rng.choice(600, 512, replace=False) for _ in range(Q)]).astype(np.int32)
+    _, of, lse = oracle.sparse_attn(wl, idx)
+    ob, glse = gpu_attn(to_device(wl), idx)
+    check_attn(ob, of, f"attn fp8={fp8} rope={rope} Q{Q}")
+    check_lse(glse, lse, "lse")
+
+
+def test_sparse_attn_fp8_window_edge_cases():
+    wl = synth.with_window_options(synth.full_decode(2, 300, seed=6, n_swa=37), swa_fp8=True, rope=True)
+    db = to_device(wl)
+    _, of, lse = oracle.sparse_attn(wl, np.zeros((2, 0), np.int32))  # window only, ragged
+    ob, glse = gpu_attn(db, None)
+    check_attn(ob, of, "fp8 window only")
+    check_lse(glse, lse, "fp8 window only lse")
+    rng = np.random.default_rng(6)
+    idx = np.full((2, 45), -1, np.int32)  # mixed tile: selection ends inside a tile
+    idx[:, :40] = rng.choice(300, 40, replace=False)
+    _, of, lse = oracle.sparse_attn(wl, idx)
+    ob, glse = gpu_attn(db, idx)
+    check_attn(ob, of, "fp8 mixed tile")
+
+
 # ------------------------------------------------------------ fused decode
 
 def _check_decode(wl, queries=None, what=""):
@@ -381,6 +410,16 @@ def _check_decode(wl, queries=None, what=""):
 
 def test_decode_full_small():
     _check_decode(synth.full_decode(2, 4096 + 300, seed=21), what="full small")
+
+
+def test_decode_fp8_window_and_rope():
+    wl = synth.with_window_options(synth.full_decode(3, 3000, seed=24), swa_fp8=True, rope=True)
+    _check_decode(wl, what="decode fp8 rope")
+
+
+def test_decode_prefill_fp8_window_and_rope():
+    wl = synth.with_window_options(synth.prefill(40, 2048, 3000, seed=25), swa_fp8=True, rope=True)
+    _check_decode(wl, what="prefill fp8 rope")
 
 
 def test_decode_reindex_small_poisoned():

@@ -43,6 +43,12 @@ MUTANTS = [
      "codes[ch >> 1] |= (uint8_t)(code << ((ch & 1) ? 0 : 4));"),
     ("quant_zero_scale_codes", "if (s == 0.0) continue;", ""),
     ("quant_amax_one_channel", "double a = abs_or_zero(xi[16 * g + c]);", "double a = abs_or_zero(xi[16 * g]);"),
+    ("swa_fp8_scale_block", "orc_e8m0(row[512 + c / 32])", "orc_e8m0(row[512 + c / 16 % 16])"),
+    ("swa_fp8_row_stride", "* 528, kv + (size_t)nj * 512);", "* 512, kv + (size_t)nj * 512);"),
+    ("rope_sign", "o[449 + 2 * i] = b * cs - a * sn;", "o[449 + 2 * i] = b * cs + a * sn;"),
+    ("rope_offset", "double a = o[448 + 2 * i], b = o[449 + 2 * i];", "double a = o[446 + 2 * i], b = o[447 + 2 * i];"),
+    ("rope_cos_sin_swapped", "double cs = rope_cs[((size_t)qi * 32 + i) * 2], sn = rope_cs[((size_t)qi * 32 + i) * 2 + 1];",
+     "double sn = rope_cs[((size_t)qi * 32 + i) * 2], cs = rope_cs[((size_t)qi * 32 + i) * 2 + 1];"),
     ("quant_mx_zero_block", "if (amax > 0.0) {\n        e = -127;", "if (amax >= 0.0) {\n        e = -127;"),
 ]
 
