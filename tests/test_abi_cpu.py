@@ -130,7 +130,8 @@ def test_validation_rejects_before_launch():
     aa = csa.AttnArgs(ctypes.sizeof(csa.AttnArgs), 4, 100, 100, A, A, 512, A, A, 128, 128, 0.04, A, None)
     for field, value, code in (("k_sel", 1025, csa.CSA2_ERR_SHAPE), ("n_swa", 129, csa.CSA2_ERR_SHAPE),
                                ("swa", None, csa.CSA2_ERR_NULL), ("q", A + 4, csa.CSA2_ERR_ALIGN),
-                               ("out", None, csa.CSA2_ERR_NULL), ("idx", None, csa.CSA2_ERR_NULL)):
+                               ("out", None, csa.CSA2_ERR_NULL), ("idx", None, csa.CSA2_ERR_NULL),
+                               ("swa_format", 2, csa.CSA2_ERR_ARG), ("rope_cos_sin", A + 4, csa.CSA2_ERR_ALIGN)):
         bad = csa.AttnArgs.from_buffer_copy(aa)
         setattr(bad, field, value)
         assert L.csa2_sparse_attn(ctypes.byref(bad), A, 1 << 30, None) == code, field
@@ -143,6 +144,9 @@ def test_validation_rejects_before_launch():
     bad = csa.DecodeArgs.from_buffer_copy(da)
     bad.k = 0
     assert L.csa2_decode(ctypes.byref(bad), A, 1 << 30, None) == csa.CSA2_ERR_SHAPE
+    bad = csa.DecodeArgs.from_buffer_copy(da)
+    bad.swa_format = -1
+    assert L.csa2_decode(ctypes.byref(bad), A, 1 << 30, None) == csa.CSA2_ERR_ARG
     need = csa.csa2_workspace_size(csa.CSA2_WS_DECODE, da)
     assert need >= 2 * 100 * 4
     assert L.csa2_decode(ctypes.byref(da), A, need - 1, None) == csa.CSA2_ERR_WORKSPACE
