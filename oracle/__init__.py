@@ -44,6 +44,7 @@ def _bind(L):
     L.orc_decode.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp, i64, i32, dbl, vp, vp,
                              vp, vp, vp, i32, vp]
     L.orc_dequant_swa_fp8.argtypes = [vp, i64, vp]
+    L.orc_pool_blocks.argtypes = [vp, i32, i64, vp, i32, vp]
     L.orc_quantize_main.argtypes = [vp, i64, vp]
     L.orc_quantize_index.argtypes = [vp, i64, vp, vp]
     L.orc_set_threads.argtypes = [i32]
@@ -177,6 +178,16 @@ def topk(scores: np.ndarray, wl=None, k: int = 512, n_valid=None, n_entries=None
     ts = np.empty((Q, k), np.float32)
     (L or lib()).orc_topk(_p(scores), Q, n_cand, _p(_i32(n_valid)), n_entries, _p(cb), nb, k, _p(idx), _p(ts))
     return idx, ts
+
+
+def pool_blocks(scores: np.ndarray, n_pool: int = 2048, n_valid=None, L=None) -> np.ndarray:
+    """Reindex pool [Q][n_pool] (ascending block ids, -1 padded) from Full-layer
+    scores [Q][n_entries] and an optional causal limit [Q]."""
+    scores = np.ascontiguousarray(scores, np.float32)
+    Q, n = scores.shape
+    out = np.empty((Q, n_pool), np.int32)
+    (L or lib()).orc_pool_blocks(_p(scores), Q, n, _p(_i32(n_valid)), n_pool, _p(out))
+    return out
 
 
 def sparse_attn(wl, idx: np.ndarray, want_probs: bool = False, L=None, queries=None, n_swa=None):

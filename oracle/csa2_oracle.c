@@ -44,6 +44,11 @@
  *       channels are 448..511 in adjacent pairs (448+2i, 449+2i); a caller
  *       table gives each query's (cos, sin) per pair; the pair (a, b) of the
  *       normalised output becomes (a c + b s, b c - a s).
+ *   R16 a Reindex pool ([ATLAS] indexer bullet: a 16,384-entry pool that
+ *       layer 20 chose by blocks of 8) is built from that layer's own scores:
+ *       a block scores the best of its entries inside the causal limit (rank
+ *       order of R5); the n_pool best blocks by (block score descending, block
+ *       id ascending) are kept and listed in ascending block id, -1 padded.
  *   (R9-R12 concern the workload and its generator; they are listed with the
  *   design notes.)
  */
@@ -355,6 +360,40 @@ static void swa_fp8_row_f64(const uint8_t* row, double* out512) {
 
 ORC_API void orc_dequant_swa_fp8(const uint8_t* rows, int64_t n, double* out) {
   for (int64_t i = 0; i < n; ++i) swa_fp8_row_f64(rows + (size_t)i * 528, out + (size_t)i * 512);
+}
+
+/* ------------------------------------------------------------------ O8 --- */
+/* Reindex pool construction (R16): block b covers entries 8b..8b+7 (R6); its
+ * score is the best valid entry score in the top-k order (NaN below every
+ * number, -0 == +0); the n_pool best blocks are chosen exactly as O4 chooses
+ * entries. out: [Q][n_pool] ascending block ids, -1 padded. */
+static int score_better(float x, float y) { /* x ranks above y */
+  if (isnan(x)) return 0;
+  if (isnan(y)) return 1;
+  return x > y;
+}
+
+ORC_API void orc_pool_blocks(const float* scores, int Q, int64_t n_entries, const int32_t* n_valid, int n_pool,
+                             int32_t* out) {
+  int64_t nb = (n_entries + 7) / 8;
+  float* bs = (float*)malloc(sizeof(float) * (size_t)(Q > 0 ? Q : 1) * (size_t)(nb > 0 ? nb : 1));
+  int32_t* nvb = (int32_t*)malloc(sizeof(int32_t) * (size_t)(Q > 0 ? Q : 1));
+  for (int q = 0; q < Q; ++q) {
+    int64_t lim = n_entries;
+    if (n_valid && n_valid[q] < lim) lim = n_valid[q] < 0 ? 0 : n_valid[q];
+    nvb[q] = (int32_t)((lim + 7) / 8);
+    for (int64_t b = 0; b < nb; ++b) {
+      float best = NAN;
+      for (int64_t e = 8 * b; e < 8 * b + 8 && e < lim; ++e) {
+        float x = scores[(size_t)q * (size_t)n_entries + (size_t)e];
+        if (e == 8 * b || score_better(x, best)) best = x;
+      }
+      bs[(size_t)q * (size_t)nb + (size_t)b] = best;
+    }
+  }
+  orc_topk(bs, Q, nb, nvb, nb, NULL, 0, n_pool, out, NULL);
+  free(nvb);
+  free(bs);
 }
 
 /* ------------------------------------------------------------------ O5 --- */

@@ -531,5 +531,55 @@ def check_window_options(L, seed=23):
     assert np.array_equal(un[1][:, :, :448], pf[:, :, :448])
 
 
+# ------------------------------------------------------- pool construction ---
+
+def _ref_pool(scores_row: np.ndarray, lim: int, n_pool: int) -> list:
+    """Brute force of R16: block max over valid entries (NaN lowest), then a
+    plain sort by (score desc, block asc) with NaN last."""
+    n = len(scores_row)
+    nb_valid = (min(lim, n) + 7) // 8
+    blocks = []
+    for b in range(nb_valid):
+        seg = scores_row[8 * b:min(8 * b + 8, lim)].astype(np.float64)
+        num = seg[~np.isnan(seg)]
+        best = float(num.max()) if num.size else float("nan")
+        blocks.append((b, best))
+    blocks.sort(key=lambda t: (1, 0.0, t[0]) if math.isnan(t[1]) else (0, -t[1], t[0]))
+    keep = sorted(b for b, _ in blocks[:n_pool])
+    return keep + [-1] * (n_pool - len(keep))
+
+
+def check_pool(L, seed=29):
+    rng = np.random.default_rng(seed)
+    # random scores with ties (coarse grid), NaNs, -0 / +0 and -inf
+    n = 8 * 300 + 5  # ragged last block
+    sc = np.round(rng.standard_normal((4, n)) * 4) / 4
+    sc = sc.astype(np.float32)
+    sc[0, rng.integers(0, n, 200)] = np.nan
+    sc[1, ::7] = -0.0
+    sc[1, 3::7] = 0.0
+    sc[2, rng.integers(0, n, 100)] = -np.inf
+    sc[3, :] = 1.0  # every block ties: the lowest ids win
+    n_valid = np.array([n, 1001, 8 * 17 + 3, 777], np.int32)
+    for n_pool in (1, 16, 100, 303):
+        got = oracle.pool_blocks(sc, n_pool, n_valid, L=L)
+        for q in range(4):
+            assert list(got[q]) == _ref_pool(sc[q], int(n_valid[q]), n_pool), (n_pool, q)
+    # a straddling block ignores its entries past the limit
+    s1 = np.zeros((1, 64), np.float32)
+    s1[0, 13] = 100.0  # entry 13 lies in block 1, past a limit of 12
+    s1[0, 2] = 1.0
+    assert list(oracle.pool_blocks(s1, 1, np.array([12], np.int32), L=L)[0]) == [0]
+    assert list(oracle.pool_blocks(s1, 1, np.array([14], np.int32), L=L)[0]) == [1]
+    # more blocks requested than valid: all valid blocks in order, then -1
+    got = oracle.pool_blocks(s1, 5, np.array([20], np.int32), L=L)[0]
+    assert list(got) == [0, 1, 2, -1, -1]
+    # no limit given: the whole row, and the last block is the ragged one
+    s2 = np.full((1, 21), -1.0, np.float32)
+    s2[0, 20] = 5.0
+    assert list(oracle.pool_blocks(s2, 1, L=L)[0]) == [2]
+
+
 ALL_CHECKS = [check_format_tables, check_layout, check_dequant, check_index_scores, check_candidate_sets,
-              check_topk, check_attention, check_decode_composition, check_quantize, check_window_options]
+              check_topk, check_attention, check_decode_composition, check_quantize, check_window_options,
+              check_pool]

@@ -49,6 +49,13 @@ MUTANTS = [
     ("rope_offset", "double a = o[448 + 2 * i], b = o[449 + 2 * i];", "double a = o[446 + 2 * i], b = o[447 + 2 * i];"),
     ("rope_cos_sin_swapped", "double cs = rope_cs[((size_t)qi * 32 + i) * 2], sn = rope_cs[((size_t)qi * 32 + i) * 2 + 1];",
      "double sn = rope_cs[((size_t)qi * 32 + i) * 2], cs = rope_cs[((size_t)qi * 32 + i) * 2 + 1];"),
+    ("pool_block_of_4", "for (int64_t e = 8 * b; e < 8 * b + 8 && e < lim; ++e) {",
+     "for (int64_t e = 8 * b; e < 8 * b + 4 && e < lim; ++e) {"),
+    ("pool_min_not_max", "if (e == 8 * b || score_better(x, best)) best = x;",
+     "if (e == 8 * b || score_better(best, x)) best = x;"),
+    ("pool_ignores_limit", "for (int64_t e = 8 * b; e < 8 * b + 8 && e < lim; ++e) {",
+     "for (int64_t e = 8 * b; e < 8 * b + 8 && e < n_entries; ++e) {"),
+    ("pool_nan_ranks_high", "  if (isnan(x)) return 0;\n  if (isnan(y)) return 1;", "  if (isnan(x)) return 1;\n  if (isnan(y)) return 0;"),
     ("quant_mx_zero_block", "if (amax > 0.0) {\n        e = -127;", "if (amax >= 0.0) {\n        e = -127;"),
 ]
 
