@@ -52,6 +52,7 @@ SCORE_SOURCES = ("index_score.hip", "csa2_device.h")
 CSRC = os.path.join(ROOT, "compressed_sparse_attention_score_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_index_score_hbm_traffic.md")
 COPY_MIB = 512
+POOL_BLOCKS = 2048                  # Reindex pool: 16,384 entries in blocks of 8
 CACHE_WRITE_ROWS = 131072           # new entries quantised per cache-write launch (a long prefill chunk)
 
 
@@ -332,7 +333,7 @@ def main():
                      dtype=torch.uint8, device="cuda")
     K, W = args.steps, args.warmup
     S = min(K, 50)
-    ev = HipEvents(2 + 4 * S + 10)
+    ev = HipEvents(2 + 4 * S + 12)
 
     # ---- phase 1: timed decode steps
     dec_args = [reps[i % R].decode_args(out, lse, idx) for i in range(R)]
@@ -374,6 +375,24 @@ def main():
     ev.record(e0 + 1, stream)
     torch.cuda.synchronize()
     score_ms = ev.ms(e0, e0 + 1) / K
+    # Reindex pool construction from these Full-layer scores (decode layouts
+    # over a whole cache only): 2,048 blocks of 8, or every block if fewer
+    pool_ms = None
+    if wl.cand_blocks is None and wl.n_valid is None:
+        n_pool = int(min(POOL_BLOCKS, (wl.n_cand + 7) // 8))
+        pool_out = torch.empty((Q, n_pool), dtype=torch.int32, device="cuda")
+        pa = csa.pool_args(scores, n_pool, pool_out)
+        pool_ws = torch.empty(max(1, csa.csa2_workspace_size(csa.CSA2_WS_POOL, pa)), dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            csa.csa2_build_pool(pa, pool_ws, stream)
+        torch.cuda.synchronize()
+        ev.record(e0 + 10, stream)
+        for _ in range(K):
+            csa.csa2_build_pool(pa, pool_ws, stream)
+        ev.record(e0 + 11, stream)
+        torch.cuda.synchronize()
+        pool_ms = ev.ms(e0 + 10, e0 + 11) / K
+        del pool_out, pool_ws
     at_out = torch.empty_like(out)
     at_lse = torch.empty_like(lse)
     at_args = [reps[i % R].attn_args(idx, at_out, at_lse) for i in range(R)]
@@ -460,6 +479,11 @@ def main():
             "algorithmic_bytes": work["attn_fp8_bytes"],
             "GB_s": round(work["attn_fp8_bytes"] / (attn8_ms * 1e-3) / 1e9, 1)},
     }
+    if pool_ms is not None:
+        pb = Q * (4 * wl.n_cand + 4 * n_pool)  # scores read once, pool ids written
+        kernels["build_pool"] = {"kernels": ["k_block_max", "k_score_maxima", "k_select_*"], "blocks_kept": n_pool,
+                                 "us_per_launch": round(1e3 * pool_ms, 3), "algorithmic_bytes": pb,
+                                 "GB_s": round(pb / (pool_ms * 1e-3) / 1e9, 1)}
     for kname, kind, ms_ in (("quantize_main", "k_quantize<f32, main>", q_ms[0]),
                              ("quantize_index", "k_quantize<f32, index>", q_ms[1])):
         per_row = (512 * 4 + ENTRY_BYTES_MAIN) if kname == "quantize_main" else (128 * 4 + ENTRY_BYTES_INDEX)

@@ -21,8 +21,8 @@ CSA2_KIND_MAIN, CSA2_KIND_INDEX = 0, 1
 CSA2_OUT_F32, CSA2_OUT_BF16 = 0, 1
 CSA2_IN_F32, CSA2_IN_BF16 = 0, 1
 CSA2_SWA_BF16, CSA2_SWA_FP8 = 0, 1
-CSA2_WS_TOPK, CSA2_WS_ATTN, CSA2_WS_DECODE = 0, 1, 2
-EXPORTED = ("csa2_dequant", "csa2_quantize", "csa2_index_score", "csa2_topk", "csa2_sparse_attn", "csa2_decode",
+CSA2_WS_TOPK, CSA2_WS_ATTN, CSA2_WS_DECODE, CSA2_WS_POOL = 0, 1, 2, 3
+EXPORTED = ("csa2_dequant", "csa2_quantize", "csa2_build_pool", "csa2_index_score", "csa2_topk", "csa2_sparse_attn", "csa2_decode",
             "csa2_workspace_size", "csa2_status_string", "csa2_version")
 
 _vp, _i32, _i64, _sz, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
@@ -38,6 +38,11 @@ class TopkArgs(ctypes.Structure):
     _fields_ = [("struct_size", _sz), ("n_queries", _i32), ("n_cand", _i64), ("n_entries", _i64), ("scores", _vp),
                 ("cand_blocks", _vp), ("n_blocks", _i32), ("n_valid", _vp), ("k", _i32), ("idx", _vp),
                 ("top_scores", _vp)]
+
+
+class PoolArgs(ctypes.Structure):
+    _fields_ = [("struct_size", _sz), ("n_queries", _i32), ("n_entries", _i64), ("scores", _vp), ("n_valid", _vp),
+                ("n_pool_blocks", _i32), ("pool_blocks", _vp)]
 
 
 class AttnArgs(ctypes.Structure):
@@ -62,6 +67,7 @@ def _load():
     L.csa2_dequant.argtypes = [ctypes.c_int, _vp, _vp, _i64, ctypes.c_int, _vp, _vp]
     L.csa2_quantize.argtypes = [ctypes.c_int, _vp, ctypes.c_int, _i64, _vp, _i64, _vp, _vp, _vp]
     L.csa2_index_score.argtypes = [ctypes.POINTER(IndexArgs), _vp, _vp]
+    L.csa2_build_pool.argtypes = [ctypes.POINTER(PoolArgs), _vp, _sz, _vp]
     L.csa2_topk.argtypes = [ctypes.POINTER(TopkArgs), _vp, _sz, _vp]
     L.csa2_sparse_attn.argtypes = [ctypes.POINTER(AttnArgs), _vp, _sz, _vp]
     L.csa2_decode.argtypes = [ctypes.POINTER(DecodeArgs), _vp, _sz, _vp]
@@ -70,7 +76,7 @@ def _load():
     L.csa2_status_string.argtypes = [ctypes.c_int]
     L.csa2_status_string.restype = ctypes.c_char_p
     L.csa2_version.restype = ctypes.c_int
-    for name in ("csa2_dequant", "csa2_quantize", "csa2_index_score", "csa2_topk", "csa2_sparse_attn", "csa2_decode"):
+    for name in ("csa2_dequant", "csa2_quantize", "csa2_build_pool", "csa2_index_score", "csa2_topk", "csa2_sparse_attn", "csa2_decode"):
         getattr(L, name).restype = ctypes.c_int
     return L
 
@@ -132,6 +138,18 @@ def csa2_quantize(kind: int, x, in_dtype: int, n_entries: int, dst_rows, n_cache
                   stream=None) -> None:
     _check("csa2_quantize", lib.csa2_quantize(kind, _ptr(x), in_dtype, n_entries, _ptr(dst_rows), n_cache_rows,
                                               _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def pool_args(scores, n_pool_blocks, pool_blocks, n_valid=None) -> PoolArgs:
+    Q, n = int(scores.shape[0]), int(scores.shape[1])
+    return PoolArgs(ctypes.sizeof(PoolArgs), Q, n, _ptr(scores), _ptr(n_valid), n_pool_blocks, _ptr(pool_blocks))
+
+
+def csa2_build_pool(args: PoolArgs, workspace=None, stream=None, device="cuda") -> None:
+    need = csa2_workspace_size(CSA2_WS_POOL, args)
+    ws = workspace if workspace is not None else _alloc_ws(need, device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("csa2_build_pool", lib.csa2_build_pool(ctypes.byref(args), _ptr(ws), nbytes, _stream(stream)))
 
 
 def index_args(Q, n_entries, cache_q_stride, key_codes, key_scales, iq_codes, iq_scales, head_weights,

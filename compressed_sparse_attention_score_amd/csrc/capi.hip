@@ -137,6 +137,39 @@ size_t ws_topk(const csa2_topk_args* a) {
   return carve_topk(nullptr, a->n_queries, a->n_cand, sp, c).bytes;
 }
 
+// Pool construction: block scores, valid-block counts, then a top-k workspace
+// over the blocks.
+struct PoolWs {
+  float* bmax;    // [Q][nb]
+  int32_t* nvb;   // [Q]
+  TopkWs tk;
+  size_t bytes;
+};
+
+PoolWs carve_pool(void* ws, int Q, int64_t n_entries, int n_pool) {
+  const int64_t nb = (n_entries + 7) / 8;
+  ScorePlan sp = plan_score(nb, Q, n_pool);
+  Carve c(ws);
+  PoolWs w;
+  w.bmax = c.take<float>((size_t)Q * (size_t)(nb > 0 ? nb : 1));
+  w.nvb = c.take<int32_t>((size_t)Q);
+  w.tk = carve_topk(ws, Q, nb, sp, c);
+  w.bytes = c.off;
+  return w;
+}
+
+int check_pool(const csa2_pool_args* a) {
+  if (!a) return CSA2_ERR_NULL;
+  if (a->struct_size != sizeof(csa2_pool_args)) return CSA2_ERR_ARG;
+  if (a->n_queries < 0 || a->n_queries > kMaxQ) return CSA2_ERR_SHAPE;
+  if (a->n_entries < 0 || a->n_entries > kMaxI32) return CSA2_ERR_SHAPE;
+  if (a->n_pool_blocks < 1 || a->n_pool_blocks > CSA2_MAX_POOL_BLOCKS) return CSA2_ERR_SHAPE;
+  if (a->n_queries == 0) return CSA2_OK;
+  if (!a->pool_blocks || (a->n_entries > 0 && !a->scores)) return CSA2_ERR_NULL;
+  if (!aligned(a->scores, 4) || !aligned(a->n_valid, 4) || !aligned(a->pool_blocks, 4)) return CSA2_ERR_ALIGN;
+  return CSA2_OK;
+}
+
 size_t ws_attn(int Q, int nj) {
   if (Q == 0) return 0;
   AttnPlan ap = plan_attn(Q, nj);
@@ -222,6 +255,27 @@ int csa2_quantize(int kind, const void* x, int in_dtype, int64_t n_entries, cons
     return CSA2_ERR_ALIGN;
   return hip_status(launch_quantize(kind, x, in_dtype == CSA2_IN_BF16, n_entries, dst_rows, n_cache_rows,
                                     (uint8_t*)codes, (uint8_t*)scales, (hipStream_t)stream));
+}
+
+int csa2_build_pool(const csa2_pool_args* a, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_pool(a);
+  if (st) return st;
+  if (a->n_queries == 0) return CSA2_OK;
+  const int Q = a->n_queries;
+  const int64_t nb = (a->n_entries + 7) / 8;
+  PoolWs w = carve_pool(nullptr, Q, a->n_entries, a->n_pool_blocks);
+  st = check_ws(ws, ws_bytes, w.bytes);
+  if (st) return st;
+  w = carve_pool(ws, Q, a->n_entries, a->n_pool_blocks);
+  hipStream_t s = (hipStream_t)stream;
+  ScorePlan sp = plan_score(nb, Q, a->n_pool_blocks);
+  hipError_t e = launch_block_max(a->scores, Q, a->n_entries, a->n_valid, w.bmax, w.nvb, s);
+  // an empty cache leaves no block: the selection pads every row with -1
+  if (e == hipSuccess && nb > 0) e = launch_score_maxima(w.bmax, Q, nb, nb, nullptr, 0, w.nvb, sp, w.tk.gmax, s);
+  if (e == hipSuccess)
+    e = launch_select(w.bmax, Q, nb, nb, nullptr, 0, nb > 0 ? w.nvb : nullptr, a->n_pool_blocks, sp,
+                      nb > 0 ? w.tk.gmax : nullptr, w.tk.counts, w.tk.cand, a->pool_blocks, nullptr, s);
+  return hip_status(e);
 }
 
 int csa2_index_score(const csa2_index_args* a, float* scores, void* stream) {
@@ -342,6 +396,15 @@ size_t csa2_workspace_size(int which, const void* args) {
         a->n_swa > CSA2_MAX_SWA)
       return SIZE_MAX;
     return ws_attn(a->n_queries, a->k_sel + a->n_swa);
+  }
+  if (which == CSA2_WS_POOL) {
+    const csa2_pool_args* a = (const csa2_pool_args*)args;
+    if (a->struct_size != sizeof(csa2_pool_args)) return SIZE_MAX;
+    if (a->n_queries < 0 || a->n_queries > kMaxQ || a->n_entries < 0 || a->n_entries > kMaxI32 ||
+        a->n_pool_blocks < 1 || a->n_pool_blocks > CSA2_MAX_POOL_BLOCKS)
+      return SIZE_MAX;
+    if (a->n_queries == 0) return 0;
+    return carve_pool(nullptr, a->n_queries, a->n_entries, a->n_pool_blocks).bytes;
   }
   if (which == CSA2_WS_DECODE) {
     const csa2_decode_args* a = (const csa2_decode_args*)args;

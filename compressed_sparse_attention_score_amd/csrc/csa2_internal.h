@@ -72,6 +72,12 @@ hipError_t launch_select(const float* scores, int Q, int64_t n_cand, int64_t n_e
                          int n_blocks, const int32_t* n_valid, int k, const ScorePlan& sp, const unsigned* gmax,
                          unsigned* counts, unsigned long long* cand, int32_t* idx, float* top_scores, hipStream_t s);
 
+// Reindex pool construction: bmax [Q][ceil(n/8)] = best score of each block
+// of 8 inside the causal limit (as a score whose key is the block's best
+// key), nvb [Q] = blocks holding at least one valid entry.
+hipError_t launch_block_max(const float* scores, int Q, int64_t n, const int32_t* n_valid, float* bmax, int32_t* nvb,
+                            hipStream_t s);
+
 struct AttnLaunch {
   int Q;
   int64_t n_entries, cache_q_stride;

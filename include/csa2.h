@@ -122,6 +122,32 @@ enum { CSA2_IN_F32 = 0, CSA2_IN_BF16 = 1 };
 CSA2_API int csa2_quantize(int kind, const void* x, int in_dtype, int64_t n_entries, const int64_t* dst_rows,
                            int64_t n_cache_rows, void* codes, void* scales, void* stream);
 
+/* ---------------------------------------------------- pool construction */
+#define CSA2_MAX_POOL_BLOCKS 8192  /* largest pool, in blocks of 8 (the method: 2048) */
+
+typedef struct csa2_pool_args {
+  size_t struct_size;
+  int32_t n_queries;          /* Q >= 0                                          */
+  int64_t n_entries;          /* scores per query (the whole cache), < 2^31      */
+  const float* scores;        /* [Q][n_entries] a Full layer's indexer scores, 4-B aligned */
+  const int32_t* n_valid;     /* [Q] causal limit (entries >= n_valid[q] ignored) or NULL */
+  int32_t n_pool_blocks;      /* blocks to keep, 1..CSA2_MAX_POOL_BLOCKS          */
+  int32_t* pool_blocks;       /* out [Q][n_pool_blocks], 4-B aligned             */
+} csa2_pool_args;
+
+/* csa2_build_pool — the candidate pool of the Reindex layers ("An
+ * infra-oriented diagram ...", indexer bullet: a 16,384-entry pool chosen by
+ * layer 20 by blocks of 8; "DeepSeek V4.1 Flash: Why Its Encoder, Engram and
+ * KV Cache Matter", CSA2 section: a hierarchical index narrows later searches
+ * to a pool chosen earlier). The pages do not give the block ranking; here
+ * block b (entries 8b..8b+7) scores the best of its entries below the causal
+ * limit, in the csa2_topk order (NaN lowest, -0 == +0), and the
+ * n_pool_blocks best blocks by (block score descending, block id ascending)
+ * are written in ascending block id, -1 padded when fewer blocks hold a valid
+ * entry: exactly the cand_blocks input of a Reindex csa2_index_score.
+ * Workspace: csa2_workspace_size(CSA2_WS_POOL, args) bytes, 256-B aligned. */
+CSA2_API int csa2_build_pool(const csa2_pool_args* args, void* workspace, size_t ws_bytes, void* stream);
+
 /* --------------------------------------------------------- index score */
 typedef struct csa2_index_args {
   size_t struct_size;
@@ -254,11 +280,11 @@ typedef struct csa2_decode_args {
 CSA2_API int csa2_decode(const csa2_decode_args* args, void* workspace, size_t ws_bytes, void* stream);
 
 /* ----------------------------------------------------------- utilities */
-enum { CSA2_WS_TOPK = 0, CSA2_WS_ATTN = 1, CSA2_WS_DECODE = 2 };
+enum { CSA2_WS_TOPK = 0, CSA2_WS_ATTN = 1, CSA2_WS_DECODE = 2, CSA2_WS_POOL = 3 };
 
 /* Bytes of workspace the call `which` needs for `args` (a csa2_topk_args*,
- * csa2_attn_args* or csa2_decode_args*); 0 if none; SIZE_MAX if the args are
- * invalid. */
+ * csa2_attn_args*, csa2_decode_args* or csa2_pool_args*); 0 if none;
+ * SIZE_MAX if the args are invalid. */
 CSA2_API size_t csa2_workspace_size(int which, const void* args);
 
 /* Static, human-readable text for a status code. */

@@ -92,6 +92,18 @@ def test_validation_rejects_before_launch():
     assert L.csa2_quantize(0, A + 4, 1, 10, None, 10, A, None, None) == csa.CSA2_ERR_ALIGN  # bf16 needs 8 B
     assert L.csa2_quantize(0, A, 0, 10, A + 4, 3, A, None, None) == csa.CSA2_ERR_ALIGN
     assert L.csa2_quantize(0, None, 0, 0, None, 0, None, None, None) == csa.CSA2_OK  # empty: no-op
+    # pool construction
+    pa = csa.PoolArgs(ctypes.sizeof(csa.PoolArgs), 2, 1000, A, None, 2048, A)
+    for field, value, code in (("n_pool_blocks", 0, csa.CSA2_ERR_SHAPE), ("n_pool_blocks", 8193, csa.CSA2_ERR_SHAPE),
+                               ("n_entries", 1 << 31, csa.CSA2_ERR_SHAPE), ("scores", None, csa.CSA2_ERR_NULL),
+                               ("pool_blocks", None, csa.CSA2_ERR_NULL), ("scores", A + 2, csa.CSA2_ERR_ALIGN),
+                               ("struct_size", 8, csa.CSA2_ERR_ARG)):
+        bad = csa.PoolArgs.from_buffer_copy(pa)
+        setattr(bad, field, value)
+        assert L.csa2_build_pool(ctypes.byref(bad), A, 1 << 30, None) == code, field
+    need = csa.csa2_workspace_size(csa.CSA2_WS_POOL, pa)
+    assert need >= 2 * 125 * 4
+    assert L.csa2_build_pool(ctypes.byref(pa), A, need - 1, None) == csa.CSA2_ERR_WORKSPACE
     # index score
     ia = csa.IndexArgs(ctypes.sizeof(csa.IndexArgs), 2, 100, 100, A, A, A, A, A, None, 0, None)
     bad = csa.IndexArgs.from_buffer_copy(ia)

@@ -391,6 +391,57 @@ def test_sparse_attn_fp8_window_edge_cases():
     check_attn(ob, of, "fp8 mixed tile")
 
 
+# -------------------------------------------------------- pool construction
+
+def _gpu_pool(scores_np, n_pool, n_valid=None):
+    s = torch.from_numpy(np.ascontiguousarray(scores_np, np.float32)).cuda()
+    out = torch.empty((s.shape[0], n_pool), dtype=torch.int32, device="cuda")
+    nv = None if n_valid is None else torch.from_numpy(np.ascontiguousarray(n_valid, np.int32)).cuda()
+    csa.csa2_build_pool(csa.pool_args(s, n_pool, out, nv))
+    torch.cuda.synchronize()
+    return to_np_i32(out)
+
+
+def to_np_i32(t):
+    return t.detach().cpu().numpy()
+
+
+@pytest.mark.parametrize("Q,n,n_pool,limit", [(2, 1 << 20, 2048, False), (3, 8 * 3000 + 5, 1000, True),
+                                               (64, 65536, 2048, True), (1, 100, 2048, False),
+                                               (5, 4096, 8192, True), (4, 4097, 1, False)])
+def test_build_pool_exact(Q, n, n_pool, limit):
+    """Same scores on both sides: the pool ids are compared exactly (ties on a
+    coarse grid, NaN, -0 / +0, -inf, ragged last block, causal limits, more
+    blocks asked for than hold a valid entry)."""
+    rng = np.random.default_rng(n + Q)
+    sc = (np.round(rng.standard_normal((Q, n)) * 8) / 8).astype(np.float32)
+    sc[0, rng.integers(0, n, 50)] = np.nan
+    if Q > 1:
+        sc[1, ::5] = -0.0
+    if Q > 2:
+        sc[2, rng.integers(0, n, 50)] = -np.inf
+    n_valid = rng.integers(n // 3, n + 1, Q).astype(np.int32) if limit else None
+    ref = oracle.pool_blocks(sc, n_pool, n_valid)
+    got = _gpu_pool(sc, n_pool, n_valid)
+    bad = np.nonzero((got != ref).any(axis=1))[0]
+    assert bad.size == 0, f"queries {bad[:5]} differ"
+
+
+def test_pool_feeds_reindex_layer():
+    """A Full layer's GPU scores -> pool -> the Reindex layer's scores over
+    that pool on the same cache, against the oracle."""
+    wl = synth.full_decode(2, 1 << 16, seed=31)
+    sc = gpu_scores(to_device(wl))
+    pool = _gpu_pool(sc, 2048)
+    assert np.array_equal(pool, oracle.pool_blocks(sc, 2048))
+    wl.cand_blocks = pool
+    ref, dots = oracle.index_score(wl, want_dots=True)
+    got = gpu_scores(to_device(wl))
+    check_scores(got, ref, dots, wl.w, "reindex over the built pool")
+    ents = (8 * pool[:, :, None] + np.arange(8)[None, None, :]).reshape(2, -1)
+    np.testing.assert_array_equal(got, np.take_along_axis(sc, ents, axis=1))
+
+
 # ------------------------------------------------------------ fused decode
 
 def _check_decode(wl, queries=None, what=""):
