@@ -333,7 +333,7 @@ def main():
                      dtype=torch.uint8, device="cuda")
     K, W = args.steps, args.warmup
     S = min(K, 50)
-    ev = HipEvents(2 + 4 * S + 12)
+    ev = HipEvents(2 + 4 * S + 14)
 
     # ---- phase 1: timed decode steps
     dec_args = [reps[i % R].decode_args(out, lse, idx) for i in range(R)]
@@ -450,6 +450,23 @@ def main():
         torch.cuda.synchronize()
         q_ms.append(ev.ms(e0 + 6 + 2 * j, e0 + 7 + 2 * j) / K)
     del xm, xk, qm, qc, qs
+    # the encoder's cache write: m=2 gated pooling of token pairs, then the
+    # main-entry encoding, with per-channel gate logits and the pooled rows out
+    npool = CACHE_WRITE_ROWS // 2
+    xp = torch.randn((2 * npool, 512), generator=gen, device="cuda")
+    gp = torch.randn((2 * npool, 512), generator=gen, device="cuda")
+    cp = torch.empty((npool, 288), dtype=torch.uint8, device="cuda")
+    pp = torch.empty((npool, 512), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        csa.csa2_pool_quantize(xp, gp, npool, None, npool, cp, pp, stream)
+    torch.cuda.synchronize()
+    ev.record(e0 + 12, stream)
+    for _ in range(K):
+        csa.csa2_pool_quantize(xp, gp, npool, None, npool, cp, pp, stream)
+    ev.record(e0 + 13, stream)
+    torch.cuda.synchronize()
+    pq_ms = ev.ms(e0 + 12, e0 + 13) / K
+    del xp, gp, cp, pp
     ev.close()
     if args.copy_calibration:
         src = torch.ones(COPY_MIB << 18, dtype=torch.float32, device="cuda")
@@ -479,6 +496,11 @@ def main():
             "algorithmic_bytes": work["attn_fp8_bytes"],
             "GB_s": round(work["attn_fp8_bytes"] / (attn8_ms * 1e-3) / 1e9, 1)},
     }
+    pqb = npool * (2 * 2048 * 2 + ENTRY_BYTES_MAIN + 2048)  # two rows + two gate rows in, entry + pooled out
+    kernels["pool_quantize_m2"] = {"kernels": ["k_quantize<f32, main, gate 512>"], "entries": npool,
+                                   "us_per_launch": round(1e3 * pq_ms, 3), "algorithmic_bytes": pqb,
+                                   "GB_s": round(pqb / (pq_ms * 1e-3) / 1e9, 1),
+                                   "hbm_frac": round(pqb / (pq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     if pool_ms is not None:
         pb = Q * (4 * wl.n_cand + 4 * n_pool)  # scores read once, pool ids written
         kernels["build_pool"] = {"kernels": ["k_block_max", "k_score_maxima", "k_select_*"], "blocks_kept": n_pool,

@@ -257,6 +257,20 @@ int csa2_quantize(int kind, const void* x, int in_dtype, int64_t n_entries, cons
                                     (uint8_t*)codes, (uint8_t*)scales, (hipStream_t)stream));
 }
 
+int csa2_pool_quantize(const float* x, const float* gate, int gate_width, int64_t n_entries,
+                       const int64_t* dst_rows, int64_t n_cache_rows, void* cache, float* pooled, void* stream) {
+  if (gate_width != 1 && gate_width != 512) return CSA2_ERR_ARG;
+  if (n_entries < 0 || n_entries > kMaxI32 / 2 || n_cache_rows < 0) return CSA2_ERR_SHAPE;
+  if (!dst_rows && n_cache_rows < n_entries) return CSA2_ERR_SHAPE;
+  if (n_entries == 0) return CSA2_OK;
+  if (!x || !gate || !cache) return CSA2_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(gate, gate_width == 1 ? 4 : 16) || !aligned(cache, 16) || !aligned(pooled, 16) ||
+      !aligned(dst_rows, 8))
+    return CSA2_ERR_ALIGN;
+  return hip_status(launch_pool_quantize(x, gate, gate_width, n_entries, dst_rows, n_cache_rows, (uint8_t*)cache,
+                                         pooled, (hipStream_t)stream));
+}
+
 int csa2_build_pool(const csa2_pool_args* a, void* ws, size_t ws_bytes, void* stream) {
   int st = check_pool(a);
   if (st) return st;

@@ -56,6 +56,13 @@ hipError_t launch_dequant(int kind, const uint8_t* codes, const uint8_t* scales,
 hipError_t launch_quantize(int kind, const void* x, int in_bf16, int64_t n, const int64_t* rows, int64_t n_rows,
                            uint8_t* codes, uint8_t* scales, hipStream_t s);
 
+// m=2 pooling then main-entry quantisation: x [2n][512] fp32 token latents,
+// gate [2n][gate_width] logits (gate_width 1 or 512); entry i pools rows 2i
+// and 2i+1 and goes to cache row rows[i] (i when rows == NULL); pooled
+// (optional) [n][512] receives the fp32 pooled rows.
+hipError_t launch_pool_quantize(const float* x, const float* gate, int gate_width, int64_t n, const int64_t* rows,
+                                int64_t n_rows, uint8_t* cache, float* pooled, hipStream_t s);
+
 // Scores [Q][n_cand] and, if gmax != NULL, the maximum selection key of each
 // sub-chunk [Q][plan.n_groups].
 hipError_t launch_index_score(const IndexLaunch& a, const ScorePlan& plan, float* scores, unsigned* gmax,

@@ -185,10 +185,26 @@ __device__ __forceinline__ float pair_max(float a) {
 // instead would touch every cache line four times per load instruction and
 // cost a third of the bandwidth. The next tile's loads are issued before the
 // current one is encoded.
-template <bool BF16, bool INDEX>
+// Softmax-gated mean of two tokens' channel values (m=2 pooling): weights
+// 1/(1+e) and e/(1+e) with e = exp(-|g_b - g_a|), the larger going to the
+// token with the larger logit, so nothing overflows.
+__device__ __forceinline__ float gated_pair(float xa, float xb, float ga, float gb) {
+  const float d = gb - ga;
+  const float e = expf(-fabsf(d));
+  const float big = 1.0f / (1.0f + e), small = e * big;
+  const float pa = d <= 0.0f ? big : small, pb = d <= 0.0f ? small : big;
+  return pa * xa + pb * xb;
+}
+
+// GATE = 0: rows quantised as given. GATE = 1 / 512 (main latents, fp32 only):
+// row i of the output is the m=2 pooling of input rows 2i and 2i+1 under one
+// gate logit per token / per channel, optionally stored as fp32 in `pooled`.
+template <bool BF16, bool INDEX, int GATE>
 __global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, int64_t n,
                                                   const int64_t* __restrict__ rows, int64_t n_rows,
-                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                  const float* __restrict__ gate, float* __restrict__ pooled) {
+  static_assert(GATE == 0 || (!BF16 && !INDEX), "pooling takes fp32 main latents");
   constexpr int C = BF16 ? 2 : 4;  // 16-B chunks per half-block
   constexpr int S = C + 1;         // padded stride: lanes read distinct LDS banks
   constexpr int SHIFT = INDEX ? 3 : 5;  // half-blocks per entry: 8 (index), 32 (main)
@@ -200,6 +216,9 @@ __global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, in
   if (tile >= ntile) return;
   const v4u* src = (const v4u*)x;
   v4u reg[C];
+  // pooling: the second token's chunks and both tokens' gates (per token: x
+  // lane of ga/gb holds the logit)
+  v4u xb[GATE ? C : 1], ga[GATE ? C : 1], gb[GATE ? C : 1];
   int64_t row_next;
   // Loads of tile t; indexes past the end are clamped to the last chunk (their
   // half-blocks are never stored), so no load sits behind a branch. The
@@ -211,11 +230,40 @@ __global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, in
 #pragma unroll
     for (int j = 0; j < C; ++j) {
       int64_t c = min(t * 64 * C + lane + 64 * j, nchunk - 1);
-      reg[j] = __builtin_nontemporal_load(src + c);
+      if constexpr (GATE == 0) {
+        reg[j] = __builtin_nontemporal_load(src + c);
+      } else {
+        // output chunk c = entry c/128, channels 4(c%128)..+3; token rows 2e, 2e+1
+        const int64_t ca = c + (c >> 7) * 128;
+        reg[j] = __builtin_nontemporal_load(src + ca);
+        xb[j] = __builtin_nontemporal_load(src + ca + 128);
+        if constexpr (GATE == 512) {
+          ga[j] = __builtin_nontemporal_load((const v4u*)gate + ca);
+          gb[j] = __builtin_nontemporal_load((const v4u*)gate + ca + 128);
+        } else {
+          ga[j][0] = __float_as_uint(gate[2 * (c >> 7)]);
+          gb[j][0] = __float_as_uint(gate[2 * (c >> 7) + 1]);
+        }
+      }
     }
   };
   fetch(tile);
   for (;;) {
+    if constexpr (GATE != 0) {
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        v4u p;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int kg = GATE == 512 ? k : 0;
+          p[k] = __float_as_uint(gated_pair(__uint_as_float(reg[j][k]), __uint_as_float(xb[j][k]),
+                                            __uint_as_float(ga[j][kg]), __uint_as_float(gb[j][kg])));
+        }
+        reg[j] = p;
+        const int64_t c = tile * 64 * C + lane + 64 * j;
+        if (pooled && c < nchunk) *((v4u*)pooled + c) = p;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < C; ++j) {
       int c = lane + 64 * j;
@@ -285,15 +333,27 @@ hipError_t launch_quantize(int kind, const void* x, int in_bf16, int64_t n, cons
   dim3 grid((unsigned)(groups < kQuantGroups ? groups : kQuantGroups));
   if (kind == 0) {
     if (in_bf16)
-      k_quantize<true, false><<<grid, 256, 0, s>>>(x, n, rows, n_rows, codes, scales);
+      k_quantize<true, false, 0><<<grid, 256, 0, s>>>(x, n, rows, n_rows, codes, scales, nullptr, nullptr);
     else
-      k_quantize<false, false><<<grid, 256, 0, s>>>(x, n, rows, n_rows, codes, scales);
+      k_quantize<false, false, 0><<<grid, 256, 0, s>>>(x, n, rows, n_rows, codes, scales, nullptr, nullptr);
   } else {
     if (in_bf16)
-      k_quantize<true, true><<<grid, 256, 0, s>>>(x, n, rows, n_rows, codes, scales);
+      k_quantize<true, true, 0><<<grid, 256, 0, s>>>(x, n, rows, n_rows, codes, scales, nullptr, nullptr);
     else
-      k_quantize<false, true><<<grid, 256, 0, s>>>(x, n, rows, n_rows, codes, scales);
+      k_quantize<false, true, 0><<<grid, 256, 0, s>>>(x, n, rows, n_rows, codes, scales, nullptr, nullptr);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_quantize(const float* x, const float* gate, int gate_width, int64_t n, const int64_t* rows,
+                                int64_t n_rows, uint8_t* cache, float* pooled, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t ntile = (n * 32 + 63) / 64, groups = (ntile + 3) / 4;
+  dim3 grid((unsigned)(groups < kQuantGroups ? groups : kQuantGroups));
+  if (gate_width == 1)
+    k_quantize<false, false, 1><<<grid, 256, 0, s>>>(x, n, rows, n_rows, cache, nullptr, gate, pooled);
+  else
+    k_quantize<false, false, 512><<<grid, 256, 0, s>>>(x, n, rows, n_rows, cache, nullptr, gate, pooled);
   return hipGetLastError();
 }
 

@@ -122,6 +122,25 @@ enum { CSA2_IN_F32 = 0, CSA2_IN_BF16 = 1 };
 CSA2_API int csa2_quantize(int kind, const void* x, int in_dtype, int64_t n_entries, const int64_t* dst_rows,
                            int64_t n_cache_rows, void* codes, void* scales, void* stream);
 
+/* csa2_pool_quantize — the encoder's cache write: m=2 pooling then the main
+ * entry encoding of csa2_quantize ("An infra-oriented diagram ...",
+ * Full-layer cache bullet: in the encoder two consecutive tokens are pooled
+ * into one entry with a learned softmax gate). Entry i is
+ *     p * x[2i] + (1 - p) * x[2i+1],  p = 1 / (1 + exp(g[2i+1] - g[2i])),
+ * the two-way softmax of the pair's gate logits, per channel (gate_width
+ * 512) or once per token (gate_width 1); the logits come from the caller
+ * (their projection needs trained weights). Computed in fp32 (exp to about an ulp),
+ * then encoded exactly as csa2_quantize encodes that fp32 row.
+ *   x          [2n][512] fp32 token latents, 16-B aligned
+ *   gate       [2n][gate_width] fp32 logits, 16-B (512) or 4-B (1) aligned
+ *   dst_rows / n_cache_rows / cache   as csa2_quantize (CSA2_KIND_MAIN)
+ *   pooled     [n][512] fp32 out (the pooled rows, for the index-key
+ *              projection), 16-B aligned, or NULL
+ * n_entries = n >= 0 (0 = no-op). */
+CSA2_API int csa2_pool_quantize(const float* x, const float* gate, int gate_width, int64_t n_entries,
+                                const int64_t* dst_rows, int64_t n_cache_rows, void* cache, float* pooled,
+                                void* stream);
+
 /* ---------------------------------------------------- pool construction */
 #define CSA2_MAX_POOL_BLOCKS 8192  /* largest pool, in blocks of 8 (the method: 2048) */
 

@@ -45,6 +45,7 @@ def _bind(L):
                              vp, vp, vp, i32, vp]
     L.orc_dequant_swa_fp8.argtypes = [vp, i64, vp]
     L.orc_pool_blocks.argtypes = [vp, i32, i64, vp, i32, vp]
+    L.orc_pool_latents.argtypes = [vp, vp, i32, i64, vp]
     L.orc_quantize_main.argtypes = [vp, i64, vp]
     L.orc_quantize_index.argtypes = [vp, i64, vp, vp]
     L.orc_set_threads.argtypes = [i32]
@@ -137,6 +138,16 @@ def dequant_swa_fp8(rows: np.ndarray, L=None) -> np.ndarray:
     rows = np.ascontiguousarray(rows, np.uint8).reshape(-1, 528)
     out = np.empty((rows.shape[0], 512), np.float64)
     (L or lib()).orc_dequant_swa_fp8(_p(rows), rows.shape[0], _p(out))
+    return out
+
+
+def pool_latents(x: np.ndarray, gate: np.ndarray, L=None) -> np.ndarray:
+    """m=2 softmax-gated pooling: x [2n][512], gate [2n][512] or [2n][1] -> [n][512] fp64."""
+    x = np.ascontiguousarray(x, np.float32).reshape(-1, 512)
+    gate = np.ascontiguousarray(gate, np.float32).reshape(x.shape[0], -1)
+    n = x.shape[0] // 2
+    out = np.empty((n, 512), np.float64)
+    (L or lib()).orc_pool_latents(_p(x), _p(gate), gate.shape[1], n, _p(out))
     return out
 
 

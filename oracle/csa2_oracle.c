@@ -49,6 +49,12 @@
  *       a block scores the best of its entries inside the causal limit (rank
  *       order of R5); the n_pool best blocks by (block score descending, block
  *       id ascending) are kept and listed in ascending block id, -1 padded.
+ *   R17 m=2 pooling ([ATLAS] Full-layer cache bullet: two consecutive tokens
+ *       pooled into one entry with a learned softmax gate): entry i is
+ *       p x_{2i} + (1 - p) x_{2i+1} with p = 1 / (1 + exp(g_{2i+1} - g_{2i})),
+ *       the two-way softmax of the gate logits, taken per channel (or one
+ *       logit per token); the logits are inputs (their projection needs
+ *       trained weights); the pooled row is then quantised as in R13.
  *   (R9-R12 concern the workload and its generator; they are listed with the
  *   design notes.)
  */
@@ -245,6 +251,22 @@ ORC_API void orc_quantize_index(const float* x, int64_t n, uint8_t* codes, uint8
         int ch = 32 * g + c;
         put_code(co, ch, xi[ch], e2m1_nearest_mag(fabs((double)xi[ch]), s));
       }
+    }
+  }
+}
+
+/* m=2 pooling (R17): x [2n][512] token latents, gate [2n][gate_width] logits
+ * (gate_width 512: per channel; 1: per token). out [n][512] pooled, fp64. */
+ORC_API void orc_pool_latents(const float* x, const float* gate, int gate_width, int64_t n, double* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    const float* xa = x + (size_t)(2 * i) * 512;
+    const float* xb = xa + 512;
+    for (int c = 0; c < 512; ++c) {
+      int gc = gate_width == 1 ? 0 : c;
+      double ga = gate[(size_t)(2 * i) * gate_width + gc], gb = gate[(size_t)(2 * i + 1) * gate_width + gc];
+      double pa = 1.0 / (1.0 + exp(gb - ga)), pb = 1.0 / (1.0 + exp(ga - gb));
+      out[(size_t)i * 512 + c] = pa * (double)xa[c] + pb * (double)xb[c];
     }
   }
 }

@@ -6,7 +6,8 @@ assembles whole workloads as numpy arrays. Nothing here scores, selects or
 attends.
 
 Stream ids (the ``tensor_id`` of the counter): 0 main latents, 1 indexer keys,
-2 indexer queries, 3 head weights, 4 attention queries, 5 SWA rows, 6 pool blocks.
+2 indexer queries, 3 head weights, 4 attention queries, 5 SWA rows, 6 pool blocks,
+7 m=2 pooling gate logits.
 """
 from __future__ import annotations
 
@@ -22,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "csa2_synth.c")
 _LIB = os.path.join(_HERE, "libcsa2synth.so")
 
-TID_MAIN, TID_IKEY, TID_IQ, TID_W, TID_Q, TID_SWA, TID_POOL = range(7)
+TID_MAIN, TID_IKEY, TID_IQ, TID_W, TID_Q, TID_SWA, TID_POOL, TID_GATE = range(8)
 
 MAIN_BYTES = 288
 IKEY_CODE_BYTES = 64

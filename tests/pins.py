@@ -580,6 +580,35 @@ def check_pool(L, seed=29):
     assert list(oracle.pool_blocks(s2, 1, L=L)[0]) == [2]
 
 
+# ------------------------------------------------------------ m=2 pooling ---
+
+def check_pooling(L, seed=31):
+    from scipy.special import softmax
+    rng = np.random.default_rng(seed)
+    n = 40
+    x = rng.standard_normal((2 * n, 512)).astype(np.float32)
+    g = (rng.standard_normal((2 * n, 512)) * 2).astype(np.float32)
+    got = oracle.pool_latents(x, g, L=L)
+    # the two-way softmax of the gates, from a library routine, weights the pair
+    w = softmax(np.stack([g[0::2], g[1::2]]).astype(np.float64), axis=0)
+    ref = w[0] * x[0::2] + w[1] * x[1::2]
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-14)
+    lo, hi = np.minimum(x[0::2], x[1::2]), np.maximum(x[0::2], x[1::2])
+    assert np.all(got >= lo - 1e-12) and np.all(got <= hi + 1e-12)  # a convex mix
+    # equal gates: the plain mean; a gate 60 higher: that token alone
+    eq = oracle.pool_latents(x, np.zeros_like(g), L=L)
+    assert np.array_equal(eq, (x[0::2].astype(np.float64) + x[1::2]) / 2)
+    far = np.zeros_like(g)
+    far[0::2] = 60.0
+    assert np.allclose(oracle.pool_latents(x, far, L=L), x[0::2], rtol=1e-15, atol=0)
+    # swapping the two tokens (and their gates) changes nothing
+    xs, gs = x.reshape(n, 2, 512)[:, ::-1].reshape(2 * n, 512), g.reshape(n, 2, 512)[:, ::-1].reshape(2 * n, 512)
+    assert np.array_equal(oracle.pool_latents(xs, gs, L=L), got)
+    # one logit per token equals that logit in every channel
+    gt = g[:, :1]
+    assert np.array_equal(oracle.pool_latents(x, gt, L=L), oracle.pool_latents(x, np.repeat(gt, 512, axis=1), L=L))
+
+
 ALL_CHECKS = [check_format_tables, check_layout, check_dequant, check_index_scores, check_candidate_sets,
               check_topk, check_attention, check_decode_composition, check_quantize, check_window_options,
-              check_pool]
+              check_pool, check_pooling]

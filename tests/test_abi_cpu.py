@@ -92,6 +92,14 @@ def test_validation_rejects_before_launch():
     assert L.csa2_quantize(0, A + 4, 1, 10, None, 10, A, None, None) == csa.CSA2_ERR_ALIGN  # bf16 needs 8 B
     assert L.csa2_quantize(0, A, 0, 10, A + 4, 3, A, None, None) == csa.CSA2_ERR_ALIGN
     assert L.csa2_quantize(0, None, 0, 0, None, 0, None, None, None) == csa.CSA2_OK  # empty: no-op
+    # m=2 pooling + quantise
+    assert L.csa2_pool_quantize(A, A, 3, 10, None, 10, A, None, None) == csa.CSA2_ERR_ARG
+    assert L.csa2_pool_quantize(A, A, 512, 10, None, 9, A, None, None) == csa.CSA2_ERR_SHAPE
+    assert L.csa2_pool_quantize(None, A, 512, 10, None, 10, A, None, None) == csa.CSA2_ERR_NULL
+    assert L.csa2_pool_quantize(A, None, 1, 10, None, 10, A, None, None) == csa.CSA2_ERR_NULL
+    assert L.csa2_pool_quantize(A, A + 4, 512, 10, None, 10, A, None, None) == csa.CSA2_ERR_ALIGN
+    assert L.csa2_pool_quantize(A, A + 4, 1, 10, None, 10, A, A + 8, None) == csa.CSA2_ERR_ALIGN
+    assert L.csa2_pool_quantize(None, None, 1, 0, None, 0, None, None, None) == csa.CSA2_OK
     # pool construction
     pa = csa.PoolArgs(ctypes.sizeof(csa.PoolArgs), 2, 1000, A, None, 2048, A)
     for field, value, code in (("n_pool_blocks", 0, csa.CSA2_ERR_SHAPE), ("n_pool_blocks", 8193, csa.CSA2_ERR_SHAPE),

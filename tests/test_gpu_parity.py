@@ -197,6 +197,48 @@ def test_quantize_full_size_sampled():
     assert np.array_equal(c[rows], rc) and np.array_equal(s[rows], rs)
 
 
+def _pool_inputs(n, gw, seed):
+    x = synth.f32_rows(seed, synth.TID_MAIN, 7, 0, 2 * n, 512)
+    g = synth.f32_rows(seed, synth.TID_GATE, 0, 0, 2 * n, 512 if gw == 512 else 2)[:, :gw] * 2.0
+    g = np.ascontiguousarray(g, np.float32)
+    g[0:2] = 0.0                      # equal gates: the mean
+    g[2], g[3] = 80.0, -80.0          # one token only
+    g[4], g[5] = -80.0, 80.0
+    x[6:8] *= 1e-30                   # tiny pair
+    return x, g
+
+
+@pytest.mark.parametrize("gw", [512, 1], ids=["per-channel", "per-token"])
+def test_pool_quantize(gw):
+    """m=2 pooling + encoding: the fp32 pooled rows within a few ulp of the
+    fp64 pooling; the codes equal the oracle's encoding of those very fp32
+    rows (the rounding decisions are taken on the same values)."""
+    n = 1001
+    x, g = _pool_inputs(n, gw, seed=61)
+    xt, gt = torch.from_numpy(x).cuda(), torch.from_numpy(g).cuda()
+    cache = torch.full((n, 288), 0xA5, dtype=torch.uint8, device="cuda")
+    pooled = torch.empty((n, 512), dtype=torch.float32, device="cuda")
+    csa.csa2_pool_quantize(xt, gt, n, None, n, cache, pooled)
+    torch.cuda.synchronize()
+    pg, cg = pooled.cpu().numpy(), cache.cpu().numpy()
+    ref = oracle.pool_latents(x, g)
+    mag = np.maximum(np.abs(x[0::2]), np.abs(x[1::2])).astype(np.float64)
+    err = np.abs(pg.astype(np.float64) - ref)
+    assert np.all(err <= 4e-6 * mag + 1e-37), f"pooled off by {np.max(err / (mag + 1e-37)):.3g} relative"
+    assert np.array_equal(cg, oracle.quantize_main(pg))
+    # without the pooled output, and scattered through a row list
+    rng = np.random.default_rng(61)
+    dst = rng.permutation(2 * n)[:n].astype(np.int64)
+    dst[::97] = -1
+    cache2 = torch.full((2 * n, 288), 0xA5, dtype=torch.uint8, device="cuda")
+    csa.csa2_pool_quantize(xt, gt, n, torch.from_numpy(dst).cuda(), 2 * n, cache2, None)
+    torch.cuda.synchronize()
+    c2 = cache2.cpu().numpy()
+    ok = dst >= 0
+    assert np.array_equal(c2[dst[ok]], cg[ok])
+    assert (c2[np.setdiff1d(np.arange(2 * n), dst[ok])] == 0xA5).all()
+
+
 def test_quantize_empty_and_errors():
     x = torch.zeros((4, 512), dtype=torch.float32, device="cuda")
     c = torch.zeros((4, 288), dtype=torch.uint8, device="cuda")

@@ -56,6 +56,9 @@ MUTANTS = [
     ("pool_ignores_limit", "for (int64_t e = 8 * b; e < 8 * b + 8 && e < lim; ++e) {",
      "for (int64_t e = 8 * b; e < 8 * b + 8 && e < n_entries; ++e) {"),
     ("pool_nan_ranks_high", "  if (isnan(x)) return 0;\n  if (isnan(y)) return 1;", "  if (isnan(x)) return 1;\n  if (isnan(y)) return 0;"),
+    ("gate_sign", "double pa = 1.0 / (1.0 + exp(gb - ga)), pb", "double pa = 1.0 / (1.0 + exp(ga - gb)), pb"),
+    ("gate_one_channel", "int gc = gate_width == 1 ? 0 : c;", "int gc = 0;"),
+    ("pooled_same_token", "const float* xb = xa + 512;", "const float* xb = xa;"),
     ("quant_mx_zero_block", "if (amax > 0.0) {\n        e = -127;", "if (amax >= 0.0) {\n        e = -127;"),
 ]
 
