@@ -333,7 +333,7 @@ def main():
                      dtype=torch.uint8, device="cuda")
     K, W = args.steps, args.warmup
     S = min(K, 50)
-    ev = HipEvents(2 + 4 * S + 14)
+    ev = HipEvents(2 + 4 * S + 18)
 
     # ---- phase 1: timed decode steps
     dec_args = [reps[i % R].decode_args(out, lse, idx) for i in range(R)]
@@ -428,6 +428,32 @@ def main():
     torch.cuda.synchronize()
     attn8_ms = ev.ms(e0 + 4, e0 + 5) / K
     del swa8, rope_t
+    # Reuse layers: the selection gathered once into a dense list, then a
+    # layer's attention over it (the later layers read contiguous rows)
+    kk = int(idx.shape[1])
+    g_out = torch.empty((Q, kk, ENTRY_BYTES_MAIN), dtype=torch.uint8, device="cuda")
+    g_dense = torch.empty((Q, kk), dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        csa.csa2_gather_selected(reps[0].main_cache, wl.n_entries, wl.cache_q_stride, idx, g_out, g_dense, stream)
+    torch.cuda.synchronize()
+    ev.record(e0 + 14, stream)
+    for i in range(K):
+        csa.csa2_gather_selected(reps[i % R].main_cache, wl.n_entries, wl.cache_q_stride, idx, g_out, g_dense, stream)
+    ev.record(e0 + 15, stream)
+    torch.cuda.synchronize()
+    gather_ms = ev.ms(e0 + 14, e0 + 15) / K
+    ad_args = dataclasses.replace(reps[0], main_cache=g_out.view(-1, ENTRY_BYTES_MAIN), n_entries=kk,
+                                  cache_q_stride=kk).attn_args(g_dense, at_out, at_lse)
+    for _ in range(3):
+        csa.csa2_sparse_attn(ad_args, at_ws, stream)
+    torch.cuda.synchronize()
+    ev.record(e0 + 16, stream)
+    for _ in range(K):
+        csa.csa2_sparse_attn(ad_args, at_ws, stream)
+    ev.record(e0 + 17, stream)
+    torch.cuda.synchronize()
+    attn_dense_ms = ev.ms(e0 + 16, e0 + 17) / K
+    del g_out, g_dense
     # ---- phase 4: cache write of a long prefill chunk's new entries (not part
     # of the step): fp32 rows -> FP4 main entries and indexer keys
     gen = torch.Generator(device="cuda")
@@ -496,6 +522,11 @@ def main():
             "algorithmic_bytes": work["attn_fp8_bytes"],
             "GB_s": round(work["attn_fp8_bytes"] / (attn8_ms * 1e-3) / 1e9, 1)},
     }
+    kernels["reuse_layer"] = {"kernels": ["k_gather_selected", "k_sparse_attn", "k_attn_combine"],
+                              "gather_us": round(1e3 * gather_ms, 3),
+                              "gather_GB_s": round(2 * Q * kk * ENTRY_BYTES_MAIN / (gather_ms * 1e-3) / 1e9, 1),
+                              "attn_over_dense_list_us": round(1e3 * attn_dense_ms, 3),
+                              "attn_over_cache_us": round(1e3 * attn_ms, 3)}
     pqb = npool * (2 * 2048 * 2 + ENTRY_BYTES_MAIN + 2048)  # two rows + two gate rows in, entry + pooled out
     kernels["pool_quantize_m2"] = {"kernels": ["k_quantize<f32, main, gate 512>"], "entries": npool,
                                    "us_per_launch": round(1e3 * pq_ms, 3), "algorithmic_bytes": pqb,

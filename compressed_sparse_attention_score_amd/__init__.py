@@ -22,8 +22,9 @@ CSA2_OUT_F32, CSA2_OUT_BF16 = 0, 1
 CSA2_IN_F32, CSA2_IN_BF16 = 0, 1
 CSA2_SWA_BF16, CSA2_SWA_FP8 = 0, 1
 CSA2_WS_TOPK, CSA2_WS_ATTN, CSA2_WS_DECODE, CSA2_WS_POOL = 0, 1, 2, 3
-EXPORTED = ("csa2_dequant", "csa2_quantize", "csa2_pool_quantize", "csa2_build_pool", "csa2_index_score", "csa2_topk", "csa2_sparse_attn", "csa2_decode",
-            "csa2_workspace_size", "csa2_status_string", "csa2_version")
+EXPORTED = ("csa2_dequant", "csa2_quantize", "csa2_pool_quantize", "csa2_build_pool", "csa2_gather_selected",
+            "csa2_index_score", "csa2_topk", "csa2_sparse_attn", "csa2_decode", "csa2_workspace_size",
+            "csa2_status_string", "csa2_version")
 
 _vp, _i32, _i64, _sz, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
 
@@ -69,6 +70,7 @@ def _load():
     L.csa2_index_score.argtypes = [ctypes.POINTER(IndexArgs), _vp, _vp]
     L.csa2_build_pool.argtypes = [ctypes.POINTER(PoolArgs), _vp, _sz, _vp]
     L.csa2_pool_quantize.argtypes = [_vp, _vp, ctypes.c_int, _i64, _vp, _i64, _vp, _vp, _vp]
+    L.csa2_gather_selected.argtypes = [_vp, _i64, _i64, _vp, _i32, _i32, _vp, _vp, _vp]
     L.csa2_topk.argtypes = [ctypes.POINTER(TopkArgs), _vp, _sz, _vp]
     L.csa2_sparse_attn.argtypes = [ctypes.POINTER(AttnArgs), _vp, _sz, _vp]
     L.csa2_decode.argtypes = [ctypes.POINTER(DecodeArgs), _vp, _sz, _vp]
@@ -77,7 +79,7 @@ def _load():
     L.csa2_status_string.argtypes = [ctypes.c_int]
     L.csa2_status_string.restype = ctypes.c_char_p
     L.csa2_version.restype = ctypes.c_int
-    for name in ("csa2_dequant", "csa2_quantize", "csa2_pool_quantize", "csa2_build_pool", "csa2_index_score", "csa2_topk", "csa2_sparse_attn", "csa2_decode"):
+    for name in ("csa2_dequant", "csa2_quantize", "csa2_pool_quantize", "csa2_build_pool", "csa2_gather_selected", "csa2_index_score", "csa2_topk", "csa2_sparse_attn", "csa2_decode"):
         getattr(L, name).restype = ctypes.c_int
     return L
 
@@ -146,6 +148,12 @@ def csa2_pool_quantize(x, gate, n_entries: int, dst_rows, n_cache_rows: int, cac
     gate_width = int(gate.shape[-1])
     _check("csa2_pool_quantize", lib.csa2_pool_quantize(_ptr(x), _ptr(gate), gate_width, n_entries, _ptr(dst_rows),
                                                         n_cache_rows, _ptr(cache), _ptr(pooled), _stream(stream)))
+
+
+def csa2_gather_selected(main_cache, n_entries: int, cache_q_stride: int, idx, out, dense_idx, stream=None) -> None:
+    Q, k = int(idx.shape[0]), int(idx.shape[1])
+    _check("csa2_gather_selected", lib.csa2_gather_selected(_ptr(main_cache), n_entries, cache_q_stride, _ptr(idx), Q,
+                                                            k, _ptr(out), _ptr(dense_idx), _stream(stream)))
 
 
 def pool_args(scores, n_pool_blocks, pool_blocks, n_valid=None) -> PoolArgs:

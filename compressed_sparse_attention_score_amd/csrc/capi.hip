@@ -271,6 +271,18 @@ int csa2_pool_quantize(const float* x, const float* gate, int gate_width, int64_
                                          pooled, (hipStream_t)stream));
 }
 
+int csa2_gather_selected(const uint8_t* main_cache, int64_t n_entries, int64_t cache_q_stride, const int32_t* idx,
+                         int32_t n_queries, int32_t k_sel, uint8_t* out, int32_t* dense_idx, void* stream) {
+  if (n_queries < 0 || n_queries > kMaxQ || k_sel < 0 || k_sel > CSA2_MAX_K) return CSA2_ERR_SHAPE;
+  if (n_entries < 0 || n_entries > kMaxI32 || cache_q_stride < 0) return CSA2_ERR_SHAPE;
+  if (n_queries == 0 || k_sel == 0) return CSA2_OK;
+  if (!idx || !out || !dense_idx || (n_entries > 0 && !main_cache)) return CSA2_ERR_NULL;
+  if (!aligned(main_cache, 16) || !aligned(out, 16) || !aligned(idx, 4) || !aligned(dense_idx, 4))
+    return CSA2_ERR_ALIGN;
+  return hip_status(launch_gather_selected(main_cache, n_entries, cache_q_stride, idx, n_queries, k_sel, out,
+                                           dense_idx, (hipStream_t)stream));
+}
+
 int csa2_build_pool(const csa2_pool_args* a, void* ws, size_t ws_bytes, void* stream) {
   int st = check_pool(a);
   if (st) return st;

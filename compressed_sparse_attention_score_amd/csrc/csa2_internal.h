@@ -85,6 +85,11 @@ hipError_t launch_select(const float* scores, int Q, int64_t n_cand, int64_t n_e
 hipError_t launch_block_max(const float* scores, int Q, int64_t n, const int32_t* n_valid, float* bmax, int32_t* nvb,
                             hipStream_t s);
 
+// Dense copies out [Q][k][288] of the selected entries and dense ids [Q][k]
+// (j for a valid id, -1 for a skipped one, whose slot is zeroed).
+hipError_t launch_gather_selected(const uint8_t* cache, int64_t n_entries, int64_t cache_q_stride, const int32_t* idx,
+                                  int Q, int k, uint8_t* out, int32_t* dense, hipStream_t s);
+
 struct AttnLaunch {
   int Q;
   int64_t n_entries, cache_q_stride;

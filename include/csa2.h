@@ -269,6 +269,21 @@ enum { CSA2_SWA_BF16 = 0, CSA2_SWA_FP8 = 1 };
  * csa2_workspace_size(CSA2_WS_ATTN, args) bytes, 256-B aligned. */
 CSA2_API int csa2_sparse_attn(const csa2_attn_args* args, void* workspace, size_t ws_bytes, void* stream);
 
+/* csa2_gather_selected — for the Reuse layers, which share the global KV and
+ * the selected positions of an earlier layer ("DeepSeek V4.1 Flash: Why Its
+ * Encoder, Engram and KV Cache Matter", CSA2 section): copy each query's
+ * selected main entries once into a dense list, so that every later layer
+ * attends over contiguous rows.
+ *   main_cache, n_entries, cache_q_stride, idx [Q][k_sel]: as csa2_attn_args
+ *   out        [Q][k_sel][288], 16-B aligned: slot j = entry idx[q][j], or
+ *              zeros when that id is skipped (outside [0, n_entries))
+ *   dense_idx  [Q][k_sel] out: j, or -1 for a skipped id
+ * csa2_sparse_attn with main_cache = out, n_entries = cache_q_stride = k_sel
+ * and idx = dense_idx gives the same result as over the original cache. */
+CSA2_API int csa2_gather_selected(const uint8_t* main_cache, int64_t n_entries, int64_t cache_q_stride,
+                                  const int32_t* idx, int32_t n_queries, int32_t k_sel, uint8_t* out,
+                                  int32_t* dense_idx, void* stream);
+
 /* -------------------------------------------------------- fused decode */
 typedef struct csa2_decode_args {
   size_t struct_size;

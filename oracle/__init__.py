@@ -46,6 +46,7 @@ def _bind(L):
     L.orc_dequant_swa_fp8.argtypes = [vp, i64, vp]
     L.orc_pool_blocks.argtypes = [vp, i32, i64, vp, i32, vp]
     L.orc_pool_latents.argtypes = [vp, vp, i32, i64, vp]
+    L.orc_gather_selected.argtypes = [vp, i64, i64, vp, i32, i32, vp, vp]
     L.orc_quantize_main.argtypes = [vp, i64, vp]
     L.orc_quantize_index.argtypes = [vp, i64, vp, vp]
     L.orc_set_threads.argtypes = [i32]
@@ -149,6 +150,17 @@ def pool_latents(x: np.ndarray, gate: np.ndarray, L=None) -> np.ndarray:
     out = np.empty((n, 512), np.float64)
     (L or lib()).orc_pool_latents(_p(x), _p(gate), gate.shape[1], n, _p(out))
     return out
+
+
+def gather_selected(main_cache: np.ndarray, n_entries: int, cache_q_stride: int, idx: np.ndarray, L=None):
+    """Dense copies [Q][k][288] of each query's selected entries and the dense ids [Q][k]."""
+    idx = np.ascontiguousarray(idx, np.int32)
+    Q, k = idx.shape
+    out = np.empty((Q, k, 288), np.uint8)
+    dense = np.empty((Q, k), np.int32)
+    (L or lib()).orc_gather_selected(_p(np.ascontiguousarray(main_cache, np.uint8)), n_entries, cache_q_stride,
+                                     _p(idx), Q, k, _p(out), _p(dense))
+    return out, dense
 
 
 def _f32(a):

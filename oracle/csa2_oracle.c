@@ -55,6 +55,13 @@
  *       the two-way softmax of the gate logits, taken per channel (or one
  *       logit per token); the logits are inputs (their projection needs
  *       trained weights); the pooled row is then quantised as in R13.
+ *   R18 Reuse layers ([HELIX] CSA2 section: they share the global KV and the
+ *       selected positions of an earlier layer) attend over the same
+ *       selection with their own queries; the selected entries may first be
+ *       copied into a dense per-query list (slot j = the j-th selected id;
+ *       skipped ids keep a slot whose dense id is -1), and attention over
+ *       that list with dense ids equals attention over the cache with the
+ *       original ids.
  *   (R9-R12 concern the workload and its generator; they are listed with the
  *   design notes.)
  */
@@ -416,6 +423,23 @@ ORC_API void orc_pool_blocks(const float* scores, int Q, int64_t n_entries, cons
   orc_topk(bs, Q, nb, nvb, nb, NULL, 0, n_pool, out, NULL);
   free(nvb);
   free(bs);
+}
+
+/* Gather of the selected entries (R18): out [Q][k][288], dense_idx [Q][k] = j
+ * for a valid id (copied), -1 for a skipped one (its slot left zero). */
+ORC_API void orc_gather_selected(const uint8_t* main_cache, int64_t n_entries, int64_t cache_q_stride,
+                                 const int32_t* idx, int Q, int k, uint8_t* out, int32_t* dense_idx) {
+  for (int q = 0; q < Q; ++q)
+    for (int j = 0; j < k; ++j) {
+      int64_t e = idx[(size_t)q * k + j];
+      uint8_t* dst = out + ((size_t)q * k + j) * 288;
+      int ok = e >= 0 && e < n_entries;
+      if (ok)
+        memcpy(dst, main_cache + (size_t)((int64_t)q * cache_q_stride + e) * 288, 288);
+      else
+        memset(dst, 0, 288);
+      dense_idx[(size_t)q * k + j] = ok ? j : -1;
+    }
 }
 
 /* ------------------------------------------------------------------ O5 --- */

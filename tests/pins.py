@@ -609,6 +609,32 @@ def check_pooling(L, seed=31):
     assert np.array_equal(oracle.pool_latents(x, gt, L=L), oracle.pool_latents(x, np.repeat(gt, 512, axis=1), L=L))
 
 
+# ---------------------------------------------------- Reuse-layer gather ---
+
+def check_gather(L, seed=37):
+    wl = synth.full_decode(3, 700, seed=seed)
+    rng = np.random.default_rng(seed)
+    idx = np.stack([rng.choice(700, 300, replace=False) for _ in range(3)]).astype(np.int32)
+    idx[0, 5] = -1
+    idx[1, 7] = 700
+    idx[2, -1] = 10 ** 6
+    g, dense = oracle.gather_selected(wl.main_cache, 700, 700, idx, L=L)
+    for q in range(3):
+        for j in range(300):
+            e = idx[q, j]
+            if 0 <= e < 700:
+                assert dense[q, j] == j and np.array_equal(g[q, j], wl.main_cache[q * 700 + e])
+            else:
+                assert dense[q, j] == -1 and not g[q, j].any()
+    # attention over the dense list with dense ids = attention over the cache
+    dl = copy.copy(wl)
+    dl.main_cache, dl.n_entries, dl.cache_q_stride = g.reshape(-1, 288), 300, 300
+    a, b = oracle.sparse_attn(wl, idx, L=L), oracle.sparse_attn(dl, dense, L=L)
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint32) if x.dtype == np.float32 else x,
+                              y.view(np.uint32) if y.dtype == np.float32 else y)
+
+
 ALL_CHECKS = [check_format_tables, check_layout, check_dequant, check_index_scores, check_candidate_sets,
               check_topk, check_attention, check_decode_composition, check_quantize, check_window_options,
-              check_pool, check_pooling]
+              check_pool, check_pooling, check_gather]

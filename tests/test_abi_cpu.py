@@ -100,6 +100,11 @@ def test_validation_rejects_before_launch():
     assert L.csa2_pool_quantize(A, A + 4, 512, 10, None, 10, A, None, None) == csa.CSA2_ERR_ALIGN
     assert L.csa2_pool_quantize(A, A + 4, 1, 10, None, 10, A, A + 8, None) == csa.CSA2_ERR_ALIGN
     assert L.csa2_pool_quantize(None, None, 1, 0, None, 0, None, None, None) == csa.CSA2_OK
+    # gather of the selected entries
+    assert L.csa2_gather_selected(A, 100, 100, A, 2, 1025, A, A, None) == csa.CSA2_ERR_SHAPE
+    assert L.csa2_gather_selected(A, 100, 100, None, 2, 512, A, A, None) == csa.CSA2_ERR_NULL
+    assert L.csa2_gather_selected(A, 100, 100, A, 2, 512, A + 8, A, None) == csa.CSA2_ERR_ALIGN
+    assert L.csa2_gather_selected(None, 100, 100, None, 2, 0, None, None, None) == csa.CSA2_OK
     # pool construction
     pa = csa.PoolArgs(ctypes.sizeof(csa.PoolArgs), 2, 1000, A, None, 2048, A)
     for field, value, code in (("n_pool_blocks", 0, csa.CSA2_ERR_SHAPE), ("n_pool_blocks", 8193, csa.CSA2_ERR_SHAPE),

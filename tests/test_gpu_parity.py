@@ -484,6 +484,35 @@ def test_pool_feeds_reindex_layer():
     np.testing.assert_array_equal(got, np.take_along_axis(sc, ents, axis=1))
 
 
+# -------------------------------------------------------- Reuse layers
+
+def test_gather_selected_and_reuse_attention():
+    """The dense copy of the selection matches the oracle byte for byte, and a
+    later layer's attention over it (dense ids) equals attention over the
+    original cache with the original ids, bit for bit."""
+    wl = synth.full_decode(5, 3000, seed=71)
+    rng = np.random.default_rng(71)
+    idx = np.stack([rng.choice(3000, 512, replace=False) for _ in range(5)]).astype(np.int32)
+    idx[0, 3] = -1
+    idx[1, 100] = 3000
+    idx[4, -5:] = -1
+    db = to_device(wl)
+    it = torch.from_numpy(idx).cuda()
+    out = torch.empty((5, 512, 288), dtype=torch.uint8, device="cuda")
+    dense = torch.empty((5, 512), dtype=torch.int32, device="cuda")
+    csa.csa2_gather_selected(db.main_cache, wl.n_entries, wl.cache_q_stride, it, out, dense)
+    torch.cuda.synchronize()
+    ref_g, ref_d = oracle.gather_selected(wl.main_cache, wl.n_entries, wl.cache_q_stride, idx)
+    assert np.array_equal(out.cpu().numpy(), ref_g) and np.array_equal(dense.cpu().numpy(), ref_d)
+    ob, glse = gpu_attn(db, idx)
+    import dataclasses
+    dd = dataclasses.replace(db, main_cache=out.view(-1, 288), n_entries=512, cache_q_stride=512)
+    ob2, glse2 = gpu_attn(dd, dense.cpu().numpy())
+    assert np.array_equal(ob, ob2) and np.array_equal(glse.view(np.uint32), glse2.view(np.uint32))
+    _, of, _ = oracle.sparse_attn(wl, idx)
+    check_attn(ob2, of, "reuse layer over the gathered list")
+
+
 # ------------------------------------------------------------ fused decode
 
 def _check_decode(wl, queries=None, what=""):

@@ -59,6 +59,9 @@ MUTANTS = [
     ("gate_sign", "double pa = 1.0 / (1.0 + exp(gb - ga)), pb", "double pa = 1.0 / (1.0 + exp(ga - gb)), pb"),
     ("gate_one_channel", "int gc = gate_width == 1 ? 0 : c;", "int gc = 0;"),
     ("pooled_same_token", "const float* xb = xa + 512;", "const float* xb = xa;"),
+    ("gather_wrong_query", "main_cache + (size_t)((int64_t)q * cache_q_stride + e) * 288, 288);",
+     "main_cache + (size_t)((int64_t)0 * cache_q_stride + e) * 288, 288);"),
+    ("gather_dense_id", "dense_idx[(size_t)q * k + j] = ok ? j : -1;", "dense_idx[(size_t)q * k + j] = ok ? (int)e : -1;"),
     ("quant_mx_zero_block", "if (amax > 0.0) {\n        e = -127;", "if (amax >= 0.0) {\n        e = -127;"),
 ]
 
