@@ -130,6 +130,25 @@ __device__ __forceinline__ float row16_max(float x) {
   return x;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave in six DPP adds, no LDS:
+// row_shr 1, 2, 4, 8 scan each row of 16 lanes, then row_bcast:15 adds the
+// last lane of rows 0 and 2 to rows 1 and 3, and row_bcast:31 the last lane
+// of row 1 to rows 2 and 3. Every lane must be active.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ unsigned dpp_add_u32(unsigned x) {
+  return x + (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWS, 0xF, false);
+}
+
+__device__ __forceinline__ unsigned wave_incl_scan(unsigned x) {
+  x = dpp_add_u32<0x111, 0xF>(x);  // row_shr:1
+  x = dpp_add_u32<0x112, 0xF>(x);  // row_shr:2
+  x = dpp_add_u32<0x114, 0xF>(x);  // row_shr:4
+  x = dpp_add_u32<0x118, 0xF>(x);  // row_shr:8
+  x = dpp_add_u32<0x142, 0xA>(x);  // row_bcast:15 into rows 1, 3
+  x = dpp_add_u32<0x143, 0xC>(x);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
 // x + x[lane ^ 32] and x + x[lane ^ 16] with gfx950 lane swaps (no LDS).
 __device__ __forceinline__ float add_xor32(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

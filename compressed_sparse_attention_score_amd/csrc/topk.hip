@@ -36,16 +36,24 @@ constexpr int kRegCand = 16;  // candidates per thread held in registers by the 
 constexpr int kRadixBits = 8;
 constexpr int kBins = 1 << kRadixBits;
 
+// Score staging of the compaction: thread t's 16 scores at 20t (4 pad
+// floats per 16 keep its 16-B reads on distinct banks).
+constexpr int kStageStride = kPer + 4;
+
 struct SelShared {
   unsigned hist[kBins];
-  unsigned wsum[NT / 64];
+  alignas(16) unsigned wsum[NT / 64];
   unsigned res[4];
   unsigned off[NT + 1];  // exclusive offsets of the chunk regions in the joined list
+  alignas(16) float stage[NT * kStageStride];
 };
 }  // namespace
 
 // Inclusive prefix sum of x over the workgroup (thread order); *total gets the
-// sum of all. Uses wsum (NT/64 entries); contains barriers.
+// sum of all. Uses wsum (NT/64 entries, 16-B aligned); contains barriers.
+// (The DPP wave scan of q_scan, inlined at this kernel's many call sites,
+// made the final-selection kernel keep ~480 registers live; lane shuffles
+// keep it at ~60.)
 __device__ __forceinline__ unsigned block_incl_scan(unsigned x, unsigned* wsum, unsigned* total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
 #pragma unroll
@@ -56,12 +64,12 @@ __device__ __forceinline__ unsigned block_incl_scan(unsigned x, unsigned* wsum, 
   __syncthreads();
   if (lane == 63) wsum[wv] = x;
   __syncthreads();
+  const v4u s = *(const v4u*)wsum;  // NT / 64 == 4
   unsigned before = 0, all = 0;
 #pragma unroll
   for (int w = 0; w < NT / 64; ++w) {
-    const unsigned s = wsum[w];
-    before += (w < wv) ? s : 0u;
-    all += s;
+    before += (w < wv) ? s[w] : 0u;
+    all += s[w];
   }
   *total = all;
   return x + before;
@@ -162,13 +170,31 @@ __global__ __launch_bounds__(NT) void k_select_compact(const float* __restrict__
   int64_t limit = n_entries;
   if (n_valid) limit = min(limit, (int64_t)n_valid[q]);
 
-  // this thread's 16 consecutive positions (loads issued before the threshold work)
+  // this thread's 16 consecutive positions. The chunk's scores are read with
+  // coalesced 16-B loads (lane l takes vector l of each 4-KiB slice; a list
+  // whose rows are not 16-B aligned takes 4-B loads in the same order) and
+  // staged in LDS before the threshold work; the thread picks its 16 up after
+  // it, whose barriers order the stores before the reads.
   const int64_t c0 = (int64_t)blockIdx.x * kChunk;
   const int64_t p0 = c0 + (int64_t)tid * kPer;
   const float* srow = scores + (int64_t)q * n_cand;
-  float sc[kPer];
+  {
+    const bool vec = ((uintptr_t)srow & 15) == 0;  // rows 16-B aligned (base and length)
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) sc[j] = (p0 + j < n_cand) ? srow[p0 + j] : 0.f;
+    for (int i = 0; i < kPer / 4; ++i) {
+      const int v = i * NT + tid;  // float4 index inside the chunk
+      const int64_t f0 = c0 + 4 * (int64_t)v;
+      v4f x;
+      if (vec && f0 + 4 <= n_cand) {
+        x = *(const v4f*)(srow + f0);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[u] = srow[min(f0 + u, n_cand - 1)];
+      }
+      *(v4f*)(sh.stage + (v >> 2) * kStageStride + 4 * (v & 3)) = x;
+    }
+  }
+  float sc[kPer];
   int64_t ent[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
@@ -198,6 +224,13 @@ __global__ __launch_bounds__(NT) void k_select_compact(const float* __restrict__
       t = radix_kth_stream<unsigned>(gq, n_groups, (unsigned)k, sh);
     }
     theta = t > 1u ? t : 1u;
+  }
+
+  if (n_groups < k) __syncthreads();  // no threshold pass ran: order the staging
+#pragma unroll
+  for (int i = 0; i < kPer / 4; ++i) {
+    const v4f x = *(const v4f*)(sh.stage + tid * kStageStride + 4 * i);
+    sc[4 * i] = x[0]; sc[4 * i + 1] = x[1]; sc[4 * i + 2] = x[2]; sc[4 * i + 3] = x[3];
   }
 
   // ---- keep key >= theta, in position order
@@ -350,28 +383,34 @@ constexpr int64_t kQMaxCand = 1 << 18;
 
 struct QSelShared {
   unsigned hist[kBins];
-  unsigned wsum[NQ / 64];
+  alignas(16) unsigned wsum[NQ / 64];
   unsigned res[4];
-  unsigned long long cand[kQCap];
+  unsigned long long cand[kQCap + kQCap / 16];  // survivor i at q_slot(i)
 };
+
+// LDS slot of survivor i: one pad slot after every 16. A thread writes its
+// survivors as a run, and with everything kept the runs of neighbouring
+// lanes start 16 composites (128 bytes) apart, i.e. in the same banks; the
+// pad shifts each run by one composite so a store spreads over the banks.
+__device__ __forceinline__ unsigned q_slot(unsigned i) { return i + (i >> 4); }
 
 // Inclusive prefix sum over the NQ threads; *total = sum of all. Barriers inside.
 __device__ __forceinline__ unsigned q_scan(unsigned x, QSelShared& sh, unsigned* total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const unsigned y = (unsigned)__shfl_up((int)x, off, 64);
-    if (lane >= off) x += y;
-  }
+  x = wave_incl_scan(x);
   __syncthreads();
   if (lane == 63) sh.wsum[wv] = x;
   __syncthreads();
+  const v4u* w4 = (const v4u*)sh.wsum;
   unsigned before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < NQ / 64; ++w) {
-    const unsigned v = sh.wsum[w];
-    before += (w < wv) ? v : 0u;
-    all += v;
+  for (int i = 0; i < NQ / 256; ++i) {
+    const v4u v = w4[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      before += (4 * i + j < wv) ? v[j] : 0u;
+      all += v[j];
+    }
   }
   *total = all;
   return x + before;
@@ -526,7 +565,7 @@ __global__ __launch_bounds__(NQ) void k_select_query(const float* __restrict__ s
 #pragma unroll
     for (int j = 0; j < kQPer; ++j) {
       if (comp[j]) {
-        if (pos < (unsigned)kQCap) sh.cand[pos] = comp[j];
+        if (pos < (unsigned)kQCap) sh.cand[q_slot(pos)] = comp[j];
         else gq[pos] = comp[j];
         ++pos;
       }
@@ -541,12 +580,15 @@ __global__ __launch_bounds__(NQ) void k_select_query(const float* __restrict__ s
     process(scB, bkB, (i + 1) * kStep);
   }
   for (int64_t p0 = n_full * kStep; p0 < n_cand; p0 += kStep) {  // ragged or unaligned passes
+    // positions past the end load the last score (clamped, so every load is
+    // issued at once instead of one guarded round trip after another) and
+    // are dropped by process()
     const int64_t pb = p0 + (int64_t)tid * kQPer;
 #pragma unroll
-    for (int j = 0; j < kQPer; ++j) scA[j] = (pb + j < n_cand) ? srow[pb + j] : 0.f;
+    for (int j = 0; j < kQPer; ++j) scA[j] = srow[min(pb + j, n_cand - 1)];
 #pragma unroll
     for (int j = 0; j < kQPer / 8; ++j)
-      bkA[j] = (cand_blocks && pb + 8 * j < n_cand) ? cand_blocks[(int64_t)q * n_blocks + ((pb >> 3) + j)] : 0;
+      bkA[j] = cand_blocks ? cand_blocks[(int64_t)q * n_blocks + min((pb >> 3) + j, (int64_t)n_blocks - 1)] : 0;
     process(scA, bkA, p0);
   }
   __syncthreads();
@@ -559,7 +601,7 @@ __global__ __launch_bounds__(NQ) void k_select_query(const float* __restrict__ s
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const unsigned e = (unsigned)tid * PER + j;
-      v[j] = (e < m) ? sh.cand[e] : 0ull;
+      v[j] = (e < m) ? sh.cand[q_slot(e)] : 0ull;
     }
     const unsigned long long T = (m > (unsigned)k) ? q_kth_regs<unsigned long long, PER>(v, (unsigned)k, sh) : 0ull;
     unsigned c = 0;
@@ -579,7 +621,7 @@ __global__ __launch_bounds__(NQ) void k_select_query(const float* __restrict__ s
   } else {
     // ---- long survivor lists (heavy ties): move the LDS part to global and
     // select from there
-    for (int i = tid; i < kQCap; i += NQ) gq[i] = sh.cand[i];
+    for (int i = tid; i < kQCap; i += NQ) gq[i] = sh.cand[q_slot((unsigned)i)];
     __syncthreads();
     const unsigned long long T = q_kth_stream<unsigned long long>(gq, m, (unsigned)k, sh);
     for (unsigned i0 = 0; i0 < m; i0 += NQ) {
