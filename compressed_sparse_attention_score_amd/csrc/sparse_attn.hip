@@ -489,6 +489,14 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
     ms[sp] = base[ss * kPartialFloats + h];
     ls[sp] = base[ss * kPartialFloats + 64 + h];
   }
+  // the first batch of O rows is requested with (m, l): it does not depend on them
+  v4u x0[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int ss = min(u, n_splits - 1);
+    x0[u] = *(const v4u*)((const uint16_t*)(base + ss * kPartialFloats + 128) + (int64_t)h * kDim + c0);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep every load above issued before any use
   float M = -__builtin_inff();
 #pragma unroll
   for (int sp = 0; sp < kMaxSplits; ++sp) M = (sp < n_splits) ? fmaxf(M, ms[sp]) : M;
@@ -496,14 +504,23 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
   float acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = 0.f;
-  if (M != -__builtin_inff()) {
+  {  // every weight is 0 when no split holds a slot (M = -inf), so no branch
     float f[kMaxSplits];  // weight of split s: l_s 2^(m_s - M)
 #pragma unroll
     for (int sp = 0; sp < kMaxSplits; ++sp) {
       f[sp] = (sp < n_splits && ms[sp] != -__builtin_inff()) ? ls[sp] * __builtin_amdgcn_exp2f(ms[sp] - M) : 0.f;
       L += f[sp];
     }
-    for (int s0 = 0; s0 < n_splits; s0 += 8) {
+    // splits 0..7 (straight-line, so their early loads stay early), then the rest
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        acc[2 * c] += __uint_as_float(x0[u][c] << 16) * f[u];
+        acc[2 * c + 1] += __uint_as_float(x0[u][c] & 0xFFFF0000u) * f[u];
+      }
+    }
+    for (int s0 = 8; s0 < n_splits; s0 += 8) {
       v4u x[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -514,7 +531,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
       for (int u = 0; u < 8; ++u) {
         float fu = 0.f;
 #pragma unroll
-        for (int sp = 0; sp < kMaxSplits; ++sp) fu = (sp == s0 + u) ? f[sp] : fu;
+        for (int sp = 8; sp < kMaxSplits; ++sp) fu = (sp == s0 + u) ? f[sp] : fu;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           acc[2 * c] += __uint_as_float(x[u][c] << 16) * fu;
