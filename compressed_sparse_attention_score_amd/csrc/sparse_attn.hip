@@ -57,6 +57,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 constexpr int kSwa8Bytes = 528;  // FP8 window row: 512 E4M3 codes + 16 E8M0 scales
+constexpr int kStageRow = kDim + 8;  // epilogue LDS row (bf16): 16 B of pad spreads the banks
 constexpr int kRopeFirst = 448;  // first rotary channel; pairs (448+2i, 449+2i), i < 32
 
 struct AttnArgs {
@@ -81,8 +82,13 @@ constexpr int64_t kPartialFloats = 64 + 64 + 64 * 512 / 2;
 constexpr int kMaxSplits = 32;
 
 struct AttnShared {
-  uint16_t kt[TILE * kDim];         // [slot][channel], 16-byte chunks swizzled
-  uint16_t vb[2][TILE * kDim];      // blocked V^T, double-buffered
+  union {
+    struct {
+      uint16_t kt[TILE * kDim];     // [slot][channel], 16-byte chunks swizzled
+      uint16_t vb[2][TILE * kDim];  // blocked V^T, double-buffered
+    };
+    uint16_t ostage[kHeads * kStageRow];  // epilogue: the 64 output rows (bf16)
+  };
   v4f sx[8][4][64];                 // partial S^T per wave: [wave][2*sb+hb][lane]
   uint2 pl[kHeads][TILE / 4];       // P^T as bf16: [head][slot quad] = 4 slots
   float alpha[kHeads];              // per-head rescale of O for this tile (1 = none)
@@ -430,27 +436,25 @@ __global__ __launch_bounds__(NT, 1) void k_sparse_attn(AttnArgs a) {
   }
   __syncthreads();
 
-  // ---- epilogue: this wave's heads x channel quarter, O / l as bf16, into
-  // the output (one split, rotary channels rotated back when a table is
-  // given) or this split's partial record (rotated after the merge)
+  // ---- epilogue: O / l as bf16 (rotary channels rotated back when a table is
+  // given and this is the only split; a split's partial record is rotated
+  // after the merge), staged in LDS over the free Kt / V^T area as 64 padded
+  // rows, then written as whole 1-KiB rows: one row per wave store instead of
+  // sixteen 32-byte pieces of different rows.
   const float* rope = (a.n_splits == 1 && a.rope && cc == 3) ? a.rope + (int64_t)q * 64 : nullptr;
+  uint16_t* stage = sh.ostage;  // over kt / vb, no longer read
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
     const int head = 32 * hh + 16 * hb + r16;
     const float mh = sh.fin_m[head], lh = sh.fin_l[head];
     const float inv = (lh > 0.f) ? 1.f / lh : 0.f;
-    uint16_t* orow;
     if (a.n_splits == 1) {
-      orow = a.out + ((int64_t)q * kHeads + head) * kDim + 128 * cc;
       if (a.lse && cc == 0 && g == 0)
         a.lse[(int64_t)q * kHeads + head] = (lh > 0.f) ? (mh + __log2f(lh)) * kLn2 : -__builtin_inff();
-    } else {
+    } else if (cc == 0 && g == 0) {
       float* part = a.partial + ((int64_t)q * a.n_splits + split) * kPartialFloats;
-      if (cc == 0 && g == 0) {
-        part[head] = mh;
-        part[64 + head] = lh;
-      }
-      orow = (uint16_t*)(part + 128) + (int64_t)head * kDim + 128 * cc;
+      part[head] = mh;
+      part[64 + head] = lh;
     }
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) {
@@ -464,8 +468,17 @@ __global__ __launch_bounds__(NT, 1) void k_sparse_attn(AttnArgs a) {
       uint2 pk;
       pk.x = (unsigned)__builtin_bit_cast(uint16_t, b0) | ((unsigned)__builtin_bit_cast(uint16_t, b1) << 16);
       pk.y = (unsigned)__builtin_bit_cast(uint16_t, b2) | ((unsigned)__builtin_bit_cast(uint16_t, b3) << 16);
-      *(uint2*)(orow + ch) = pk;
+      *(uint2*)(stage + head * kStageRow + 128 * cc + ch) = pk;
     }
+  }
+  __syncthreads();
+  uint16_t* obase = (a.n_splits == 1)
+                        ? a.out + (int64_t)q * kHeads * kDim
+                        : (uint16_t*)(a.partial + ((int64_t)q * a.n_splits + split) * kPartialFloats + 128);
+#pragma unroll
+  for (int k = 0; k < kHeads * kDim / 8 / NT; ++k) {  // 16-B chunks; a wave covers one head row
+    const int i = k * NT + tid, head = i >> 6, chunk = i & 63;
+    *(v4u*)(obase + head * kDim + chunk * 8) = *(const v4u*)(stage + head * kStageRow + chunk * 8);
   }
 }
 
