@@ -293,15 +293,23 @@ __global__ __launch_bounds__(NT) void k_select_final(const unsigned* __restrict_
       }
       ch = lo;
     }
-    unsigned long long v[kRegCand];
+    // addresses first (the walk reads LDS only), then every load at once: a
+    // load inside the walk would wait for the previous one each time
+    int64_t at[kRegCand];
 #pragma unroll
     for (int j = 0; j < kRegCand; ++j) {
       const unsigned e = e0 + j;
-      v[j] = 0ull;
+      at[j] = 0;
       if (e < m) {
         while (e >= sh.off[ch + 1]) ++ch;  // e < m = off[n_chunks] bounds the walk
-        v[j] = lq[(int64_t)ch * kChunk + (e - sh.off[ch])];
+        at[j] = (int64_t)ch * kChunk + (e - sh.off[ch]);
       }
+    }
+    unsigned long long v[kRegCand];
+#pragma unroll
+    for (int j = 0; j < kRegCand; ++j) {
+      const unsigned long long x = lq[at[j]];  // at[j] = 0 past the end: a valid slot, dropped
+      v[j] = (e0 + j < m) ? x : 0ull;
     }
     __syncthreads();  // offsets read before the radix passes reuse shared state
     const unsigned long long T =
