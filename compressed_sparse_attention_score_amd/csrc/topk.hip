@@ -10,9 +10,10 @@
 // No sort is needed:
 //  1. The scoring pass records the largest key of every sub-chunk of the
 //     candidate list (>= 2k sub-chunks when the list is long enough).
-//  2. theta = the k-th largest of those sub-chunk maxima is a lower bound on
-//     the k-th largest score: k distinct sub-chunks each hold an element
-//     >= theta. Each compaction workgroup finds theta by radix select and
+//  2. The k-th largest of those sub-chunk maxima is a lower bound on the
+//     k-th largest score: k distinct sub-chunks each hold an element >= it.
+//     theta is that key with its low 16 bits cleared (a lower bound still,
+//     found by two radix passes). Each compaction workgroup finds theta and
 //     writes its chunk's composites with key >= theta, in position order
 //     (block prefix sum), to a fixed region of the candidate list.
 //  3. One workgroup per query gathers the regions in chunk order, finds the
@@ -41,7 +42,7 @@ constexpr int kBins = 1 << kRadixBits;
 constexpr int kStageStride = kPer + 4;
 
 struct SelShared {
-  unsigned hist[kBins];
+  alignas(16) unsigned hist[2][kBins];
   alignas(16) unsigned wsum[NT / 64];
   unsigned res[4];
   unsigned off[NT + 1];  // exclusive offsets of the chunk regions in the joined list
@@ -51,16 +52,9 @@ struct SelShared {
 
 // Inclusive prefix sum of x over the workgroup (thread order); *total gets the
 // sum of all. Uses wsum (NT/64 entries, 16-B aligned); contains barriers.
-// (The DPP wave scan of q_scan, inlined at this kernel's many call sites,
-// made the final-selection kernel keep ~480 registers live; lane shuffles
-// keep it at ~60.)
 __device__ __forceinline__ unsigned block_incl_scan(unsigned x, unsigned* wsum, unsigned* total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const unsigned y = (unsigned)__shfl_up((int)x, off, 64);
-    if (lane >= off) x += y;
-  }
+  x = wave_incl_scan(x);
   __syncthreads();
   if (lane == 63) wsum[wv] = x;
   __syncthreads();
@@ -76,86 +70,108 @@ __device__ __forceinline__ unsigned block_incl_scan(unsigned x, unsigned* wsum, 
 }
 
 
-// One radix pass: pick the digit (bits shift..shift+7) of the k-th largest
-// value given the histogram in sh.hist. Updates prefix/remaining; returns
-// false if the histogram holds fewer than `remaining` values and true when
-// the chosen bucket is taken whole (no further pass needed) via *done.
-template <typename T>
-__device__ __forceinline__ bool radix_pick(SelShared& sh, int shift, T& prefix, unsigned& remaining, bool* done) {
-  const int tid = threadIdx.x;
-  // thread t looks at bin 255 - t: the inclusive scan is a suffix count
-  const unsigned h = sh.hist[kBins - 1 - tid];
-  unsigned total;
-  const unsigned incl = block_incl_scan(h, sh.wsum, &total);
-  if (incl - h < remaining && remaining <= incl) {
-    sh.res[0] = (unsigned)(kBins - 1 - tid);
-    sh.res[1] = incl - h;
-    sh.res[2] = h;
+// Digit pick of one radix pass, run by wave 0 alone. Lane l holds bins
+// 255-4l .. 252-4l (the digits from the top); a wave prefix sum over the lanes
+// counts the values in the bins above each lane's, and the lane whose four
+// bins hold the `remaining`-th largest value walks them. res gets the digit,
+// the count in the bins above it, the count in its bin, and the histogram's
+// total (lane 63's inclusive sum).
+__device__ __forceinline__ void pick_digit_wave0(const unsigned* hist, unsigned remaining, unsigned* res) {
+  const int lane = threadIdx.x & 63;
+  const v4u h = *(const v4u*)(hist + (kBins - 4) - 4 * lane);  // bins 252-4l .. 255-4l
+  const unsigned s = h[0] + h[1] + h[2] + h[3];
+  const unsigned incl = wave_incl_scan(s);  // values in bins >= 252 - 4l
+  unsigned above = incl - s;                // values in bins > 255 - 4l
+  if (above < remaining && remaining <= incl) {
+#pragma unroll
+    for (int r = 3; r >= 0; --r) {
+      if (above < remaining && remaining <= above + h[r]) {
+        res[0] = (unsigned)(kBins - 4 - 4 * lane + r);
+        res[1] = above;
+        res[2] = h[r];
+      }
+      above += h[r];
+    }
   }
-  __syncthreads();
-  if (total < remaining) return false;
-  const unsigned d = sh.res[0], above = sh.res[1], cnt = sh.res[2];
-  prefix |= ((T)d) << shift;
-  remaining -= above;
-  *done = (cnt == remaining);
-  __syncthreads();
-  return true;
+  if (lane == 63) res[3] = incl;
 }
 
-// k-th largest of the non-zero values held PER per thread (values may
-// repeat), by MSB-first radix passes of 8 bits over an LDS histogram.
+// k-th largest of a multiset of non-zero values (zeros are ignored), by
+// MSB-first radix passes of 8 bits over an LDS histogram, NTH threads. count(h,
+// hi, shift, prefix) adds to h every value whose bits above `hi` equal those of
+// prefix, binned by bits shift..shift+7 (all values when hi is the width).
+// Two histograms alternate: the one a pass fills was cleared during the pass
+// before, so a pass costs two barriers (histogram complete; digit picked).
 // Returns 0 when fewer than k non-zero values exist. When the bucket holding
-// the k-th value is taken whole the remaining low bits are left at zero, so
-// the values >= the result are exactly the k largest (a superset when values
-// repeat). All NT threads must call it.
-template <typename T, int PER>
-__device__ T radix_kth_regs(const T (&v)[PER], unsigned k, SelShared& sh) {
+// the k-th value is taken whole, or after max_passes passes, the remaining low
+// bits are left at zero: the result is then a lower bound on the k-th value
+// and the values >= it are a superset of the k largest (exactly them when the
+// bucket was taken whole and no value repeats).
+template <int NTH, typename T, typename Count>
+__device__ T radix_kth(Count count, unsigned k, unsigned (*hist)[kBins], unsigned* res, int max_passes) {
   constexpr int W = (int)(sizeof(T) * 8);
+  for (int i = threadIdx.x; i < 2 * kBins; i += NTH) hist[i / kBins][i % kBins] = 0u;
+  __syncthreads();
   T prefix = 0;
   unsigned remaining = k;
-  for (int hi = W; hi > 0; hi -= kRadixBits) {
+  int b = 0, pass = 0;
+  for (int hi = W; hi > 0 && pass < max_passes; hi -= kRadixBits, ++pass, b ^= 1) {
     const int shift = hi - kRadixBits;
-    sh.hist[threadIdx.x] = 0u;
+    count(hist[b], hi, shift, prefix);
+    // the other histogram was last read before the previous pass's second
+    // barrier, and the next pass fills it after this pass's second barrier
+    if (pass > 0)
+      for (int i = threadIdx.x; i < kBins; i += NTH) hist[b ^ 1][i] = 0u;
     __syncthreads();
+    if (threadIdx.x < 64) pick_digit_wave0(hist[b], remaining, res);
+    __syncthreads();
+    const unsigned d = res[0], above = res[1], cnt = res[2], total = res[3];
+    if (total < remaining) return (T)0;
+    prefix |= ((T)d) << shift;
+    remaining -= above;
+    if (cnt == remaining) break;
+  }
+  return prefix;
+}
+
+// The same over PER values per thread held in registers.
+template <int NTH, typename T, int PER>
+__device__ T radix_kth_regs(const T (&v)[PER], unsigned k, unsigned (*hist)[kBins], unsigned* res,
+                            int max_passes = 64) {
+  constexpr int W = (int)(sizeof(T) * 8);
+  auto count = [&](unsigned* h, int hi, int shift, T prefix) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const T x = v[j];
       if (x == 0) continue;
       if (hi < W && (x >> hi) != (prefix >> hi)) continue;
-      atomicAdd(&sh.hist[(unsigned)(x >> shift) & (kBins - 1)], 1u);
+      atomicAdd(&h[(unsigned)(x >> shift) & (kBins - 1)], 1u);
     }
-    __syncthreads();
-    bool done = false;
-    if (!radix_pick<T>(sh, shift, prefix, remaining, &done)) return (T)0;
-    if (done) break;
-  }
-  return prefix;
+  };
+  return radix_kth<NTH, T>(count, k, hist, res, max_passes);
 }
 
-// Same selection over values streamed from memory (lists too long for
-// registers); zeros are ignored.
-template <typename T>
-__device__ T radix_kth_stream(const T* src, int64_t n, unsigned k, SelShared& sh) {
+// The same over n values streamed from memory (lists too long for registers).
+template <int NTH, typename T>
+__device__ T radix_kth_stream(const T* src, int64_t n, unsigned k, unsigned (*hist)[kBins], unsigned* res,
+                              int max_passes = 64) {
   constexpr int W = (int)(sizeof(T) * 8);
-  T prefix = 0;
-  unsigned remaining = k;
-  for (int hi = W; hi > 0; hi -= kRadixBits) {
-    const int shift = hi - kRadixBits;
-    sh.hist[threadIdx.x] = 0u;
-    __syncthreads();
-    for (int64_t i = threadIdx.x; i < n; i += NT) {
+  auto count = [&](unsigned* h, int hi, int shift, T prefix) {
+    for (int64_t i = threadIdx.x; i < n; i += NTH) {
       const T x = src[i];
       if (x == 0) continue;
       if (hi < W && (x >> hi) != (prefix >> hi)) continue;
-      atomicAdd(&sh.hist[(unsigned)(x >> shift) & (kBins - 1)], 1u);
+      atomicAdd(&h[(unsigned)(x >> shift) & (kBins - 1)], 1u);
     }
-    __syncthreads();
-    bool done = false;
-    if (!radix_pick<T>(sh, shift, prefix, remaining, &done)) return (T)0;
-    if (done) break;
-  }
-  return prefix;
+  };
+  return radix_kth<NTH, T>(count, k, hist, res, max_passes);
 }
+
+// theta needs only to be a lower bound on the k-th largest score: two passes
+// fix the sign, exponent and top 7 mantissa bits of the k-th sub-chunk
+// maximum, which lowers the bound by less than 2^-7 of its value and adds a
+// few percent of survivors, and saves the passes over the low 16 bits.
+constexpr int kThetaPasses = 2;
 
 // Threshold + compaction: grid (n_chunks, Q). Writes cand[q][c0 .. c0+cnt) in
 // position order and counts[q][chunk] = cnt.
@@ -219,9 +235,9 @@ __global__ __launch_bounds__(NT) void k_select_compact(const float* __restrict__
         const int64_t i = (int64_t)j * NT + tid;
         g[j] = (i < n_groups) ? gq[i] : 0u;
       }
-      t = radix_kth_regs<unsigned, 16>(g, (unsigned)k, sh);
+      t = radix_kth_regs<NT, unsigned, 16>(g, (unsigned)k, sh.hist, sh.res, kThetaPasses);
     } else {
-      t = radix_kth_stream<unsigned>(gq, n_groups, (unsigned)k, sh);
+      t = radix_kth_stream<NT, unsigned>(gq, n_groups, (unsigned)k, sh.hist, sh.res, kThetaPasses);
     }
     theta = t > 1u ? t : 1u;
   }
@@ -264,12 +280,17 @@ __global__ __launch_bounds__(NT) void k_select_final(const unsigned* __restrict_
   int32_t* iq = idx + (int64_t)q * k;
   float* tq = top_scores ? top_scores + (int64_t)q * k : nullptr;
 
-  // total candidates
-  unsigned m = 0;
+  // total candidates; the first NT chunks' prefix sums are kept, as the
+  // offset table of the joined list when there are no more chunks than that
+  unsigned m = 0, cnt_c = 0, incl_c = 0;
   for (int c0 = 0; c0 < n_chunks; c0 += NT) {
     const unsigned x = (c0 + tid < n_chunks) ? cq[c0 + tid] : 0u;
     unsigned tot;
-    block_incl_scan(x, sh.wsum, &tot);
+    const unsigned incl = block_incl_scan(x, sh.wsum, &tot);
+    if (c0 == 0) {
+      cnt_c = x;
+      incl_c = incl;
+    }
     m += tot;
   }
   unsigned written = 0;
@@ -277,11 +298,8 @@ __global__ __launch_bounds__(NT) void k_select_final(const unsigned* __restrict_
     // The joined list is the chunk regions in chunk order; thread t takes its
     // elements t*kRegCand .. +kRegCand-1, locating their chunk through the
     // offset table (one binary search, then a forward walk).
-    const unsigned cnt_c = (tid < n_chunks) ? cq[tid] : 0u;
-    unsigned tot;
-    const unsigned incl = block_incl_scan(cnt_c, sh.wsum, &tot);
-    if (tid < n_chunks) sh.off[tid] = incl - cnt_c;
-    if (tid == 0) sh.off[n_chunks] = tot;
+    if (tid < n_chunks) sh.off[tid] = incl_c - cnt_c;
+    if (tid == 0) sh.off[n_chunks] = m;
     __syncthreads();
     const unsigned e0 = (unsigned)tid * kRegCand;
     int ch = 0;
@@ -313,7 +331,7 @@ __global__ __launch_bounds__(NT) void k_select_final(const unsigned* __restrict_
     }
     __syncthreads();  // offsets read before the radix passes reuse shared state
     const unsigned long long T =
-        (m > (unsigned)k) ? radix_kth_regs<unsigned long long, kRegCand>(v, (unsigned)k, sh) : 0ull;
+        (m > (unsigned)k) ? radix_kth_regs<NT, unsigned long long, kRegCand>(v, (unsigned)k, sh.hist, sh.res) : 0ull;
     unsigned c = 0;
 #pragma unroll
     for (int j = 0; j < kRegCand; ++j) c += (v[j] != 0ull && v[j] >= T) ? 1u : 0u;
@@ -332,26 +350,17 @@ __global__ __launch_bounds__(NT) void k_select_final(const unsigned* __restrict_
     // long lists (heavy ties or huge candidate sets): stream the chunk regions
     unsigned long long T = 0ull;
     if (m > (unsigned)k) {
-      unsigned long long prefix = 0;
-      unsigned remaining = (unsigned)k;
-      for (int hi = 64; hi > 0; hi -= kRadixBits) {
-        const int shift = hi - kRadixBits;
-        sh.hist[tid] = 0u;
-        __syncthreads();
+      auto count = [&](unsigned* h, int hi, int shift, unsigned long long prefix) {
         for (int c = 0; c < n_chunks; ++c) {
           const unsigned n_c = cq[c];
           for (unsigned i = tid; i < n_c; i += NT) {
             const unsigned long long x = lq[(int64_t)c * kChunk + i];
             if (hi < 64 && (x >> hi) != (prefix >> hi)) continue;
-            atomicAdd(&sh.hist[(unsigned)(x >> shift) & (kBins - 1)], 1u);
+            atomicAdd(&h[(unsigned)(x >> shift) & (kBins - 1)], 1u);
           }
         }
-        __syncthreads();
-        bool done = false;
-        radix_pick<unsigned long long>(sh, shift, prefix, remaining, &done);
-        if (done) break;
-      }
-      T = prefix;
+      };
+      T = radix_kth<NT, unsigned long long>(count, (unsigned)k, sh.hist, sh.res, 64);
     }
     // ordered write: chunk by chunk, NT elements at a time
     for (int c = 0; c < n_chunks; ++c) {
@@ -390,7 +399,7 @@ constexpr int kQCap = 8192;         // survivors held in LDS (8 per thread)
 constexpr int64_t kQMaxCand = 1 << 18;
 
 struct QSelShared {
-  unsigned hist[kBins];
+  alignas(16) unsigned hist[2][kBins];
   alignas(16) unsigned wsum[NQ / 64];
   unsigned res[4];
   unsigned long long cand[kQCap + kQCap / 16];  // survivor i at q_slot(i)
@@ -424,77 +433,6 @@ __device__ __forceinline__ unsigned q_scan(unsigned x, QSelShared& sh, unsigned*
   return x + before;
 }
 
-// Digit of the k-th largest from the histogram (threads 0..255 scan the bins
-// from the top). Returns false if fewer than `remaining` values are counted.
-template <typename T>
-__device__ __forceinline__ bool q_pick(QSelShared& sh, int shift, T& prefix, unsigned& remaining, bool* done) {
-  const int tid = threadIdx.x;
-  const unsigned h = (tid < kBins) ? sh.hist[kBins - 1 - tid] : 0u;
-  unsigned total;
-  const unsigned incl = q_scan(h, sh, &total);
-  if (tid < kBins && incl - h < remaining && remaining <= incl) {
-    sh.res[0] = (unsigned)(kBins - 1 - tid);
-    sh.res[1] = incl - h;
-    sh.res[2] = h;
-  }
-  __syncthreads();
-  if (total < remaining) return false;
-  const unsigned d = sh.res[0], above = sh.res[1], cnt = sh.res[2];
-  prefix |= ((T)d) << shift;
-  remaining -= above;
-  *done = (cnt == remaining);
-  __syncthreads();
-  return true;
-}
-
-// k-th largest non-zero value (see radix_kth_regs), NQ threads, PER values each.
-template <typename T, int PER>
-__device__ T q_kth_regs(const T (&v)[PER], unsigned k, QSelShared& sh) {
-  constexpr int W = (int)(sizeof(T) * 8);
-  T prefix = 0;
-  unsigned remaining = k;
-  for (int hi = W; hi > 0; hi -= kRadixBits) {
-    const int shift = hi - kRadixBits;
-    if (threadIdx.x < kBins) sh.hist[threadIdx.x] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const T x = v[j];
-      if (x == 0) continue;
-      if (hi < W && (x >> hi) != (prefix >> hi)) continue;
-      atomicAdd(&sh.hist[(unsigned)(x >> shift) & (kBins - 1)], 1u);
-    }
-    __syncthreads();
-    bool done = false;
-    if (!q_pick<T>(sh, shift, prefix, remaining, &done)) return (T)0;
-    if (done) break;
-  }
-  return prefix;
-}
-
-// Same over values in memory (global or LDS), zeros ignored.
-template <typename T>
-__device__ T q_kth_stream(const T* src, int64_t n, unsigned k, QSelShared& sh) {
-  constexpr int W = (int)(sizeof(T) * 8);
-  T prefix = 0;
-  unsigned remaining = k;
-  for (int hi = W; hi > 0; hi -= kRadixBits) {
-    const int shift = hi - kRadixBits;
-    if (threadIdx.x < kBins) sh.hist[threadIdx.x] = 0u;
-    __syncthreads();
-    for (int64_t i = threadIdx.x; i < n; i += NQ) {
-      const T x = src[i];
-      if (x == 0) continue;
-      if (hi < W && (x >> hi) != (prefix >> hi)) continue;
-      atomicAdd(&sh.hist[(unsigned)(x >> shift) & (kBins - 1)], 1u);
-    }
-    __syncthreads();
-    bool done = false;
-    if (!q_pick<T>(sh, shift, prefix, remaining, &done)) return (T)0;
-    if (done) break;
-  }
-  return prefix;
-}
 }  // namespace
 
 __global__ __launch_bounds__(NQ) void k_select_query(const float* __restrict__ scores, int64_t n_cand,
@@ -544,9 +482,9 @@ __global__ __launch_bounds__(NQ) void k_select_query(const float* __restrict__ s
         const int64_t i = (int64_t)j * NQ + tid;
         g[j] = (i < n_groups) ? gm[i] : 0u;
       }
-      t = q_kth_regs<unsigned, 4>(g, (unsigned)k, sh);
+      t = radix_kth_regs<NQ, unsigned, 4>(g, (unsigned)k, sh.hist, sh.res, kThetaPasses);
     } else {
-      t = q_kth_stream<unsigned>(gm, n_groups, (unsigned)k, sh);
+      t = radix_kth_stream<NQ, unsigned>(gm, n_groups, (unsigned)k, sh.hist, sh.res, kThetaPasses);
     }
     theta = t > 1u ? t : 1u;
   }
@@ -611,7 +549,7 @@ __global__ __launch_bounds__(NQ) void k_select_query(const float* __restrict__ s
       const unsigned e = (unsigned)tid * PER + j;
       v[j] = (e < m) ? sh.cand[q_slot(e)] : 0ull;
     }
-    const unsigned long long T = (m > (unsigned)k) ? q_kth_regs<unsigned long long, PER>(v, (unsigned)k, sh) : 0ull;
+    const unsigned long long T = (m > (unsigned)k) ? radix_kth_regs<NQ, unsigned long long, PER>(v, (unsigned)k, sh.hist, sh.res) : 0ull;
     unsigned c = 0;
 #pragma unroll
     for (int j = 0; j < PER; ++j) c += (v[j] != 0ull && v[j] >= T) ? 1u : 0u;
@@ -631,7 +569,7 @@ __global__ __launch_bounds__(NQ) void k_select_query(const float* __restrict__ s
     // select from there
     for (int i = tid; i < kQCap; i += NQ) gq[i] = sh.cand[q_slot((unsigned)i)];
     __syncthreads();
-    const unsigned long long T = q_kth_stream<unsigned long long>(gq, m, (unsigned)k, sh);
+    const unsigned long long T = radix_kth_stream<NQ, unsigned long long>(gq, m, (unsigned)k, sh.hist, sh.res);
     for (unsigned i0 = 0; i0 < m; i0 += NQ) {
       const unsigned i = i0 + tid;
       const unsigned long long x = (i < m) ? gq[i] : 0ull;
