@@ -108,7 +108,7 @@ __device__ __forceinline__ void pick_digit_wave0(const unsigned* hist, unsigned 
 // and the values >= it are a superset of the k largest (exactly them when the
 // bucket was taken whole and no value repeats).
 template <int NTH, typename T, typename Count>
-__device__ T radix_kth(Count count, unsigned k, unsigned (*hist)[kBins], unsigned* res, int max_passes) {
+__device__ __forceinline__ T radix_kth(Count count, unsigned k, unsigned (*hist)[kBins], unsigned* res, int max_passes) {
   constexpr int W = (int)(sizeof(T) * 8);
   for (int i = threadIdx.x; i < 2 * kBins; i += NTH) hist[i / kBins][i % kBins] = 0u;
   __syncthreads();
@@ -136,7 +136,7 @@ __device__ T radix_kth(Count count, unsigned k, unsigned (*hist)[kBins], unsigne
 
 // The same over PER values per thread held in registers.
 template <int NTH, typename T, int PER>
-__device__ T radix_kth_regs(const T (&v)[PER], unsigned k, unsigned (*hist)[kBins], unsigned* res,
+__device__ __forceinline__ T radix_kth_regs(const T (&v)[PER], unsigned k, unsigned (*hist)[kBins], unsigned* res,
                             int max_passes = 64) {
   constexpr int W = (int)(sizeof(T) * 8);
   auto count = [&](unsigned* h, int hi, int shift, T prefix) {
@@ -153,7 +153,7 @@ __device__ T radix_kth_regs(const T (&v)[PER], unsigned k, unsigned (*hist)[kBin
 
 // The same over n values streamed from memory (lists too long for registers).
 template <int NTH, typename T>
-__device__ T radix_kth_stream(const T* src, int64_t n, unsigned k, unsigned (*hist)[kBins], unsigned* res,
+__device__ __forceinline__ T radix_kth_stream(const T* src, int64_t n, unsigned k, unsigned (*hist)[kBins], unsigned* res,
                               int max_passes = 64) {
   constexpr int W = (int)(sizeof(T) * 8);
   auto count = [&](unsigned* h, int hi, int shift, T prefix) {
@@ -269,6 +269,29 @@ __global__ __launch_bounds__(NT) void k_select_compact(const float* __restrict__
   if (tid == 0) counts[(int64_t)q * n_chunks + blockIdx.x] = total;
 }
 
+// Exact top-k of the non-zero composites held kRegCand per thread, thread
+// order being list order: the k-th largest T (when there are more than k),
+// then every composite >= T written in list order. Returns the count written.
+__device__ __forceinline__ unsigned select_write(const unsigned long long (&v)[kRegCand], unsigned m, int k,
+                                                 SelShared& sh, int32_t* iq, float* tq) {
+  const unsigned long long T =
+      (m > (unsigned)k) ? radix_kth_regs<NT, unsigned long long, kRegCand>(v, (unsigned)k, sh.hist, sh.res) : 0ull;
+  unsigned c = 0;
+#pragma unroll
+  for (int j = 0; j < kRegCand; ++j) c += (v[j] != 0ull && v[j] >= T) ? 1u : 0u;
+  unsigned all;
+  unsigned pos = block_incl_scan(c, sh.wsum, &all) - c;
+#pragma unroll
+  for (int j = 0; j < kRegCand; ++j) {
+    if (v[j] != 0ull && v[j] >= T && pos < (unsigned)k) {
+      iq[pos] = (int32_t)(~(unsigned)(v[j] & 0xFFFFFFFFull));
+      if (tq) tq[pos] = key_score((unsigned)(v[j] >> 32));
+      ++pos;
+    }
+  }
+  return min(all, (unsigned)k);
+}
+
 // Exact top-k of each query's candidate list: grid (Q). Output in list order.
 __global__ __launch_bounds__(NT) void k_select_final(const unsigned* __restrict__ counts, int n_chunks,
                                                      int64_t n_cand, int k, const unsigned long long* __restrict__ cand,
@@ -280,21 +303,48 @@ __global__ __launch_bounds__(NT) void k_select_final(const unsigned* __restrict_
   int32_t* iq = idx + (int64_t)q * k;
   float* tq = top_scores ? top_scores + (int64_t)q * k : nullptr;
 
-  // total candidates; the first NT chunks' prefix sums are kept, as the
-  // offset table of the joined list when there are no more chunks than that
-  unsigned m = 0, cnt_c = 0, incl_c = 0;
-  for (int c0 = 0; c0 < n_chunks; c0 += NT) {
-    const unsigned x = (c0 + tid < n_chunks) ? cq[c0 + tid] : 0u;
-    unsigned tot;
-    const unsigned incl = block_incl_scan(x, sh.wsum, &tot);
-    if (c0 == 0) {
-      cnt_c = x;
-      incl_c = incl;
-    }
-    m += tot;
-  }
   unsigned written = 0;
-  if (m <= (unsigned)(NT * kRegCand) && n_chunks <= NT) {
+  bool done = false;
+  unsigned m = 0, cnt_c = 0, incl_c = 0;
+  if (n_chunks <= NT && n_cand > 0) {
+    // Chunk c's region starts at c*kChunk whatever the counts, so each thread
+    // loads kRegCand fixed slots of one chunk (threads c*tpc .. c*tpc+tpc-1
+    // take chunk c in order, so thread order is list order) together with
+    // the counts, and masks the slots past its chunk's count afterwards.
+    // When some chunk holds more survivors than its threads' slots, the
+    // offset-table pass below runs instead.
+    const int tpc = NT / n_chunks;
+    const int c_t = tid / tpc, sub = tid - c_t * tpc;
+    const bool own = c_t < n_chunks;
+    const unsigned slot0 = (unsigned)sub * kRegCand;
+    cnt_c = (tid < n_chunks) ? cq[tid] : 0u;
+    const unsigned my_cnt = own ? cq[c_t] : 0u;
+    const int64_t rb = (own ? (int64_t)c_t * kChunk : 0) + slot0;
+    unsigned long long v[kRegCand];
+#pragma unroll
+    for (int j = 0; j < kRegCand; ++j) v[j] = lq[min(rb + j, n_cand - 1)];  // slots past the list: dropped below
+    incl_c = block_incl_scan(cnt_c, sh.wsum, &m);
+    const bool fits = __syncthreads_and(!own || my_cnt <= (unsigned)tpc * kRegCand) != 0;
+    if (fits) {
+#pragma unroll
+      for (int j = 0; j < kRegCand; ++j) v[j] = (own && slot0 + j < my_cnt) ? v[j] : 0ull;
+      written = select_write(v, m, k, sh, iq, tq);
+      done = true;
+    }
+  } else {
+    for (int c0 = 0; c0 < n_chunks; c0 += NT) {
+      const unsigned x = (c0 + tid < n_chunks) ? cq[c0 + tid] : 0u;
+      unsigned tot;
+      const unsigned incl = block_incl_scan(x, sh.wsum, &tot);
+      if (c0 == 0) {
+        cnt_c = x;
+        incl_c = incl;
+      }
+      m += tot;
+    }
+  }
+  if (done) {
+  } else if (m <= (unsigned)(NT * kRegCand) && n_chunks <= NT) {
     // The joined list is the chunk regions in chunk order; thread t takes its
     // elements t*kRegCand .. +kRegCand-1, locating their chunk through the
     // offset table (one binary search, then a forward walk).
@@ -329,23 +379,7 @@ __global__ __launch_bounds__(NT) void k_select_final(const unsigned* __restrict_
       const unsigned long long x = lq[at[j]];  // at[j] = 0 past the end: a valid slot, dropped
       v[j] = (e0 + j < m) ? x : 0ull;
     }
-    __syncthreads();  // offsets read before the radix passes reuse shared state
-    const unsigned long long T =
-        (m > (unsigned)k) ? radix_kth_regs<NT, unsigned long long, kRegCand>(v, (unsigned)k, sh.hist, sh.res) : 0ull;
-    unsigned c = 0;
-#pragma unroll
-    for (int j = 0; j < kRegCand; ++j) c += (v[j] != 0ull && v[j] >= T) ? 1u : 0u;
-    unsigned all;
-    unsigned pos = block_incl_scan(c, sh.wsum, &all) - c;
-#pragma unroll
-    for (int j = 0; j < kRegCand; ++j) {
-      if (v[j] != 0ull && v[j] >= T && pos < (unsigned)k) {
-        iq[pos] = (int32_t)(~(unsigned)(v[j] & 0xFFFFFFFFull));
-        if (tq) tq[pos] = key_score((unsigned)(v[j] >> 32));
-        ++pos;
-      }
-    }
-    written = min(all, (unsigned)k);
+    written = select_write(v, m, k, sh, iq, tq);
   } else {
     // long lists (heavy ties or huge candidate sets): stream the chunk regions
     unsigned long long T = 0ull;

@@ -325,6 +325,21 @@ def test_topk_ties_nan_negzero(n):
     _assert_topk_exact(s, 512, n, what=f"ties n{n}")
 
 
+def test_topk_survivors_concentrated_in_one_chunk():
+    """Chunk-parallel selection (3 queries x 70,001 candidates, 18 chunks of
+    4,096). The final pass loads a fixed number of slots per chunk before it
+    knows the counts; row 0 puts 600 top scores inside one chunk, more than
+    those slots, so it takes the offset-table gather instead; row 1 is plain
+    random (fixed slots); row 2 has 3,000 top scores over the first chunk."""
+    rng = np.random.default_rng(9)
+    n = 70001
+    s = rng.standard_normal((3, n)).astype(np.float32)
+    s[0, 5 * 4096:5 * 4096 + 600] = 10 + rng.standard_normal(600).astype(np.float32)
+    s[2, :3000] = 10 + rng.standard_normal(3000).astype(np.float32)
+    _assert_topk_exact(s, 512, n, what="concentrated")
+    _assert_topk_exact(s, 1024, n, what="concentrated k1024")
+
+
 def test_topk_many_queries_long_lists():
     """64 queries of 30,000 candidates: one workgroup per query with several
     compaction passes; some rows tie heavily."""
