@@ -4,8 +4,8 @@
 One step = one csa2_decode call (indexer scoring -> top-512 selection ->
 sparse attention over 512 FP4 latents + 128 SWA rows) over one batch of
 synthetic input already resident in HBM. Steps rotate over device replicas of
-the batch so that consecutive steps cannot be served from the 256 MB
-memory-side cache.
+the batch (enough that one rotation's key reads exceed three times the 256 MB
+memory-side cache) so that consecutive steps cannot be served from it.
 
 Phases (all on one stream):
   1. warm-up, then K timed decode steps bracketed by synchronisation and two
@@ -89,12 +89,51 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
-def replicate(db, R):
+def replica_count(work, resident, requested):
+    """Device replicas rotated per step: enough that the keys the scan reads
+    over one rotation exceed three times the 256 MB memory-side cache, at most
+    64, and at most 16 GB of copies."""
+    if requested:
+        return requested
+    per_step = max(1, work["score_bytes"])
+    R = -(-768_000_000 // per_step)
+    return int(max(1, min(64, R, 16_000_000_000 // max(1, resident))))
+
+
+def replicate(db, wl, R):
+    """R device replicas of the batch. Caches are cloned; a Reindex batch whose
+    cache holds only its pool rows (the rest poison) instead gets, per further
+    replica, a fresh random pool of the same size drawn from blocks no earlier
+    replica uses, over the same cache tensors, with replica 0's pool rows
+    copied there (so every replica scores real entries)."""
     import torch
     reps = [db]
-    for _ in range(R - 1):
-        reps.append(dataclasses.replace(db, main_cache=db.main_cache.clone(), key_codes=db.key_codes.clone(),
-                                        key_scales=db.key_scales.clone()))
+    pool_rows = wl.extra.get("pool_rows") if wl.cand_blocks is not None else None
+    if pool_rows is None:
+        for _ in range(R - 1):
+            reps.append(dataclasses.replace(db, main_cache=db.main_cache.clone(), key_codes=db.key_codes.clone(),
+                                            key_scales=db.key_scales.clone()))
+    else:
+        Q, nb, N = wl.Q, wl.n_blocks, wl.cache_q_stride
+        n_blk = wl.n_entries // 8
+        used = np.zeros((Q, n_blk), bool)
+        for i in range(Q):
+            used[i, wl.cand_blocks[i]] = True
+        src = torch.from_numpy(pool_rows).to(db.main_cache.device)
+        for r in range(1, R):
+            rng = np.random.default_rng(7919 + r)
+            blocks = np.empty((Q, nb), np.int32)
+            for i in range(Q):
+                b = np.sort(rng.choice(np.flatnonzero(~used[i]), nb, replace=False))
+                used[i, b] = True
+                blocks[i] = b
+            rows = (np.arange(Q)[:, None, None] * N + 8 * blocks[:, :, None].astype(np.int64)
+                    + np.arange(8)[None, None, :]).reshape(-1)
+            dst = torch.from_numpy(rows).to(db.main_cache.device)
+            db.main_cache[dst] = db.main_cache[src]
+            db.key_codes[dst] = db.key_codes[src]
+            db.key_scales[dst] = db.key_scales[src]
+            reps.append(dataclasses.replace(db, cand_blocks=torch.from_numpy(blocks).to(db.main_cache.device)))
     torch.cuda.synchronize()
     return reps
 
@@ -323,9 +362,12 @@ def main():
     db = to_device(wl)
     Q = wl.Q
     work = work_of(wl)
-    resident = sum(t.numel() * t.element_size() for t in (db.main_cache, db.key_codes, db.key_scales))
-    R = args.replicas or int(min(8, max(1, -(-768_000_000 // max(1, resident)))))
-    reps = replicate(db, R)
+    if wl.cand_blocks is not None and "pool_rows" in wl.extra:
+        resident = len(wl.extra["pool_rows"]) * (ENTRY_BYTES_MAIN + ENTRY_BYTES_INDEX)  # pool rows copied per replica
+    else:
+        resident = sum(t.numel() * t.element_size() for t in (db.main_cache, db.key_codes, db.key_scales))
+    R = replica_count(work, resident, args.replicas)
+    reps = replicate(db, wl, R)
     stream = torch.cuda.current_stream()
 
     out, lse, idx = db.new_outputs()
