@@ -59,10 +59,10 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
   const int q = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, kb = lane >> 4;
-  // Scores and sub-chunk maxima are staged in LDS and written once per wave
-  // after the loop, so the loop's only vector-memory operations are loads.
-  __shared__ float s_score[4][kMaxWaveSpan];
-  __shared__ unsigned s_gmax[4][kMaxWaveSpan / 16];
+  // Scores are staged in LDS and written once per wave after the loop, so the
+  // loop's only vector-memory operations are loads; the sub-chunk maxima are
+  // formed from the staged scores at that point.
+  __shared__ __attribute__((aligned(16))) float s_score[4][kMaxWaveSpan];
 
   // A operands: query heads r16 and 16+r16, scale block kb.
   const uint8_t* iqc = a.iq_codes + (int64_t)q * kIHeads * 64;
@@ -87,7 +87,6 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
   const int64_t w0p = ((int64_t)blockIdx.x * 4 + wave) * a.wave_span;
   if (w0p >= a.n_cand) return;
   const int64_t w1p = min(w0p + a.wave_span, a.n_cand);
-  float gm = -__builtin_inff();
 
   // Key loads run one batch of UNROLL groups ahead of the matrix cores (two
   // statically indexed buffers, alternated by a 2x unrolled loop). Loads are
@@ -135,18 +134,6 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
       // every lane now holds the score of entry r16 of this group
       const float sv = ok[u] ? sc : -__builtin_inff();
       if (kb == 0) s_score[wave][gp - w0p + r16] = sv;
-      if (a.gmax) {
-        // running maximum as a float (invalid entries are -inf; a NaN score
-        // can only lower it, which keeps the selection bound valid); the
-        // order key is formed once per sub-chunk
-        gm = fmaxf(gm, sv);
-        const int64_t gend = gp + 16;
-        if ((gend & (a.group - 1)) == 0 || gend >= w1p) {
-          const float v = row16_max(gm);
-          if (lane == 0) s_gmax[wave][(gp - w0p) / a.group] = (v == -__builtin_inff()) ? 0u : score_key(v);
-          gm = -__builtin_inff();
-        }
-      }
     }
   };
   constexpr int64_t kStep = 16 * UNROLL;
@@ -158,12 +145,46 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
     if (g0 + 2 * kStep < w1p) issue(bcA, bsA, okA, g0 + 2 * kStep);
     compute(bcB, bsB, okB, g0 + kStep);
   }
-  // flush this wave's staged scores and maxima (wave-private LDS rows)
+  // flush this wave's staged scores (wave-private LDS rows)
   const int span = (int)(w1p - w0p);
   for (int i = lane; i < span; i += 64) out[w0p + i] = s_score[wave][i];
   if (a.gmax) {
-    const int ng = (span + a.group - 1) / a.group;
-    for (int i = lane; i < ng; i += 64) a.gmax[(int64_t)q * a.n_groups + w0p / a.group + i] = s_gmax[wave][i];
+    // Sub-chunk maxima (sub-chunks start at multiples of the group size, and
+    // so does the wave's range). In each pass over 256 staged scores lane l
+    // takes scores 4l..4l+3, and the group/4 lanes of a sub-chunk reduce into
+    // its first lane; a 512-entry sub-chunk spans two passes. Invalid entries
+    // are -inf and a NaN score is passed over by the maximum, which can only
+    // lower it and so keeps the selection bound valid. Order key 0 = empty.
+    const int lpg = a.group >> 2;
+    const int64_t grow = (int64_t)q * a.n_groups;
+    float carry = -__builtin_inff();
+    for (int base = 0; base < span; base += 256) {
+      const int i = base + 4 * lane;
+      float m = -__builtin_inff();
+      if (i < span) {
+        const v4f x = *(const v4f*)&s_score[wave][i];
+        m = x[0];
+#pragma unroll
+        for (int e = 1; e < 4; ++e) m = (i + e < span) ? fmaxf(m, x[e]) : m;
+      }
+      m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, false)));  // lane ^ 1
+      m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, false)));  // lane ^ 2
+      // row rotations: the first lane of each 8- or 16-lane group collects it
+      if (lpg >= 8) m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x124, 0xF, 0xF, false)));
+      if (lpg >= 16) m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x128, 0xF, 0xF, false)));
+      if (lpg >= 32) m = max_xor16(m);
+      if (lpg >= 64) m = max_xor32(m);
+      bool emit = true;
+      if (lpg > 64) {  // 512-entry sub-chunk: finish it on its second pass (or at the range end)
+        carry = fmaxf(carry, m);
+        m = carry;
+        emit = ((base + 256) & (a.group - 1)) == 0 || base + 256 >= span;
+        if (emit) carry = -__builtin_inff();
+      }
+      const int first = (lpg > 64) ? base - (base & (a.group - 1)) : i;  // first score of the sub-chunk
+      if (emit && (lane & (min(lpg, 64) - 1)) == 0 && i < span)
+        a.gmax[grow + (w0p + first) / a.group] = (m == -__builtin_inff()) ? 0u : score_key(m);
+    }
   }
 }
 
