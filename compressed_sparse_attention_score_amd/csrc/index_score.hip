@@ -56,6 +56,7 @@ __device__ __forceinline__ int64_t cand_entry(const ScoreArgs& a, int q, int64_t
 
 template <bool POOL, int UNROLL = kUnroll>
 __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
+  static_assert(UNROLL == 4, "a batch is 64 entries: one staged score per lane");
   const int q = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, kb = lane >> 4;
@@ -113,17 +114,32 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
       bs[u] = __builtin_nontemporal_load((const unsigned*)(a.key_scales + row * 4));
     }
   };
+  // Both MFMAs of one 16-entry group. A lane without a valid candidate
+  // holds the codes of a clamped row with a unit scale: FP4 codes are all
+  // finite, each entry is its own MFMA column, and the column's score is
+  // replaced by -inf below, so those bytes never reach a valid score.
+  auto mfma2 = [&](const v4u& bcu, unsigned bsu, bool oku, v4f& c0, v4f& c1) {
+    const int sb = oku ? (int)((bsu >> (8 * kb)) & 0xFFu) : 127;
+    const v8i B = {(int)bcu[0], (int)bcu[1], (int)bcu[2], (int)bcu[3], 0, 0, 0, 0};
+    c0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A0, B, v4f{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, sa0, 0, sb);
+    c1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1, B, v4f{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, sa1, 0, sb);
+  };
+  // One batch of UNROLL groups, software-pipelined: the MFMAs of group u+1
+  // are issued before the vector epilogue of group u (the scheduling
+  // barriers keep that order), so the matrix core and the vector unit work
+  // at the same time. Groups past the wave's range are computed on masked
+  // lanes and land in staging slots past the range, which the flush skips
+  // (the range is a multiple of 64 entries except at the list end, and the
+  // slots stay inside the wave's row).
   auto compute = [&](const v4u* bc, const unsigned* bs, const bool* ok, int64_t g0) {
+    v4f c0, c1, n0, n1;
+    float sv[UNROLL];
+    mfma2(bc[0], bs[0], ok[0], c0, c1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-      const int64_t gp = g0 + 16 * u;
-      if (gp >= w1p) break;
-      const v4u c = ok[u] ? bc[u] : v4u{0u, 0u, 0u, 0u};
-      const int sb = ok[u] ? (int)((bs[u] >> (8 * kb)) & 0xFFu) : 127;
-      v8i B = {(int)c[0], (int)c[1], (int)c[2], (int)c[3], 0, 0, 0, 0};
-      v4f c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
-      c0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A0, B, c0, 4, 4, 0, sa0, 0, sb);
-      c1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1, B, c1, 4, 4, 0, sa1, 0, sb);
+      if (u + 1 < UNROLL) mfma2(bc[u + 1], bs[u + 1], ok[u + 1], n0, n1);
+      __builtin_amdgcn_sched_barrier(0);
       float sc = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) sc = fmaf(w0[r], relu_bits(c0[r]), sc);
@@ -131,10 +147,17 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
       for (int r = 0; r < 4; ++r) sc = fmaf(w1[r], relu_bits(c1[r]), sc);
       sc = add_xor16(sc);
       sc = add_xor32(sc);
-      // every lane now holds the score of entry r16 of this group
-      const float sv = ok[u] ? sc : -__builtin_inff();
-      if (kb == 0) s_score[wave][gp - w0p + r16] = sv;
+      // every lane now holds the score of entry r16 of group u
+      sv[u] = ok[u] ? sc : -__builtin_inff();
+      __builtin_amdgcn_sched_barrier(0);
+      c0 = n0;
+      c1 = n1;
     }
+    // lane (kb, r16) stages entry r16 of group kb: one conflict-free store
+    float mine = sv[0];
+#pragma unroll
+    for (int u = 1; u < UNROLL; ++u) mine = (kb == u) ? sv[u] : mine;
+    s_score[wave][g0 - w0p + lane] = mine;
   };
   constexpr int64_t kStep = 16 * UNROLL;
   issue(bcA, bsA, okA, w0p);
@@ -205,6 +228,12 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
 namespace {
 constexpr int kQSets = 2;  // 4-query sets per wave
 constexpr int kTileUnroll = 4;  // 16-entry steps per load batch
+// Buffer resource word 3 for untyped dword access on gfx9-family parts, the
+// nontemporal cache-policy bit of a buffer store, and an offset that is past
+// every resource this kernel builds (their sizes stay below 2 GiB).
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kNonTemporal = 2;
+constexpr unsigned kStoreDrop = 0x80000000u;
 }  // namespace
 
 template <bool GMAX, int QSETS = kQSets, int BB = kTileUnroll>
@@ -213,7 +242,9 @@ __global__ __launch_bounds__(256) void k_index_score_qtile(ScoreArgs a, int rang
   __shared__ unsigned s_scl[2][BB * 16];
   constexpr int kQPerWave = 4 * QSETS;
   constexpr int kQPerWg = 4 * kQPerWave;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is uniform across the wave; saying so keeps the output
+  // buffer resources in scalar registers
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, kb = lane >> 4;
   const int q0 = blockIdx.y * kQPerWg + wave * kQPerWave;
   const int64_t e_begin = (int64_t)blockIdx.x * range;
@@ -248,7 +279,13 @@ __global__ __launch_bounds__(256) void k_index_score_qtile(ScoreArgs a, int rang
   float wt[QSETS][32];
   int lim[QSETS];
   bool qok[QSETS];
-  float* obase[QSETS];
+  // Score stores go through a buffer resource per set whose base is the
+  // set's first output row at e_begin (wave-uniform) and whose size is what
+  // remains of the score array from there. A lane with nothing to store
+  // passes an offset past that size and the hardware drops the store, so a
+  // step has no branches and the scheduler can interleave its MFMAs with the
+  // vector epilogue.
+  __amdgpu_buffer_rsrc_t orsrc[QSETS];
 #pragma unroll
   for (int s = 0; s < QSETS; ++s) {
     const int qo = q0 + 4 * s + kb;
@@ -258,7 +295,9 @@ __global__ __launch_bounds__(256) void k_index_score_qtile(ScoreArgs a, int rang
     int64_t l = a.n_entries;
     if (a.n_valid && qok[s]) l = min(l, (int64_t)a.n_valid[qo]);
     lim[s] = (int)max((int64_t)0, min(l - e_begin, (int64_t)span));
-    obase[s] = a.scores + (int64_t)(q0 + 4 * s) * a.n_cand + e_begin;
+    const int64_t first = (int64_t)(q0 + 4 * s) * a.n_cand + e_begin;
+    const int64_t room = max((int64_t)0, min((int64_t)a.Q * a.n_cand - first, (int64_t)kStoreDrop / 4 - 1));
+    orsrc[s] = __builtin_amdgcn_make_buffer_rsrc(a.scores + first, 0, (int)(room * 4), kBufferWord3);
   }
   const unsigned orow_off = (unsigned)kb * (unsigned)a.n_cand + (unsigned)r16;
   // running maximum score of the current sub-chunk (invalid entries as -inf;
@@ -306,28 +345,41 @@ __global__ __launch_bounds__(256) void k_index_score_qtile(ScoreArgs a, int rang
       const int sb = (int)((bs >> (8 * kb)) & 0xFFu);
       const int p = off + r16;
       const bool in_range = p < span;
-      // the query sets interleaved: independent MFMAs in flight
+      // Software pipeline: the MFMAs of head block hb+1 are issued before the
+      // vector epilogue of block hb, so the matrix core and the vector unit
+      // work at the same time within one wave.
       float acc[QSETS];
+      v4f cur[QSETS], nxt[QSETS];
 #pragma unroll
-      for (int s = 0; s < QSETS; ++s) acc[s] = 0.f;
+      for (int s = 0; s < QSETS; ++s) {
+        acc[s] = 0.f;
+        cur[s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[s][0], B, v4f{0.f, 0.f, 0.f, 0.f}, 4, 4, 0,
+                                                                  sA[s][0], 0, sb);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int hb = 0; hb < 8; ++hb) {
-        v4f c[QSETS];
+        if (hb + 1 < 8) {
 #pragma unroll
-        for (int s = 0; s < QSETS; ++s) {
-          c[s] = v4f{0.f, 0.f, 0.f, 0.f};
-          c[s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[s][hb], B, c[s], 4, 4, 0, sA[s][hb], 0, sb);
+          for (int s = 0; s < QSETS; ++s)
+            nxt[s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[s][hb + 1], B, v4f{0.f, 0.f, 0.f, 0.f}, 4,
+                                                                      4, 0, sA[s][hb + 1], 0, sb);
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < QSETS; ++s)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[s] = fmaf(wt[s][4 * hb + r], relu_bits(c[s][r]), acc[s]);
+          for (int r = 0; r < 4; ++r) acc[s] = fmaf(wt[s][4 * hb + r], relu_bits(cur[s][r]), acc[s]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < QSETS; ++s) cur[s] = nxt[s];
       }
 #pragma unroll
       for (int s = 0; s < QSETS; ++s) {
         const float sv = (p < lim[s]) ? acc[s] : ninf;
         // scores stream out past L2 (the selection pass reads them much later)
-        if (qok[s] && in_range) __builtin_nontemporal_store(sv, obase[s] + orow_off + (unsigned)off);
+        const unsigned boff = (qok[s] && in_range) ? 4u * (orow_off + (unsigned)off) : kStoreDrop;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sv), orsrc[s], boff, 0, kNonTemporal);
         if (GMAX) gm[s] = fmaxf(gm[s], sv);  // lim <= span, so sv is -inf outside the range
       }
       if (GMAX) {
@@ -408,8 +460,8 @@ ScorePlan plan_score(int64_t n_cand, int Q, int k) {
 
 // The query-tiled kernel applies when all queries share one cache (prefill).
 static bool use_query_tiles(const IndexLaunch& L) {
-  // 32-bit in-range offsets: 4*n_cand must stay below 2^32
-  return L.cache_q_stride == 0 && L.cand_blocks == nullptr && L.Q >= 16 * kQSets && L.n_cand < (1ll << 28);
+  // store offsets (up to 4 rows of 4-byte scores) stay below 2 GiB: 16*n_cand < 2^31
+  return L.cache_q_stride == 0 && L.cand_blocks == nullptr && L.Q >= 16 * kQSets && L.n_cand < (1ll << 27);
 }
 
 hipError_t launch_index_score(const IndexLaunch& L, const ScorePlan& plan, float* scores, unsigned* gmax,
