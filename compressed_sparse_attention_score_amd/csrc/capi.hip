@@ -389,9 +389,18 @@ int csa2_decode(const csa2_decode_args* a, void* ws, size_t ws_bytes, void* stre
   if (e == hipSuccess) e = launch_index_score(L, sp, w.scores, w.tk.gmax, s);
   if (e == hipSuccess) e = mark(1);
   if (e != hipSuccess) return CSA2_ERR_HIP;
-  // 2. threshold + compaction, exact top-k
-  e = launch_select(w.scores, Q, n_cand, a->index.n_entries, a->index.cand_blocks, a->index.n_blocks,
-                    a->index.n_valid, a->k, sp, w.tk.gmax, w.tk.counts, w.tk.cand, w.idx, nullptr, s);
+  // 2. threshold + compaction, exact top-k. In the chunk-parallel form the
+  // final selection runs inside the attention kernel, whose every split
+  // finishes its query's selection from the compacted candidates: one kernel
+  // boundary and one id round trip fewer.
+  const SelectPlan pl = plan_select(n_cand);
+  const bool fused = select_is_chunked(Q, n_cand) && pl.n_chunks <= kFusedSelectMaxChunks;
+  if (fused)
+    e = launch_select_compact(w.scores, Q, n_cand, a->index.n_entries, a->index.cand_blocks, a->index.n_blocks,
+                              a->index.n_valid, a->k, sp, w.tk.gmax, w.tk.counts, w.tk.cand, s);
+  else
+    e = launch_select(w.scores, Q, n_cand, a->index.n_entries, a->index.cand_blocks, a->index.n_blocks,
+                      a->index.n_valid, a->k, sp, w.tk.gmax, w.tk.counts, w.tk.cand, w.idx, nullptr, s);
   if (e == hipSuccess) e = mark(2);
   if (e != hipSuccess) return CSA2_ERR_HIP;
   // 3. attention over the selection + window
@@ -400,6 +409,14 @@ int csa2_decode(const csa2_decode_args* a, void* ws, size_t ws_bytes, void* stre
                w.idx,  a->k,               a->q,                    a->swa,
                a->swa_q_stride, a->n_swa, a->softmax_scale,        a->out,
                a->lse, a->swa_format == CSA2_SWA_FP8, a->rope_cos_sin};
+  if (fused) {
+    A.sel_counts = w.tk.counts;
+    A.sel_cand = w.tk.cand;
+    A.sel_n_cand = n_cand;
+    A.sel_chunks = pl.n_chunks;
+    A.sel_chunk = pl.chunk;
+    A.idx_out = a->idx_out;
+  }
   e = launch_attn(A, ap, w.partial, s);
   if (e == hipSuccess) e = mark(3);
   return hip_status(e);

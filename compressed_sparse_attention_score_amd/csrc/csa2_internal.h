@@ -79,6 +79,19 @@ hipError_t launch_select(const float* scores, int Q, int64_t n_cand, int64_t n_e
                          int n_blocks, const int32_t* n_valid, int k, const ScorePlan& sp, const unsigned* gmax,
                          unsigned* counts, unsigned long long* cand, int32_t* idx, float* top_scores, hipStream_t s);
 
+// Whether launch_select takes the chunk-parallel form (compaction, then a
+// per-query final selection) for these sizes, and that form's compaction
+// kernel alone (its final selection then runs inside the attention kernel).
+bool select_is_chunked(int Q, int64_t n_cand);
+hipError_t launch_select_compact(const float* scores, int Q, int64_t n_cand, int64_t n_entries,
+                                 const int32_t* cand_blocks, int n_blocks, const int32_t* n_valid, int k,
+                                 const ScorePlan& sp, const unsigned* gmax, unsigned* counts, unsigned long long* cand,
+                                 hipStream_t s);
+
+// Largest number of compaction chunks per query for which the attention
+// kernel finishes the selection (one workgroup of that many threads).
+constexpr int kFusedSelectMaxChunks = 512;
+
 // Reindex pool construction: bmax [Q][ceil(n/8)] = best score of each block
 // of 8 inside the causal limit (as a score whose key is the block's best
 // key), nvb [Q] = blocks holding at least one valid entry.
@@ -105,6 +118,14 @@ struct AttnLaunch {
   float* lse;
   int swa_fp8;
   const float* rope;  // [Q][32][2] (cos, sin) or nullptr
+  // Selection finished by the attention kernel (decode): the compaction's
+  // counts [Q][sel_chunks] and composites [Q][sel_n_cand], or sel_counts =
+  // nullptr to read the ids from idx. idx_out receives the ids (or nullptr).
+  const unsigned* sel_counts;
+  const unsigned long long* sel_cand;
+  int64_t sel_n_cand;
+  int sel_chunks, sel_chunk;
+  int32_t* idx_out;
 };
 
 // partial: workspace for the per-split records (plan.n_splits > 1); the merge

@@ -46,6 +46,7 @@
 //    rotated back by each query's angles in the epilogue that writes it.
 #include "csa2_device.h"
 #include "csa2_internal.h"
+#include "select_device.h"
 
 namespace csa2 {
 
@@ -59,6 +60,11 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kSwa8Bytes = 528;  // FP8 window row: 512 E4M3 codes + 16 E8M0 scales
 constexpr int kStageRow = kDim + 8;  // epilogue LDS row (bf16): 16 B of pad spreads the banks
 constexpr int kRopeFirst = 448;  // first rotary channel; pairs (448+2i, 449+2i), i < 32
+// Compacted candidates per thread when a split finishes the selection: 8 x
+// 512 threads give each of up to 512 chunks at least 8 slots (a decode chunk
+// keeps a few dozen survivors at most for random scores; more take the
+// offset-table or streaming path).
+constexpr int kSelReg = 8;
 
 struct AttnArgs {
   const uint8_t* main_cache;
@@ -70,6 +76,13 @@ struct AttnArgs {
   uint16_t* out;
   float* lse;
   float* partial;
+  // Selection finished here (decode): chunk c of query q's compacted list
+  // holds sel_counts[q][c] composites from sel_cand[q][c*sel_chunk] on.
+  const unsigned* sel_counts;
+  const unsigned long long* sel_cand;
+  int64_t sel_n_cand;
+  int sel_chunks, sel_chunk;
+  int32_t* idx_out;  // selected ids [Q][k_sel] written by the split that holds them, or nullptr
   int64_t n_entries, cache_q_stride, swa_q_stride;
   int k_sel, n_swa, nj, n_tiles, tiles_per_split, n_splits;
   float scale_log2;
@@ -88,6 +101,7 @@ struct AttnShared {
       uint16_t vb[2][TILE * kDim];  // blocked V^T, double-buffered
     };
     uint16_t ostage[kHeads * kStageRow];  // epilogue: the 64 output rows (bf16)
+    SelScratch<NT> sel;                   // prologue: finishing the selection
   };
   v4f sx[8][4][64];                 // partial S^T per wave: [wave][2*sb+hb][lane]
   uint2 pl[kHeads][TILE / 4];       // P^T as bf16: [head][slot quad] = 4 slots
@@ -265,7 +279,7 @@ __device__ __forceinline__ void unrotate(float& x, float& y, float2 cs) {
   y = b * cs.x - a * cs.y;
 }
 
-template <bool SWA8>
+template <bool SWA8, bool FUSED>
 __global__ __launch_bounds__(NT, 1) void k_sparse_attn(AttnArgs a) {
   const int q = blockIdx.y, split = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -314,12 +328,28 @@ __global__ __launch_bounds__(NT, 1) void k_sparse_attn(AttnArgs a) {
     }
   };
 
-  // The split's selected ids, read once into LDS.
+  // The split's selected ids, into LDS once: read from the id list, or
+  // (FUSED) taken from the exact selection over the query's compacted
+  // candidates, which every split holding selected slots finishes for itself
+  // (the same result in each) and writes its own range of to idx_out.
   {
     const int sbeg = t0 * TILE, send = min(t1 * TILE, a.k_sel);
-    for (int sl = sbeg + tid; sl < send; sl += NT) sh.ids[sl - sbeg] = a.idx[(int64_t)q * a.k_sel + sl];
+    if (FUSED) {
+      if (sbeg < send) {  // uniform over the workgroup
+        int32_t* io = a.idx_out ? a.idx_out + (int64_t)q * a.k_sel : nullptr;
+        select_from_regions<NT, kSelReg>(a.sel_counts + (int64_t)q * a.sel_chunks, a.sel_chunks, a.sel_chunk, a.sel_n_cand,
+                                a.k_sel, a.sel_cand + (int64_t)q * a.sel_n_cand, sh.sel, sbeg, send,
+                                [&](unsigned pos, unsigned long long x) {
+                                  const int32_t id = x ? (int32_t)(~(unsigned)(x & 0xFFFFFFFFull)) : -1;
+                                  sh.ids[pos - sbeg] = id;
+                                  if (io) io[pos] = id;
+                                });
+      }
+    } else {
+      for (int sl = sbeg + tid; sl < send; sl += NT) sh.ids[sl - sbeg] = a.idx[(int64_t)q * a.k_sel + sl];
+    }
   }
-  __syncthreads();
+  __syncthreads();  // ids in LDS; the selection scratch (over the tile area) is free
 
   // Pipeline: tile t is multiplied from LDS while tile t+1 (raw data already
   // in registers) is dequantised into the other buffer and the latents of
@@ -608,6 +638,12 @@ hipError_t launch_attn(const AttnLaunch& L, const AttnPlan& plan, float* partial
   a.out = L.out;
   a.lse = L.lse;
   a.partial = partial;
+  a.sel_counts = L.sel_counts;
+  a.sel_cand = L.sel_cand;
+  a.sel_n_cand = L.sel_n_cand;
+  a.sel_chunks = L.sel_chunks;
+  a.sel_chunk = L.sel_chunk;
+  a.idx_out = L.idx_out;
   a.n_entries = L.n_entries;
   a.cache_q_stride = L.cache_q_stride;
   a.swa_q_stride = L.swa_q_stride;
@@ -619,10 +655,18 @@ hipError_t launch_attn(const AttnLaunch& L, const AttnPlan& plan, float* partial
   a.n_splits = plan.n_splits;
   a.scale_log2 = L.scale * kLog2e;
   dim3 grid((unsigned)plan.n_splits, (unsigned)L.Q);
-  if (L.swa_fp8)
-    k_sparse_attn<true><<<grid, NT, 0, s>>>(a);
-  else
-    k_sparse_attn<false><<<grid, NT, 0, s>>>(a);
+  const bool fused = L.sel_counts != nullptr;
+  if (L.swa_fp8) {
+    if (fused)
+      k_sparse_attn<true, true><<<grid, NT, 0, s>>>(a);
+    else
+      k_sparse_attn<true, false><<<grid, NT, 0, s>>>(a);
+  } else {
+    if (fused)
+      k_sparse_attn<false, true><<<grid, NT, 0, s>>>(a);
+    else
+      k_sparse_attn<false, false><<<grid, NT, 0, s>>>(a);
+  }
   if (plan.n_splits > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

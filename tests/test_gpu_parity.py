@@ -578,6 +578,28 @@ def test_decode_prefill_query_tiles(T, n, t0):
     _check_decode(synth.prefill(T, n, t0, seed=50 + T), what=f"prefill tiles T={T}")
 
 
+def test_decode_chunked_selection_paths():
+    """Lists long enough for the chunk-parallel selection (3 queries x 20,000
+    entries, 5 compaction chunks of 4,096), whose final step runs inside the
+    attention kernel. Query 0: every key equal, so every score ties, every
+    candidate survives the compaction and the lowest 512 ids win (streaming
+    path). Query 1: 1,000 entries of chunk 1 carry the query's best key, a tie
+    set larger than that chunk's register slots (offset-table path). Query 2:
+    random (fixed slots). The tied queries' id sets are compared exactly."""
+    wl = synth.full_decode(3, 20000, seed=31)
+    n = wl.n_entries
+    wl.key_codes[0:n] = wl.key_codes[0]
+    wl.key_scales[0:n] = wl.key_scales[0]
+    s1 = oracle.index_score(wl, queries=[1])[0]
+    best = n + int(np.argmax(s1))
+    wl.key_codes[n + 4196:n + 5196] = wl.key_codes[best]
+    wl.key_scales[n + 4196:n + 5196] = wl.key_scales[best]
+    gidx = _check_decode(wl, what="chunked selection")
+    ref = oracle.decode(wl, queries=[0, 1])
+    assert np.array_equal(gidx[0], np.arange(512, dtype=np.int32))
+    assert np.array_equal(np.sort(gidx[1]), np.sort(ref["idx"][1][:512]))
+
+
 def test_decode_fewer_than_k_entries():
     _check_decode(synth.full_decode(2, 300, seed=24), what="n<k")
 
