@@ -156,19 +156,21 @@ __device__ __forceinline__ T radix_kth_stream(const T* src, int64_t n, unsigned 
   return radix_kth<NTH, T>(count, k, hist, res, max_passes);
 }
 
-// The bits every non-zero composite shares: with kmax and kmin the largest
-// and smallest score key, the composites agree above bit 32 + bitlen(kmax ^
-// kmin). *top gets that bit (64 when they differ in the sign bit or there are
-// no values) and *prefix the shared bits above it. One barrier.
-template <int NTH, int REG>
-__device__ __forceinline__ void shared_top_bits(const unsigned long long (&v)[REG], SelScratch<NTH>& sc, int* top,
-                                                unsigned long long* prefix) {
+// The bits every non-zero value shares. Each lies between the smallest and
+// the largest, so all agree above the highest bit where those two differ;
+// 64-bit composites are ranged by their score keys (the top 32 bits), below
+// which they may differ anywhere. *top gets that bit (the width when there are
+// no values or they differ in the top bit) and *prefix the shared bits above
+// it. ext: 2*(NTH/64) words of LDS. One barrier.
+template <int NTH, typename T, int REG>
+__device__ __forceinline__ void shared_top_bits(const T (&v)[REG], unsigned* ext, int* top, T* prefix) {
+  constexpr int W = (int)(sizeof(T) * 8), S = W - 32;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   unsigned kmax = 0u, kmin = ~0u;
 #pragma unroll
   for (int j = 0; j < REG; ++j) {
-    if (v[j] != 0ull) {
-      const unsigned key = (unsigned)(v[j] >> 32);
+    if (v[j] != 0) {
+      const unsigned key = (unsigned)(v[j] >> S);
       kmax = max(kmax, key);
       kmin = min(kmin, key);
     }
@@ -179,19 +181,19 @@ __device__ __forceinline__ void shared_top_bits(const unsigned long long (&v)[RE
     kmin = min(kmin, (unsigned)__shfl_xor((int)kmin, o, 64));
   }
   if (lane == 0) {
-    sc.ext[2 * wv] = kmax;
-    sc.ext[2 * wv + 1] = kmin;
+    ext[2 * wv] = kmax;
+    ext[2 * wv + 1] = kmin;
   }
   __syncthreads();
 #pragma unroll
   for (int w = 0; w < NTH / 64; ++w) {
-    kmax = max(kmax, sc.ext[2 * w]);
-    kmin = min(kmin, sc.ext[2 * w + 1]);
+    kmax = max(kmax, ext[2 * w]);
+    kmin = min(kmin, ext[2 * w + 1]);
   }
   const unsigned diff = kmax ^ kmin;
-  const int t = (kmax == 0u || (diff >> 31)) ? 64 : 32 + (diff ? 32 - __clz(diff) : 0);
+  const int t = (kmax == 0u || (diff >> 31)) ? W : S + (diff ? 32 - __clz((int)diff) : 0);
   *top = t;
-  *prefix = (t >= 64) ? 0ull : ((((unsigned long long)kmax) << 32) >> t) << t;
+  *prefix = (t >= W) ? (T)0 : ((((T)kmax) << S) >> t) << t;
 }
 
 // Exact top-k of the non-zero composites held REG per thread, thread order
@@ -205,7 +207,7 @@ __device__ __forceinline__ unsigned select_regs(const unsigned long long (&v)[RE
   if (m > (unsigned)k) {
     int top;
     unsigned long long prefix;
-    shared_top_bits<NTH, REG>(v, sc, &top, &prefix);
+    shared_top_bits<NTH, unsigned long long, REG>(v, sc.ext, &top, &prefix);
     T = radix_kth_regs<NTH, unsigned long long, REG>(v, (unsigned)k, sc.hist, sc.res, 64, top, prefix);
   }
   unsigned c = 0;

@@ -45,10 +45,12 @@ struct SelShared {
 };
 }  // namespace
 
-// theta needs only to be a lower bound on the k-th largest score: two passes
-// fix the sign, exponent and top 7 mantissa bits of the k-th sub-chunk
-// maximum, which lowers the bound by less than 2^-7 of its value and adds a
-// few percent of survivors, and saves the passes over the low 16 bits.
+// theta needs only to be a lower bound on the k-th largest score: two passes,
+// starting at the highest bit where the sub-chunk maxima differ, fix 16 bits
+// of the k-th sub-chunk maximum below the bits all maxima share (at least its
+// sign, exponent and top 7 mantissa bits), which lowers the bound by less
+// than 2^-7 of its value and adds a few percent of survivors, and saves the
+// passes over the remaining low bits.
 constexpr int kThetaPasses = 2;
 
 // Threshold + compaction: grid (n_chunks, Q). Writes cand[q][c0 .. c0+cnt) in
@@ -113,7 +115,10 @@ __global__ __launch_bounds__(NT) void k_select_compact(const float* __restrict__
         const int64_t i = (int64_t)j * NT + tid;
         g[j] = (i < n_groups) ? gq[i] : 0u;
       }
-      t = radix_kth_regs<NT, unsigned, 16>(g, (unsigned)k, sh.sel.hist, sh.sel.res, kThetaPasses);
+      int top;
+      unsigned prefix;
+      shared_top_bits<NT, unsigned, 16>(g, sh.sel.ext, &top, &prefix);
+      t = radix_kth_regs<NT, unsigned, 16>(g, (unsigned)k, sh.sel.hist, sh.sel.res, kThetaPasses, top, prefix);
     } else {
       t = radix_kth_stream<NT, unsigned>(gq, n_groups, (unsigned)k, sh.sel.hist, sh.sel.res, kThetaPasses);
     }
@@ -178,6 +183,7 @@ struct QSelShared {
   alignas(16) unsigned hist[2][kBins];
   alignas(16) unsigned wsum[NQ / 64];
   unsigned res[4];
+  unsigned ext[2 * (NQ / 64)];
   unsigned long long cand[kQCap + kQCap / 16];  // survivor i at q_slot(i)
 };
 
@@ -236,7 +242,10 @@ __global__ __launch_bounds__(NQ) void k_select_query(const float* __restrict__ s
         const int64_t i = (int64_t)j * NQ + tid;
         g[j] = (i < n_groups) ? gm[i] : 0u;
       }
-      t = radix_kth_regs<NQ, unsigned, 4>(g, (unsigned)k, sh.hist, sh.res, kThetaPasses);
+      int top;
+      unsigned prefix;
+      shared_top_bits<NQ, unsigned, 4>(g, sh.ext, &top, &prefix);
+      t = radix_kth_regs<NQ, unsigned, 4>(g, (unsigned)k, sh.hist, sh.res, kThetaPasses, top, prefix);
     } else {
       t = radix_kth_stream<NQ, unsigned>(gm, n_groups, (unsigned)k, sh.hist, sh.res, kThetaPasses);
     }
@@ -303,7 +312,13 @@ __global__ __launch_bounds__(NQ) void k_select_query(const float* __restrict__ s
       const unsigned e = (unsigned)tid * PER + j;
       v[j] = (e < m) ? sh.cand[q_slot(e)] : 0ull;
     }
-    const unsigned long long T = (m > (unsigned)k) ? radix_kth_regs<NQ, unsigned long long, PER>(v, (unsigned)k, sh.hist, sh.res) : 0ull;
+    unsigned long long T = 0ull;
+    if (m > (unsigned)k) {
+      int top;
+      unsigned long long prefix;
+      shared_top_bits<NQ, unsigned long long, PER>(v, sh.ext, &top, &prefix);
+      T = radix_kth_regs<NQ, unsigned long long, PER>(v, (unsigned)k, sh.hist, sh.res, 64, top, prefix);
+    }
     unsigned c = 0;
 #pragma unroll
     for (int j = 0; j < PER; ++j) c += (v[j] != 0ull && v[j] >= T) ? 1u : 0u;
