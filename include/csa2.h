@@ -299,8 +299,11 @@ typedef struct csa2_decode_args {
   float* lse;                 /* out [Q][64] or NULL                             */
   int32_t* idx_out;           /* out [Q][k] selected ids, or NULL                */
   void* stage_events[4];      /* optional hipEvent_t (as void*) recorded on the stream
-                                 before scoring [0], after scoring [1], after
-                                 selection [2] and after attention [3]; NULL = skip */
+                                 before scoring [0], after scoring [1], after the
+                                 selection kernels that precede attention [2]
+                                 and after attention [3]; NULL = skip. For few
+                                 long lists the last selection step runs inside
+                                 the attention kernel, so [2]..[3] includes it. */
   int32_t swa_format;         /* CSA2_SWA_BF16 or CSA2_SWA_FP8                   */
   const float* rope_cos_sin;  /* [Q][32][2] or NULL, as in csa2_attn_args        */
 } csa2_decode_args;
