@@ -39,14 +39,16 @@ struct ScoreArgs {
 };
 }  // namespace
 
-// Position p of query q's candidate list -> entry id, or -1 when p is not a
-// valid candidate (beyond the list, out-of-range block id, causal limit).
+// Position p of a candidate list -> entry id, or -1 when p is not a valid
+// candidate (beyond the list, out-of-range block id, causal limit). blk holds
+// the block ids of the wave's range, from position p0 on (pools only).
 template <bool POOL>
-__device__ __forceinline__ int64_t cand_entry(const ScoreArgs& a, int q, int64_t p, int64_t limit) {
+__device__ __forceinline__ int64_t cand_entry(const ScoreArgs& a, const int32_t* blk, int64_t p0, int64_t p,
+                                              int64_t limit) {
   if (p >= a.n_cand) return -1;
   int64_t e;
   if (POOL) {
-    int32_t b = a.cand_blocks[(int64_t)q * a.n_blocks + (p >> 3)];
+    const int32_t b = blk[(p - p0) >> 3];
     e = (b < 0) ? -1 : 8 * (int64_t)b + (p & 7);
   } else {
     e = p;
@@ -64,6 +66,9 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
   // loop's only vector-memory operations are loads; the sub-chunk maxima are
   // formed from the staged scores at that point.
   __shared__ __attribute__((aligned(16))) float s_score[4][kMaxWaveSpan];
+  // A pool's block ids for the wave's range, read once: a key load then
+  // waits on an LDS read instead of a global one.
+  __shared__ int32_t s_blk[4][POOL ? kMaxWaveSpan / 8 : 1];
 
   // A operands: query heads r16 and 16+r16, scale block kb.
   const uint8_t* iqc = a.iq_codes + (int64_t)q * kIHeads * 64;
@@ -100,6 +105,14 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
       for (int64_t g = w0p / a.group; g * a.group < w1p; ++g) a.gmax[(int64_t)q * a.n_groups + g] = 0u;
     return;
   }
+  if (POOL) {  // the range starts on a block boundary (wave spans are multiples of 64)
+    const int nb = (int)((w1p - w0p + 7) >> 3);
+    const int32_t* src = a.cand_blocks + (int64_t)q * a.n_blocks + (w0p >> 3);
+    for (int i = lane; i < nb; i += 64) s_blk[wave][i] = src[i];
+    // read back by other lanes of this wave only: its LDS accesses complete
+    // in order, and this keeps the compiler from moving the reads above
+    __builtin_amdgcn_wave_barrier();
+  }
   v4u bcA[UNROLL], bcB[UNROLL];
   unsigned bsA[UNROLL], bsB[UNROLL];
   bool okA[UNROLL], okB[UNROLL];
@@ -107,7 +120,7 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int64_t p = g0 + 16 * u + r16;
-      const int64_t e = (p < w1p) ? cand_entry<POOL>(a, q, p, limit) : -1;
+      const int64_t e = (p < w1p) ? cand_entry<POOL>(a, s_blk[wave], w0p, p, limit) : -1;
       ok[u] = e >= 0;
       const int64_t row = base_row + (e >= 0 ? e : 0);
       bc[u] = __builtin_nontemporal_load((const v4u*)(a.key_codes + row * 64 + kb * 16));
