@@ -254,29 +254,61 @@ __global__ __launch_bounds__(NQ) void k_select_query(const float* __restrict__ s
 
   // ---- keep key >= theta, in position order
   unsigned m = 0;  // survivors so far (block-uniform)
+  // Fast filter. When theta lies above the key of +0 and the list is the
+  // plain range [0, n_cand), a score passes exactly when its bit pattern u
+  // satisfies theta' <= u <= 0x7F800000 (+inf), theta' being theta without
+  // its sign bit: a non-negative score's key is u + 2^31, and every negative
+  // score, -0 and NaN has u > 0x7F800000 and a key below theta. One subtract
+  // and one unsigned compare per score; the composite is built for the
+  // survivors only.
+  const bool fast = cand_blocks == nullptr && theta > 0x80000000u;
+  const unsigned tlo = theta & 0x7FFFFFFFu, tspan = 0x7F800000u - tlo;
+  const int64_t vlim = min(n_cand, limit);  // valid positions of the plain range
   auto process = [&](const float* sc, const int32_t* blk, int64_t p0) {
     const int64_t pb = p0 + (int64_t)tid * kQPer;
-    unsigned long long comp[kQPer];
-    unsigned cnt = 0;
-#pragma unroll
-    for (int j = 0; j < kQPer; ++j) {
-      const int64_t p = pb + j;
-      int64_t e = p;
-      if (cand_blocks) e = (blk[j >> 3] < 0) ? -1 : 8 * (int64_t)blk[j >> 3] + (p & 7);
-      const bool valid = p < n_cand && e >= 0 && e < limit;
-      const unsigned key = score_key(sc[j]);
-      const bool keep = valid && key >= theta;
-      comp[j] = keep ? (((unsigned long long)key << 32) | (unsigned long long)(~(unsigned)e)) : 0ull;
-      cnt += keep ? 1u : 0u;
-    }
     unsigned total;
-    unsigned pos = m + block_incl_scan<NQ>(cnt, sh.wsum, &total) - cnt;
+    if (fast) {
+      const int nv = (int)max((int64_t)0, min(vlim - pb, (int64_t)kQPer));
+      bool keep[kQPer];
+      unsigned cnt = 0;
 #pragma unroll
-    for (int j = 0; j < kQPer; ++j) {
-      if (comp[j]) {
-        if (pos < (unsigned)kQCap) sh.cand[q_slot(pos)] = comp[j];
-        else gq[pos] = comp[j];
-        ++pos;
+      for (int j = 0; j < kQPer; ++j) {
+        keep[j] = j < nv && __float_as_uint(sc[j]) - tlo <= tspan;
+        cnt += keep[j] ? 1u : 0u;
+      }
+      unsigned pos = m + block_incl_scan<NQ>(cnt, sh.wsum, &total) - cnt;
+#pragma unroll
+      for (int j = 0; j < kQPer; ++j) {
+        if (keep[j]) {  // a non-negative score: its key is its bits with the sign bit set
+          const unsigned long long comp = ((unsigned long long)(__float_as_uint(sc[j]) | 0x80000000u) << 32) |
+                                          (unsigned long long)(~(unsigned)(pb + j));
+          if (pos < (unsigned)kQCap) sh.cand[q_slot(pos)] = comp;
+          else gq[pos] = comp;
+          ++pos;
+        }
+      }
+    } else {
+      unsigned long long comp[kQPer];
+      unsigned cnt = 0;
+#pragma unroll
+      for (int j = 0; j < kQPer; ++j) {
+        const int64_t p = pb + j;
+        int64_t e = p;
+        if (cand_blocks) e = (blk[j >> 3] < 0) ? -1 : 8 * (int64_t)blk[j >> 3] + (p & 7);
+        const bool valid = p < n_cand && e >= 0 && e < limit;
+        const unsigned key = score_key(sc[j]);
+        const bool keep = valid && key >= theta;
+        comp[j] = keep ? (((unsigned long long)key << 32) | (unsigned long long)(~(unsigned)e)) : 0ull;
+        cnt += keep ? 1u : 0u;
+      }
+      unsigned pos = m + block_incl_scan<NQ>(cnt, sh.wsum, &total) - cnt;
+#pragma unroll
+      for (int j = 0; j < kQPer; ++j) {
+        if (comp[j]) {
+          if (pos < (unsigned)kQCap) sh.cand[q_slot(pos)] = comp[j];
+          else gq[pos] = comp[j];
+          ++pos;
+        }
       }
     }
     m += total;
