@@ -132,15 +132,30 @@ __global__ __launch_bounds__(NT) void k_select_compact(const float* __restrict__
     sc[4 * i] = x[0]; sc[4 * i + 1] = x[1]; sc[4 * i + 2] = x[2]; sc[4 * i + 3] = x[3];
   }
 
-  // ---- keep key >= theta, in position order
+  // ---- keep key >= theta, in position order. Above the key of +0 and on a
+  // plain range, the same one-compare filter as the per-query kernel below
+  // (a score passes exactly when theta' <= its bits <= those of +inf).
   unsigned long long comp[kPer];
   unsigned cnt = 0;
+  if (cand_blocks == nullptr && theta > 0x80000000u) {
+    const unsigned tlo = theta & 0x7FFFFFFFu, tspan = 0x7F800000u - tlo;
+    const int nv = (int)max((int64_t)0, min(min(n_cand, limit) - p0, (int64_t)kPer));
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const unsigned key = score_key(sc[j]);
-    const bool keep = ent[j] >= 0 && key >= theta;
-    comp[j] = keep ? (((unsigned long long)key << 32) | (unsigned long long)(~(unsigned)ent[j])) : 0ull;
-    cnt += keep ? 1u : 0u;
+    for (int j = 0; j < kPer; ++j) {
+      const unsigned u = __float_as_uint(sc[j]);
+      const bool keep = j < nv && u - tlo <= tspan;
+      comp[j] = keep ? (((unsigned long long)(u | 0x80000000u) << 32) | (unsigned long long)(~(unsigned)(p0 + j)))
+                     : 0ull;
+      cnt += keep ? 1u : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const unsigned key = score_key(sc[j]);
+      const bool keep = ent[j] >= 0 && key >= theta;
+      comp[j] = keep ? (((unsigned long long)key << 32) | (unsigned long long)(~(unsigned)ent[j])) : 0ull;
+      cnt += keep ? 1u : 0u;
+    }
   }
   unsigned total;
   const unsigned incl = block_incl_scan<NT>(cnt, sh.sel.wsum, &total);
