@@ -216,7 +216,9 @@ typedef struct csa2_topk_args {
  * candidates by (score descending, entry id ascending) are kept: equal scores
  * go to the lower id, -0 equals +0, NaN ranks below every number. The kept set
  * is written in ascending entry id (the selection fixes a set, not an order);
- * top_scores[q][j] is the score of idx[q][j]. When fewer than k candidates are
+ * top_scores[q][j] is the score of idx[q][j], as ranked: a selected -0 is
+ * reported as +0, the two being one value for the ranking; a selected NaN is
+ * reported as the quiet NaN 0x7FC00000. When fewer than k candidates are
  * valid the tail is -1 / -inf. Needs a workspace of
  * csa2_workspace_size(CSA2_WS_TOPK, args) bytes, 256-B aligned, contents
  * ignored on entry. */

@@ -300,7 +300,10 @@ def _assert_topk_exact(scores, k, n_entries, cand_blocks=None, n_valid=None, wha
     assert np.array_equal(gi, ref_i), f"{what}: ids differ at {np.argwhere(gi != ref_i)[:5].tolist()}"
     assert np.array_equal(np.isnan(gs), np.isnan(ref_s))
     m = ~np.isnan(ref_s)
-    assert np.array_equal(gs[m].view(np.uint32), ref_s[m].view(np.uint32)), what
+    # bit-exact, except that a selected -0 is reported as +0 (the ranking
+    # treats them as one value, and the kernels report the ranked value)
+    ref_b = np.where(ref_s[m] == 0, np.float32(0.0), ref_s[m]).view(np.uint32)
+    assert np.array_equal(gs[m].view(np.uint32), ref_b), what
 
 
 @pytest.mark.parametrize("n", [1, 100, 511, 512, 513, 4096, 4097, 70001])
@@ -323,6 +326,25 @@ def test_topk_ties_nan_negzero(n):
     s[2, :300] = np.nan
     s[3, :] = 2.5  # all equal: the whole list is one tie set
     _assert_topk_exact(s, 512, n, what=f"ties n{n}")
+
+
+@pytest.mark.parametrize("n", [20000, 16000])
+def test_topk_threshold_at_or_below_zero(n):
+    """Thresholds at or below the key of +0 take the general compaction test
+    (above it a single compare of the score bits decides). Row 0: every score
+    negative. Row 1: 600 zeros of both signs, the rest negative, so the
+    threshold is the key of +0 and -0 must tie with +0 (lower id first).
+    Row 2: 300 positive scores, 600 zeros, the rest negative: the 512th score
+    is a zero. Row 3: 1,000 values of +inf and NaN among negatives. Same
+    kernels as the tie test: 4 x 20,000 chunk-parallel, 4 x 16,000 per query."""
+    rng = np.random.default_rng(7)
+    s = -np.abs(rng.standard_normal((4, n))).astype(np.float32) - np.float32(0.01)
+    z = rng.choice(n, 600, replace=False)
+    s[1, z] = np.where(np.arange(600) % 2 == 0, np.float32(0.0), np.float32(-0.0))
+    s[2, z] = np.where(np.arange(600) % 3 == 0, np.float32(-0.0), np.float32(0.0))
+    s[2, rng.choice(np.setdiff1d(np.arange(n), z), 300, replace=False)] = np.abs(rng.standard_normal(300)) + 0.5
+    s[3, rng.choice(n, 1000, replace=False)] = np.where(np.arange(1000) % 2 == 0, np.float32(np.inf), np.float32(np.nan))
+    _assert_topk_exact(s, 512, n, what=f"threshold <= 0 n{n}")
 
 
 def test_topk_survivors_concentrated_in_one_chunk():
