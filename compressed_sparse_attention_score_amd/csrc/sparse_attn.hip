@@ -515,72 +515,44 @@ __global__ __launch_bounds__(NT, 1) void k_sparse_attn(AttnArgs a) {
 // Merge the splits of one query: with O_s stored as O_s / l_s,
 // out = sum_s (O_s / l_s) l_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), in split
 // order. grid (16, Q), 256 threads:
-// thread -> head blockIdx.x*4 + tid/64, channels (tid%64)*8 .. +7. Every
-// split's (m, l) and each batch of 8 splits' O rows are requested together
-// (clamped indices, zero weight past the last split), so the merge costs a
-// few memory round trips however many splits there are.
+// thread -> head blockIdx.x*4 + tid/64, channels (tid%64)*8 .. +7. MS is the
+// split capacity of the instantiation (n_splits <= MS): every split's (m, l)
+// and O row are requested together (clamped indices, zero weight past the
+// last split), so the merge costs one memory round trip.
+template <int MS>
 __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ partial, int n_splits,
                                                       const float* __restrict__ rope, uint16_t* __restrict__ out,
                                                       float* __restrict__ lse) {
   const int q = blockIdx.y, tid = threadIdx.x;
   const int h = blockIdx.x * 4 + (tid >> 6), c0 = (tid & 63) * 8;
   const float* base = partial + (int64_t)q * n_splits * kPartialFloats;
-  float ms[kMaxSplits], ls[kMaxSplits];
+  float ms[MS], ls[MS];
+  v4u x[MS];
 #pragma unroll
-  for (int sp = 0; sp < kMaxSplits; ++sp) {
+  for (int sp = 0; sp < MS; ++sp) {
     const int ss = min(sp, n_splits - 1);
     ms[sp] = base[ss * kPartialFloats + h];
     ls[sp] = base[ss * kPartialFloats + 64 + h];
-  }
-  // the first batch of O rows is requested with (m, l): it does not depend on them
-  v4u x0[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int ss = min(u, n_splits - 1);
-    x0[u] = *(const v4u*)((const uint16_t*)(base + ss * kPartialFloats + 128) + (int64_t)h * kDim + c0);
+    x[sp] = *(const v4u*)((const uint16_t*)(base + ss * kPartialFloats + 128) + (int64_t)h * kDim + c0);
   }
   __builtin_amdgcn_sched_barrier(0);  // keep every load above issued before any use
   float M = -__builtin_inff();
 #pragma unroll
-  for (int sp = 0; sp < kMaxSplits; ++sp) M = (sp < n_splits) ? fmaxf(M, ms[sp]) : M;
+  for (int sp = 0; sp < MS; ++sp) M = (sp < n_splits) ? fmaxf(M, ms[sp]) : M;
+  // every weight is 0 when no split holds a slot (M = -inf), so no branch
   float L = 0.f;
   float acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = 0.f;
-  {  // every weight is 0 when no split holds a slot (M = -inf), so no branch
-    float f[kMaxSplits];  // weight of split s: l_s 2^(m_s - M)
 #pragma unroll
-    for (int sp = 0; sp < kMaxSplits; ++sp) {
-      f[sp] = (sp < n_splits && ms[sp] != -__builtin_inff()) ? ls[sp] * __builtin_amdgcn_exp2f(ms[sp] - M) : 0.f;
-      L += f[sp];
-    }
-    // splits 0..7 (straight-line, so their early loads stay early), then the rest
+  for (int sp = 0; sp < MS; ++sp) {
+    const float f =  // weight of split sp: l 2^(m - M)
+        (sp < n_splits && ms[sp] != -__builtin_inff()) ? ls[sp] * __builtin_amdgcn_exp2f(ms[sp] - M) : 0.f;
+    L += f;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        acc[2 * c] += __uint_as_float(x0[u][c] << 16) * f[u];
-        acc[2 * c + 1] += __uint_as_float(x0[u][c] & 0xFFFF0000u) * f[u];
-      }
-    }
-    for (int s0 = 8; s0 < n_splits; s0 += 8) {
-      v4u x[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int ss = min(s0 + u, n_splits - 1);
-        x[u] = *(const v4u*)((const uint16_t*)(base + ss * kPartialFloats + 128) + (int64_t)h * kDim + c0);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        float fu = 0.f;
-#pragma unroll
-        for (int sp = 8; sp < kMaxSplits; ++sp) fu = (sp == s0 + u) ? f[sp] : fu;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          acc[2 * c] += __uint_as_float(x[u][c] << 16) * fu;
-          acc[2 * c + 1] += __uint_as_float(x[u][c] & 0xFFFF0000u) * fu;
-        }
-      }
+    for (int c = 0; c < 4; ++c) {
+      acc[2 * c] += __uint_as_float(x[sp][c] << 16) * f;
+      acc[2 * c + 1] += __uint_as_float(x[sp][c] & 0xFFFF0000u) * f;
     }
   }
   const float inv = (L > 0.f) ? 1.f / L : 0.f;
@@ -670,7 +642,15 @@ hipError_t launch_attn(const AttnLaunch& L, const AttnPlan& plan, float* partial
   if (plan.n_splits > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    k_attn_combine<<<dim3(16, (unsigned)L.Q), 256, 0, s>>>(partial, plan.n_splits, L.rope, L.out, L.lse);
+    const dim3 grid(16, (unsigned)L.Q);
+    if (plan.n_splits <= 4)
+      k_attn_combine<4><<<grid, 256, 0, s>>>(partial, plan.n_splits, L.rope, L.out, L.lse);
+    else if (plan.n_splits <= 8)
+      k_attn_combine<8><<<grid, 256, 0, s>>>(partial, plan.n_splits, L.rope, L.out, L.lse);
+    else if (plan.n_splits <= 16)
+      k_attn_combine<16><<<grid, 256, 0, s>>>(partial, plan.n_splits, L.rope, L.out, L.lse);
+    else
+      k_attn_combine<kMaxSplits><<<grid, 256, 0, s>>>(partial, plan.n_splits, L.rope, L.out, L.lse);
   }
   return hipGetLastError();
 }
