@@ -508,7 +508,7 @@ __global__ __launch_bounds__(NT, 1) void k_sparse_attn(AttnArgs a) {
 #pragma unroll
   for (int k = 0; k < kHeads * kDim / 8 / NT; ++k) {  // 16-B chunks; a wave covers one head row
     const int i = k * NT + tid, head = i >> 6, chunk = i & 63;
-    *(v4u*)(obase + head * kDim + chunk * 8) = *(const v4u*)(stage + head * kStageRow + chunk * 8);
+    __builtin_nontemporal_store(*(const v4u*)(stage + head * kStageRow + chunk * 8), (v4u*)(obase + head * kDim + chunk * 8));
   }
 }
 
