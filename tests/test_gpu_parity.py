@@ -622,6 +622,26 @@ def test_decode_chunked_selection_paths():
     assert np.array_equal(np.sort(gidx[1]), np.sort(ref["idx"][1][:512]))
 
 
+def test_decode_chunked_causal_limits_and_no_ids():
+    """A 40-query prefill over 20,000 entries at positions 990..1029: the
+    causal limits (495..514 entries) straddle k = 512, so some queries select
+    every valid entry and pad with -1, inside the attention kernel's final
+    selection (chunk-parallel lists: fewer than 64 queries, more than 16,384
+    candidates). The same call without an id output gives the same
+    attention, bit for bit."""
+    wl = synth.prefill(40, 20000, 990, seed=33)
+    assert wl.n_valid.min() < 512 < wl.n_valid.max()
+    gidx = _check_decode(wl, what="chunked causal")
+    db = to_device(wl)
+    out, lse, idx = db.new_outputs()
+    csa.csa2_decode(db.decode_args(out, lse, idx))
+    out2, lse2, _ = db.new_outputs()
+    csa.csa2_decode(db.decode_args(out2, lse2, None))
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), gidx)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
 def test_decode_fewer_than_k_entries():
     _check_decode(synth.full_decode(2, 300, seed=24), what="n<k")
 
