@@ -576,14 +576,15 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
 
 AttnPlan plan_attn(int Q, int nj) {
   // As many splits as keep every workgroup of the launch resident at once
-  // (one per CU), with at least 2 tiles per split so the gather of the next
-  // tile overlaps the current one; at most kMaxSplits splits.
+  // (one per CU): one tile per split when that fits, else at least 2 tiles
+  // per split so the gather of the next tile overlaps the current one; at
+  // most kMaxSplits splits.
   AttnPlan p;
   p.n_tiles = (nj + TILE - 1) / TILE;
   if (p.n_tiles < 1) p.n_tiles = 1;
   const int want = (Q > 0) ? 256 / Q : 1;
   int tps = (want > 0) ? (p.n_tiles + want - 1) / want : p.n_tiles;
-  if (tps < 2) tps = 2;
+  if (tps < 2 && !(tps == 1 && p.n_tiles <= kMaxSplits)) tps = 2;
   p.tiles_per_split = tps;
   p.n_splits = (p.n_tiles + tps - 1) / tps;
   if (p.n_splits > kMaxSplits) {
