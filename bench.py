@@ -14,7 +14,9 @@ Phases (all on one stream):
   3. isolated kernel timing for the roofline: K back-to-back launches of
      csa2_index_score (the scan kernel) and of csa2_sparse_attn, each
      bracketed by two HIP events on the launch stream;
-  4. the CPU oracle on the host cores over a bounded sample (>= --cpu-seconds).
+  4. the box's streaming bandwidth (torch row sums and copy over 1 GiB), the
+     reference the scan kernel's bytes per second are also quoted against;
+  5. the CPU oracle on the host cores over a bounded sample (>= --cpu-seconds).
 
 Prints one JSON line. `python bench.py --pmc-summary DIR` instead summarises
 the counter CSVs of `rocprofv3 --pmc ... --output-format csv -d DIR` runs of
@@ -162,6 +164,34 @@ def work_of(wl):
     attn_fp8_bytes = attn_bytes - (1024 - 528) * swa_rows + Q * 32 * 2 * 4
     return dict(pairs=pairs, score_bytes=score_bytes, score_flops=pairs * FLOP_PER_PAIR, attn_bytes=attn_bytes,
                 attn_flops=attn_flops, step_bytes=score_bytes + attn_bytes, attn_fp8_bytes=attn_fp8_bytes)
+
+
+def stream_bandwidth(reps=20):
+    """The box's own streaming bandwidth, for comparison with the scan
+    kernel, over 1 GiB of fp32 (four times the 256 MB memory-side cache):
+    torch's row sums over 16 KB rows (the fastest read-only torch pattern
+    measured here; a whole-tensor sum reaches about two thirds of it), bytes
+    read per mean launch time, and torch's copy, bytes read + written per
+    mean launch time. GB/s."""
+    import torch
+    x = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    rows = x.view(-1, 4096)
+    out = []
+    for op, nbytes in ((lambda: rows.sum(1), 1 << 30), (lambda: y.copy_(x), 2 << 30)):
+        for _ in range(3):
+            op()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            op()
+        b.record()
+        torch.cuda.synchronize()
+        out.append(nbytes / (a.elapsed_time(b) / reps * 1e-3) / 1e9)
+    del x, y
+    return out
 
 
 def source_digest(names=SCORE_SOURCES):
@@ -536,6 +566,7 @@ def main():
     pq_ms = ev.ms(e0 + 12, e0 + 13) / K
     del xp, gp, cp, pp
     ev.close()
+    read_gbs, copy_gbs = stream_bandwidth()
     if args.copy_calibration:
         src = torch.ones(COPY_MIB << 18, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -618,6 +649,10 @@ def main():
                      "attention": round(1e3 * stage_ms[2], 2), "steps": S},
         "path_hbm_frac": round(work["step_bytes"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": roof,
+        "measured_stream": {"read_GB_s": round(read_gbs, 1), "copy_GB_s": round(copy_gbs, 1),
+                            "what": "torch row sums over 16 KB rows (read) and copy (read + write), 1 GiB fp32, "
+                                    "on this box",
+                            "scan_frac_of_read": None if prefill else round(score_gbs / read_gbs, 4)},
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
