@@ -358,7 +358,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=1, help="workload shape 0..4 (default 1: batch 16 x 65,536)")
+    ap.add_argument("--workload", "--config", dest="workload", type=int, default=1,
+                    help="workload shape: 0 decode 1 x 4,096; 1 decode 16 x 65,536 (default); 2 reindex decode "
+                         "64 x 16,384-entry pools; 3 prefill 4,096 x 131,072; 4 decode 4 x 1,048,576")
     ap.add_argument("--replicas", type=int, default=0, help="device copies rotated per step (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum wall time of the oracle sample")
@@ -387,7 +389,7 @@ def main():
 
     torch.cuda.set_device(0)
     t_gen = time.perf_counter()
-    wl = synth.make_config(args.config, dense_rows=False)
+    wl = synth.make_workload(args.workload, dense_rows=False)
     gen_s = time.perf_counter() - t_gen
     db = to_device(wl)
     Q = wl.Q
@@ -578,7 +580,7 @@ def main():
     ms_per_step = 1e3 * elapsed / K
     value = Q * K / elapsed
     prefill = wl.n_valid is not None
-    name = synth.CONFIG_NAMES[args.config]
+    name = synth.WORKLOAD_NAMES[args.workload]
     score_gbs = work["score_bytes"] / (score_ms * 1e-3) / 1e9
     score_tfs = work["score_flops"] / (score_ms * 1e-3) / 1e12
     attn_gbs = work["attn_bytes"] / (attn_ms * 1e-3) / 1e9
@@ -641,7 +643,7 @@ def main():
         "vs_baseline": None,
         "dtype": "fp4(mx)+bf16",
         "data": "synthetic (seeded N(0,1) latents/keys/queries quantised to FP4 per the pages' formats)",
-        "config": {"workload": name, "config_index": args.config, "queries": Q, "candidates_per_query": wl.n_cand,
+        "config": {"workload": name, "workload_index": args.workload, "queries": Q, "candidates_per_query": wl.n_cand,
                    "top_k": wl.k, "swa_rows": wl.n_swa, "replicas": R},
         "entries_scored_per_s": round(work["pairs"] * K / elapsed, 1),
         "gpu_ms_per_step": round(gpu_ms / K, 5),

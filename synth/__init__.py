@@ -323,8 +323,8 @@ def prefill(T: int, n_cache: int, t0: int, seed: int = 0, m: int = 2, name: str 
     return wl
 
 
-# The five workload shapes of the CSA2 decode/prefill hot path.
-CONFIGS = {
+# The five workload shapes of the CSA2 decode/prefill hot path, by index.
+WORKLOADS = {
     0: dict(kind="full_decode", Q=1, N=4096),
     1: dict(kind="full_decode", Q=16, N=65536),
     2: dict(kind="reindex_decode", Q=64, N=1 << 20, n_blocks=2048),
@@ -332,7 +332,7 @@ CONFIGS = {
     4: dict(kind="full_decode", Q=4, N=1 << 20),
 }
 
-CONFIG_NAMES = {
+WORKLOAD_NAMES = {
     0: "full-layer decode, 1 query x 4,096 entries",
     1: "full-layer decode, batch 16 x 65,536 entries",
     2: "reindex-layer decode, batch 64, 16,384-entry pool of a 1,048,576-entry cache",
@@ -341,13 +341,14 @@ CONFIG_NAMES = {
 }
 
 
-def make_config(i: int, seed: int = 0, dense_rows: Optional[bool] = None) -> Workload:
-    c = CONFIGS[i]
+def make_workload(i: int, seed: int = 0, dense_rows: Optional[bool] = None) -> Workload:
+    c = WORKLOADS[i]
+    name = WORKLOAD_NAMES[i]
     if c["kind"] == "full_decode":
-        return full_decode(c["Q"], c["N"], seed, name=f"config{i}")
+        return full_decode(c["Q"], c["N"], seed, name=name)
     if c["kind"] == "reindex_decode":
-        return reindex_decode(c["Q"], c["N"], c["n_blocks"], seed, dense_rows=bool(dense_rows), name=f"config{i}")
-    return prefill(c["T"], c["n_cache"], c["t0"], seed, name=f"config{i}")
+        return reindex_decode(c["Q"], c["N"], c["n_blocks"], seed, dense_rows=bool(dense_rows), name=name)
+    return prefill(c["T"], c["n_cache"], c["t0"], seed, name=name)
 
 
 def compact_pool_view(wl: Workload) -> Workload:

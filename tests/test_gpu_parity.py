@@ -657,22 +657,22 @@ def test_decode_deterministic():
 
 # ------------------------------------------------- full-size workload shapes
 
-def test_config0_full():
-    _check_decode(synth.make_config(0), what="config0")
+def test_decode_1x4096_full():
+    _check_decode(synth.make_workload(0), what="decode 1 x 4,096")
 
 
-def test_config1_full():
-    _check_decode(synth.make_config(1), what="config1")
+def test_decode_16x65536_full():
+    _check_decode(synth.make_workload(1), what="decode 16 x 65,536")
 
 
-def test_config4_full():
-    _check_decode(synth.make_config(4), what="config4")
+def test_decode_4x1048576_full():
+    _check_decode(synth.make_workload(4), what="decode 4 x 1,048,576")
 
 
-def test_config2_full_pool():
+def test_reindex_decode_64x16384_pool_full():
     """1,048,576-entry caches, 2,048 random blocks of 8 per query; the oracle
     runs on the pool rows re-indexed into a compact cache."""
-    wl = synth.make_config(2, dense_rows=False)
+    wl = synth.make_workload(2, dense_rows=False)
     db = to_device(wl)
     ob, glse, gidx = gpu_decode(db)
     # compact view: query i's pool becomes entries 0..16383 of its own cache
@@ -683,13 +683,13 @@ def test_config2_full_pool():
     comp_gidx = np.stack([np.searchsorted(pools[i], gidx[i]) for i in range(wl.Q)]).astype(np.int32)
     for i in range(wl.Q):
         assert np.array_equal(pools[i][comp_gidx[i]], gidx[i]), "GPU selected an entry outside the pool"
-    check_topk_band(comp_gidx, ref["scores"], ref["idx"], comp, wl.k, "config2")
+    check_topk_band(comp_gidx, ref["scores"], ref["idx"], comp, wl.k, "reindex 64 x 16,384")
     _, of_own, _ = oracle.sparse_attn(comp, comp_gidx)
-    check_attn(ob, of_own, "config2 (own ids)")
-    check_attn(ob, ref["out_f32"], "config2 (oracle ids)")
+    check_attn(ob, of_own, "reindex 64 x 16,384 (own ids)")
+    check_attn(ob, ref["out_f32"], "reindex 64 x 16,384 (oracle ids)")
 
 
-def test_config3_sampled_queries():
-    wl = synth.make_config(3)
+def test_prefill_4096x131072_sampled_queries():
+    wl = synth.make_workload(3)
     qs = [0, 1, 1000, 2047, 2048, 3001, 4094, 4095]
-    _check_decode(wl, queries=qs, what="config3")
+    _check_decode(wl, queries=qs, what="prefill 4,096 x 131,072")
