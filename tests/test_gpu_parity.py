@@ -1,6 +1,8 @@
 """GPU parity: every C-ABI entry point against the CPU oracle on the same
 seeded inputs (small ragged cases spanning several tiles, edge cases, and the
 five workload shapes at full size)."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -620,6 +622,15 @@ def test_decode_chunked_selection_paths():
     ref = oracle.decode(wl, queries=[0, 1])
     assert np.array_equal(gidx[0], np.arange(512, dtype=np.int32))
     assert np.array_equal(np.sort(gidx[1]), np.sort(ref["idx"][1][:512]))
+
+
+@pytest.mark.parametrize("k", [7, 1024])
+def test_decode_chunked_other_k(k):
+    """k other than 512 through the chunk-parallel selection finished in the
+    attention kernel (3 queries x 20,000 entries): 7 selected slots leave
+    most of the first tile to the window; 1,024 fill 32 tiles before it."""
+    wl = dataclasses.replace(synth.full_decode(3, 20000, seed=34 + k), k=k)
+    _check_decode(wl, what=f"chunked k={k}")
 
 
 def test_decode_chunked_causal_limits_and_no_ids():
