@@ -104,7 +104,11 @@ struct AttnShared {
     SelScratch<NT> sel;                   // prologue: finishing the selection
   };
   v4f sx[8][4][64];                 // partial S^T per wave: [wave][2*sb+hb][lane]
-  uint2 pl[kHeads][TILE / 4];       // P^T as bf16: [head][slot quad] = 4 slots
+  // P^T as bf16, 4 slots per entry: [slot quad][head]. A reader's 16 lanes
+  // take 16 consecutive heads of one quad (128 contiguous bytes), and the
+  // 64-byte pad puts the two quads one writer's 16 lanes store on disjoint
+  // banks.
+  uint2 pl[TILE / 4][kHeads + 8];
   float alpha[kHeads];              // per-head rescale of O for this tile (1 = none)
   float fin_m[kHeads], fin_l[kHeads];
   unsigned ok[2][TILE / 4];         // slot validity bytes per tile (double-buffered)
@@ -430,7 +434,7 @@ __global__ __launch_bounds__(NT, 1) void k_sparse_attn(AttnArgs a) {
              ((unsigned)__builtin_bit_cast(uint16_t, (__bf16)p[1]) << 16);
       pk.y = (unsigned)__builtin_bit_cast(uint16_t, (__bf16)p[2]) |
              ((unsigned)__builtin_bit_cast(uint16_t, (__bf16)p[3]) << 16);
-      sh.pl[sh_head][quad] = pk;
+      sh.pl[quad][sh_head] = pk;
       if (quad == 0) sh.alpha[sh_head] = al;
     }
     // ---- tile t+1 to LDS
@@ -445,7 +449,7 @@ __global__ __launch_bounds__(NT, 1) void k_sparse_attn(AttnArgs a) {
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       const int head = 32 * hh + 16 * hb + r16;
-      const uint2 lo = sh.pl[head][g], hi = sh.pl[head][4 + g];
+      const uint2 lo = sh.pl[g][head], hi = sh.pl[4 + g][head];
       pb[hb] = __builtin_bit_cast(v8bf, v4u{lo.x, lo.y, hi.x, hi.y});
       const float al = sh.alpha[head];
       if (__any(al != 1.f)) {
