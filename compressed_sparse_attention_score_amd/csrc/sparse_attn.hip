@@ -244,14 +244,22 @@ __device__ __forceinline__ void decode_tile(const AttnArgs& a, int t, int eg, co
 __device__ __forceinline__ int kt_offset(int slot, int chunk) { return slot * kDim + ((chunk ^ (slot & 15)) << 3); }
 
 // V^T block of (channel group cg, slot group sg): 16 channels x 4 slots, 128
-// bytes. Block order within a channel group alternates with cg's parity and
-// chunk c (channel c of the group, 4 slots = 8 bytes) sits at (c + cg) & 15:
-// a fragment read (16 channels of 4 consecutive slot groups) covers 512
-// contiguous bytes, and a store of one slot group by 64 lanes (32 channel
-// groups) spreads over every bank twice.
+// bytes. Block order within a channel group alternates with the parity of
+// cg ^ (cg >> 3), and chunk c (channel c of the group, 4 slots = 8 bytes)
+// sits at (c + cg) & 15: a fragment read (16 channels of 4 consecutive slot
+// groups) covers 512 contiguous bytes, and in a store of one slot group by 64
+// lanes (32 channel groups) each 32 lanes served together touch 32 distinct
+// 8-byte bank pairs (groups cg and cg + 8, which share a chunk position, sit
+// in opposite 128-byte halves).
 __device__ __forceinline__ int vb_offset(int cg, int sg, int c) {
-  return ((cg * 8 + (sg ^ (cg & 1))) * 16 + ((c + cg) & 15)) * 4;
+  return ((cg * 8 + (sg ^ ((cg ^ (cg >> 3)) & 1))) * 16 + ((c + cg) & 15)) * 4;
 }
+
+// Slot of element e (a lane's partial S^T fragment) in a wave's row of the
+// partial-sum exchange: bit 3 flipped in the upper half, so that a softmax
+// read (8 consecutive elements from each of two halves) touches 16 distinct
+// 16-byte bank groups.
+__device__ __forceinline__ int sx_slot(int e) { return e ^ ((e & 16) >> 1); }
 
 // Store this thread's 4 dequantised slots (8 channels each) as tile data:
 // Kt rows, V^T buffer vbuf, validity flags okbuf.
@@ -395,15 +403,16 @@ __global__ __launch_bounds__(NT, 1) void k_sparse_attn(AttnArgs a) {
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) sh.sx[wave][2 * sb + hb][lane] = s[sb][hb];
+        for (int hb = 0; hb < 2; ++hb) sh.sx[wave][2 * sb + hb][sx_slot(lane)] = s[sb][hb];
     }
     __syncthreads();  // partial sums written; Kt and vb[b^1] are no longer read
 
     // ---- phase 2: softmax of this lane's head over slots 4quad..4quad+3
     {
-      v4f tot = sh.sx[s_hh][2 * s_sb + s_hb][16 * s_g + s_r16];
+      const int sxe = sx_slot(16 * s_g + s_r16);
+      v4f tot = sh.sx[s_hh][2 * s_sb + s_hb][sxe];
 #pragma unroll
-      for (int c = 1; c < 4; ++c) tot += sh.sx[s_hh + 2 * c][2 * s_sb + s_hb][16 * s_g + s_r16];
+      for (int c = 1; c < 4; ++c) tot += sh.sx[s_hh + 2 * c][2 * s_sb + s_hb][sxe];
       const unsigned okw = sh.ok[b][quad];
       float x[4];
 #pragma unroll
