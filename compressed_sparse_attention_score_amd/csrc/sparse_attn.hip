@@ -104,11 +104,12 @@ struct AttnShared {
     SelScratch<NT> sel;                   // prologue: finishing the selection
   };
   v4f sx[8][4][64];                 // partial S^T per wave: [wave][2*sb+hb][lane]
-  // P^T as bf16, 4 slots per entry: [slot quad][head]. A reader's 16 lanes
-  // take 16 consecutive heads of one quad (128 contiguous bytes), and the
-  // 64-byte pad puts the two quads one writer's 16 lanes store on disjoint
-  // banks.
-  uint2 pl[TILE / 4][kHeads + 8];
+  // P^T as bf16, 4 slots per entry: [slot quad][head], head h of quad q at
+  // column h ^ (8 * (q >> 1)) of a 640-byte row (pl_col). A reader's 32
+  // lanes take 16 consecutive heads of two quads (two 128-byte runs, 128
+  // bytes apart modulo the 256-byte bank width); a writer's 32 lanes store 8
+  // heads of four quads (four 64-byte runs, moved apart by the swizzle).
+  uint2 pl[TILE / 4][kHeads + 16];
   float alpha[kHeads];              // per-head rescale of O for this tile (1 = none)
   float fin_m[kHeads], fin_l[kHeads];
   unsigned ok[2][TILE / 4];         // slot validity bytes per tile (double-buffered)
@@ -260,6 +261,9 @@ __device__ __forceinline__ int vb_offset(int cg, int sg, int c) {
 // read (8 consecutive elements from each of two halves) touches 16 distinct
 // 16-byte bank groups.
 __device__ __forceinline__ int sx_slot(int e) { return e ^ ((e & 16) >> 1); }
+
+// Column of head h in row q of the P^T exchange (see AttnShared::pl).
+__device__ __forceinline__ int pl_col(int q, int h) { return h ^ (8 * (q >> 1)); }
 
 // Store this thread's 4 dequantised slots (8 channels each) as tile data:
 // Kt rows, V^T buffer vbuf, validity flags okbuf.
@@ -443,7 +447,7 @@ __global__ __launch_bounds__(NT, 1) void k_sparse_attn(AttnArgs a) {
              ((unsigned)__builtin_bit_cast(uint16_t, (__bf16)p[1]) << 16);
       pk.y = (unsigned)__builtin_bit_cast(uint16_t, (__bf16)p[2]) |
              ((unsigned)__builtin_bit_cast(uint16_t, (__bf16)p[3]) << 16);
-      sh.pl[quad][sh_head] = pk;
+      sh.pl[quad][pl_col(quad, sh_head)] = pk;
       if (quad == 0) sh.alpha[sh_head] = al;
     }
     // ---- tile t+1 to LDS
@@ -458,7 +462,7 @@ __global__ __launch_bounds__(NT, 1) void k_sparse_attn(AttnArgs a) {
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       const int head = 32 * hh + 16 * hb + r16;
-      const uint2 lo = sh.pl[g][head], hi = sh.pl[4 + g][head];
+      const uint2 lo = sh.pl[g][pl_col(g, head)], hi = sh.pl[4 + g][pl_col(4 + g, head)];
       pb[hb] = __builtin_bit_cast(v8bf, v4u{lo.x, lo.y, hi.x, hi.y});
       const float al = sh.alpha[head];
       if (__any(al != 1.f)) {
