@@ -20,12 +20,12 @@
 //    slots of the tile (4 values per lane), adds the four partial sums from
 //    LDS, and writes P^T (bf16, laid out as the PV B operand) and the
 //    per-head rescale factor back to LDS for the product waves.
-//  * Per tile t, three barrier-separated phases: (1) S^T of tile t and
+//  * Per tile t, two barrier-separated phases: (1) P^T of tile t-1 picked
+//    up (O^T rescaled if a head's reference moved), then S^T of tile t and
 //    O^T += V^T P^T of tile t-1 back to back on the matrix cores; (2) the
 //    softmax of tile t, and tile t+1 dequantised into LDS (V^T
-//    double-buffered, K single-buffered) with the latents of tile t+2
-//    requested; (3) P^T of tile t picked up and O^T rescaled if a head's
-//    reference moved.
+//    double-buffered, K single-buffered), with the latents of tile t+2
+//    requested at the start of the step.
 //  * The PV product's k-slot order is permuted (slots 4g..4g+3 and
 //    16+4g..16+4g+3 for lane group g) so that S^T fragments, P^T fragments
 //    and V^T reads line up without shuffles.
@@ -380,11 +380,30 @@ __global__ __launch_bounds__(NT, 1) void k_sparse_attn(AttnArgs a) {
     if (t0 + 1 < t1) issue_raw<SWA8>(a, sh, q, t0 + 1, t0, eg, c8, rawA);
   }
 
+  // Pick up P^T of the last softmaxed tile; rescale O^T where a head's
+  // reference moved. Runs after the barrier that follows that softmax, and
+  // before the barrier after which the next softmax rewrites pl and alpha.
+  auto pickup = [&]() {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int head = 32 * hh + 16 * hb + r16;
+      const uint2 lo = sh.pl[g][pl_col(g, head)], hi = sh.pl[4 + g][pl_col(4 + g, head)];
+      pb[hb] = __builtin_bit_cast(v8bf, v4u{lo.x, lo.y, hi.x, hi.y});
+      const float al = sh.alpha[head];
+      if (__any(al != 1.f)) {
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) o[cb][hb] *= al;
+      }
+    }
+  };
+
   // One tile: nxt holds the raw data of tile t+1, fut receives tile t+2's.
+  // Two barriers per tile: the P^T pickup of tile t-1 opens the step.
   auto step = [&](int t, RawSlot* nxt, RawSlot* fut) {
     const int b = (t - t0) & 1;
-    __syncthreads();  // tile t is in Kt and vb[b]; sx, pl and alpha are free
+    __syncthreads();  // tile t is in Kt and vb[b]; P^T(t-1) and its rescale factors are written; sx is free
     if (t + 2 < t1) issue_raw<SWA8>(a, sh, q, t + 2, t0, eg, c8, fut);
+    if (t > t0) pickup();
 
     // ---- phase 1: S^T(t) over this wave's channel quarter; O^T += V^T(t-1) P^T(t-1)
     {
@@ -456,27 +475,17 @@ __global__ __launch_bounds__(NT, 1) void k_sparse_attn(AttnArgs a) {
       decode_tile<SWA8>(a, t + 1, eg, nxt, kw, &okb);
       store_tile(sh, b ^ 1, eg, c8, kw, okb);
     }
-    __syncthreads();  // P^T and the rescale factors of tile t are written
-
-    // ---- phase 3: pick up P^T(t); rescale O^T where a reference moved
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const int head = 32 * hh + 16 * hb + r16;
-      const uint2 lo = sh.pl[g][pl_col(g, head)], hi = sh.pl[4 + g][pl_col(4 + g, head)];
-      pb[hb] = __builtin_bit_cast(v8bf, v4u{lo.x, lo.y, hi.x, hi.y});
-      const float al = sh.alpha[head];
-      if (__any(al != 1.f)) {
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb) o[cb][hb] *= al;
-      }
-    }
   };
   for (int t = t0; t < t1; t += 2) {
     step(t, rawA, rawB);
     if (t + 1 < t1) step(t + 1, rawB, rawA);
   }
   // O^T += V^T P^T of the last tile (its V^T buffer is no longer written)
-  if (t0 < t1) pv_product((t1 - 1 - t0) & 1);
+  __syncthreads();  // P^T of the last tile and its rescale factors are written
+  if (t0 < t1) {
+    pickup();
+    pv_product((t1 - 1 - t0) & 1);
+  }
   if (quad == 0) {
     sh.fin_m[sh_head] = m_ref;
     sh.fin_l[sh_head] = l_run;
