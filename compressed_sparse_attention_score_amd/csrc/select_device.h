@@ -53,6 +53,41 @@ __device__ __forceinline__ unsigned block_incl_scan(unsigned x, unsigned* wsum, 
   return x + before;
 }
 
+// Two inclusive prefix sums at once (x0 and x1 scanned independently, one
+// barrier pair for both). wsum holds 2*(NTH/64) entries, 16-B aligned.
+template <int NTH>
+__device__ __forceinline__ void block_incl_scan2(unsigned& x0, unsigned& x1, unsigned* wsum, unsigned* total0,
+                                                 unsigned* total1) {
+  static_assert(NTH % 256 == 0, "wave sums are read four at a time");
+  constexpr int W = NTH / 64;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  x0 = wave_incl_scan(x0);
+  x1 = wave_incl_scan(x1);
+  __syncthreads();
+  if (lane == 63) {
+    wsum[wv] = x0;
+    wsum[W + wv] = x1;
+  }
+  __syncthreads();
+  unsigned b0 = 0, b1 = 0, a0 = 0, a1 = 0;
+#pragma unroll
+  for (int i = 0; i < W / 4; ++i) {
+    const v4u s0 = *(const v4u*)(wsum + 4 * i);
+    const v4u s1 = *(const v4u*)(wsum + W + 4 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      b0 += (4 * i + j < wv) ? s0[j] : 0u;
+      b1 += (4 * i + j < wv) ? s1[j] : 0u;
+      a0 += s0[j];
+      a1 += s1[j];
+    }
+  }
+  *total0 = a0;
+  *total1 = a1;
+  x0 += b0;
+  x1 += b1;
+}
+
 // Digit pick of one radix pass, run by wave 0 alone. Lane l holds bins
 // 255-4l .. 252-4l (the digits from the top); a wave prefix sum over the lanes
 // counts the values in the bins above each lane's, and the lane whose four

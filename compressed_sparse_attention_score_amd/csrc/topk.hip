@@ -189,34 +189,47 @@ __global__ __launch_bounds__(NT) void k_select_final(const unsigned* __restrict_
 // id: pools list their blocks in ascending order), then the exact k-th
 // composite among the survivors and the ordered write.
 namespace {
-constexpr int NQ = 1024;            // threads
-constexpr int kQPer = 16;           // consecutive positions per thread per pass
-constexpr int kQCap = 8192;         // survivors held in LDS (8 per thread)
+// The workgroup size is a template parameter. Large batches take 256-thread
+// workgroups limited to 128 VGPRs, four to a CU, so that some stream their
+// query's scores while others run their barrier-bound radix passes; small
+// batches take 1,024 threads, so that their few queries still spread over
+// the CU's waves.
+constexpr int kQPer = 16;           // positions per thread per pass
 constexpr int64_t kQMaxCand = 1 << 18;
+constexpr int kQSmallBatch = 1024;  // queries from which the 256-thread workgroup is used
 
+// Survivors held in LDS: 8 per thread at 1,024 threads, 16 per thread below.
+template <int NQ>
+constexpr int q_cap() { return NQ >= 1024 ? 8192 : 16 * NQ; }
+
+template <int NQ>
 struct QSelShared {
   alignas(16) unsigned hist[2][kBins];
-  alignas(16) unsigned wsum[NQ / 64];
+  alignas(16) unsigned wsum[2 * (NQ / 64)];
   unsigned res[4];
   unsigned ext[2 * (NQ / 64)];
-  unsigned long long cand[kQCap + kQCap / 16];  // survivor i at q_slot(i)
+  unsigned long long cand[q_cap<NQ>() + q_cap<NQ>() / 16];  // survivor i at q_slot(i)
 };
 
-// LDS slot of survivor i: one pad slot after every 16. A thread writes its
-// survivors as a run, and with everything kept the runs of neighbouring
-// lanes start 16 composites (128 bytes) apart, i.e. in the same banks; the
-// pad shifts each run by one composite so a store spreads over the banks.
+// LDS slot of survivor i: one pad slot after every 16, so that the runs of
+// survivors that neighbouring lanes write spread over the banks.
 __device__ __forceinline__ unsigned q_slot(unsigned i) { return i + (i >> 4); }
 
 }  // namespace
 
-__global__ __launch_bounds__(NQ) void k_select_query(const float* __restrict__ scores, int64_t n_cand,
+// POOL: the lists are pools of blocks of 8 (cand_blocks given); otherwise
+// the plain range [0, n_cand) (cand_blocks NULL).
+template <int NQ, int RUN, bool POOL>
+__global__ __launch_bounds__(NQ) __attribute__((amdgpu_waves_per_eu(NQ >= 1024 ? 1 : 4))) void k_select_query(const float* __restrict__ scores, int64_t n_cand,
                                                      int64_t n_entries, const int32_t* __restrict__ cand_blocks,
                                                      int n_blocks, const int32_t* __restrict__ n_valid, int k,
                                                      const unsigned* __restrict__ gmax, int64_t n_groups,
                                                      unsigned long long* __restrict__ gcand, int32_t* __restrict__ idx,
                                                      float* __restrict__ top_scores) {
-  __shared__ QSelShared sh;
+  constexpr int kQCap = q_cap<NQ>();
+  constexpr int kQGrp = kQPer / RUN;  // groups per pass
+  static_assert(RUN == 4 || RUN == 8 || RUN == 16, "a run is 4, 8 or 16 positions");
+  __shared__ QSelShared<NQ> sh;
   const int q = blockIdx.x, tid = threadIdx.x;
   int64_t limit = n_entries;
   if (n_valid) limit = min(limit, (int64_t)n_valid[q]);
@@ -225,24 +238,35 @@ __global__ __launch_bounds__(NQ) void k_select_query(const float* __restrict__ s
   const float* srow = scores + (int64_t)q * n_cand;
   unsigned long long* gq = gcand + (int64_t)q * n_cand;
 
-  // Positions are taken in passes of NQ*kQPer; thread t owns positions
-  // 16t..16t+15 of each pass. Full passes (rows 16-byte aligned) load with
-  // aligned vectors and no per-thread conditions, the next pass's scores
-  // in flight while this one is compacted; a ragged last pass is guarded.
-  constexpr int64_t kStep = (int64_t)NQ * kQPer;
+  // Positions are taken in passes of NQ*kQPer, split into kQGrp groups of
+  // NQ*RUN consecutive positions; thread t owns positions RUN*t..RUN*t+RUN-1
+  // of each group (with RUN = 4 every load instruction of the workgroup
+  // reads one contiguous NQ*16-byte span). Survivors keep position order:
+  // group g's go after those of the groups before it, within a group in
+  // thread order. Full passes (rows
+  // 16-byte aligned) load with aligned vectors and no per-thread
+  // conditions, the next pass's scores in flight while this one is
+  // compacted; a ragged last pass is guarded.
+  constexpr int64_t kGrpLen = (int64_t)NQ * RUN;
+  constexpr int kBlk = (RUN + 7) / 8;  // pool blocks a run touches
+  constexpr int64_t kStep = kGrpLen * kQGrp;
   const int64_t n_full = ((n_cand & 3) == 0) ? n_cand / kStep : 0;
   auto load_full = [&](float* sc, int32_t* blk, int64_t p0) {
-    const int64_t pb = p0 + (int64_t)tid * kQPer;
 #pragma unroll
-    for (int j = 0; j < kQPer; j += 4) {
-      const v4f v = *(const v4f*)(srow + pb + j);
-      sc[j] = v[0]; sc[j + 1] = v[1]; sc[j + 2] = v[2]; sc[j + 3] = v[3];
+    for (int g = 0; g < kQGrp; ++g) {
+      const int64_t pb = p0 + g * kGrpLen + RUN * tid;
+#pragma unroll
+      for (int j = 0; j < RUN; j += 4) {
+        const v4f v = *(const v4f*)(srow + pb + j);
+        sc[RUN * g + j] = v[0]; sc[RUN * g + j + 1] = v[1]; sc[RUN * g + j + 2] = v[2]; sc[RUN * g + j + 3] = v[3];
+      }
+#pragma unroll
+      for (int b = 0; b < kBlk; ++b)
+        blk[kBlk * g + b] = POOL ? cand_blocks[(int64_t)q * n_blocks + (pb >> 3) + b] : 0;
     }
-#pragma unroll
-    for (int j = 0; j < kQPer / 8; ++j) blk[j] = cand_blocks ? cand_blocks[(int64_t)q * n_blocks + ((pb >> 3) + j)] : 0;
   };
   float scA[kQPer], scB[kQPer];
-  int32_t bkA[kQPer / 8], bkB[kQPer / 8];
+  int32_t bkA[kQGrp * kBlk], bkB[kQGrp * kBlk];
   if (n_full > 0) load_full(scA, bkA, 0);  // in flight during the threshold search
 
   // ---- theta = k-th largest sub-chunk maximum (1 = keep every valid candidate)
@@ -276,57 +300,102 @@ __global__ __launch_bounds__(NQ) void k_select_query(const float* __restrict__ s
   // score, -0 and NaN has u > 0x7F800000 and a key below theta. One subtract
   // and one unsigned compare per score; the composite is built for the
   // survivors only.
-  const bool fast = cand_blocks == nullptr && theta > 0x80000000u;
+  const bool fast = !POOL && theta > 0x80000000u;
   const unsigned tlo = theta & 0x7FFFFFFFu, tspan = 0x7F800000u - tlo;
   const int64_t vlim = min(n_cand, limit);  // valid positions of the plain range
+  // Each group's count (at most RUN per thread, NQ*RUN <= 16,384 per
+  // workgroup) takes 16 bits of a scanned word: one word for one or two
+  // groups, two words (one scan) for four.
+  static_assert(NQ * RUN <= 65535, "a group's count fits 16 bits");
+  auto place = [&](const unsigned (&cnt)[kQGrp], unsigned (&pos)[kQGrp]) {
+    if constexpr (kQGrp == 4) {
+      unsigned w0 = cnt[0] | (cnt[1] << 16), w1 = cnt[2] | (cnt[3] << 16);
+      const unsigned e0 = w0, e1 = w1;
+      unsigned t0, t1;
+      block_incl_scan2<NQ>(w0, w1, sh.wsum, &t0, &t1);
+      w0 -= e0;  // exclusive
+      w1 -= e1;
+      const unsigned T0 = t0 & 0xFFFFu, T1 = t0 >> 16, T2 = t1 & 0xFFFFu;
+      pos[0] = m + (w0 & 0xFFFFu);
+      pos[1] = m + T0 + (w0 >> 16);
+      pos[2] = m + T0 + T1 + (w1 & 0xFFFFu);
+      pos[3] = m + T0 + T1 + T2 + (w1 >> 16);
+      m += T0 + T1 + T2 + (t1 >> 16);
+    } else {
+      const unsigned w = kQGrp == 2 ? (cnt[0] | (cnt[kQGrp - 1] << 16)) : cnt[0];
+      unsigned t;
+      const unsigned x = block_incl_scan<NQ>(w, sh.wsum, &t) - w;  // exclusive
+      const unsigned T0 = kQGrp == 2 ? (t & 0xFFFFu) : t;
+      pos[0] = m + (kQGrp == 2 ? (x & 0xFFFFu) : x);
+      pos[kQGrp - 1] = kQGrp == 2 ? m + T0 + (x >> 16) : pos[0];
+      m += kQGrp == 2 ? T0 + (t >> 16) : t;
+    }
+  };
+  auto put = [&](unsigned pos, unsigned long long comp) {
+    if (pos < (unsigned)kQCap) sh.cand[q_slot(pos)] = comp;
+    else gq[pos] = comp;
+  };
+  // The survivors of a pass are marked in a bit mask (bit 4g+i: position
+  // 4t+i of group g) and their composites rebuilt at the store, so no
+  // per-position composite is held across the scan.
+  // entry of position p = RUN*t + i of group g
+  auto entry_of = [&](const int32_t* blk, int g, int i, int64_t p) -> int64_t {
+    if constexpr (!POOL) return p;
+    const int32_t b = blk[kBlk * g + (RUN >= 8 ? i >> 3 : 0)];
+    return (b < 0) ? -1 : 8 * (int64_t)b + (p & 7);
+  };
   auto process = [&](const float* sc, const int32_t* blk, int64_t p0) {
-    const int64_t pb = p0 + (int64_t)tid * kQPer;
-    unsigned total;
-    if (fast) {
-      const int nv = (int)max((int64_t)0, min(vlim - pb, (int64_t)kQPer));
-      bool keep[kQPer];
-      unsigned cnt = 0;
+    unsigned cnt[kQGrp], pos[kQGrp];
+    unsigned keep = 0;  // bit RUN*g+i: position RUN*t+i of group g survives
+    // Pools with one group (runs of 16): the composites are built once,
+    // before the scan, and held (32 VGPRs, which that variant has to spare);
+    // otherwise they are rebuilt at the store.
+    constexpr bool kHold = POOL && kQGrp == 1;
+    unsigned long long comp[kHold ? kQPer : 1];
 #pragma unroll
-      for (int j = 0; j < kQPer; ++j) {
-        keep[j] = j < nv && __float_as_uint(sc[j]) - tlo <= tspan;
-        cnt += keep[j] ? 1u : 0u;
-      }
-      unsigned pos = m + block_incl_scan<NQ>(cnt, sh.wsum, &total) - cnt;
+    for (int g = 0; g < kQGrp; ++g) {
+      const int64_t pb = p0 + g * kGrpLen + RUN * tid;
+      unsigned kg = 0;
+      if (fast) {
+        const int nv = (int)max((int64_t)0, min(vlim - pb, (int64_t)RUN));
 #pragma unroll
-      for (int j = 0; j < kQPer; ++j) {
-        if (keep[j]) {  // a non-negative score: its key is its bits with the sign bit set
-          const unsigned long long comp = ((unsigned long long)(__float_as_uint(sc[j]) | 0x80000000u) << 32) |
-                                          (unsigned long long)(~(unsigned)(pb + j));
-          if (pos < (unsigned)kQCap) sh.cand[q_slot(pos)] = comp;
-          else gq[pos] = comp;
-          ++pos;
+        for (int i = 0; i < RUN; ++i)
+          kg |= (i < nv && __float_as_uint(sc[RUN * g + i]) - tlo <= tspan) ? (1u << i) : 0u;
+      } else {
+#pragma unroll
+        for (int i = 0; i < RUN; ++i) {
+          const int64_t e = entry_of(blk, g, i, pb + i);
+          const bool valid = pb + i < n_cand && e >= 0 && e < limit;
+          const unsigned key = score_key(sc[RUN * g + i]);
+          const bool kp = valid && key >= theta;
+          if constexpr (kHold) comp[i] = kp ? (((unsigned long long)key << 32) | (unsigned long long)(~(unsigned)e)) : 0ull;
+          kg |= kp ? (1u << i) : 0u;
         }
       }
-    } else {
-      unsigned long long comp[kQPer];
-      unsigned cnt = 0;
+      cnt[g] = __builtin_popcount(kg);
+      keep |= kg << (RUN * g);
+    }
+    place(cnt, pos);
+    if constexpr (kHold) {
 #pragma unroll
-      for (int j = 0; j < kQPer; ++j) {
-        const int64_t p = pb + j;
-        int64_t e = p;
-        if (cand_blocks) e = (blk[j >> 3] < 0) ? -1 : 8 * (int64_t)blk[j >> 3] + (p & 7);
-        const bool valid = p < n_cand && e >= 0 && e < limit;
-        const unsigned key = score_key(sc[j]);
-        const bool keep = valid && key >= theta;
-        comp[j] = keep ? (((unsigned long long)key << 32) | (unsigned long long)(~(unsigned)e)) : 0ull;
-        cnt += keep ? 1u : 0u;
-      }
-      unsigned pos = m + block_incl_scan<NQ>(cnt, sh.wsum, &total) - cnt;
+      for (int i = 0; i < kQPer; ++i)
+        if (comp[i]) put(pos[0]++, comp[i]);
+      return;
+    }
 #pragma unroll
-      for (int j = 0; j < kQPer; ++j) {
-        if (comp[j]) {
-          if (pos < (unsigned)kQCap) sh.cand[q_slot(pos)] = comp[j];
-          else gq[pos] = comp[j];
-          ++pos;
+    for (int g = 0; g < kQGrp; ++g) {
+      const int64_t pb = p0 + g * kGrpLen + RUN * tid;
+#pragma unroll
+      for (int i = 0; i < RUN; ++i) {
+        if (keep & (1u << (RUN * g + i))) {
+          // in the fast filter every survivor is a non-negative score of the
+          // plain range: key = bits with the sign bit set, entry = position
+          const unsigned key = fast ? (__float_as_uint(sc[RUN * g + i]) | 0x80000000u) : score_key(sc[RUN * g + i]);
+          const unsigned e = fast ? (unsigned)(pb + i) : (unsigned)entry_of(blk, g, i, pb + i);
+          put(pos[g]++, ((unsigned long long)key << 32) | (unsigned long long)(~e));
         }
       }
     }
-    m += total;
   };
   for (int64_t i = 0; i < n_full; i += 2) {
     if (i + 1 < n_full) load_full(scB, bkB, (i + 1) * kStep);
@@ -339,19 +408,23 @@ __global__ __launch_bounds__(NQ) void k_select_query(const float* __restrict__ s
     // positions past the end load the last score (clamped, so every load is
     // issued at once instead of one guarded round trip after another) and
     // are dropped by process()
-    const int64_t pb = p0 + (int64_t)tid * kQPer;
 #pragma unroll
-    for (int j = 0; j < kQPer; ++j) scA[j] = srow[min(pb + j, n_cand - 1)];
+    for (int g = 0; g < kQGrp; ++g) {
+      const int64_t pb = p0 + g * kGrpLen + RUN * tid;
 #pragma unroll
-    for (int j = 0; j < kQPer / 8; ++j)
-      bkA[j] = cand_blocks ? cand_blocks[(int64_t)q * n_blocks + min((pb >> 3) + j, (int64_t)n_blocks - 1)] : 0;
+      for (int i = 0; i < RUN; ++i) scA[RUN * g + i] = srow[min(pb + i, n_cand - 1)];
+#pragma unroll
+      for (int b = 0; b < kBlk; ++b)
+        bkA[kBlk * g + b] =
+            POOL ? cand_blocks[(int64_t)q * n_blocks + min((pb >> 3) + b, (int64_t)n_blocks - 1)] : 0;
+    }
     process(scA, bkA, p0);
   }
   __syncthreads();
 
   unsigned written = 0;
   if (m <= (unsigned)kQCap) {
-    // ---- survivors in LDS: thread t holds list elements 8t..8t+7
+    // ---- survivors in LDS: thread t holds list elements PER*t..PER*t+PER-1
     constexpr int PER = kQCap / NQ;
     unsigned long long v[PER];
 #pragma unroll
@@ -435,8 +508,23 @@ hipError_t launch_select(const float* scores, int Q, int64_t n_cand, int64_t n_e
                          unsigned* counts, unsigned long long* cand, int32_t* idx, float* top_scores, hipStream_t s) {
   if (Q <= 0) return hipSuccess;
   if (!select_is_chunked(Q, n_cand)) {
-    k_select_query<<<(unsigned)Q, NQ, 0, s>>>(scores, n_cand, n_entries, cand_blocks, n_blocks, n_valid, k, gmax,
-                                             sp.n_groups, cand, idx, top_scores);
+    // Small batches: 1,024 threads, pools in runs of 16 (composites held),
+    // plain ranges in runs of 4 (coalesced loads); large batches: 256
+    // threads in runs of 4.
+    const bool pool = cand_blocks != nullptr;
+    const dim3 g((unsigned)Q);
+    if (Q >= kQSmallBatch && pool)
+      k_select_query<256, 4, true><<<g, 256, 0, s>>>(scores, n_cand, n_entries, cand_blocks, n_blocks, n_valid, k, gmax,
+                                                     sp.n_groups, cand, idx, top_scores);
+    else if (Q >= kQSmallBatch)
+      k_select_query<256, 4, false><<<g, 256, 0, s>>>(scores, n_cand, n_entries, nullptr, n_blocks, n_valid, k, gmax,
+                                                      sp.n_groups, cand, idx, top_scores);
+    else if (pool)
+      k_select_query<1024, 16, true><<<g, 1024, 0, s>>>(scores, n_cand, n_entries, cand_blocks, n_blocks, n_valid, k,
+                                                        gmax, sp.n_groups, cand, idx, top_scores);
+    else
+      k_select_query<1024, 4, false><<<g, 1024, 0, s>>>(scores, n_cand, n_entries, nullptr, n_blocks, n_valid, k,
+                                                        gmax, sp.n_groups, cand, idx, top_scores);
     return hipGetLastError();
   }
   hipError_t e = launch_select_compact(scores, Q, n_cand, n_entries, cand_blocks, n_blocks, n_valid, k, sp, gmax,

@@ -377,6 +377,43 @@ def test_topk_many_queries_long_lists():
     _assert_topk_exact(s, 512, 30000, n_valid=nv, what="many queries")
 
 
+@pytest.mark.parametrize("n", [20000, 5003])
+def test_topk_large_batch(n):
+    """1,100 queries take the 256-thread per-query workgroup (smaller batches
+    the 1,024-thread one). n=20,000: four full passes of 4,096 positions and a
+    ragged one; n=5,003 (not a multiple of 4): every pass guarded. Rows mix
+    plain random scores, heavy ties, an all-equal row (every candidate
+    survives, more than the workgroup holds in LDS), -0/NaN rows, all-negative
+    rows (the general compaction test) and causal limits down to 0."""
+    rng = np.random.default_rng(n)
+    Q = 1100
+    s = rng.standard_normal((Q, n)).astype(np.float32)
+    s[1::50] = np.round(s[1::50] * 2)
+    s[2] = 2.5
+    s[3::50, ::7] = -0.0
+    s[4::50, :200] = np.nan
+    s[5::50] = -np.abs(s[5::50]) - np.float32(0.01)
+    nv = np.full(Q, n, np.int32)
+    nv[6::50] = rng.integers(0, n, len(nv[6::50]))
+    nv[7] = 0
+    nv[8] = 511
+    announce(f"topk large batch Q={Q} n={n}")
+    _assert_topk_exact(s, 512, n, n_valid=nv, what=f"large batch n{n}")
+
+
+def test_topk_large_batch_pool():
+    """The 256-thread workgroup on Reindex-style lists: 1,024 queries, pools of
+    2,048 blocks of 8 (16,384 candidates, four full passes) with absent
+    blocks and blocks past the cache end."""
+    rng = np.random.default_rng(12)
+    Q, nb, n_entries = 1024, 2048, 1 << 20
+    blocks = np.stack([np.sort(rng.choice(n_entries // 8 + 64, nb, replace=False)) for _ in range(Q)]).astype(np.int32)
+    blocks[::37, 100:110] = -1
+    s = rng.standard_normal((Q, 8 * nb)).astype(np.float32)
+    announce(f"topk large batch pool Q={Q} blocks={nb}")
+    _assert_topk_exact(s, 512, n_entries, cand_blocks=blocks, what="large batch pool")
+
+
 def test_topk_pool_and_causal():
     rng = np.random.default_rng(2)
     blocks = np.stack([np.sort(rng.choice(50000, 700, replace=False)) for _ in range(3)]).astype(np.int32)
