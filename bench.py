@@ -16,7 +16,8 @@ Phases (all on one stream):
      bracketed by two HIP events on the launch stream;
   4. the box's streaming bandwidth (torch row sums and copy over 1 GiB), the
      reference the scan kernel's bytes per second are also quoted against;
-  5. the CPU oracle on the host cores over a bounded sample (>= --cpu-seconds).
+  5. the CPU oracle on all host threads over a bounded sample (>= --cpu-seconds),
+     then one query per call on a single thread for half that time.
 
 Prints one JSON line. `python bench.py --pmc-summary DIR` instead summarises
 the counter CSVs of `rocprofv3 --pmc ... --output-format csv -d DIR` runs of
@@ -217,18 +218,10 @@ def recorded_traffic(workload_name):
     return None
 
 
-def cpu_baseline(wl, seconds):
-    """The oracle as it stands, timed over a bounded sample of the workload:
-    whole batches (or, when one batch is too long, strided query subsets) until
-    `seconds` of wall time have passed."""
+def _time_oracle(wl, view, per_call, seconds):
+    """Oracle decode calls on `per_call` queries each (strided subsets when
+    fewer than the batch) until `seconds` of wall time have passed."""
     import oracle
-    import synth
-    view = synth.compact_pool_view(wl) if (wl.cand_blocks is not None and not wl.extra.get("dense_rows", True)) \
-        else wl
-    threads = oracle.get_threads()
-    per_call = wl.Q
-    if wl.n_valid is not None and wl.Q > 2 * threads:   # prefill: strided subsets of `threads` queries
-        per_call = threads
     done, calls = 0, 0
     t0 = time.perf_counter()
     first = None
@@ -245,11 +238,47 @@ def cpu_baseline(wl, seconds):
         calls += 1
         dt = time.perf_counter() - t0
         if dt >= seconds or calls >= 100000:
-            break
+            return first, done, calls, dt
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, seconds):
+    """The oracle as it stands, timed over a bounded sample of the workload:
+    whole batches (or, when one batch is too long, strided query subsets) on
+    all host threads until `seconds` of wall time have passed; then one query
+    per call on a single thread for half that time."""
+    import oracle
+    import synth
+    view = synth.compact_pool_view(wl) if (wl.cand_blocks is not None and not wl.extra.get("dense_rows", True)) \
+        else wl
+    threads = oracle.get_threads()
+    per_call = wl.Q
+    if wl.n_valid is not None and wl.Q > 2 * threads:   # prefill: strided subsets of `threads` queries
+        per_call = threads
+    first, done, calls, dt = _time_oracle(wl, view, per_call, seconds)
     what = "the whole batch" if per_call == wl.Q else f"strided subsets of {per_call} queries"
-    return first, dict(value=round(done / dt, 3), unit="queries/s", cores=int(min(threads, per_call)), kind="oracle",
-                       sample=f"{calls} oracle decode call(s) on {what} of this workload ({done} queries, "
-                              f"{wl.n_cand} candidates each), fp64, {dt:.1f} s wall")
+    res = dict(value=round(done / dt, 3), unit="queries/s", cores=int(min(threads, per_call)), kind="oracle",
+               sample=f"{calls} oracle decode call(s) on {what} of this workload ({done} queries, "
+                      f"{wl.n_cand} candidates each), fp64, {dt:.1f} s wall",
+               cpu_model=_cpu_model(), host_threads=int(threads))
+    oracle.set_threads(1)
+    try:
+        _, done1, calls1, dt1 = _time_oracle(wl, view, 1, max(1.0, seconds / 2))
+    finally:
+        oracle.set_threads(threads)
+    res["one_thread"] = dict(value=round(done1 / dt1, 3), unit="queries/s", cores=1,
+                             sample=f"{calls1} oracle decode call(s) of one query each (strided), fp64, "
+                                    f"{dt1:.1f} s wall")
+    return first, res
 
 
 def parity_summary(wl, first, out_bf16, idx):

@@ -208,6 +208,7 @@ struct QSelShared {
   alignas(16) unsigned wsum[2 * (NQ / 64)];
   unsigned res[4];
   unsigned ext[2 * (NQ / 64)];
+  unsigned short glist[4 * NQ];  // sub-chunks that can hold survivors, ascending
   unsigned long long cand[q_cap<NQ>() + q_cap<NQ>() / 16];  // survivor i at q_slot(i)
 };
 
@@ -223,7 +224,7 @@ template <int NQ, int RUN, bool POOL>
 __global__ __launch_bounds__(NQ) __attribute__((amdgpu_waves_per_eu(NQ >= 1024 ? 1 : 4))) void k_select_query(const float* __restrict__ scores, int64_t n_cand,
                                                      int64_t n_entries, const int32_t* __restrict__ cand_blocks,
                                                      int n_blocks, const int32_t* __restrict__ n_valid, int k,
-                                                     const unsigned* __restrict__ gmax, int64_t n_groups,
+                                                     const unsigned* __restrict__ gmax, int64_t n_groups, int group,
                                                      unsigned long long* __restrict__ gcand, int32_t* __restrict__ idx,
                                                      float* __restrict__ top_scores) {
   constexpr int kQCap = q_cap<NQ>();
@@ -267,15 +268,23 @@ __global__ __launch_bounds__(NQ) __attribute__((amdgpu_waves_per_eu(NQ >= 1024 ?
   };
   float scA[kQPer], scB[kQPer];
   int32_t bkA[kQGrp * kBlk], bkB[kQGrp * kBlk];
-  if (n_full > 0) load_full(scA, bkA, 0);  // in flight during the threshold search
+  // Sub-chunk skipping (plain ranges, maxima held in registers): a sub-chunk
+  // whose maximum key lies below theta holds no survivor, so only the others
+  // are read. The maxima pass over NaN and give an all-invalid or all -inf
+  // sub-chunk key 0, so they bound every key above that of -inf; skipping is
+  // taken only with theta above the key of +0, where NaN and -inf cannot pass.
+  const bool can_skip = !POOL && gmax && n_groups >= k && n_groups <= 4 * NQ && group >= RUN &&
+                        (group & (group - 1)) == 0;
+  const bool pre = n_full > 0 && !can_skip;
+  if (pre) load_full(scA, bkA, 0);  // in flight during the threshold search
 
   // ---- theta = k-th largest sub-chunk maximum (1 = keep every valid candidate)
   unsigned theta = 1u;
+  unsigned g[4] = {0u, 0u, 0u, 0u};  // maxima of sub-chunks j*NQ + tid
   if (gmax && n_groups >= k) {
     const unsigned* gm = gmax + (int64_t)q * n_groups;
     unsigned t;
     if (n_groups <= 4 * NQ) {
-      unsigned g[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t i = (int64_t)j * NQ + tid;
@@ -344,7 +353,9 @@ __global__ __launch_bounds__(NQ) __attribute__((amdgpu_waves_per_eu(NQ >= 1024 ?
     const int32_t b = blk[kBlk * g + (RUN >= 8 ? i >> 3 : 0)];
     return (b < 0) ? -1 : 8 * (int64_t)b + (p & 7);
   };
-  auto process = [&](const float* sc, const int32_t* blk, int64_t p0) {
+  // run_pos(g): first position of this thread's run in group g (runs hold
+  // consecutive positions)
+  auto process_at = [&](const float* sc, const int32_t* blk, auto&& run_pos) {
     unsigned cnt[kQGrp], pos[kQGrp];
     unsigned keep = 0;  // bit RUN*g+i: position RUN*t+i of group g survives
     // Pools with one group (runs of 16): the composites are built once,
@@ -354,7 +365,7 @@ __global__ __launch_bounds__(NQ) __attribute__((amdgpu_waves_per_eu(NQ >= 1024 ?
     unsigned long long comp[kHold ? kQPer : 1];
 #pragma unroll
     for (int g = 0; g < kQGrp; ++g) {
-      const int64_t pb = p0 + g * kGrpLen + RUN * tid;
+      const int64_t pb = run_pos(g);
       unsigned kg = 0;
       if (fast) {
         const int nv = (int)max((int64_t)0, min(vlim - pb, (int64_t)RUN));
@@ -384,7 +395,7 @@ __global__ __launch_bounds__(NQ) __attribute__((amdgpu_waves_per_eu(NQ >= 1024 ?
     }
 #pragma unroll
     for (int g = 0; g < kQGrp; ++g) {
-      const int64_t pb = p0 + g * kGrpLen + RUN * tid;
+      const int64_t pb = run_pos(g);
 #pragma unroll
       for (int i = 0; i < RUN; ++i) {
         if (keep & (1u << (RUN * g + i))) {
@@ -397,28 +408,88 @@ __global__ __launch_bounds__(NQ) __attribute__((amdgpu_waves_per_eu(NQ >= 1024 ?
       }
     }
   };
-  for (int64_t i = 0; i < n_full; i += 2) {
-    if (i + 1 < n_full) load_full(scB, bkB, (i + 1) * kStep);
-    process(scA, bkA, i * kStep);
-    if (i + 1 >= n_full) break;
-    if (i + 2 < n_full) load_full(scA, bkA, (i + 2) * kStep);
-    process(scB, bkB, (i + 1) * kStep);
-  }
-  for (int64_t p0 = n_full * kStep; p0 < n_cand; p0 += kStep) {  // ragged or unaligned passes
-    // positions past the end load the last score (clamped, so every load is
-    // issued at once instead of one guarded round trip after another) and
-    // are dropped by process()
+  auto process = [&](const float* sc, const int32_t* blk, int64_t p0) {
+    process_at(sc, blk, [&](int g) { return p0 + g * kGrpLen + RUN * tid; });
+  };
+  if (can_skip && fast) {
+    // ordered list of the sub-chunks with maximum >= theta (sub-chunk
+    // j*NQ + t is this thread's g[j]; at most NQ per j, so 16-bit fields)
+    const int lg = __builtin_ctz((unsigned)group);
+    unsigned f[4];
 #pragma unroll
-    for (int g = 0; g < kQGrp; ++g) {
-      const int64_t pb = p0 + g * kGrpLen + RUN * tid;
+    for (int j = 0; j < 4; ++j) f[j] = ((int64_t)j * NQ + tid < n_groups && g[j] >= theta) ? 1u : 0u;
+    unsigned w0 = f[0] | (f[1] << 16), w1 = f[2] | (f[3] << 16);
+    const unsigned e0 = w0, e1 = w1;
+    unsigned t0, t1;
+    block_incl_scan2<NQ>(w0, w1, sh.wsum, &t0, &t1);
+    w0 -= e0;
+    w1 -= e1;
+    const unsigned T0 = t0 & 0xFFFFu, T1 = t0 >> 16, T2 = t1 & 0xFFFFu;
+    const unsigned at[4] = {w0 & 0xFFFFu, T0 + (w0 >> 16), T0 + T1 + (w1 & 0xFFFFu), T0 + T1 + T2 + (w1 >> 16)};
 #pragma unroll
-      for (int i = 0; i < RUN; ++i) scA[RUN * g + i] = srow[min(pb + i, n_cand - 1)];
+    for (int j = 0; j < 4; ++j)
+      if (f[j]) sh.glist[at[j]] = (unsigned short)(j * NQ + tid);
+    __syncthreads();
+    const int64_t V = (int64_t)(T0 + T1 + T2 + (t1 >> 16)) << lg;  // positions of the listed sub-chunks
+    const bool vec = (n_cand & 3) == 0;
+    // virtual position v -> position: listed sub-chunk v >> lg, offset
+    // v & (group-1); a run never crosses a sub-chunk (group >= RUN, both
+    // powers of two)
+    auto load_v = [&](float* sc, int64_t* pbs, int64_t v0) {
 #pragma unroll
-      for (int b = 0; b < kBlk; ++b)
-        bkA[kBlk * g + b] =
-            POOL ? cand_blocks[(int64_t)q * n_blocks + min((pb >> 3) + b, (int64_t)n_blocks - 1)] : 0;
+      for (int gg = 0; gg < kQGrp; ++gg) {
+        const int64_t v = v0 + gg * kGrpLen + RUN * tid;
+        int64_t pb = n_cand;  // past the list: dropped by the filter
+        if (v < V) pb = ((int64_t)sh.glist[v >> lg] << lg) + (v & (group - 1));
+        pbs[gg] = pb;
+        if (vec && pb + RUN <= n_cand) {
+#pragma unroll
+          for (int jj = 0; jj < RUN; jj += 4) {
+            const v4f x = *(const v4f*)(srow + pb + jj);
+            sc[RUN * gg + jj] = x[0]; sc[RUN * gg + jj + 1] = x[1];
+            sc[RUN * gg + jj + 2] = x[2]; sc[RUN * gg + jj + 3] = x[3];
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < RUN; ++i) sc[RUN * gg + i] = srow[min(pb + i, n_cand - 1)];
+        }
+      }
+    };
+    int64_t pA[kQGrp], pB[kQGrp];
+    const int64_t n_pass = (V + kStep - 1) / kStep;
+    if (n_pass > 0) load_v(scA, pA, 0);
+    for (int64_t i = 0; i < n_pass; i += 2) {
+      if (i + 1 < n_pass) load_v(scB, pB, (i + 1) * kStep);
+      process_at(scA, bkA, [&](int gg) { return pA[gg]; });
+      if (i + 1 >= n_pass) break;
+      if (i + 2 < n_pass) load_v(scA, pA, (i + 2) * kStep);
+      process_at(scB, bkB, [&](int gg) { return pB[gg]; });
     }
-    process(scA, bkA, p0);
+  } else {
+    if (n_full > 0 && !pre) load_full(scA, bkA, 0);
+    for (int64_t i = 0; i < n_full; i += 2) {
+      if (i + 1 < n_full) load_full(scB, bkB, (i + 1) * kStep);
+      process(scA, bkA, i * kStep);
+      if (i + 1 >= n_full) break;
+      if (i + 2 < n_full) load_full(scA, bkA, (i + 2) * kStep);
+      process(scB, bkB, (i + 1) * kStep);
+    }
+    for (int64_t p0 = n_full * kStep; p0 < n_cand; p0 += kStep) {  // ragged or unaligned passes
+      // positions past the end load the last score (clamped, so every load is
+      // issued at once instead of one guarded round trip after another) and
+      // are dropped by process()
+  #pragma unroll
+      for (int g = 0; g < kQGrp; ++g) {
+        const int64_t pb = p0 + g * kGrpLen + RUN * tid;
+  #pragma unroll
+        for (int i = 0; i < RUN; ++i) scA[RUN * g + i] = srow[min(pb + i, n_cand - 1)];
+  #pragma unroll
+        for (int b = 0; b < kBlk; ++b)
+          bkA[kBlk * g + b] =
+              POOL ? cand_blocks[(int64_t)q * n_blocks + min((pb >> 3) + b, (int64_t)n_blocks - 1)] : 0;
+      }
+      process(scA, bkA, p0);
+    }
   }
   __syncthreads();
 
@@ -515,16 +586,16 @@ hipError_t launch_select(const float* scores, int Q, int64_t n_cand, int64_t n_e
     const dim3 g((unsigned)Q);
     if (Q >= kQSmallBatch && pool)
       k_select_query<256, 4, true><<<g, 256, 0, s>>>(scores, n_cand, n_entries, cand_blocks, n_blocks, n_valid, k, gmax,
-                                                     sp.n_groups, cand, idx, top_scores);
+                                                     sp.n_groups, sp.group, cand, idx, top_scores);
     else if (Q >= kQSmallBatch)
       k_select_query<256, 4, false><<<g, 256, 0, s>>>(scores, n_cand, n_entries, nullptr, n_blocks, n_valid, k, gmax,
-                                                      sp.n_groups, cand, idx, top_scores);
+                                                      sp.n_groups, sp.group, cand, idx, top_scores);
     else if (pool)
       k_select_query<1024, 16, true><<<g, 1024, 0, s>>>(scores, n_cand, n_entries, cand_blocks, n_blocks, n_valid, k,
-                                                        gmax, sp.n_groups, cand, idx, top_scores);
+                                                        gmax, sp.n_groups, sp.group, cand, idx, top_scores);
     else
       k_select_query<1024, 4, false><<<g, 1024, 0, s>>>(scores, n_cand, n_entries, nullptr, n_blocks, n_valid, k,
-                                                        gmax, sp.n_groups, cand, idx, top_scores);
+                                                        gmax, sp.n_groups, sp.group, cand, idx, top_scores);
     return hipGetLastError();
   }
   hipError_t e = launch_select_compact(scores, Q, n_cand, n_entries, cand_blocks, n_blocks, n_valid, k, sp, gmax,

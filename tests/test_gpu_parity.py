@@ -401,6 +401,28 @@ def test_topk_large_batch(n):
     _assert_topk_exact(s, 512, n, n_valid=nv, what=f"large batch n{n}")
 
 
+@pytest.mark.parametrize("Q,n", [(1024, 16380), (1024, 16381), (64, 30001)])
+def test_topk_subchunk_skipping(Q, n):
+    """With the threshold above zero, the per-query kernel reads only the
+    sub-chunks (16 scores here) whose maximum reaches it. 1,024 queries take
+    the 256-thread workgroup, 64 the 1,024-thread one; n = 16,380 leaves a
+    partial last sub-chunk on aligned rows, 16,381 and 30,001 unaligned rows.
+    Rows mix random scores, the top scores packed into the last sub-chunk,
+    heavy ties, negative rows (no skipping), NaN and +inf, and causal limits."""
+    rng = np.random.default_rng(Q + n)
+    s = rng.standard_normal((Q, n)).astype(np.float32)
+    s[0, -10:] = 50 + rng.standard_normal(10).astype(np.float32)
+    s[1::40] = np.round(s[1::40] * 2)
+    s[2::40] = -np.abs(s[2::40]) - np.float32(0.01)
+    s[3::40, rng.choice(n, 40, replace=False)] = np.inf
+    s[4::40, ::5] = np.nan
+    nv = np.full(Q, n, np.int32)
+    nv[5::40] = rng.integers(0, n, len(nv[5::40]))
+    nv[6] = n - 5
+    announce(f"topk sub-chunk skipping Q={Q} n={n}")
+    _assert_topk_exact(s, 512, n, n_valid=nv, what=f"skipping Q{Q} n{n}")
+
+
 def test_topk_large_batch_pool():
     """The 256-thread workgroup on Reindex-style lists: 1,024 queries, pools of
     2,048 blocks of 8 (16,384 candidates, four full passes) with absent
