@@ -244,10 +244,11 @@ __global__ __launch_bounds__(NQ) __attribute__((amdgpu_waves_per_eu(NQ >= 1024 ?
   // of each group (with RUN = 4 every load instruction of the workgroup
   // reads one contiguous NQ*16-byte span). Survivors keep position order:
   // group g's go after those of the groups before it, within a group in
-  // thread order. Full passes (rows
-  // 16-byte aligned) load with aligned vectors and no per-thread
-  // conditions, the next pass's scores in flight while this one is
-  // compacted; a ragged last pass is guarded.
+  // thread order. Full passes (rows 16-byte aligned) load with aligned
+  // vectors and no per-thread conditions, the next pass's scores in flight
+  // while this one is compacted; a ragged last pass is guarded. (These
+  // "groups" are the pass's thread layout; the "sub-chunks" below are the
+  // ranges whose maxima the scan wrote.)
   constexpr int64_t kGrpLen = (int64_t)NQ * RUN;
   constexpr int kBlk = (RUN + 7) / 8;  // pool blocks a run touches
   constexpr int64_t kStep = kGrpLen * kQGrp;
