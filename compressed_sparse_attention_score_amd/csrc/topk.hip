@@ -52,6 +52,13 @@ struct SelShared {
 // than 2^-7 of its value and adds a few percent of survivors, and saves the
 // passes over the remaining low bits.
 constexpr int kThetaPasses = 2;
+// The chunk compaction takes one pass (8 bits below the shared ones): its
+// survivors only pass through LDS and a final selection, and one pass fewer
+// shortened the batch-16 x 65,536 decode step by about 0.6 us. The per-query
+// kernel keeps two: it reads only the sub-chunks whose maximum reaches theta,
+// and the coarser bound let enough more through to cost the 4,096-query
+// prefill selection over 100 us.
+constexpr int kCompactThetaPasses = 1;
 
 // Threshold + compaction: grid (n_chunks, Q). Writes cand[q][c0 .. c0+cnt) in
 // position order and counts[q][chunk] = cnt.
@@ -118,7 +125,8 @@ __global__ __launch_bounds__(NT) void k_select_compact(const float* __restrict__
       int top;
       unsigned prefix;
       shared_top_bits<NT, unsigned, 16>(g, sh.sel.ext, &top, &prefix);
-      t = radix_kth_regs<NT, unsigned, 16>(g, (unsigned)k, sh.sel.hist, sh.sel.res, kThetaPasses, top, prefix);
+      t = radix_kth_regs<NT, unsigned, 16>(g, (unsigned)k, sh.sel.hist, sh.sel.res, kCompactThetaPasses, top,
+                                            prefix);
     } else {
       t = radix_kth_stream<NT, unsigned>(gq, n_groups, (unsigned)k, sh.sel.hist, sh.sel.res, kThetaPasses);
     }
