@@ -674,8 +674,12 @@ hipError_t launch_attn(const AttnLaunch& L, const AttnPlan& plan, float* partial
       k_attn_combine<4><<<grid, 256, 0, s>>>(partial, plan.n_splits, L.rope, L.out, L.lse);
     else if (plan.n_splits <= 8)
       k_attn_combine<8><<<grid, 256, 0, s>>>(partial, plan.n_splits, L.rope, L.out, L.lse);
+    else if (plan.n_splits <= 12)  // 640 slots over 16 queries: 10 splits
+      k_attn_combine<12><<<grid, 256, 0, s>>>(partial, plan.n_splits, L.rope, L.out, L.lse);
     else if (plan.n_splits <= 16)
       k_attn_combine<16><<<grid, 256, 0, s>>>(partial, plan.n_splits, L.rope, L.out, L.lse);
+    else if (plan.n_splits <= 24)  // 640 slots over 4 or fewer queries: 20 splits
+      k_attn_combine<24><<<grid, 256, 0, s>>>(partial, plan.n_splits, L.rope, L.out, L.lse);
     else
       k_attn_combine<kMaxSplits><<<grid, 256, 0, s>>>(partial, plan.n_splits, L.rope, L.out, L.lse);
   }
