@@ -35,6 +35,8 @@ def _bind(L):
         getattr(L, n).restype = dbl
         getattr(L, n).argtypes = [ctypes.c_uint]
     L.orc_main_entry_bytes.restype = i32
+    L.orc_f64_to_bf16.restype = ctypes.c_uint16
+    L.orc_f64_to_bf16.argtypes = [dbl]
     L.orc_index_entry_bytes.restype = i32
     L.orc_dequant_main.argtypes = [vp, i64, vp, vp]
     L.orc_dequant_index.argtypes = [vp, vp, i64, vp, vp]
@@ -96,6 +98,11 @@ def e4m3(b: int, L=None) -> float:
 
 def e8m0(b: int, L=None) -> float:
     return (L or lib()).orc_e8m0(b)
+
+
+def f64_to_bf16(v: float, L=None) -> int:
+    """bf16 bit pattern of the fp64 value v, one round-to-nearest-even step."""
+    return int((L or lib()).orc_f64_to_bf16(float(v)))
 
 
 def dequant_main(entries: np.ndarray, L=None):

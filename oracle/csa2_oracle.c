@@ -120,14 +120,38 @@ static void index_row_f64(const uint8_t* codes, const uint8_t* scales, double* o
 ORC_API int orc_main_entry_bytes(void) { return 512 / 2 + 512 / 16; }  /* 288 */
 ORC_API int orc_index_entry_bytes(void) { return 128 / 2 + 128 / 32; } /* 68 */
 
-static uint16_t f64_to_bf16(double v) {
-  float f = (float)v; /* RNE */
-  uint32_t u;
-  memcpy(&u, &f, 4);
-  if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0x007FFFFFu) ? 0x40u : 0u));
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+/* fp64 -> bf16 (1 sign, 8 exponent bits with bias 127, 7 mantissa bits) in
+ * ONE round-to-nearest-even step, on the integer fields of the fp64 value, so
+ * that no intermediate fp32 rounding can move a value that lies just off a
+ * bf16 midpoint onto it. bf16 subnormals (|v| < 2^-126) keep 7 fraction bits
+ * of 2^-126; overflow gives +-inf; NaN stays a (quiet) NaN. */
+ORC_API uint16_t orc_f64_to_bf16(double v) {
+  uint64_t u;
+  memcpy(&u, &v, 8);
+  const uint16_t sign = (uint16_t)((u >> 48) & 0x8000u);
+  const int e = (int)((u >> 52) & 0x7FF);
+  const uint64_t frac = u & ((1ull << 52) - 1);
+  if (e == 0x7FF) return (uint16_t)(sign | (frac ? 0x7FC0u : 0x7F80u));
+  if (e == 0) return sign; /* fp64 zero or subnormal: below half the least bf16 subnormal */
+  /* |v| = full * 2^(e - 1075), full = 2^52 + frac (53 bits). The bf16
+   * result counts units of 2^(eb - 134) for a normal result (eb = e - 896,
+   * the bf16 biased exponent) and of 2^-133 for a subnormal one; shift is
+   * the number of low bits of full below that unit. */
+  const uint64_t full = (1ull << 52) | frac;
+  const int eb = e - 1023 + 127;
+  const int shift = (eb >= 1) ? 45 : 45 + (1 - eb);
+  if (shift > 54) return sign; /* |v| < 2^-134: below half the least subnormal */
+  uint64_t keep = full >> shift;
+  const uint64_t rem = full & ((1ull << shift) - 1), half = 1ull << (shift - 1);
+  if (rem > half || (rem == half && (keep & 1))) ++keep;
+  /* normal: keep = 2^7 + mantissa (a carry to 2^8 moves into the exponent);
+   * subnormal: keep is the bf16 bit pattern itself (2^7 = least normal) */
+  uint32_t bits = (eb >= 1) ? ((uint32_t)eb << 7) + (uint32_t)(keep - 128) : (uint32_t)keep;
+  if (bits >= 0x7F80u) bits = 0x7F80u;
+  return (uint16_t)(sign | bits);
 }
+
+static uint16_t f64_to_bf16(double v) { return orc_f64_to_bf16(v); }
 
 static double bf16_to_f64(uint16_t h) {
   uint32_t u = (uint32_t)h << 16;

@@ -157,6 +157,72 @@ def check_dequant(L, seed=3):
         assert np.array_equal(f[~nan].view(np.uint32), ref32[~nan].view(np.uint32))
 
 
+def ref_bf16_rne(v: float) -> int:
+    """bf16 bit pattern nearest to the fp64 value v, ties to the even
+    mantissa, by exact rational arithmetic (fractions.Fraction): the value is
+    divided by the bf16 unit of its binade (2^(E-7), or 2^-133 below 2^-126),
+    the quotient rounded to an integer, and the result encoded. Magnitudes
+    from the largest finite bf16 plus half a unit up become infinity."""
+    from fractions import Fraction
+    if math.isnan(v):
+        return 0x7FC0
+    sign = 0x8000 if math.copysign(1.0, v) < 0 else 0
+    if math.isinf(v):
+        return sign | 0x7F80
+    a = abs(Fraction(v))
+    if a == 0:
+        return sign
+    E = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** E > a:
+        E -= 1
+    assert Fraction(2) ** E <= a < Fraction(2) ** (E + 1)
+    sub = E < -126
+    unit = Fraction(2) ** (-133 if sub else E - 7)
+    n = a / unit
+    r = n.numerator // n.denominator
+    rem = n - r
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and r % 2 == 1):
+        r += 1
+    if sub:
+        return sign | r  # r = 128 is the least normal, 0x0080
+    if r == 256:
+        E, r = E + 1, 128
+    if E > 127:
+        return sign | 0x7F80
+    return sign | ((E + 127) << 7) | (r - 128)
+
+
+def check_bf16_rounding(L, seed=2):
+    """The oracle's fp64 -> bf16 conversion is one round-to-nearest-even step.
+    1 + 2^-8 + 2^-30 lies just above the midpoint of 1 and 1 + 2^-7 and must
+    give 1 + 2^-7 (rounding through fp32 first lands on the midpoint and then
+    on 1.0). Random values just off bf16 midpoints (by 2^-30 to 2^-50 of
+    their size), exact midpoints of both mantissa parities, the subnormal
+    range, the overflow boundary, zeros of both signs, infinities and NaN are
+    checked against the rational reference above."""
+    assert oracle.f64_to_bf16(1 + 2.0 ** -8 + 2.0 ** -30, L) == 0x3F81
+    assert oracle.f64_to_bf16(1 + 2.0 ** -8, L) == 0x3F80          # tie, even mantissa 0
+    assert oracle.f64_to_bf16(1 + 3 * 2.0 ** -8, L) == 0x3F82      # tie, odd mantissa 1 rounds up
+    assert oracle.f64_to_bf16(-(1 + 2.0 ** -8 + 2.0 ** -30), L) == 0xBF81
+    rng = np.random.default_rng(seed)
+    vals = [0.0, -0.0, math.inf, -math.inf, 2.0 ** -133, 2.0 ** -134, 3 * 2.0 ** -135, 2.0 ** -135,
+            2.0 ** -126 - 2.0 ** -134, 2.0 ** -126 - 2.0 ** -135, 5e-324, -5e-324,
+            (2 - 2.0 ** -7) * 2.0 ** 127, (2 - 2.0 ** -8) * 2.0 ** 127, (2 - 2.0 ** -8 - 2.0 ** -40) * 2.0 ** 127,
+            2.0 ** 128, 1e300, -1e300]
+    for _ in range(3000):
+        e = int(rng.integers(-140, 128))
+        m = int(rng.integers(0, 256))
+        mid = (1 + (2 * m + 1) / 256.0) * 2.0 ** e  # a bf16 midpoint (exact in fp64)
+        off = 2.0 ** -float(rng.integers(30, 51))
+        vals += [mid, mid * (1 + off), mid * (1 - off), -mid * (1 + off)]
+        vals.append(float(rng.standard_normal()) * 2.0 ** float(rng.integers(-135, 128)))
+    for v in vals:
+        got, want = oracle.f64_to_bf16(v, L), ref_bf16_rne(v)
+        assert got == want, (v.hex(), hex(got), hex(want))
+    got_nan = oracle.f64_to_bf16(math.nan, L)
+    assert (got_nan & 0x7F80) == 0x7F80 and (got_nan & 0x7F) != 0
+
+
 # ---------------------------------------------------------------- indexer ---
 
 def _ref_scores(wl, queries=None):
@@ -303,6 +369,28 @@ def _dense_ref(q_bf16, kv_f64, scale):
     return o[:, 0, :].numpy(), lse.numpy()
 
 
+def assert_nearest_bf16(bits: np.ndarray, x: np.ndarray, rel_slack: float = 1e-12) -> None:
+    """Each bf16 value is a nearest bf16 to the fp64 reference x: no farther
+    from x than the bf16 values one unit below and above it (same sign), up to
+    rel_slack of |x| for the reference's own fp64 rounding."""
+    b = np.asarray(bits, np.uint16).reshape(-1).astype(np.int64)
+    xv = np.asarray(x, np.float64).reshape(-1)
+    mag = b & 0x7FFF
+    neg = (b & 0x8000) != 0
+    nonzero = mag != 0
+    assert np.all(~nonzero | (neg == (xv < 0))), "bf16 sign differs from the reference"
+
+    def val(m):
+        return bf16_to_f64(m.astype(np.uint16))
+
+    ax = np.abs(xv)
+    d0 = np.abs(ax - val(mag))
+    dn = np.abs(ax - val(np.maximum(mag - 1, 0)))
+    dp = np.abs(ax - val(np.minimum(mag + 1, 0x7F7F)))
+    slack = rel_slack * ax + 1e-300
+    assert np.all(d0 <= np.minimum(dn, dp) + slack), "a bf16 output is not a nearest bf16 of the reference"
+
+
 def check_attention(L, seed=13):
     n = 200
     wl = synth.full_decode(2, n, seed)
@@ -315,6 +403,7 @@ def check_attention(L, seed=13):
         assert np.allclose(of[i], o_ref, rtol=1e-6, atol=1e-7), np.abs(of[i] - o_ref).max()
         assert np.allclose(lse[i], lse_ref, rtol=1e-6)
         assert np.allclose(bf16_to_f64(ob[i]), o_ref, rtol=8e-3, atol=1e-6)
+        assert_nearest_bf16(ob[i], o_ref)
     assert np.allclose(probs.sum(axis=-1), 1.0, atol=1e-12)
     # permutation invariance of the selected list
     perm = np.random.default_rng(seed).permutation(n)
@@ -635,6 +724,6 @@ def check_gather(L, seed=37):
                               y.view(np.uint32) if y.dtype == np.float32 else y)
 
 
-ALL_CHECKS = [check_format_tables, check_layout, check_dequant, check_index_scores, check_candidate_sets,
+ALL_CHECKS = [check_format_tables, check_layout, check_bf16_rounding, check_dequant, check_index_scores, check_candidate_sets,
               check_topk, check_attention, check_decode_composition, check_quantize, check_window_options,
               check_pool, check_pooling, check_gather]

@@ -62,6 +62,9 @@ MUTANTS = [
     ("gather_wrong_query", "main_cache + (size_t)((int64_t)q * cache_q_stride + e) * 288, 288);",
      "main_cache + (size_t)((int64_t)0 * cache_q_stride + e) * 288, 288);"),
     ("gather_dense_id", "dense_idx[(size_t)q * k + j] = ok ? j : -1;", "dense_idx[(size_t)q * k + j] = ok ? (int)e : -1;"),
+    ("bf16_through_f32", "  uint64_t u;\n  memcpy(&u, &v, 8);", "  uint64_t u;\n  v = (double)(float)v;\n  memcpy(&u, &v, 8);"),
+    ("bf16_ties_away", "if (rem > half || (rem == half && (keep & 1))) ++keep;", "if (rem >= half) ++keep;"),
+    ("bf16_truncate", "if (rem > half || (rem == half && (keep & 1))) ++keep;", ""),
     ("quant_mx_zero_block", "if (amax > 0.0) {\n        e = -127;", "if (amax >= 0.0) {\n        e = -127;"),
 ]
 
