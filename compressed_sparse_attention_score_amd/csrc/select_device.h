@@ -195,8 +195,8 @@ __device__ __forceinline__ T radix_kth_stream(const T* src, int64_t n, unsigned 
 // the largest, so all agree above the highest bit where those two differ;
 // 64-bit composites are ranged by their score keys (the top 32 bits), below
 // which they may differ anywhere. *top gets that bit (the width when there are
-// no values or they differ in the top bit) and *prefix the shared bits above
-// it. ext: 2*(NTH/64) words of LDS. One barrier.
+// no values or they differ in the top bit, and at least 1) and *prefix the
+// shared bits above it. ext: 2*(NTH/64) words of LDS. One barrier.
 template <int NTH, typename T, int REG>
 __device__ __forceinline__ void shared_top_bits(const T (&v)[REG], unsigned* ext, int* top, T* prefix) {
   constexpr int W = (int)(sizeof(T) * 8), S = W - 32;
@@ -226,7 +226,12 @@ __device__ __forceinline__ void shared_top_bits(const T (&v)[REG], unsigned* ext
     kmin = min(kmin, ext[2 * w + 1]);
   }
   const unsigned diff = kmax ^ kmin;
-  const int t = (kmax == 0u || (diff >> 31)) ? W : S + (diff ? 32 - __clz((int)diff) : 0);
+  int t = (kmax == 0u || (diff >> 31)) ? W : S + (diff ? 32 - __clz((int)diff) : 0);
+  // All values equal (32-bit values: t would be 0): start one bit up, so that
+  // radix_kth still runs one pass, whose total tells whether k values exist
+  // at all (with none run it would return the common value even when fewer
+  // than k are present, e.g. a causal limit inside the first sub-chunk).
+  if (t < 1) t = 1;
   *top = t;
   *prefix = (t >= W) ? (T)0 : ((((T)kmax) << S) >> t) << t;
 }

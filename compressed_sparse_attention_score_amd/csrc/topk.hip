@@ -12,10 +12,11 @@
 //     candidate list (>= 2k sub-chunks when the list is long enough).
 //  2. The k-th largest of those sub-chunk maxima is a lower bound on the
 //     k-th largest score: k distinct sub-chunks each hold an element >= it.
-//     theta is that key with its low 16 bits cleared (a lower bound still,
-//     found by two radix passes). Each compaction workgroup finds theta and
-//     writes its chunk's composites with key >= theta, in position order
-//     (block prefix sum), to a fixed region of the candidate list.
+//     theta is that key with its low bits cleared (a lower bound still):
+//     radix passes fix the 8 (compaction) or 16 (per-query kernel) bits
+//     below those every maximum shares. Each compaction workgroup finds
+//     theta and writes its chunk's composites with key >= theta, in position
+//     order (block prefix sum), to a fixed region of the candidate list.
 //  3. One workgroup per query gathers the regions in chunk order, finds the
 //     k-th largest composite T by radix select and writes every candidate
 //     >= T in list order, which is ascending entry id.

@@ -76,16 +76,50 @@ def gpu_decode(db):
     return to_np(out).view(np.uint16), to_np(lse), to_np(idx)
 
 
-def check_scores(gpu: np.ndarray, ref: np.ndarray, dots: np.ndarray, w: np.ndarray, what=""):
-    """dots [Q][32][n] from the oracle; w [Q][32]."""
+FP32_U = 2.0 ** -24   # unit roundoff of fp32
+
+
+def check_scores(gpu: np.ndarray, ref: np.ndarray, dots: np.ndarray, w: np.ndarray, what="", block_abs=None):
+    """dots [Q][32][n] from the oracle; w [Q][32]. block_abs [Q][32][n]
+    (optional) = sum over the four 32-channel blocks of |block dot|: when block
+    scales lie far apart the four block dots no longer sum exactly in fp32,
+    and each head may be off by the fp32 summation bound gamma_4 = 4u of that
+    sum (ReLU is 1-Lipschitz, so the score by sum_h |w_h| times it)."""
     inv_ref = np.isneginf(ref)
     assert np.array_equal(np.isneginf(gpu), inv_ref), f"{what}: invalid-candidate pattern differs"
-    s_abs = np.einsum("qh,qhn->qn", np.abs(w.astype(np.float64)), np.maximum(dots, 0.0))
+    wa = np.abs(w.astype(np.float64))
+    s_abs = np.einsum("qh,qhn->qn", wa, np.maximum(dots, 0.0))
     with np.errstate(invalid="ignore"):
         err = np.abs(gpu.astype(np.float64) - ref.astype(np.float64))
     bound = SCORE_RTOL * s_abs + 1e-30
+    if block_abs is not None:
+        bound = bound + 4 * FP32_U * np.einsum("qh,qhn->qn", wa, block_abs)
     bad = (err > bound) & ~inv_ref
     assert not bad.any(), f"{what}: {bad.sum()} scores off, worst {np.max(err[~inv_ref] / bound[~inv_ref]):.3g}x bound"
+
+
+E2M1_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def mxfp4_values(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """[..., 64] E2M1 code bytes (channel 2j low nibble) and [..., 4] E8M0
+    scales -> [..., 128] fp64 values (tolerance helper, not a reference)."""
+    nib = np.stack([codes & 15, codes >> 4], axis=-1).reshape(*codes.shape[:-1], 128)
+    v = E2M1_MAG[nib & 7] * np.where(nib & 8, -1.0, 1.0)
+    return v * np.repeat(np.ldexp(1.0, scales.astype(np.int64) - 127), 32, axis=-1)
+
+
+def block_abs_dots(wl) -> np.ndarray:
+    """[Q][32][n_cand] sum over the 32-channel blocks of |q_h . k| of each
+    block (independent caches, plain ranges)."""
+    assert wl.cand_blocks is None and wl.cache_q_stride == wl.n_entries
+    out = np.empty((wl.Q, 32, wl.n_entries))
+    for i in range(wl.Q):
+        qv = mxfp4_values(wl.iq_codes[i], wl.iq_scales[i]).reshape(32, 4, 32)
+        rows = slice(i * wl.n_entries, (i + 1) * wl.n_entries)
+        kv = mxfp4_values(wl.key_codes[rows], wl.key_scales[rows]).reshape(-1, 4, 32)
+        out[i] = np.abs(np.einsum("hbc,nbc->hnb", qv, kv)).sum(axis=-1)
+    return out
 
 
 def valid_entries(wl, qi):
@@ -155,5 +189,5 @@ def check_lse(gpu: np.ndarray, ref: np.ndarray, what=""):
     assert np.allclose(gpu[~inf_r], ref[~inf_r], rtol=1e-4, atol=1e-3), f"{what}: lse"
 
 
-__all__ = ["announce", "to_device", "gpu_scores", "gpu_topk", "gpu_attn", "gpu_decode", "check_scores",
+__all__ = ["block_abs_dots", "mxfp4_values", "announce", "to_device", "gpu_scores", "gpu_topk", "gpu_attn", "gpu_decode", "check_scores",
            "check_topk_band", "QueryView", "check_attn", "check_lse", "oracle", "bf16_np_to_f64", "valid_entries"]

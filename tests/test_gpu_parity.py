@@ -8,8 +8,8 @@ import pytest
 import torch
 
 import synth
-from gpu_util import (QueryView, announce, bf16_np_to_f64, check_attn, check_lse, check_scores, check_topk_band, gpu_attn,
-                      gpu_decode, gpu_scores, gpu_topk, oracle, to_device)
+from gpu_util import (QueryView, announce, bf16_np_to_f64, block_abs_dots, check_attn, check_lse, check_scores,
+                      check_topk_band, gpu_attn, gpu_decode, gpu_scores, gpu_topk, oracle, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -294,6 +294,24 @@ def test_index_score_prefill_query_tiles(T, n, t0):
     check_scores(got, ref, dots, wl.w, f"prefill tiles T={T}")
 
 
+def test_index_score_wide_block_scales():
+    """E8M0 block scales far apart: key blocks at exponents -60..60, query
+    blocks at -40..40 (any E8M0 byte is a valid scale per 32 channels), codes
+    of both signs. The matrix core applies each block's two scales and sums
+    the four block dots in fp32, where the oracle's dot is exact up to fp64
+    rounding, so the score bound adds that sum's fp32 error bound; top-k over
+    the GPU's scores must then match the oracle's exactly."""
+    wl = synth.full_decode(3, 3000, seed=77)
+    rng = np.random.default_rng(77)
+    wl.key_scales = (127 + rng.integers(-60, 61, wl.key_scales.shape)).astype(np.uint8)
+    wl.iq_scales = (127 + rng.integers(-40, 41, wl.iq_scales.shape)).astype(np.uint8)
+    ref, dots = oracle.index_score(wl, want_dots=True)
+    got = gpu_scores(to_device(wl))
+    assert np.all(np.isfinite(got))
+    check_scores(got, ref, dots, wl.w, "wide block scales", block_abs=block_abs_dots(wl))
+    _assert_topk_exact(got, 512, wl.n_entries, what="wide block scales")
+
+
 # ------------------------------------------------------------------- top-k
 
 def _assert_topk_exact(scores, k, n_entries, cand_blocks=None, n_valid=None, what=""):
@@ -444,6 +462,44 @@ def test_topk_pool_and_causal():
     s2 = rng.standard_normal((5, 9000)).astype(np.float32)
     nv = np.array([0, 1, 511, 512, 8999], np.int32)
     _assert_topk_exact(s2, 512, 9000, n_valid=nv, what="causal")
+
+
+@pytest.mark.parametrize("Q,n", [(14, 65536), (64, 65536), (6, 1 << 20)])
+def test_topk_valid_entries_inside_first_subchunk(Q, n):
+    """Causal limits small enough that every valid candidate lies in the first
+    one or two sub-chunks of a list with more than k sub-chunks: the other
+    sub-chunk maxima are empty, fewer than k are non-zero, and they may all be
+    one value. Every valid candidate must then be selected. 14 x 65,536 and
+    6 x 2^20 take the chunk-parallel selection, 64 x 65,536 the per-query
+    kernel. Limits: 0, 1, 2, 17, 40, around a sub-chunk (64 or 512 entries
+    here), 511..513; some rows hold one score repeated, so that two sub-chunk
+    maxima are equal."""
+    rng = np.random.default_rng(Q + n)
+    s = rng.standard_normal((Q, n)).astype(np.float32)
+    lims = [2, 17, 40, 63, 64, 65, 100, 511, 512, 513, 0, 1, 511, 1023]
+    nv = np.array([lims[i % len(lims)] for i in range(Q)], np.int32)
+    s[1, :] = 1.5
+    if Q > 4:
+        s[4::7, :] = -2.0
+    announce(f"topk first sub-chunk Q={Q} n={n}")
+    _assert_topk_exact(s, 512, n, n_valid=nv, what=f"first sub-chunk Q{Q} n{n}")
+
+
+@pytest.mark.parametrize("Q,n", [(2, 1 << 20), (64, 1 << 19)])
+def test_build_pool_few_valid_blocks(Q, n):
+    """Pools asked for 2,048 blocks where the causal limit leaves only a few
+    blocks inside the first sub-chunk of block maxima: every valid block must
+    be kept and the rest padded (2 x 2^20: chunk-parallel selection over
+    131,072 blocks; 64 x 2^19: the per-query kernel over 65,536 blocks)."""
+    rng = np.random.default_rng(n + Q)
+    sc = rng.standard_normal((Q, n)).astype(np.float32)
+    lims = [40, 130, 8, 1, 257, 0, 4000]
+    nv = np.array([lims[i % len(lims)] for i in range(Q)], np.int32)
+    sc[min(1, Q - 1), :] = 0.75
+    ref = oracle.pool_blocks(sc, 2048, nv)
+    got = _gpu_pool(sc, 2048, nv)
+    bad = np.nonzero((got != ref).any(axis=1))[0]
+    assert bad.size == 0, f"queries {bad[:5]} differ"
 
 
 def test_topk_empty_candidates():
@@ -712,6 +768,16 @@ def test_decode_chunked_causal_limits_and_no_ids():
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
 
 
+@pytest.mark.parametrize("T,t0", [(40, 0), (70, 0), (40, 120), (70, 960)])
+def test_decode_prefill_from_position_zero(T, t0):
+    """A prefill chunk over a long (65,536-entry) m=2 cache starting at
+    position t0: limits floor(t/2) from 0 up, all inside the first sub-chunks
+    of the list (t0 = 0), around one sub-chunk (t0 = 120) or around k
+    (t0 = 960). 40 queries take the chunk-parallel selection finished in the
+    attention kernel, 70 the per-query kernel."""
+    _check_decode(synth.prefill(T, 65536, t0, seed=60 + T + t0), what=f"prefill from t0={t0} T={T}")
+
+
 def test_decode_fewer_than_k_entries():
     _check_decode(synth.full_decode(2, 300, seed=24), what="n<k")
 
@@ -760,6 +826,10 @@ def test_reindex_decode_64x16384_pool_full():
 
 
 def test_prefill_4096x131072_sampled_queries():
+    """64 of the 4,096 queries: every position a query takes inside a
+    32-query scorer workgroup (4 waves x 2 sets x 4 queries) twice, spread
+    over the chunk, plus the first and last query."""
     wl = synth.make_workload(3)
-    qs = [0, 1, 1000, 2047, 2048, 3001, 4094, 4095]
+    qs = sorted({r + 32 * ((37 * r + 61 * s) % 128) for r in range(32) for s in range(2)} | {0, 4095})
+    assert len(qs) >= 64 and {q % 32 for q in qs} == set(range(32))
     _check_decode(wl, queries=qs, what="prefill 4,096 x 131,072")
