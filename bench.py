@@ -1,5 +1,5 @@
 #!/usr/bin/env python3
-"""Throughput of the CSA2 decode hot path on one MI355X.
+"""Throughput of the CSA2 hot path on one MI355X, over the five workload shapes.
 
 One step = one csa2_decode call (indexer scoring -> top-512 selection ->
 sparse attention over 512 FP4 latents + 128 SWA rows) over one batch of
@@ -7,17 +7,21 @@ synthetic input already resident in HBM. Steps rotate over device replicas of
 the batch (enough that one rotation's key reads exceed three times the 256 MB
 memory-side cache) so that consecutive steps cannot be served from it.
 
-Phases (all on one stream):
+The headline (`value`, `config`, `roofline`, `cpu_baseline`) is the largest
+single-GPU workload, decode of 4 sequences x 1,048,576 entries; `workloads`
+holds the same figures for all five. Per workload (all on one stream):
   1. warm-up, then K timed decode steps bracketed by synchronisation and two
      HIP events (no other event inside the timed region);
   2. per-stage times: up to 50 more steps with the library's stage events;
-  3. isolated kernel timing for the roofline: K back-to-back launches of
-     csa2_index_score (the scan kernel) and of csa2_sparse_attn, each
-     bracketed by two HIP events on the launch stream;
-  4. the box's streaming bandwidth (torch row sums and copy over 1 GiB), the
-     reference the scan kernel's bytes per second are also quoted against;
-  5. the CPU oracle on all host threads over a bounded sample (>= --cpu-seconds),
-     then one query per call on a single thread for half that time.
+  3. isolated kernel timing: K back-to-back launches of csa2_index_score (the
+     scan kernel) and of csa2_sparse_attn over the decode's ids, each
+     bracketed by two HIP events on the launch stream; the roofline is that
+     of whichever takes longer, the kernel with the larger share of the step;
+  4. the CPU oracle on all host threads over a bounded sample, then one query
+     per call on a single thread for half that time.
+The headline workload also times the kernels of the rows beside the path
+(FP8 window + RoPE attention, pool construction, Reuse gather, cache writes);
+at the end, the box's streaming bandwidth (torch row sums and copy, 1 GiB).
 
 Prints one JSON line. `python bench.py --pmc-summary DIR` instead summarises
 the counter CSVs of `rocprofv3 --pmc ... --output-format csv -d DIR` runs of
@@ -45,15 +49,21 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 FP4_PEAK_TFLOPS = 10100.0    # MI355X dense MXFP4 MFMA, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
 METRIC = "CSA2 decode queries/s + indexer entries scored/s; % HBM / FP4-MFMA roofline"
 IQ_BYTES = 32 * 64 + 32 * 4 + 32 * 4   # indexer query codes + E8M0 scales + head weights
 ENTRY_BYTES_INDEX = 68                 # 64 B codes + 4 B scales per scored entry
 ENTRY_BYTES_MAIN = 288
 FLOP_PER_PAIR = 2 * 32 * 128
-SCORE_KERNEL = "k_index_score"
-SCORE_SOURCES = ("index_score.hip", "csa2_device.h")
+# Kernel families whose roofline a workload may report, with the sources a
+# counter summary of them depends on (a summary taken on other sources is stale).
+KERNEL_SOURCES = {
+    "k_index_score": ("index_score.hip", "csa2_device.h"),
+    "k_index_score_qtile": ("index_score.hip", "csa2_device.h"),
+    "k_sparse_attn": ("sparse_attn.hip", "csa2_device.h", "select_device.h"),
+}
 CSRC = os.path.join(ROOT, "compressed_sparse_attention_score_amd", "csrc")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_index_score_hbm_traffic.md")
+PROFILES = os.path.join(ROOT, "profiles")
 COPY_MIB = 512
 POOL_BLOCKS = 2048                  # Reindex pool: 16,384 entries in blocks of 8
 CACHE_WRITE_ROWS = 131072           # new entries quantised per cache-write launch (a long prefill chunk)
@@ -195,26 +205,26 @@ def stream_bandwidth(reps=20):
     return out
 
 
-def source_digest(names=SCORE_SOURCES):
+def source_digest(kernel):
     h = hashlib.sha256()
-    for n in names:
+    for n in KERNEL_SOURCES[kernel]:
         with open(os.path.join(CSRC, n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload_name):
-    """HBM bytes per launch of the scan kernel from the committed counter
-    summary, or None if absent or taken on a different kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
-    digest = source_digest()
-    for line in open(TRAFFIC_FILE):
-        # machine-readable lines: "traffic: <digest> <bytes_per_launch> <workload name>"
-        if line.startswith("traffic: "):
-            parts = line[len("traffic: "):].strip().split(" ", 2)
-            if len(parts) == 3 and parts[0] == digest and parts[2] == workload_name:
-                return float(parts[1])
+def recorded_traffic(kernel, workload_name):
+    """HBM bytes per launch of `kernel` on `workload_name` from the committed
+    counter summaries (profiles/*hbm_traffic*.md), or None if absent or taken
+    on different kernel sources."""
+    digest = source_digest(kernel)
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*hbm_traffic*.md"))):
+        for line in open(path):
+            # machine-readable lines: "traffic: <digest> <kernel> <bytes_per_launch> <workload name>"
+            if line.startswith("traffic: "):
+                parts = line[len("traffic: "):].strip().split(" ", 3)
+                if len(parts) == 4 and parts[0] == digest and parts[1] == kernel and parts[3] == workload_name:
+                    return float(parts[2])
     return None
 
 
@@ -342,7 +352,8 @@ def print_pmc_summary(root):
             f = fetch_f if cn == "FETCH_SIZE" else write_f if cn == "WRITE_SIZE" else None
             cal = f"{v * 1024 / f / 1e6:14.3f}" if f else f"{'':14s}"
             print(f"{name[:70]:70s} {cn:12s} {v:18.1f} {n:10d} {cal}")
-    print(f"kernel source digest ({', '.join(SCORE_SOURCES)}): {source_digest()}")
+    for kern, srcs in KERNEL_SOURCES.items():
+        print(f"kernel source digest of {kern} ({', '.join(srcs)}): {source_digest(kern)}")
 
 
 def print_trace_summary(root):
@@ -368,31 +379,283 @@ def print_trace_summary(root):
     for name, m in meta.items():
         if "csa2" in name:
             print(f"  {name[:60]:60s} grid {m[0]}x{m[1]} wg {m[2]} lds {m[3]} vgpr {m[4]} agpr {m[5]} scratch {m[6]}")
+    # each library kernel split into launches inside decode steps (a neighbour
+    # is another kernel) and the back-to-back launches bench.py times alone
     lib = [r for r in rows if "csa2" in r[2]]
-    iso, dec = [], []
+    split = {}
     for i, (st, en, name, *_) in enumerate(lib):
-        if SCORE_KERNEL not in name:
-            continue
         nb = [lib[j][2] for j in (i - 1, i + 1) if 0 <= j < len(lib)]
-        (iso if all(SCORE_KERNEL in n for n in nb) else dec).append((en - st) / 1e3)
-    for label, v in (("inside decode steps", dec), ("isolated back-to-back", iso)):
-        if v:
-            print(f"{SCORE_KERNEL} {label}: {len(v)} launches, avg {sum(v) / len(v):.2f} us")
+        iso = all(n == name for n in nb)
+        split.setdefault(name, ([], []))[1 if iso else 0].append((en - st) / 1e3)
+    for name, (dec, iso) in split.items():
+        for label, v in (("inside decode steps", dec), ("isolated back-to-back", iso)):
+            if v:
+                print(f"{name[:60]} {label}: {len(v)} launches, avg {sum(v) / len(v):.2f} us")
 
 
 # -------------------------------------------------------------------- main
 
+HEADLINE = 4   # the largest single-GPU workload: decode of 4 sequences x 1,048,576 entries
+
+
+def _timed(ev, i0, stream, K, launch):
+    """Mean ms of K back-to-back launches of `launch(i)`, by two HIP events on
+    the launch stream (after 3 untimed launches)."""
+    import torch
+    for i in range(3):
+        launch(i)
+    torch.cuda.synchronize()
+    ev.record(i0, stream)
+    for i in range(K):
+        launch(i)
+    ev.record(i0 + 1, stream)
+    torch.cuda.synchronize()
+    return ev.ms(i0, i0 + 1) / K
+
+
+def run_workload(wi, args, extras, cpu_seconds):
+    """Every figure of one workload: decode steps, stage times, isolated
+    kernels and their rooflines, the oracle's CPU baseline and a parity
+    report. Frees its device memory before returning."""
+    import torch
+
+    import compressed_sparse_attention_score_amd as csa
+    import synth
+    from synth.device import to_device
+
+    name = synth.WORKLOAD_NAMES[wi]
+    print(f"[bench] workload {wi}: {name}", file=sys.stderr, flush=True)
+    t_gen = time.perf_counter()
+    wl = synth.make_workload(wi, dense_rows=False)
+    gen_s = time.perf_counter() - t_gen
+    db = to_device(wl)
+    Q = wl.Q
+    work = work_of(wl)
+    if wl.cand_blocks is not None and "pool_rows" in wl.extra:
+        resident = len(wl.extra["pool_rows"]) * (ENTRY_BYTES_MAIN + ENTRY_BYTES_INDEX)  # pool rows copied per replica
+    else:
+        resident = sum(t.numel() * t.element_size() for t in (db.main_cache, db.key_codes, db.key_scales))
+    R = replica_count(work, resident, args.replicas)
+    reps = replicate(db, wl, R)
+    stream = torch.cuda.current_stream()
+    out, lse, idx = db.new_outputs()
+    ws = torch.empty(max(1, csa.csa2_workspace_size(csa.CSA2_WS_DECODE, db.decode_args(out, lse, idx))),
+                     dtype=torch.uint8, device="cuda")
+    K, W = args.steps, args.warmup
+    S = min(K, 50)
+    ev = HipEvents(2 + 4 * S + 24)
+
+    # ---- timed decode steps
+    dec_args = [reps[i % R].decode_args(out, lse, idx) for i in range(R)]
+    for i in range(W):
+        csa.csa2_decode(dec_args[i % R], ws, stream)
+    csa.csa2_decode(dec_args[0], ws, stream)   # replica 0's outputs for the parity report
+    torch.cuda.synchronize()
+    first_out = out.cpu().numpy().view(np.uint16).copy()
+    first_idx = idx.cpu().numpy().copy()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev.record(0, stream)
+    for i in range(K):
+        csa.csa2_decode(dec_args[i % R], ws, stream)
+    ev.record(1, stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    gpu_ms = ev.ms(0, 1)
+
+    # ---- per-stage times (events between the kernels cost a few us each)
+    st_args = [reps[i % R].decode_args(out, lse, idx, stage_events=tuple(ev.ev[2 + 4 * i:6 + 4 * i]))
+               for i in range(S)]
+    for i in range(S):
+        csa.csa2_decode(st_args[i], ws, stream)
+    torch.cuda.synchronize()
+    st = np.array([[ev.ms(2 + 4 * i + j, 3 + 4 * i + j) for j in range(3)] for i in range(S)])
+    stage_ms = st.mean(axis=0)
+
+    # ---- isolated kernels: the scan and the attention (ids of the decode)
+    e0 = 2 + 4 * S
+    scores = torch.empty((Q, max(1, wl.n_cand)), dtype=torch.float32, device="cuda")
+    sc_args = [reps[i % R].index_args() for i in range(R)]
+    score_ms = _timed(ev, e0, stream, K, lambda i: csa.csa2_index_score(sc_args[i % R], scores, stream))
+    at_out, at_lse = torch.empty_like(out), torch.empty_like(lse)
+    at_args = [reps[i % R].attn_args(idx, at_out, at_lse) for i in range(R)]
+    at_ws = torch.empty(max(1, csa.csa2_workspace_size(csa.CSA2_WS_ATTN, at_args[0])), dtype=torch.uint8,
+                        device="cuda")
+    attn_ms = _timed(ev, e0 + 2, stream, K, lambda i: csa.csa2_sparse_attn(at_args[i % R], at_ws, stream))
+
+    prefill = wl.n_valid is not None
+    scan_kernel = "k_index_score_qtile" if (wl.cache_q_stride == 0 and Q >= 32) else "k_index_score"
+    score_gbs = work["score_bytes"] / (score_ms * 1e-3) / 1e9
+    score_tfs = work["score_flops"] / (score_ms * 1e-3) / 1e12
+    attn_gbs = work["attn_bytes"] / (attn_ms * 1e-3) / 1e9
+    attn_tfs = work["attn_flops"] / (attn_ms * 1e-3) / 1e12
+    kernels = {
+        "index_score": {"kernels": [scan_kernel], "us_per_launch": round(1e3 * score_ms, 3),
+                        "algorithmic_bytes": work["score_bytes"], "GB_s": round(score_gbs, 1),
+                        "hbm_frac": round(score_gbs / HBM_PEAK_GBS, 4), "TFLOP_s": round(score_tfs, 2),
+                        "fp4_mfma_frac": round(score_tfs / FP4_PEAK_TFLOPS, 4)},
+        "sparse_attn": {"kernels": ["k_sparse_attn"], "us_per_launch": round(1e3 * attn_ms, 3),
+                        "algorithmic_bytes": work["attn_bytes"], "GB_s": round(attn_gbs, 1),
+                        "hbm_frac": round(attn_gbs / HBM_PEAK_GBS, 4), "TFLOP_s": round(attn_tfs, 2),
+                        "bf16_mfma_frac": round(attn_tfs / BF16_PEAK_TFLOPS, 4)},
+    }
+    if extras:
+        kernels.update(extra_kernels(wl, reps, R, idx, out, lse, scores, at_ws, ev, e0 + 4, stream, K))
+
+    # ---- roofline of the kernel with the larger share of the step
+    if score_ms >= attn_ms:
+        kern = scan_kernel
+        if prefill:
+            roof = {"bound": "mfma", "achieved": round(score_tfs, 2), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(score_tfs / FP4_PEAK_TFLOPS, 4),
+                    "algorithmic_flops_per_launch": work["score_flops"]}
+        else:
+            roof = {"bound": "hbm", "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(score_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": work["score_bytes"]}
+        launch_ms = score_ms
+    else:
+        kern = "k_sparse_attn"
+        roof = {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": work["attn_bytes"],
+                "bf16_mfma_frac": round(attn_tfs / BF16_PEAK_TFLOPS, 4)}
+        launch_ms = attn_ms
+    roof["traffic"] = recorded_traffic(kern, name)
+    roof["kernel"] = kern
+    roof["launch_us"] = round(1e3 * launch_ms, 3)
+    roof["share_of_step"] = round(launch_ms / (gpu_ms / K), 4)
+
+    ms_per_step = 1e3 * elapsed / K
+    res = {
+        "workload": name,
+        "workload_index": wi,
+        "queries": Q,
+        "candidates_per_query": wl.n_cand,
+        "top_k": wl.k,
+        "swa_rows": wl.n_swa,
+        "replicas": R,
+        "queries_per_s": round(Q * K / elapsed, 1),
+        "entries_scored_per_s": round(work["pairs"] * K / elapsed, 1),
+        "ms_per_step": round(ms_per_step, 5),
+        "gpu_ms_per_step": round(gpu_ms / K, 5),
+        "algorithmic_bytes_per_step": work["step_bytes"],
+        "path_hbm_frac": round(work["step_bytes"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "stage_us": {"index_score": round(1e3 * stage_ms[0], 2), "select": round(1e3 * stage_ms[1], 2),
+                     "attention": round(1e3 * stage_ms[2], 2), "steps": S},
+        "roofline": roof,
+        "kernels": kernels,
+        "gen_s": round(gen_s, 2),
+    }
+    if prefill:
+        res["indexer_pairs_per_s"] = round(work["pairs"] / (score_ms * 1e-3), 1)
+    ev.close()
+    del reps, db, scores, ws, at_ws, at_out, at_lse, dec_args, st_args, sc_args, at_args
+    out, lse, idx = None, None, None
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if cpu_seconds > 0:
+        first, cb = cpu_baseline(wl, cpu_seconds)
+        res["cpu_baseline"] = cb
+        res["parity"] = parity_summary(wl, first, first_out, first_idx)
+    return res
+
+
+def extra_kernels(wl, reps, R, idx, out, lse, scores, at_ws, ev, e0, stream, K):
+    """The kernels of the rows built beside the hot path, timed on this
+    workload: attention with FP8 window rows and the RoPE epilogue, Reindex
+    pool construction from these scores, the Reuse-layer gather and attention
+    over the gathered list, and the cache writes (131,072 new rows; 65,536
+    m=2 pooled entries)."""
+    import torch
+
+    import compressed_sparse_attention_score_amd as csa
+    import synth
+    Q = wl.Q
+    work = work_of(wl)
+    res = {}
+    at_out, at_lse = torch.empty_like(out), torch.empty_like(lse)
+    if wl.extra.get("shared_swa"):
+        rows8 = synth.fp8_rows(0, synth.TID_SWA, 0, 0, wl.swa.shape[0])
+    else:
+        rows8 = np.concatenate([synth.fp8_rows(0, synth.TID_SWA, i, 0, wl.n_swa) for i in range(Q)])
+    pos = wl.extra["t0"] + np.arange(Q) if "t0" in wl.extra else wl.n_entries + 7 * np.arange(Q)
+    swa8 = torch.from_numpy(np.ascontiguousarray(rows8)).cuda()
+    rope_t = torch.from_numpy(synth.rope_table(pos)).cuda()
+    a8 = [dataclasses.replace(reps[i % R], swa=swa8, swa_format=csa.CSA2_SWA_FP8, rope=rope_t)
+          .attn_args(idx, at_out, at_lse) for i in range(R)]
+    ms = _timed(ev, e0, stream, K, lambda i: csa.csa2_sparse_attn(a8[i % R], at_ws, stream))
+    res["sparse_attn_fp8_window_rope"] = {"kernels": ["k_sparse_attn<fp8 window>"], "us_per_launch": round(1e3 * ms, 3),
+                                          "algorithmic_bytes": work["attn_fp8_bytes"],
+                                          "GB_s": round(work["attn_fp8_bytes"] / (ms * 1e-3) / 1e9, 1)}
+    del swa8, rope_t, a8
+    if wl.cand_blocks is None and wl.n_valid is None:
+        n_pool = int(min(POOL_BLOCKS, (wl.n_cand + 7) // 8))
+        pool_out = torch.empty((Q, n_pool), dtype=torch.int32, device="cuda")
+        pa = csa.pool_args(scores, n_pool, pool_out)
+        pool_ws = torch.empty(max(1, csa.csa2_workspace_size(csa.CSA2_WS_POOL, pa)), dtype=torch.uint8, device="cuda")
+        ms = _timed(ev, e0 + 2, stream, K, lambda i: csa.csa2_build_pool(pa, pool_ws, stream))
+        pb = Q * (4 * wl.n_cand + 4 * n_pool)  # scores read once, pool ids written
+        res["build_pool"] = {"kernels": ["k_block_max", "k_score_maxima", "k_select_*"], "blocks_kept": n_pool,
+                             "us_per_launch": round(1e3 * ms, 3), "algorithmic_bytes": pb,
+                             "GB_s": round(pb / (ms * 1e-3) / 1e9, 1)}
+        del pool_out, pool_ws
+    kk = int(idx.shape[1])
+    g_out = torch.empty((Q, kk, ENTRY_BYTES_MAIN), dtype=torch.uint8, device="cuda")
+    g_dense = torch.empty((Q, kk), dtype=torch.int32, device="cuda")
+    ms_g = _timed(ev, e0 + 4, stream, K, lambda i: csa.csa2_gather_selected(
+        reps[i % R].main_cache, wl.n_entries, wl.cache_q_stride, idx, g_out, g_dense, stream))
+    ad = dataclasses.replace(reps[0], main_cache=g_out.view(-1, ENTRY_BYTES_MAIN), n_entries=kk,
+                             cache_q_stride=kk).attn_args(g_dense, at_out, at_lse)
+    ms_d = _timed(ev, e0 + 6, stream, K, lambda i: csa.csa2_sparse_attn(ad, at_ws, stream))
+    res["reuse_layer"] = {"kernels": ["k_gather_selected", "k_sparse_attn"], "gather_us": round(1e3 * ms_g, 3),
+                          "gather_GB_s": round(2 * Q * kk * ENTRY_BYTES_MAIN / (ms_g * 1e-3) / 1e9, 1),
+                          "attn_over_dense_list_us": round(1e3 * ms_d, 3)}
+    del g_out, g_dense
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4242)
+    xm = torch.randn((CACHE_WRITE_ROWS, 512), generator=gen, device="cuda")
+    xk = torch.randn((CACHE_WRITE_ROWS, 128), generator=gen, device="cuda")
+    qm = torch.empty((CACHE_WRITE_ROWS, 288), dtype=torch.uint8, device="cuda")
+    qc = torch.empty((CACHE_WRITE_ROWS, 64), dtype=torch.uint8, device="cuda")
+    qs = torch.empty((CACHE_WRITE_ROWS, 4), dtype=torch.uint8, device="cuda")
+    for j, (kname, kind, xin, co, so, per_row) in enumerate(
+            (("quantize_main", 0, xm, qm, None, 512 * 4 + ENTRY_BYTES_MAIN),
+             ("quantize_index", 1, xk, qc, qs, 128 * 4 + ENTRY_BYTES_INDEX))):
+        ms = _timed(ev, e0 + 8 + 2 * j, stream, K, lambda i: csa.csa2_quantize(
+            kind, xin, csa.CSA2_IN_F32, CACHE_WRITE_ROWS, None, CACHE_WRITE_ROWS, co, so, stream))
+        qb = CACHE_WRITE_ROWS * per_row
+        res[kname] = {"kernels": [f"k_quantize<f32, {'main' if kind == 0 else 'index'}>"], "rows": CACHE_WRITE_ROWS,
+                      "us_per_launch": round(1e3 * ms, 3), "algorithmic_bytes": qb,
+                      "GB_s": round(qb / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(qb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del xm, xk, qm, qc, qs
+    npool = CACHE_WRITE_ROWS // 2
+    xp = torch.randn((2 * npool, 512), generator=gen, device="cuda")
+    gp = torch.randn((2 * npool, 512), generator=gen, device="cuda")
+    cp = torch.empty((npool, 288), dtype=torch.uint8, device="cuda")
+    pp = torch.empty((npool, 512), dtype=torch.float32, device="cuda")
+    ms = _timed(ev, e0 + 12, stream, K, lambda i: csa.csa2_pool_quantize(xp, gp, npool, None, npool, cp, pp, stream))
+    pqb = npool * (2 * 2048 * 2 + ENTRY_BYTES_MAIN + 2048)  # two rows + two gate rows in, entry + pooled out
+    res["pool_quantize_m2"] = {"kernels": ["k_quantize<f32, main, gate 512>"], "entries": npool,
+                               "us_per_launch": round(1e3 * ms, 3), "algorithmic_bytes": pqb,
+                               "GB_s": round(pqb / (ms * 1e-3) / 1e9, 1),
+                               "hbm_frac": round(pqb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del xp, gp, cp, pp
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", "--config", dest="workload", type=int, default=1,
-                    help="workload shape: 0 decode 1 x 4,096; 1 decode 16 x 65,536 (default); 2 reindex decode "
-                         "64 x 16,384-entry pools; 3 prefill 4,096 x 131,072; 4 decode 4 x 1,048,576")
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", "--config", dest="workload", type=int, default=None,
+                    help="run one workload only: 0 decode 1 x 4,096; 1 decode 16 x 65,536; 2 reindex decode "
+                         "64 x 16,384-entry pools of 1,048,576-entry caches; 3 prefill 4,096 x 131,072; 4 decode "
+                         "4 x 1,048,576 (the headline). Default: all five, headline 4")
     ap.add_argument("--replicas", type=int, default=0, help="device copies rotated per step (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum wall time of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum wall time of the headline's oracle sample (a third of it for the other workloads)")
+    ap.add_argument("--no-extras", action="store_true", help="skip the kernels of the rows beside the hot path")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"also run an elementwise {COPY_MIB} MiB negation (counter calibration)")
     ap.add_argument("--pmc-summary", metavar="DIR", help="summarise rocprofv3 counter CSVs under DIR and exit")
@@ -412,191 +675,14 @@ def main():
 
     import torch
 
-    import compressed_sparse_attention_score_amd as csa
     import synth
-    from synth.device import to_device
-
     torch.cuda.set_device(0)
-    t_gen = time.perf_counter()
-    wl = synth.make_workload(args.workload, dense_rows=False)
-    gen_s = time.perf_counter() - t_gen
-    db = to_device(wl)
-    Q = wl.Q
-    work = work_of(wl)
-    if wl.cand_blocks is not None and "pool_rows" in wl.extra:
-        resident = len(wl.extra["pool_rows"]) * (ENTRY_BYTES_MAIN + ENTRY_BYTES_INDEX)  # pool rows copied per replica
-    else:
-        resident = sum(t.numel() * t.element_size() for t in (db.main_cache, db.key_codes, db.key_scales))
-    R = replica_count(work, resident, args.replicas)
-    reps = replicate(db, wl, R)
-    stream = torch.cuda.current_stream()
-
-    out, lse, idx = db.new_outputs()
-    ws = torch.empty(max(1, csa.csa2_workspace_size(csa.CSA2_WS_DECODE, db.decode_args(out, lse, idx))),
-                     dtype=torch.uint8, device="cuda")
-    K, W = args.steps, args.warmup
-    S = min(K, 50)
-    ev = HipEvents(2 + 4 * S + 18)
-
-    # ---- phase 1: timed decode steps
-    dec_args = [reps[i % R].decode_args(out, lse, idx) for i in range(R)]
-    for i in range(W):
-        csa.csa2_decode(dec_args[i % R], ws, stream)
-    csa.csa2_decode(dec_args[0], ws, stream)   # replica 0's outputs for the parity report
-    torch.cuda.synchronize()
-    first_out = out.cpu().numpy().view(np.uint16).copy()
-    first_idx = idx.cpu().numpy().copy()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev.record(0, stream)
-    for i in range(K):
-        csa.csa2_decode(dec_args[i % R], ws, stream)
-    ev.record(1, stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    gpu_ms = ev.ms(0, 1)
-
-    # ---- phase 2: per-stage times (events between kernels cost a few us each)
-    st_args = [reps[i % R].decode_args(out, lse, idx, stage_events=tuple(ev.ev[2 + 4 * i:6 + 4 * i]))
-               for i in range(S)]
-    for i in range(S):
-        csa.csa2_decode(st_args[i], ws, stream)
-    torch.cuda.synchronize()
-    st = np.array([[ev.ms(2 + 4 * i + j, 3 + 4 * i + j) for j in range(3)] for i in range(S)])
-    stage_ms = st.mean(axis=0)
-
-    # ---- phase 3: isolated kernels
-    e0 = 2 + 4 * S
-    scores = torch.empty((Q, max(1, wl.n_cand)), dtype=torch.float32, device="cuda")
-    sc_args = [reps[i % R].index_args() for i in range(R)]
-    for i in range(3):
-        csa.csa2_index_score(sc_args[i % R], scores, stream)
-    torch.cuda.synchronize()
-    ev.record(e0, stream)
-    for i in range(K):
-        csa.csa2_index_score(sc_args[i % R], scores, stream)
-    ev.record(e0 + 1, stream)
-    torch.cuda.synchronize()
-    score_ms = ev.ms(e0, e0 + 1) / K
-    # Reindex pool construction from these Full-layer scores (decode layouts
-    # over a whole cache only): 2,048 blocks of 8, or every block if fewer
-    pool_ms = None
-    if wl.cand_blocks is None and wl.n_valid is None:
-        n_pool = int(min(POOL_BLOCKS, (wl.n_cand + 7) // 8))
-        pool_out = torch.empty((Q, n_pool), dtype=torch.int32, device="cuda")
-        pa = csa.pool_args(scores, n_pool, pool_out)
-        pool_ws = torch.empty(max(1, csa.csa2_workspace_size(csa.CSA2_WS_POOL, pa)), dtype=torch.uint8, device="cuda")
-        for _ in range(3):
-            csa.csa2_build_pool(pa, pool_ws, stream)
-        torch.cuda.synchronize()
-        ev.record(e0 + 10, stream)
-        for _ in range(K):
-            csa.csa2_build_pool(pa, pool_ws, stream)
-        ev.record(e0 + 11, stream)
-        torch.cuda.synchronize()
-        pool_ms = ev.ms(e0 + 10, e0 + 11) / K
-        del pool_out, pool_ws
-    at_out = torch.empty_like(out)
-    at_lse = torch.empty_like(lse)
-    at_args = [reps[i % R].attn_args(idx, at_out, at_lse) for i in range(R)]
-    at_ws = torch.empty(max(1, csa.csa2_workspace_size(csa.CSA2_WS_ATTN, at_args[0])), dtype=torch.uint8,
-                        device="cuda")
-    for i in range(3):
-        csa.csa2_sparse_attn(at_args[i % R], at_ws, stream)
-    torch.cuda.synchronize()
-    ev.record(e0 + 2, stream)
-    for i in range(K):
-        csa.csa2_sparse_attn(at_args[i % R], at_ws, stream)
-    ev.record(e0 + 3, stream)
-    torch.cuda.synchronize()
-    attn_ms = ev.ms(e0 + 2, e0 + 3) / K
-    # the same attention with the pages' FP8 window rows (528 B each) and the
-    # RoPE un-rotation epilogue (rows from the same seeded streams)
-    if wl.extra.get("shared_swa"):
-        rows8 = synth.fp8_rows(0, synth.TID_SWA, 0, 0, wl.swa.shape[0])
-    else:
-        rows8 = np.concatenate([synth.fp8_rows(0, synth.TID_SWA, i, 0, wl.n_swa) for i in range(Q)])
-    pos = wl.extra["t0"] + np.arange(Q) if "t0" in wl.extra else wl.n_entries + 7 * np.arange(Q)
-    swa8 = torch.from_numpy(np.ascontiguousarray(rows8)).cuda()
-    rope_t = torch.from_numpy(synth.rope_table(pos)).cuda()
-    a8_args = [dataclasses.replace(reps[i % R], swa=swa8, swa_format=csa.CSA2_SWA_FP8, rope=rope_t)
-               .attn_args(idx, at_out, at_lse) for i in range(R)]
-    for i in range(3):
-        csa.csa2_sparse_attn(a8_args[i % R], at_ws, stream)
-    torch.cuda.synchronize()
-    ev.record(e0 + 4, stream)
-    for i in range(K):
-        csa.csa2_sparse_attn(a8_args[i % R], at_ws, stream)
-    ev.record(e0 + 5, stream)
-    torch.cuda.synchronize()
-    attn8_ms = ev.ms(e0 + 4, e0 + 5) / K
-    del swa8, rope_t
-    # Reuse layers: the selection gathered once into a dense list, then a
-    # layer's attention over it (the later layers read contiguous rows)
-    kk = int(idx.shape[1])
-    g_out = torch.empty((Q, kk, ENTRY_BYTES_MAIN), dtype=torch.uint8, device="cuda")
-    g_dense = torch.empty((Q, kk), dtype=torch.int32, device="cuda")
-    for _ in range(3):
-        csa.csa2_gather_selected(reps[0].main_cache, wl.n_entries, wl.cache_q_stride, idx, g_out, g_dense, stream)
-    torch.cuda.synchronize()
-    ev.record(e0 + 14, stream)
-    for i in range(K):
-        csa.csa2_gather_selected(reps[i % R].main_cache, wl.n_entries, wl.cache_q_stride, idx, g_out, g_dense, stream)
-    ev.record(e0 + 15, stream)
-    torch.cuda.synchronize()
-    gather_ms = ev.ms(e0 + 14, e0 + 15) / K
-    ad_args = dataclasses.replace(reps[0], main_cache=g_out.view(-1, ENTRY_BYTES_MAIN), n_entries=kk,
-                                  cache_q_stride=kk).attn_args(g_dense, at_out, at_lse)
-    for _ in range(3):
-        csa.csa2_sparse_attn(ad_args, at_ws, stream)
-    torch.cuda.synchronize()
-    ev.record(e0 + 16, stream)
-    for _ in range(K):
-        csa.csa2_sparse_attn(ad_args, at_ws, stream)
-    ev.record(e0 + 17, stream)
-    torch.cuda.synchronize()
-    attn_dense_ms = ev.ms(e0 + 16, e0 + 17) / K
-    del g_out, g_dense
-    # ---- phase 4: cache write of a long prefill chunk's new entries (not part
-    # of the step): fp32 rows -> FP4 main entries and indexer keys
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(4242)
-    xm = torch.randn((CACHE_WRITE_ROWS, 512), generator=gen, device="cuda")
-    xk = torch.randn((CACHE_WRITE_ROWS, 128), generator=gen, device="cuda")
-    qm = torch.empty((CACHE_WRITE_ROWS, 288), dtype=torch.uint8, device="cuda")
-    qc = torch.empty((CACHE_WRITE_ROWS, 64), dtype=torch.uint8, device="cuda")
-    qs = torch.empty((CACHE_WRITE_ROWS, 4), dtype=torch.uint8, device="cuda")
-    qargs = [(0, xm, qm, None), (1, xk, qc, qs)]
-    q_ms = []
-    for j, (kind, xin, co, so) in enumerate(qargs):
-        for _ in range(3):
-            csa.csa2_quantize(kind, xin, csa.CSA2_IN_F32, CACHE_WRITE_ROWS, None, CACHE_WRITE_ROWS, co, so, stream)
-        torch.cuda.synchronize()
-        ev.record(e0 + 6 + 2 * j, stream)
-        for _ in range(K):
-            csa.csa2_quantize(kind, xin, csa.CSA2_IN_F32, CACHE_WRITE_ROWS, None, CACHE_WRITE_ROWS, co, so, stream)
-        ev.record(e0 + 7 + 2 * j, stream)
-        torch.cuda.synchronize()
-        q_ms.append(ev.ms(e0 + 6 + 2 * j, e0 + 7 + 2 * j) / K)
-    del xm, xk, qm, qc, qs
-    # the encoder's cache write: m=2 gated pooling of token pairs, then the
-    # main-entry encoding, with per-channel gate logits and the pooled rows out
-    npool = CACHE_WRITE_ROWS // 2
-    xp = torch.randn((2 * npool, 512), generator=gen, device="cuda")
-    gp = torch.randn((2 * npool, 512), generator=gen, device="cuda")
-    cp = torch.empty((npool, 288), dtype=torch.uint8, device="cuda")
-    pp = torch.empty((npool, 512), dtype=torch.float32, device="cuda")
-    for _ in range(3):
-        csa.csa2_pool_quantize(xp, gp, npool, None, npool, cp, pp, stream)
-    torch.cuda.synchronize()
-    ev.record(e0 + 12, stream)
-    for _ in range(K):
-        csa.csa2_pool_quantize(xp, gp, npool, None, npool, cp, pp, stream)
-    ev.record(e0 + 13, stream)
-    torch.cuda.synchronize()
-    pq_ms = ev.ms(e0 + 12, e0 + 13) / K
-    del xp, gp, cp, pp
-    ev.close()
+    order = [args.workload] if args.workload is not None else [0, 1, 2, 3, HEADLINE]
+    head = order[-1]
+    per = {}
+    for wi in order:
+        cpu_s = 0.0 if args.no_cpu_baseline else (args.cpu_seconds if wi == head else args.cpu_seconds / 3)
+        per[str(wi)] = run_workload(wi, args, extras=(wi == head and not args.no_extras), cpu_seconds=cpu_s)
     read_gbs, copy_gbs = stream_bandwidth()
     if args.copy_calibration:
         src = torch.ones(COPY_MIB << 18, dtype=torch.float32, device="cuda")
@@ -605,92 +691,38 @@ def main():
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-
-    ms_per_step = 1e3 * elapsed / K
-    value = Q * K / elapsed
-    prefill = wl.n_valid is not None
-    name = synth.WORKLOAD_NAMES[args.workload]
-    score_gbs = work["score_bytes"] / (score_ms * 1e-3) / 1e9
-    score_tfs = work["score_flops"] / (score_ms * 1e-3) / 1e12
-    attn_gbs = work["attn_bytes"] / (attn_ms * 1e-3) / 1e9
-    kernels = {
-        "index_score": {"kernels": [SCORE_KERNEL], "us_per_launch": round(1e3 * score_ms, 3),
-                        "algorithmic_bytes": work["score_bytes"], "GB_s": round(score_gbs, 1),
-                        "hbm_frac": round(score_gbs / HBM_PEAK_GBS, 4), "TFLOP_s": round(score_tfs, 2),
-                        "fp4_mfma_frac": round(score_tfs / FP4_PEAK_TFLOPS, 4)},
-        "sparse_attn": {"kernels": ["k_sparse_attn", "k_attn_combine"], "us_per_launch": round(1e3 * attn_ms, 3),
-                        "algorithmic_bytes": work["attn_bytes"], "GB_s": round(attn_gbs, 1),
-                        "hbm_frac": round(attn_gbs / HBM_PEAK_GBS, 4)},
-        "sparse_attn_fp8_window_rope": {
-            "kernels": ["k_sparse_attn<fp8 window>", "k_attn_combine"], "us_per_launch": round(1e3 * attn8_ms, 3),
-            "algorithmic_bytes": work["attn_fp8_bytes"],
-            "GB_s": round(work["attn_fp8_bytes"] / (attn8_ms * 1e-3) / 1e9, 1)},
-    }
-    kernels["reuse_layer"] = {"kernels": ["k_gather_selected", "k_sparse_attn", "k_attn_combine"],
-                              "gather_us": round(1e3 * gather_ms, 3),
-                              "gather_GB_s": round(2 * Q * kk * ENTRY_BYTES_MAIN / (gather_ms * 1e-3) / 1e9, 1),
-                              "attn_over_dense_list_us": round(1e3 * attn_dense_ms, 3),
-                              "attn_over_cache_us": round(1e3 * attn_ms, 3)}
-    pqb = npool * (2 * 2048 * 2 + ENTRY_BYTES_MAIN + 2048)  # two rows + two gate rows in, entry + pooled out
-    kernels["pool_quantize_m2"] = {"kernels": ["k_quantize<f32, main, gate 512>"], "entries": npool,
-                                   "us_per_launch": round(1e3 * pq_ms, 3), "algorithmic_bytes": pqb,
-                                   "GB_s": round(pqb / (pq_ms * 1e-3) / 1e9, 1),
-                                   "hbm_frac": round(pqb / (pq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    if pool_ms is not None:
-        pb = Q * (4 * wl.n_cand + 4 * n_pool)  # scores read once, pool ids written
-        kernels["build_pool"] = {"kernels": ["k_block_max", "k_score_maxima", "k_select_*"], "blocks_kept": n_pool,
-                                 "us_per_launch": round(1e3 * pool_ms, 3), "algorithmic_bytes": pb,
-                                 "GB_s": round(pb / (pool_ms * 1e-3) / 1e9, 1)}
-    for kname, kind, ms_ in (("quantize_main", "k_quantize<f32, main>", q_ms[0]),
-                             ("quantize_index", "k_quantize<f32, index>", q_ms[1])):
-        per_row = (512 * 4 + ENTRY_BYTES_MAIN) if kname == "quantize_main" else (128 * 4 + ENTRY_BYTES_INDEX)
-        qb = CACHE_WRITE_ROWS * per_row
-        kernels[kname] = {"kernels": [kind], "rows": CACHE_WRITE_ROWS, "us_per_launch": round(1e3 * ms_, 3),
-                          "algorithmic_bytes": qb, "GB_s": round(qb / (ms_ * 1e-3) / 1e9, 1),
-                          "hbm_frac": round(qb / (ms_ * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    traffic = recorded_traffic(name)
-    if prefill:
-        roof = {"bound": "mfma", "achieved": round(score_tfs, 2), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(score_tfs / FP4_PEAK_TFLOPS, 4), "traffic": traffic, "kernel": SCORE_KERNEL,
-                "algorithmic_flops_per_launch": work["score_flops"], "launch_us": round(1e3 * score_ms, 3)}
-    else:
-        roof = {"bound": "hbm", "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(score_gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": SCORE_KERNEL,
-                "algorithmic_bytes_per_launch": work["score_bytes"], "launch_us": round(1e3 * score_ms, 3)}
-    if attn_ms > score_ms and not prefill:
-        roof["note"] = "the attention stage took longer than the scan in this run; see kernels.sparse_attn"
+    h = per[str(head)]
+    for r in per.values():
+        if r["roofline"]["unit"] == "GB/s":
+            r["roofline"]["frac_of_measured_read"] = round(r["roofline"]["achieved"] / read_gbs, 4)
     res = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": h["queries_per_s"],
         "unit": "queries/s",
         "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": round(ms_per_step, 5),
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": h["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp4(mx)+bf16",
         "data": "synthetic (seeded N(0,1) latents/keys/queries quantised to FP4 per the pages' formats)",
-        "config": {"workload": name, "workload_index": args.workload, "queries": Q, "candidates_per_query": wl.n_cand,
-                   "top_k": wl.k, "swa_rows": wl.n_swa, "replicas": R},
-        "entries_scored_per_s": round(work["pairs"] * K / elapsed, 1),
-        "gpu_ms_per_step": round(gpu_ms / K, 5),
-        "stage_us": {"index_score": round(1e3 * stage_ms[0], 2), "select": round(1e3 * stage_ms[1], 2),
-                     "attention": round(1e3 * stage_ms[2], 2), "steps": S},
-        "path_hbm_frac": round(work["step_bytes"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "roofline": roof,
-        "measured_stream": {"read_GB_s": round(read_gbs, 1), "copy_GB_s": round(copy_gbs, 1),
-                            "what": "torch row sums over 16 KB rows (read) and copy (read + write), 1 GiB fp32, "
-                                    "on this box",
-                            "scan_frac_of_read": None if prefill else round(score_gbs / read_gbs, 4)},
-        "kernels": kernels,
+        "config": {"workload": h["workload"], "workload_index": h["workload_index"], "queries": h["queries"],
+                   "candidates_per_query": h["candidates_per_query"], "top_k": h["top_k"],
+                   "swa_rows": h["swa_rows"], "replicas": h["replicas"]},
+        "entries_scored_per_s": h["entries_scored_per_s"],
+        "gpu_ms_per_step": h["gpu_ms_per_step"],
+        "path_hbm_frac": h["path_hbm_frac"],
+        "stage_us": h["stage_us"],
+        "roofline": h["roofline"],
     }
-    if not args.no_cpu_baseline:
-        first, cb = cpu_baseline(wl, args.cpu_seconds)
-        res["cpu_baseline"] = cb
-        res["parity"] = parity_summary(wl, first, first_out, first_idx)
-    res["gen_s"] = round(gen_s, 2)
+    if "cpu_baseline" in h:
+        res["cpu_baseline"] = h["cpu_baseline"]
+    res["measured_stream"] = {"read_GB_s": round(read_gbs, 1), "copy_GB_s": round(copy_gbs, 1),
+                              "what": "torch row sums over 16 KB rows (read) and copy (read + write), 1 GiB fp32, "
+                                      "on this box"}
+    res["workloads"] = per
     print(json.dumps(res), flush=True)
 
 
