@@ -170,9 +170,9 @@ int check_pool(const csa2_pool_args* a) {
   return CSA2_OK;
 }
 
-size_t ws_attn(int Q, int nj) {
+size_t ws_attn(int Q, int k_sel, int n_swa) {
   if (Q == 0) return 0;
-  AttnPlan ap = plan_attn(Q, nj);
+  AttnPlan ap = plan_attn(Q, k_sel, n_swa);
   if (ap.n_splits <= 1) return 0;
   Carve c(nullptr);
   c.take<char>(attn_partial_bytes(Q, ap));
@@ -190,7 +190,7 @@ struct DecodeWs {
 DecodeWs carve_decode(void* ws, const csa2_decode_args* a, int64_t n_cand) {
   const int Q = a->index.n_queries;
   ScorePlan sp = plan_score(n_cand, Q, a->k);
-  AttnPlan ap = plan_attn(Q, a->k + a->n_swa);
+  AttnPlan ap = plan_attn(Q, a->k, a->n_swa);
   Carve c(ws);
   DecodeWs d;
   d.tk = carve_topk(ws, Q, n_cand, sp, c);
@@ -341,9 +341,9 @@ int csa2_sparse_attn(const csa2_attn_args* a, void* ws, size_t ws_bytes, void* s
   if (st) return st;
   if (a->n_queries == 0) return CSA2_OK;
   const int Q = a->n_queries;
-  st = check_ws(ws, ws_bytes, ws_attn(Q, a->k_sel + a->n_swa));
+  st = check_ws(ws, ws_bytes, ws_attn(Q, a->k_sel, a->n_swa));
   if (st) return st;
-  AttnPlan ap = plan_attn(Q, a->k_sel + a->n_swa);
+  AttnPlan ap = plan_attn(Q, a->k_sel, a->n_swa);
   hipStream_t s = (hipStream_t)stream;
   float* partial = nullptr;
   if (ap.n_splits > 1) {
@@ -404,7 +404,7 @@ int csa2_decode(const csa2_decode_args* a, void* ws, size_t ws_bytes, void* stre
   if (e == hipSuccess) e = mark(2);
   if (e != hipSuccess) return CSA2_ERR_HIP;
   // 3. attention over the selection + window
-  AttnPlan ap = plan_attn(Q, a->k + a->n_swa);
+  AttnPlan ap = plan_attn(Q, a->k, a->n_swa);
   AttnLaunch A{Q,      a->index.n_entries, a->index.cache_q_stride, a->main_cache,
                w.idx,  a->k,               a->q,                    a->swa,
                a->swa_q_stride, a->n_swa, a->softmax_scale,        a->out,
@@ -438,7 +438,7 @@ size_t csa2_workspace_size(int which, const void* args) {
     if (a->n_queries < 0 || a->n_queries > kMaxQ || a->k_sel < 0 || a->k_sel > CSA2_MAX_K || a->n_swa < 0 ||
         a->n_swa > CSA2_MAX_SWA)
       return SIZE_MAX;
-    return ws_attn(a->n_queries, a->k_sel + a->n_swa);
+    return ws_attn(a->n_queries, a->k_sel, a->n_swa);
   }
   if (which == CSA2_WS_POOL) {
     const csa2_pool_args* a = (const csa2_pool_args*)args;

@@ -39,13 +39,15 @@ struct SelectPlan {
 };
 SelectPlan plan_select(int64_t n_cand);
 
-// Attention split layout.
+// Attention layout: the joint list in 32-slot tiles (window rows and
+// selected latents tiled apart), split into n_splits ranges of
+// tiles_per_split tiles per (query, head block).
 struct AttnPlan {
-  int n_tiles;      // 32-slot tiles of the joint list
+  int n_tiles;
   int tiles_per_split;
   int n_splits;
 };
-AttnPlan plan_attn(int Q, int nj);
+AttnPlan plan_attn(int Q, int k_sel, int n_swa);
 
 hipError_t launch_dequant(int kind, const uint8_t* codes, const uint8_t* scales, int64_t n, int out_bf16, void* out,
                           hipStream_t s);
@@ -90,7 +92,7 @@ hipError_t launch_select_compact(const float* scores, int Q, int64_t n_cand, int
 
 // Largest number of compaction chunks per query for which the attention
 // kernel finishes the selection (one workgroup of that many threads).
-constexpr int kFusedSelectMaxChunks = 512;
+constexpr int kFusedSelectMaxChunks = 256;
 
 // Reindex pool construction: bmax [Q][ceil(n/8)] = best score of each block
 // of 8 inside the causal limit (as a score whose key is the block's best
@@ -128,8 +130,8 @@ struct AttnLaunch {
   int32_t* idx_out;
 };
 
-// partial: workspace for the per-split records (plan.n_splits > 1); the merge
-// runs as a second kernel.
+// partial: workspace for the per-range records (plan.n_splits > 1); the
+// merge runs as a second kernel.
 hipError_t launch_attn(const AttnLaunch& a, const AttnPlan& plan, float* partial, hipStream_t s);
 
 size_t attn_partial_bytes(int Q, const AttnPlan& plan);

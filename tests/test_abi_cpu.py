@@ -163,6 +163,9 @@ def test_validation_rejects_before_launch():
     need = csa.csa2_workspace_size(csa.CSA2_WS_ATTN, aa)
     assert need > 0  # 4 queries split their slot list
     assert L.csa2_sparse_attn(ctypes.byref(aa), A, need - 1, None) == csa.CSA2_ERR_WORKSPACE
+    big = csa.AttnArgs.from_buffer_copy(aa)
+    big.n_queries = 2000  # enough workgroups without splitting: no workspace
+    assert csa.csa2_workspace_size(csa.CSA2_WS_ATTN, big) == 0
     # decode
     da = csa.DecodeArgs(ctypes.sizeof(csa.DecodeArgs), ia, 512, A, A, A, 128, 128, 0.04, A, None, None,
                         (ctypes.c_void_p * 4)())
