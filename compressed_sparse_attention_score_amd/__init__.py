@@ -16,14 +16,17 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libcsa2.so")
 
-CSA2_OK, CSA2_ERR_NULL, CSA2_ERR_SHAPE, CSA2_ERR_ALIGN, CSA2_ERR_WORKSPACE, CSA2_ERR_HIP, CSA2_ERR_ARG = range(7)
+CSA2_OK, CSA2_ERR_NULL, CSA2_ERR_SHAPE, CSA2_ERR_ALIGN, CSA2_ERR_WORKSPACE, CSA2_ERR_HIP, CSA2_ERR_ARG, \
+    CSA2_ERR_SCRATCH = range(8)
+CSA2_ATTN_SCRATCH_BYTES = 8454144
 CSA2_KIND_MAIN, CSA2_KIND_INDEX = 0, 1
 CSA2_OUT_F32, CSA2_OUT_BF16 = 0, 1
 CSA2_IN_F32, CSA2_IN_BF16 = 0, 1
 CSA2_SWA_BF16, CSA2_SWA_FP8 = 0, 1
 CSA2_WS_TOPK, CSA2_WS_ATTN, CSA2_WS_DECODE, CSA2_WS_POOL = 0, 1, 2, 3
 EXPORTED = ("csa2_dequant", "csa2_quantize", "csa2_pool_quantize", "csa2_build_pool", "csa2_gather_selected",
-            "csa2_index_score", "csa2_topk", "csa2_sparse_attn", "csa2_decode", "csa2_workspace_size",
+            "csa2_index_score", "csa2_topk", "csa2_sparse_attn", "csa2_sparse_attn_noalloc", "csa2_decode",
+            "csa2_workspace_size",
             "csa2_status_string", "csa2_version")
 
 _vp, _i32, _i64, _sz, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
@@ -73,6 +76,7 @@ def _load():
     L.csa2_gather_selected.argtypes = [_vp, _i64, _i64, _vp, _i32, _i32, _vp, _vp, _vp]
     L.csa2_topk.argtypes = [ctypes.POINTER(TopkArgs), _vp, _sz, _vp]
     L.csa2_sparse_attn.argtypes = [ctypes.POINTER(AttnArgs), _vp, _sz, _vp]
+    L.csa2_sparse_attn_noalloc.argtypes = [ctypes.POINTER(AttnArgs), _vp]
     L.csa2_decode.argtypes = [ctypes.POINTER(DecodeArgs), _vp, _sz, _vp]
     L.csa2_workspace_size.argtypes = [ctypes.c_int, _vp]
     L.csa2_workspace_size.restype = _sz
@@ -213,6 +217,10 @@ def csa2_sparse_attn(args: AttnArgs, workspace=None, stream=None, device="cuda")
     ws = workspace if workspace is not None else _alloc_ws(need, device)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check("csa2_sparse_attn", lib.csa2_sparse_attn(ctypes.byref(args), _ptr(ws), nbytes, _stream(stream)))
+
+
+def csa2_sparse_attn_noalloc(args: AttnArgs, stream=None) -> None:
+    _check("csa2_sparse_attn_noalloc", lib.csa2_sparse_attn_noalloc(ctypes.byref(args), _stream(stream)))
 
 
 def decode_args(index: IndexArgs, k, main_cache, q, swa, swa_q_stride, n_swa, softmax_scale, out, lse=None,

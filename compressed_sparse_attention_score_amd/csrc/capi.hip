@@ -4,9 +4,18 @@
 #include "csa2_internal.h"
 
 static_assert(CSA2_MAX_K == csa2::kMaxSelected, "on-chip selected-id capacity must match the ABI limit");
+static_assert(CSA2_ATTN_SCRATCH_BYTES == csa2::kAttnPartialMaxBytes, "static scratch must hold the largest partials");
+
+// Device scratch of csa2_sparse_attn_noalloc (the attention partials), one
+// copy per GPU, held until the process ends. Host code never uses this name
+// as an address: it passes the address hipGetSymbolAddress returns for the
+// current device (scratch_on_current_device below).
+static __device__ __align__(256) unsigned char scratch[CSA2_ATTN_SCRATCH_BYTES];
 
 #include <limits.h>
 #include <stdint.h>
+
+#include <atomic>
 
 using namespace csa2;
 
@@ -204,6 +213,25 @@ DecodeWs carve_decode(void* ws, const csa2_decode_args* a, int64_t n_cand) {
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
 
+// Address of `scratch` on the current device, looked up on the first call
+// there and kept per device (each GPU holds its own copy at its own address).
+constexpr int kMaxDevices = 64;
+std::atomic<uintptr_t> g_scratch_addr[kMaxDevices];
+
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CSA2_ERR_HIP;
+  uintptr_t p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == 0) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return CSA2_ERR_HIP;
+    p = (uintptr_t)ptr;
+    g_scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *out = (void*)p;
+  return CSA2_OK;
+}
+
 int check_ws(void* ws, size_t have, size_t need) {
   if (need == 0) return CSA2_OK;
   if (!ws || have < need) return CSA2_ERR_WORKSPACE;
@@ -215,7 +243,7 @@ int check_ws(void* ws, size_t have, size_t need) {
 
 extern "C" {
 
-int csa2_version(void) { return 100; }
+int csa2_version(void) { return 200; }
 
 const char* csa2_status_string(int s) {
   switch (s) {
@@ -226,6 +254,7 @@ const char* csa2_status_string(int s) {
     case CSA2_ERR_WORKSPACE: return "workspace missing or too small";
     case CSA2_ERR_HIP: return "HIP runtime or launch error";
     case CSA2_ERR_ARG: return "bad struct_size or enum value";
+    case CSA2_ERR_SCRATCH: return "call needs more than the library's static scratch";
     default: return "unknown status";
   }
 }
@@ -355,6 +384,26 @@ int csa2_sparse_attn(const csa2_attn_args* a, void* ws, size_t ws_bytes, void* s
                a->swa_q_stride, a->n_swa,  a->softmax_scale,  a->out,
                a->lse,   a->swa_format == CSA2_SWA_FP8, a->rope_cos_sin};
   return hip_status(launch_attn(L, ap, partial, s));
+}
+
+int csa2_sparse_attn_noalloc(const csa2_attn_args* a, void* stream) {
+  int st = check_attn(a);
+  if (st) return st;
+  if (a->n_queries == 0) return CSA2_OK;
+  const int Q = a->n_queries;
+  const size_t need = ws_attn(Q, a->k_sel, a->n_swa);
+  if (need > sizeof(scratch)) return CSA2_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_on_current_device(&ws);
+    if (st) return st;
+  }
+  AttnPlan ap = plan_attn(Q, a->k_sel, a->n_swa);
+  AttnLaunch L{Q,        a->n_entries,     a->cache_q_stride, a->main_cache,
+               a->idx,   a->k_sel,         a->q,              a->swa,
+               a->swa_q_stride, a->n_swa,  a->softmax_scale,  a->out,
+               a->lse,   a->swa_format == CSA2_SWA_FP8, a->rope_cos_sin};
+  return hip_status(launch_attn(L, ap, (float*)ws, (hipStream_t)stream));
 }
 
 int csa2_decode(const csa2_decode_args* a, void* ws, size_t ws_bytes, void* stream) {

@@ -49,6 +49,14 @@ struct AttnPlan {
 };
 AttnPlan plan_attn(int Q, int k_sel, int n_swa);
 
+// Attention split plan bounds: a split launch holds at most kAttnTargetWgs
+// (query, head block, range) workgroups, each writing one partial record of
+// kAttnPartialFloats floats, so no call's partials exceed
+// kAttnPartialMaxBytes.
+constexpr int kAttnTargetWgs = 512;
+constexpr size_t kAttnPartialFloats = 2 * 16 + 16 * 512 / 2;
+constexpr size_t kAttnPartialMaxBytes = (size_t)kAttnTargetWgs * kAttnPartialFloats * sizeof(float);
+
 hipError_t launch_dequant(int kind, const uint8_t* codes, const uint8_t* scales, int64_t n, int out_bf16, void* out,
                           hipStream_t s);
 

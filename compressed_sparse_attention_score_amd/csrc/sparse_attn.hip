@@ -70,9 +70,10 @@ constexpr int kSelReg = 16;
 // l, as bf16 (an average of value rows, so of the output's magnitude; one
 // bf16 rounding). Sized in floats.
 constexpr int kPartFloats = 2 * HEADS_WG + HEADS_WG * kDim / 2;
+static_assert(kPartFloats == (int)kAttnPartialFloats, "partial record size");
 // Workgroups a launch aims at (two per CU) when it splits slot ranges, and
 // the fewest tiles a split may hold.
-constexpr int kTargetWgs = 512;
+constexpr int kTargetWgs = kAttnTargetWgs;
 constexpr int kMinTilesPerSplit = 2;
 constexpr int kMaxSplits = 16;
 
@@ -581,6 +582,8 @@ AttnPlan plan_attn(int Q, int k_sel, int n_swa) {
 
 size_t attn_partial_bytes(int Q, const AttnPlan& plan) {
   if (plan.n_splits <= 1) return 0;
+  // a split launch has kHeadBlocks * Q * n_splits <= kTargetWgs workgroups,
+  // so this stays within kAttnPartialMaxBytes
   return (size_t)Q * kHeadBlocks * plan.n_splits * kPartFloats * sizeof(float);
 }
 

@@ -58,7 +58,8 @@ enum {
   CSA2_ERR_ALIGN = 3,     /* a pointer is not aligned as documented             */
   CSA2_ERR_WORKSPACE = 4, /* workspace NULL or smaller than csa2_workspace_size */
   CSA2_ERR_HIP = 5,       /* a HIP launch or runtime call failed                */
-  CSA2_ERR_ARG = 6        /* struct_size mismatch or bad enum value             */
+  CSA2_ERR_ARG = 6,       /* struct_size mismatch or bad enum value             */
+  CSA2_ERR_SCRATCH = 7    /* the call needs more than the library's static scratch */
 };
 
 /* Fixed shapes of the method ("An infra-oriented diagram ...", Reading notes). */
@@ -270,6 +271,23 @@ enum { CSA2_SWA_BF16 = 0, CSA2_SWA_FP8 = 1 };
  * the bf16 rounding; lse is unchanged. Workspace:
  * csa2_workspace_size(CSA2_WS_ATTN, args) bytes, 256-B aligned. */
 CSA2_API int csa2_sparse_attn(const csa2_attn_args* args, void* workspace, size_t ws_bytes, void* stream);
+
+/* csa2_sparse_attn_noalloc — csa2_sparse_attn for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same arguments, results and kernels, no workspace: the
+ * partial records of small batches (the only scratch csa2_sparse_attn uses)
+ * go to a device array the library holds on every GPU it runs on, of
+ * CSA2_ATTN_SCRATCH_BYTES, until the process ends. Any valid args fit in it
+ * (a split launch has at most 512 partial records of 16,512 B); a call that
+ * would need more returns CSA2_ERR_SCRATCH before any work is enqueued. The
+ * call allocates nothing; the array's address on the current device is
+ * looked up once per device (hipGetSymbolAddress) on the first call there,
+ * so the stream must belong to the current device. Calls that overlap on one
+ * GPU (several streams, or host threads) share the array and race; the array
+ * keeps the last call's contents, and every record a call reads it wrote
+ * itself. */
+#define CSA2_ATTN_SCRATCH_BYTES 8454144
+CSA2_API int csa2_sparse_attn_noalloc(const csa2_attn_args* args, void* stream);
 
 /* csa2_gather_selected — for the Reuse layers, which share the global KV and
  * the selected positions of an earlier layer ("DeepSeek V4.1 Flash: Why Its

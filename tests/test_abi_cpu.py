@@ -60,9 +60,9 @@ def test_struct_layout_matches_header(tmp_path):
 
 
 def test_status_strings_and_version():
-    assert csa.csa2_version() == 100
-    for s in range(7):
-        assert csa.csa2_status_string(s)
+    assert csa.csa2_version() == 200
+    for s in range(8):
+        assert csa.csa2_status_string(s) != "unknown status"
     assert csa.csa2_status_string(99) == "unknown status"
 
 
@@ -160,6 +160,7 @@ def test_validation_rejects_before_launch():
         bad = csa.AttnArgs.from_buffer_copy(aa)
         setattr(bad, field, value)
         assert L.csa2_sparse_attn(ctypes.byref(bad), A, 1 << 30, None) == code, field
+        assert L.csa2_sparse_attn_noalloc(ctypes.byref(bad), None) == code, field
     need = csa.csa2_workspace_size(csa.CSA2_WS_ATTN, aa)
     assert need > 0  # 4 queries split their slot list
     assert L.csa2_sparse_attn(ctypes.byref(aa), A, need - 1, None) == csa.CSA2_ERR_WORKSPACE
