@@ -41,7 +41,7 @@ SelectPlan plan_select(int64_t n_cand);
 
 // Attention layout: the joint list in 32-slot tiles (window rows and
 // selected latents tiled apart), split into n_splits ranges of
-// tiles_per_split tiles per (query, head block).
+// tiles_per_split tiles per query.
 struct AttnPlan {
   int n_tiles;
   int tiles_per_split;
@@ -50,11 +50,12 @@ struct AttnPlan {
 AttnPlan plan_attn(int Q, int k_sel, int n_swa);
 
 // Attention split plan bounds: a split launch holds at most kAttnTargetWgs
-// (query, head block, range) workgroups, each writing one partial record of
-// kAttnPartialFloats floats, so no call's partials exceed
-// kAttnPartialMaxBytes.
-constexpr int kAttnTargetWgs = 512;
-constexpr size_t kAttnPartialFloats = 2 * 16 + 16 * 512 / 2;
+// (query, range) pairs, each with one partial record of kAttnPartialFloats
+// floats (the 64 heads' maxima and sums, then their normalised outputs as
+// bf16, written by the pair's two head-half workgroups), so no call's
+// partials exceed kAttnPartialMaxBytes.
+constexpr int kAttnTargetWgs = 128;
+constexpr size_t kAttnPartialFloats = 2 * 64 + 64 * 512 / 2;
 constexpr size_t kAttnPartialMaxBytes = (size_t)kAttnTargetWgs * kAttnPartialFloats * sizeof(float);
 
 hipError_t launch_dequant(int kind, const uint8_t* codes, const uint8_t* scales, int64_t n, int out_bf16, void* out,

@@ -5,37 +5,40 @@
 // heads, serving as both key and value; each layer attends over the 128-token
 // window plus the 512 selected entries.
 //
-// Mapping: one workgroup of 4 waves = one query x one block of 16 heads x
-// one range of the joint slot list (the whole list for large batches; small
-// batches split it so that the launch fills the chip, and a second kernel
-// merges the (max, sum, O) partials). A query's workgroups are dispatched to
-// one XCD, whose L2 then serves the repeated reads of its latents. Window
-// rows come first (their bytes do not wait for the selection), then the
-// selected latents, in tiles of 32 slots of one kind. Per tile:
-//  * QK: wave w = (slot block sb = w/2, channel half ch = w%2) decodes its 16
-//    slots x 256 channels straight from the loaded bytes into MFMA operands
-//    (lane = slot, 8 channels per k-step) and forms the partial S^T[16 slots
-//    x 16 heads] with q for its channel half in registers. Latents decode to
-//    fp16: E2M1 times the power-of-two part of the E4M3 scale in one convert,
-//    then the scale's mantissa in one packed multiply (the product has at
-//    most 6 significant bits, so both steps are exact); q enters those
-//    products as fp16 times a per-head power of two that keeps it in fp16's
-//    range, taken back out of the logits. Window rows stay bf16 (exact). The
-//    decoded rows also go to LDS (one copy of the tile, swizzled) as the
-//    values, and the four partial sums are exchanged through LDS.
-//  * Softmax: every wave adds the four partial sums and runs the same online
-//    softmax for the 16 heads over the 32 slots, so P^T stays in registers
-//    in the layout the PV product takes (lane = head, slots 4g..4g+3 and
-//    16+4g..16+4g+3), with no exchange. The running maximum is a reference
-//    that moves only when a head's tile maximum exceeds it by more than 2^8
-//    (log2 units), so O is rescaled a handful of times per query.
-//  * PV: wave w owns channels 128w..128w+127: O^T[128 x 16] += V^T P^T, the
-//    V^T operand read from the row-major tile by gfx950's transposing LDS
-//    read (ds_read_b64_tr_b16: within each 16-lane group, lanes 4j..4j+3
-//    each point at 4 consecutive elements of row j and lane i receives
-//    element i of rows 0..3).
-//  * One barrier per tile: the LDS tile and the partial sums are double
-//    buffered; the bytes of the next four latent tiles are in flight.
+// Mapping: one workgroup of 4 waves = one query, one half of the 64 heads
+// (32), one range of the joint slot list (the whole list for large batches;
+// small batches split it so that the launch fills the chip, and a second
+// kernel merges the (max, sum, O) partials). Two workgroups share a CU (56
+// KB of LDS, at most 256 VGPRs each). Wave w owns channels 128w..128w+127
+// throughout. A query's workgroups are dispatched to one XCD, whose L2 then
+// serves the second head half's reads of each slot. Window rows come first
+// (their bytes do not wait for the selection), then the selected latents, in
+// tiles of 32 slots of one kind. Per tile, between two barriers:
+//  * QK: wave w decodes the 32 slots' channels 128w.. straight from the
+//    loaded bytes into MFMA operands (lane = slot, 8 channels per k-step;
+//    lane group g takes channels 128w+32g..+31, so each lane loads 16
+//    contiguous code bytes) and forms the partial S^T[32 slots x 32 heads]
+//    over its channels with q in registers (the same channel order).
+//    Latents decode to fp16: E2M1 times the power-of-two part of the E4M3
+//    scale in one convert, then the scale's mantissa in one packed multiply
+//    (the product has at most 6 significant bits, so both steps are exact);
+//    q enters those products as fp16 times a per-head power of two that
+//    keeps it in fp16's range, taken back out of the logits. Window rows stay
+//    bf16 (exact). The decoded values also go to LDS (the tile's rows,
+//    swizzled) as the values, and the partial sums go to LDS.
+//  * Softmax: two waves, one per block of 16 heads, add the four partial
+//    sums and run the online softmax for those heads over the 32 slots; P^T
+//    goes to LDS in the layout the PV product takes (lane = head, slots
+//    4g..4g+3 and 16+4g..16+4g+3). The running maximum is a reference that
+//    moves only when a head's tile maximum exceeds it by more than 2^8 (log2
+//    units), so O is rescaled a handful of times per query; the factor goes
+//    to LDS with P.
+//  * PV: wave w owns channels 128w..128w+127 of the 32 heads:
+//    O^T[128 x 32] += V^T P^T, the V^T operand read back from the rows it
+//    decoded itself by gfx950's transposing LDS read (ds_read_b64_tr_b16:
+//    within each 16-lane group, lanes 4j..4j+3 each point at 4 consecutive
+//    elements of row j and lane i receives element i of rows 0..3).
+// The bytes of the next two latent tiles are in flight meanwhile.
 // Window rows are bf16, or FP8 (MXFP8: 512 E4M3 codes + 16 E8M0 scales, 528
 // bytes, the pages' window entry size) decoded to bf16 like the latents. With
 // a RoPE table, the 64 rotary channels of the output are rotated back by each
@@ -52,9 +55,12 @@ namespace csa2 {
 namespace {
 constexpr int TILE = 32;
 constexpr int NT = 256;     // threads per workgroup (4 waves)
-constexpr int HEADS_WG = 16;
-constexpr int kHeadBlocks = kHeads / HEADS_WG;
+constexpr int kWaves = NT / 64;
+constexpr int kHalves = 2;                 // workgroups per (query, slot range)
+constexpr int kHeadsWg = kHeads / kHalves;  // heads per workgroup
+constexpr int kHB = kHeadsWg / 16;          // head blocks of 16 (two waves run their softmax)
 constexpr float kRescaleSlack = 8.f;  // log2 units
+constexpr float kRefFloor = -0x1p126f;  // initial reference max (log2 units)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -65,17 +71,17 @@ constexpr int kRopeFirst = 448;  // first rotary channel; pairs (448+2i, 449+2i)
 // chunk keeps a few dozen survivors at most for random scores; more take the
 // offset-table or streaming path).
 constexpr int kSelReg = 16;
-// Partial record of one (query, head block, slot range): reference max m[16]
-// and sum l[16] (log2 units), then O[16][512] normalised by the range's own
-// l, as bf16 (an average of value rows, so of the output's magnitude; one
-// bf16 rounding). Sized in floats.
-constexpr int kPartFloats = 2 * HEADS_WG + HEADS_WG * kDim / 2;
+// Partial record of one (query, slot range): reference max m[64] and sum
+// l[64] (log2 units), then O[64][512] normalised by the range's own l, as
+// bf16 (an average of value rows, so of the output's magnitude; one bf16
+// rounding). Sized in floats.
+constexpr int kPartFloats = 2 * kHeads + kHeads * kDim / 2;
 static_assert(kPartFloats == (int)kAttnPartialFloats, "partial record size");
-// Workgroups a launch aims at (two per CU) when it splits slot ranges, and
-// the fewest tiles a split may hold.
+// Slot ranges a launch aims at (two workgroups each, one per CU) when it
+// splits the list, the fewest tiles a range may hold, and the most ranges.
 constexpr int kTargetWgs = kAttnTargetWgs;
 constexpr int kMinTilesPerSplit = 2;
-constexpr int kMaxSplits = 16;
+constexpr int kMaxSplits = 32;
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
@@ -92,14 +98,14 @@ struct AttnArgs {
   const float* rope;     // [Q][32][2] (cos, sin) or nullptr
   uint16_t* out;
   float* lse;
-  float* partial;        // [Q][4][n_split][kPartFloats] when n_split > 1
+  float* partial;        // [Q][n_split][kPartFloats] when n_split > 1
   // Selection finished here (decode): chunk c of query q's compacted list
   // holds sel_counts[q][c] composites from sel_cand[q][c*sel_chunk] on.
   const unsigned* sel_counts;
   const unsigned long long* sel_cand;
   int64_t sel_n_cand;
   int sel_chunks, sel_chunk;
-  int32_t* idx_out;  // selected ids [Q][k_sel] (written by head block 0), or nullptr
+  int32_t* idx_out;  // selected ids [Q][k_sel], or nullptr
   int64_t n_entries, cache_q_stride, swa_q_stride;
   int Q, k_sel, n_swa, n_split, tps;
   float scale_log2;
@@ -107,33 +113,40 @@ struct AttnArgs {
 
 struct AttnShared {
   union {
-    uint16_t v[2][TILE * kDim];  // the tile's rows (16-bit), double-buffered, swizzled (v_offset)
-    SelScratch<NT> sel;          // prologue: finishing the selection
+    uint16_t v[TILE * kDim];  // the tile's rows (16-bit), swizzled (v_offset)
+    SelScratch<NT> sel;       // prologue: finishing the selection
   };
-  v4f sx[2][2][2][64];           // partial S^T: [buffer][slot block][channel half][lane]
-  unsigned char ok[2][TILE];     // slot validity per tile (double-buffered)
-  unsigned qmax[2][HEADS_WG];    // per channel half, each head's largest |q| (bf16 bits)
-  int32_t ids[kMaxSelected];     // the query's selected ids (by list position)
+  v4f sx[kWaves][kHB][2][64];   // partial S^T: [channel quarter][head block][slot block][lane]
+  v4u px[kHB][64];              // P^T operands: [head block][lane]
+  float alpha[kHB][16];         // O rescale factor per head (1 when unchanged)
+  unsigned resc[kHB];           // nonzero when some head of the block rescales
+  alignas(16) float mask[TILE];  // per slot of the tile: 0 (valid) or -inf, added to its logits
+  unsigned qmax[kWaves][kHeadsWg];  // per channel quarter, each head's largest |q| (bf16 bits)
+  float ml[2][kHeadsWg];        // end: each head's reference max and sum
+  int32_t ids[kMaxSelected];    // the query's selected ids (by list position)
 };
 
-// Raw bytes of this lane's slot (16 slots x 4 lane groups per wave) for its
-// 256-channel half, as loaded. A selected latent: its 32 code bytes and 4
-// E4M3 scale bytes. A window row: its 64 bf16 channels (FP8 rows: 64 codes
-// in w[0..3] and the two E8M0 scale bytes in s). ok: the slot holds a valid
-// latent or window row.
+// Raw bytes of this lane's two slots (tile slots r16 and 16 + r16) for its 32
+// channels 128w+32g.., as loaded. A selected latent: 16 code bytes and 2 E4M3
+// scale bytes per slot. A window row: 64 bytes of bf16 per slot (FP8 rows: 32
+// code bytes in w.[0..1] and the E8M0 scale bytes in s0, s1). ok: the slot holds a
+// valid latent or window row.
+// Each loaded value stays in a register of its own until it is decoded: a
+// value combined from two loads right away would make the compiler wait for
+// the newest loads there, and the tiles in flight would gain nothing.
 struct RawLat {
   v4u c0, c1;
-  unsigned s;
-  bool ok;
+  unsigned s0, s1;  // scale dwords of slot r16, of slot 16 + r16 (the lane's two bytes at 16*(g&1))
+  bool ok0, ok1;
 };
 struct RawWin {
-  v4u w[8];
-  unsigned s;
-  bool ok;
+  v4u w0[4], w1[4];
+  unsigned s0, s1;
+  bool ok0, ok1;
 };
 // Latent tiles whose bytes are in flight ahead of the one being processed
 // (register ring; the loop is unrolled by this so every index is static).
-constexpr int kRing = 4;
+constexpr int kRing = 2;
 }  // namespace
 
 // Element offset of (slot, channel) in a tile: rows of 512 channels; the
@@ -145,73 +158,104 @@ __device__ __forceinline__ int v_offset(int s, int c) {
   return s * kDim + ((2 * ((c >> 4) ^ (s & 7)) + (((c >> 3) & 1) ^ ((s >> 3) & 1))) << 3) + (c & 7);
 }
 
-// Selected latent at list position `slot` (none past k_sel), channels
-// 256*ch + 64*g .. +63.
-__device__ __forceinline__ void load_latent(const AttnArgs& a, const AttnShared& sh, int q, int slot, int ch, int g,
-                                            RawLat& r) {
-  const int e = slot < a.k_sel ? sh.ids[slot] : -1;
-  r.ok = e >= 0 && (int64_t)e < a.n_entries;
-  const uint8_t* ent = a.main_cache + ((int64_t)q * a.cache_q_stride + (r.ok ? e : 0)) * kMainBytes;
-  r.c0 = *(const v4u*)(ent + 128 * ch + 32 * g);
-  r.c1 = *(const v4u*)(ent + 128 * ch + 32 * g + 16);
-  r.s = *(const unsigned*)(ent + 256 + 16 * ch + 4 * g);
+// Selected latents at list positions tile*32 + r16 and +16 (none past
+// k_sel), channels 128w + 32g .. +31.
+__device__ __forceinline__ void load_latent(const AttnArgs& a, const AttnShared& sh, int q, int tile, int w, int g,
+                                            int r16, RawLat& r) {
+  const int s0 = tile * TILE + r16, s1 = s0 + 16;
+  const int e0 = s0 < a.k_sel ? sh.ids[s0] : -1;
+  const int e1 = s1 < a.k_sel ? sh.ids[s1] : -1;
+  r.ok0 = e0 >= 0 && (int64_t)e0 < a.n_entries;
+  r.ok1 = e1 >= 0 && (int64_t)e1 < a.n_entries;
+  const int64_t base = (int64_t)q * a.cache_q_stride;
+  const uint8_t* p0 = a.main_cache + (base + (r.ok0 ? e0 : 0)) * kMainBytes;
+  const uint8_t* p1 = a.main_cache + (base + (r.ok1 ? e1 : 0)) * kMainBytes;
+  r.c0 = *(const v4u*)(p0 + 64 * w + 16 * g);
+  r.c1 = *(const v4u*)(p1 + 64 * w + 16 * g);
+  // whole aligned dwords (two 16-bit loads could share a register, and
+  // then neither could be used before both arrived)
+  r.s0 = *(const unsigned*)(p0 + 256 + 8 * w + 4 * (g >> 1));
+  r.s1 = *(const unsigned*)(p1 + 256 + 8 * w + 4 * (g >> 1));
 }
 
-// Window row j (valid when j < n_swa), channels 256*ch + 64*g .. +63.
+// Window rows tile*32 + r16 and +16 (valid below n_swa), channels
+// 128w + 32g .. +31.
 template <bool SWA8>
-__device__ __forceinline__ void load_window(const AttnArgs& a, int q, int j, int ch, int g, RawWin& r) {
-  r.ok = j < a.n_swa;
-  const int64_t row = (int64_t)q * a.swa_q_stride + (r.ok ? j : 0);
+__device__ __forceinline__ void load_window(const AttnArgs& a, int q, int tile, int w, int g, int r16, RawWin& r) {
+  const int j0 = tile * TILE + r16, j1 = j0 + 16;
+  r.ok0 = j0 < a.n_swa;
+  r.ok1 = j1 < a.n_swa;
+  const int64_t row0 = (int64_t)q * a.swa_q_stride + (r.ok0 ? j0 : 0);
+  const int64_t row1 = (int64_t)q * a.swa_q_stride + (r.ok1 ? j1 : 0);
   if (SWA8) {
-    const uint8_t* p = a.swa8 + row * kSwa8Bytes;
+    const uint8_t* p0 = a.swa8 + row0 * kSwa8Bytes;
+    const uint8_t* p1 = a.swa8 + row1 * kSwa8Bytes;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.w[i] = *(const v4u*)(p + 256 * ch + 64 * g + 16 * i);
-    r.s = *(const unsigned short*)(p + 512 + 8 * ch + 2 * g);
+    for (int i = 0; i < 2; ++i) {
+      r.w0[i] = *(const v4u*)(p0 + 128 * w + 32 * g + 16 * i);
+      r.w1[i] = *(const v4u*)(p1 + 128 * w + 32 * g + 16 * i);
+    }
+    r.s0 = p0[512 + 4 * w + g];
+    r.s1 = p1[512 + 4 * w + g];
   } else {
-    const uint16_t* p = a.swa + row * kDim + 256 * ch + 64 * g;
+    const uint16_t* p0 = a.swa + row0 * kDim + 128 * w + 32 * g;
+    const uint16_t* p1 = a.swa + row1 * kDim + 128 * w + 32 * g;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r.w[i] = *(const v4u*)(p + 8 * i);
+    for (int i = 0; i < 4; ++i) {
+      r.w0[i] = *(const v4u*)(p0 + 8 * i);
+      r.w1[i] = *(const v4u*)(p1 + 8 * i);
+    }
   }
 }
 
-// k-step ks (channels 256*ch + 64*g + 8*ks .. +7) of a latent as fp16:
-// E2M1 x 2^E by the scaled convert, times the E4M3 scale's mantissa m in
-// [1, 2) by one packed multiply (scale = 2^E m; both steps exact). An
-// invalid slot takes scale byte 0, an integer select, so that no branch
-// separates the loads from their uses; its bytes may be anything, and the
-// zero scale gives zeros.
-__device__ __forceinline__ v4u decode_latent(const RawLat& r, int ks) {
-  const unsigned sbyte = r.ok ? (r.s >> (8 * (ks >> 1))) & 0xFFu : 0u;
+// E4M3 scale byte -> (power-of-two part as f32, mantissa in [1, 2) as an
+// fp16 pair). Byte 0 (taken for an invalid slot, an integer select, so that
+// no branch separates the loads from their uses) gives zero, so that slot's
+// codes, whatever they are, decode to zeros.
+struct LatScale {
+  float p2;
+  v2h m2;
+};
+__device__ __forceinline__ LatScale lat_scale(unsigned sbyte) {
   const unsigned sb = __float_as_uint(e4m3_to_f32_hw(sbyte));
-  const float p2 = __uint_as_float(sb & 0x7F800000u);
+  LatScale s;
+  s.p2 = __uint_as_float(sb & 0x7F800000u);
   const _Float16 mh = (_Float16)__uint_as_float((sb & 0x007FFFFFu) | 0x3F800000u);
-  const v2h m2 = {mh, mh};
-  const unsigned w = (ks < 4) ? r.c0[ks] : r.c1[ks - 4];
+  s.m2 = v2h{mh, mh};
+  return s;
+}
+
+// One k-step (8 channels, one code dword) of a latent as fp16: E2M1 x 2^E by
+// the scaled convert, times the E4M3 scale's mantissa m by one packed
+// multiply (scale = 2^E m; both steps exact).
+__device__ __forceinline__ v4u decode_latent(unsigned w, const LatScale& s) {
   v2h h[4];
-  h[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 0) * m2;
-  h[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 1) * m2;
-  h[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 2) * m2;
-  h[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 3) * m2;
+  h[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.p2, 0) * s.m2;
+  h[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.p2, 1) * s.m2;
+  h[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.p2, 2) * s.m2;
+  h[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.p2, 3) * s.m2;
   return v4u{__builtin_bit_cast(unsigned, h[0]), __builtin_bit_cast(unsigned, h[1]), __builtin_bit_cast(unsigned, h[2]),
              __builtin_bit_cast(unsigned, h[3])};
 }
 
-// The same for a window row, as bf16: passed through, or E4M3 x
-// 2^(E8M0-127) (FP8), exact while it stays a normal bf16.
+// k-step ks of a window row (slot block sb) as bf16: passed through, or
+// E4M3 x 2^(E8M0-127) (FP8), exact while it stays a normal bf16.
 template <bool SWA8>
-__device__ __forceinline__ v4u decode_window(const RawWin& r, int ks) {
+__device__ __forceinline__ v4u decode_window(const RawWin& r, int sb, int ks) {
+  const v4u* wv = sb ? r.w1 : r.w0;
+  const bool ok = sb ? r.ok1 : r.ok0;
   v4u out;
   if (SWA8) {
-    const float ws = e8m0_to_f32((r.s >> (8 * (ks >> 2))) & 0xFFu);
-    const unsigned c0 = r.w[ks >> 1][2 * (ks & 1)], c1 = r.w[ks >> 1][2 * (ks & 1) + 1];
+    const float ws = e8m0_to_f32(sb ? r.s1 : r.s0);
+    const unsigned c0 = wv[ks >> 1][2 * (ks & 1)], c1 = wv[ks >> 1][2 * (ks & 1) + 1];
     const v2f v[4] = {__builtin_amdgcn_cvt_pk_f32_fp8((int)c0, false), __builtin_amdgcn_cvt_pk_f32_fp8((int)c0, true),
                       __builtin_amdgcn_cvt_pk_f32_fp8((int)c1, false), __builtin_amdgcn_cvt_pk_f32_fp8((int)c1, true)};
 #pragma unroll
     for (int j = 0; j < 4; ++j) out[j] = pack_bf16x2_exact(v[j].x * ws, v[j].y * ws);
   } else {
-    out = r.w[ks];
+    out = wv[ks];
   }
-  return r.ok ? out : v4u{0u, 0u, 0u, 0u};
+  return ok ? out : v4u{0u, 0u, 0u, 0u};
 }
 
 // Channels (a, b) of one rotary pair rotated back by the angle whose cosine
@@ -228,21 +272,26 @@ __device__ __forceinline__ unsigned bf16x2_to_f16x2(unsigned u, float f) {
   return __builtin_bit_cast(unsigned, h);
 }
 
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  return (unsigned)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((unsigned)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+}
+
 template <bool SWA8, bool FUSED>
 __global__ __launch_bounds__(NT, 2) void k_sparse_attn(AttnArgs a) {
-  // workgroup -> (query, head block, slot range): the workgroups of a query
-  // are 8 ids apart, so they land on one XCD
-  const int per_q = kHeadBlocks * a.n_split;
+  // workgroup -> (query, slot range, head half): the workgroups of a query
+  // are 8 ids apart, so they land on one XCD, whose L2 serves both head
+  // halves' reads of each latent
+  const int ns = a.n_split;
+  const int per_q = kHalves * ns;
   const int lin = blockIdx.x;
   const int q = ((lin / (8 * per_q)) << 3) | (lin & 7);
   const int w_in = (lin >> 3) % per_q;
-  const int hb = w_in / a.n_split, split = w_in - hb * a.n_split;
+  const int split = w_in >> 1, hh = w_in & 1;
   if (q >= a.Q) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
-  const int sb = wave >> 1, ch = wave & 1;  // QK role
-  const int cq = wave;                      // PV role: channels 128*cq ..
-  const int my_slot = 16 * sb + r16;        // QK role: this lane's slot within a tile
+  const int h0 = kHeadsWg * hh;  // first head of this workgroup
 
   __shared__ AttnShared sh;
 
@@ -253,28 +302,32 @@ __global__ __launch_bounds__(NT, 2) void k_sparse_attn(AttnArgs a) {
   const int w0 = min(T0, n_wt), w1 = min(T1, n_wt);
   const int l0 = max(T0, n_wt) - n_wt, l1 = max(T1, n_wt) - n_wt;
 
-  // q^T operand: head 16*hb + r16, channels 256*ch + 64*g + 8*ks .. +7
-  v8bf qf[8];
+  // q^T operands: head h0 + 16*hb + r16, channels 128w + 32g + 8ks .. +7
+  // (bf16 while the window tiles run, then fp16 scaled)
+  v4u qr[kHB][4];
   {
-    const uint16_t* qrow = a.q + ((int64_t)q * kHeads + HEADS_WG * hb + r16) * kDim + 256 * ch + 64 * g;
+    const uint16_t* qrow = a.q + ((int64_t)q * kHeads + h0 + r16) * kDim + 128 * w + 32 * g;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = __builtin_bit_cast(v8bf, *(const v4u*)(qrow + 8 * ks));
+    for (int hb = 0; hb < kHB; ++hb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qr[hb][ks] = *(const v4u*)(qrow + (int64_t)16 * hb * kDim + 8 * ks);
   }
   RawWin rwA, rwB;
-  if (w1 > w0) load_window<SWA8>(a, q, w0 * TILE + my_slot, ch, g, rwA);
-  if (w1 > w0 + 1) load_window<SWA8>(a, q, (w0 + 1) * TILE + my_slot, ch, g, rwB);
-  // this lane's largest |q| (bf16 magnitude bits order like the values),
-  // over the 4 lane groups, then the two channel halves through LDS
-  unsigned qm = 0u;
+  if (w1 > w0) load_window<SWA8>(a, q, w0, w, g, r16, rwA);
+  if (w1 > w0 + 1) load_window<SWA8>(a, q, w0 + 1, w, g, r16, rwB);
+  // each head's largest |q| over this wave's channels (bf16 magnitude bits
+  // order like the values): the lane's 32, then over the 4 lane groups
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    const v4u u = __builtin_bit_cast(v4u, qf[ks]);
+  for (int hb = 0; hb < kHB; ++hb) {
+    unsigned qm = 0u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) qm = max(qm, max(u[j] & 0x7FFFu, (u[j] >> 16) & 0x7FFFu));
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qm = max(qm, max(qr[hb][ks][j] & 0x7FFFu, (qr[hb][ks][j] >> 16) & 0x7FFFu));
+    qm = umax_xor16(qm);
+    qm = umax_xor32(qm);
+    if (g == 0) sh.qmax[w][16 * hb + r16] = qm;
   }
-  qm = umax_xor16(qm);
-  qm = umax_xor32(qm);
-  if (sb == 0 && g == 0) sh.qmax[ch][r16] = qm;
 
   // The selected ids of this workgroup's latent tiles, into LDS: read from
   // the id list, or (FUSED) taken from the exact selection over the query's
@@ -283,7 +336,7 @@ __global__ __launch_bounds__(NT, 2) void k_sparse_attn(AttnArgs a) {
   const int sbeg = l0 * TILE, send = min(l1 * TILE, a.k_sel);
   if (FUSED) {
     if (sbeg < send) {  // uniform over the workgroup
-      int32_t* io = (a.idx_out && hb == 0) ? a.idx_out + (int64_t)q * a.k_sel : nullptr;
+      int32_t* io = (a.idx_out && hh == 0) ? a.idx_out + (int64_t)q * a.k_sel : nullptr;
       select_from_regions<NT, kSelReg>(a.sel_counts + (int64_t)q * a.sel_chunks, a.sel_chunks, a.sel_chunk,
                                        a.sel_n_cand, a.k_sel, a.sel_cand + (int64_t)q * a.sel_n_cand, sh.sel, sbeg,
                                        send, [&](unsigned pos, unsigned long long x) {
@@ -296,102 +349,116 @@ __global__ __launch_bounds__(NT, 2) void k_sparse_attn(AttnArgs a) {
     for (int sl = sbeg + tid; sl < send; sl += NT) sh.ids[sl] = a.idx[(int64_t)q * a.k_sel + sl];
   }
   __syncthreads();  // ids and q maxima in LDS; the selection scratch (over the tile area) is free
-  RawLat ring[kRing];
-#pragma unroll
-  for (int j = 0; j < kRing; ++j) load_latent(a, sh, q, (l0 + j) * TILE + my_slot, ch, g, ring[j]);
 
   // q scaled into fp16's range for the latent products: 2^k with the head's
   // largest |q| times 2^k in [2^14, 2^15) (k clamped to +-100); logits of
-  // latent tiles are multiplied back by 2^-k. lane (head r16, g): its head.
-  const unsigned qmh = max(sh.qmax[0][r16], sh.qmax[1][r16]);
-  const int qe = (qmh == 0u) ? 127 : (int)(qmh >> 7);  // bf16 biased exponent
-  const int k2 = min(100, max(-100, 14 - (qe - 127)));
-  const float qscale = __uint_as_float((unsigned)(k2 + 127) << 23);
-  const float lat_log2 = a.scale_log2 * __uint_as_float((unsigned)(127 - k2) << 23);
-  // (formed when the first latent tile comes, so that the bf16 and fp16
-  // copies of q are not both held through the window tiles)
-  v8h qh[8];
-  auto make_qh = [&]() {
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const v4u u = __builtin_bit_cast(v4u, qf[ks]);
-      qh[ks] = __builtin_bit_cast(v8h, v4u{bf16x2_to_f16x2(u[0], qscale), bf16x2_to_f16x2(u[1], qscale),
-                                           bf16x2_to_f16x2(u[2], qscale), bf16x2_to_f16x2(u[3], qscale)});
-    }
+  // latent tiles are multiplied back by 2^-k. (h: head within the workgroup)
+  auto head_k2 = [&](int h) {
+    const unsigned qmh = max(max(sh.qmax[0][h], sh.qmax[1][h]), max(sh.qmax[2][h], sh.qmax[3][h]));
+    const int qe = (qmh == 0u) ? 127 : (int)(qmh >> 7);  // bf16 biased exponent
+    return min(100, max(-100, 14 - (qe - 127)));
   };
+  // softmax role: head block shb = w - 2*hh (waves 0 and 1 in the first
+  // head half, 2 and 3 in the second, so that two workgroups of different
+  // halves on one CU load its four SIMDs evenly), head h0 + 16*shb + r16
+  const int shb = w - kHB * hh;
+  const bool smax = (unsigned)shb < (unsigned)kHB;
+  const float lat_log2 = a.scale_log2 * __uint_as_float((unsigned)(127 - head_k2((16 * shb + r16) & 31)) << 23);
 
-  // O^T accumulators: channels 128*cq + 16*cb + 4*g + j, head 16*hb + r16
-  v4f o[8];
+  // O^T accumulators: channels 128w + 16cb + 4g + j, head h0 + 16hb + r16
+  v4f o[kHB][8];
 #pragma unroll
-  for (int cb = 0; cb < 8; ++cb) o[cb] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -__builtin_inff(), l_run = 0.f;
+  for (int hb = 0; hb < kHB; ++hb)
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) o[hb][cb] = v4f{0.f, 0.f, 0.f, 0.f};
+  // softmax role: reference max (log2 units; a finite floor below any
+  // logit until the first valid slot, so that no -inf - -inf arises) and sum
+  float m_ref = kRefFloor, l_run = 0.f;
 
   // transposing-read addresses (element offsets, cb = 0) of the PV operand:
   // lanes 4j..4j+3 of a 16-lane group point at row 4*g + j (then 16 + 4*g + j)
-  // and channels 128*cq + 4*(lane & 3) ..
-  const int tr_row = 4 * g + ((lane & 15) >> 2), tr_c = 128 * cq + 4 * (lane & 3);
+  // and channels 128w + 4*(lane & 3) ..
+  const int tr_row = 4 * g + ((lane & 15) >> 2), tr_c = 128 * w + 4 * (lane & 3);
 
-  // The n-th tile of this workgroup uses LDS buffer n & 1. qk(): the tile's
-  // QK with the k-step operands from `kstep` (fp16 latents or bf16 window
-  // rows), its rows to LDS, the partial sums and slot flags; sv(): after
-  // the barrier that follows qk(), the softmax and PV in the same type. The
-  // latent loop is software-pipelined: qk() of tile n+1 comes before sv() of
-  // tile n, so the decoding and matrix products of the next tile overlap the
-  // softmax and value products of this one; one barrier per tile (buffers
-  // n & 1 are next written by qk() of tile n+2, after the barrier that ends
-  // sv() of tile n in every wave).
+  // Per tile, between two barriers:
+  //  qk: decode + partial S^T of this wave's channels -> sx, rows -> v
+  //  softmax (two waves): head block shb over the tile -> px, alpha, resc
+  //  pv: O rescale (when flagged) and O += V^T P^T
+  // Each buffer is single: a wave rewrites its own rows of v only after its
+  // pv has read them, sx only after the barrier that ends every softmax
+  // read, and px, alpha, resc and ok are rewritten only after the barrier
+  // that follows every wave's pv.
   using Bf16Tag = std::integral_constant<bool, false>;
   using F16Tag = std::integral_constant<bool, true>;
-  auto qk = [&](int n, bool ok, auto f16_tag, auto&& kstep) {
+  auto qk = [&](bool ok0, bool ok1, auto f16_tag, auto&& kstep) {
     constexpr bool F16 = decltype(f16_tag)::value;
-    const int b = n & 1;
-    v4f s = v4f{0.f, 0.f, 0.f, 0.f};
-    uint16_t* vb = sh.v[b];
+    v4f s[2][kHB];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const v4u kf = kstep(ks);
-      *(v4u*)(vb + v_offset(my_slot, 256 * ch + 64 * g + 8 * ks)) = kf;
-      if constexpr (F16)
-        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, kf), qh[ks], s, 0, 0, 0);
-      else
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, kf), qf[ks], s, 0, 0, 0);
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int hb = 0; hb < kHB; ++hb) s[sb][hb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const v4u kf = kstep(sb, ks);
+        *(v4u*)(sh.v + v_offset(16 * sb + r16, 128 * w + 32 * g + 8 * ks)) = kf;
+#pragma unroll
+        for (int hb = 0; hb < kHB; ++hb) {
+          if constexpr (F16)
+            s[sb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, kf),
+                                                               __builtin_bit_cast(v8h, qr[hb][ks]), s[sb][hb], 0, 0, 0);
+          else
+            s[sb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(v8bf, kf), __builtin_bit_cast(v8bf, qr[hb][ks]), s[sb][hb], 0, 0, 0);
+        }
+      }
     }
-    sh.sx[b][sb][ch][lane] = s;
-    if (ch == 0 && g == 0) sh.ok[b][my_slot] = ok ? 1 : 0;
+#pragma unroll
+    for (int hb = 0; hb < kHB; ++hb)
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) sh.sx[w][hb][sb][lane] = s[sb][hb];
+    if (w == 0 && g == 0) {
+      sh.mask[r16] = ok0 ? 0.f : -__builtin_inff();
+      sh.mask[16 + r16] = ok1 ? 0.f : -__builtin_inff();
+    }
   };
-  auto sv = [&](int n, auto f16_tag) {
+  auto softmax = [&](auto f16_tag) {
     constexpr bool F16 = decltype(f16_tag)::value;
-    const int b = n & 1;
-    const uint16_t* vb = sh.v[b];
-    // softmax of the 16 heads over the tile (same in every wave): lane
-    // (head r16, g) holds slots 4g..4g+3 and 16+4g..16+4g+3
+    // lane (head h0 + 16*shb + r16, g) holds slots 4g..4g+3 and 16+4g..16+4g+3
     const float sl2 = F16 ? lat_log2 : a.scale_log2;
-    const v4f s0 = sh.sx[b][0][0][lane] + sh.sx[b][0][1][lane];
-    const v4f s1 = sh.sx[b][1][0][lane] + sh.sx[b][1][1][lane];
-    const unsigned ok0 = *(const unsigned*)&sh.ok[b][4 * g], ok1 = *(const unsigned*)&sh.ok[b][16 + 4 * g];
+    v4f s0 = sh.sx[0][shb][0][lane], s1 = sh.sx[0][shb][1][lane];
+#pragma unroll
+    for (int c = 1; c < kWaves; ++c) {
+      s0 += sh.sx[c][shb][0][lane];
+      s1 += sh.sx[c][shb][1][lane];
+    }
+    const v4f mk0 = *(const v4f*)&sh.mask[4 * g], mk1 = *(const v4f*)&sh.mask[16 + 4 * g];
     float x[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      x[j] = ((ok0 >> (8 * j)) & 1u) ? s0[j] * sl2 : -__builtin_inff();
-      x[4 + j] = ((ok1 >> (8 * j)) & 1u) ? s1[j] * sl2 : -__builtin_inff();
+      x[j] = fmaf(s0[j], sl2, mk0[j]);
+      x[4 + j] = fmaf(s1[j], sl2, mk1[j]);
     }
     float mt = x[0];
 #pragma unroll
     for (int j = 1; j < 8; ++j) mt = fmaxf(mt, x[j]);
     mt = max_xor16(mt);
     mt = max_xor32(mt);
-    if (mt > m_ref + kRescaleSlack) {  // also true when m_ref = -inf and mt is finite
-      const float al = (m_ref == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(m_ref - mt);
+    // the reference moves (also from the floor, when the first valid slot
+    // comes): O and l are scaled by al, 0 from the floor (both are still 0
+    // then)
+    const bool moved = mt > m_ref + kRescaleSlack;
+    float al = 1.f;
+    if (moved) {
+      al = __builtin_amdgcn_exp2f(m_ref - mt);
       l_run *= al;
       m_ref = mt;
-#pragma unroll
-      for (int cb = 0; cb < 8; ++cb) o[cb] *= al;
     }
-    const bool live = m_ref != -__builtin_inff();
     float p[8], ps = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      p[j] = live ? __builtin_amdgcn_exp2f(x[j] - m_ref) : 0.f;
+      p[j] = __builtin_amdgcn_exp2f(x[j] - m_ref);
       ps += p[j];
     }
     ps = add_xor16(ps);
@@ -403,112 +470,175 @@ __global__ __launch_bounds__(NT, 2) void k_sparse_attn(AttnArgs a) {
       if constexpr (F16)
         pk[j] = __builtin_bit_cast(unsigned, v2h{(_Float16)p[2 * j], (_Float16)p[2 * j + 1]});
       else
-        pk[j] = (unsigned)__builtin_bit_cast(uint16_t, (__bf16)p[2 * j]) |
-                ((unsigned)__builtin_bit_cast(uint16_t, (__bf16)p[2 * j + 1]) << 16);
+        pk[j] = pack_bf16x2(p[2 * j], p[2 * j + 1]);
     }
-    // PV: O^T[128 channels x 16 heads] += V^T P^T
+    sh.px[shb][lane] = pk;
+    if (g == 0) sh.alpha[shb][r16] = al;
+    const bool any = __builtin_amdgcn_ballot_w64(moved) != 0ull;
+    if (lane == 0) sh.resc[shb] = any ? 1u : 0u;
+  };
+  auto pv = [&](auto f16_tag) {
+    constexpr bool F16 = decltype(f16_tag)::value;
+#pragma unroll
+    for (int hb = 0; hb < kHB; ++hb) {
+      if (__builtin_amdgcn_readfirstlane(sh.resc[hb])) {
+        const float al = sh.alpha[hb][r16];
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) o[hb][cb] *= al;
+      }
+    }
+    v4u pk[kHB];
+#pragma unroll
+    for (int hb = 0; hb < kHB; ++hb) pk[hb] = sh.px[hb][lane];
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) {
-      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vb + v_offset(tr_row, tr_c + 16 * cb)));
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(sh.v + v_offset(tr_row, tr_c + 16 * cb)));
       const v4s hi =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vb + v_offset(16 + tr_row, tr_c + 16 * cb)));
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(sh.v + v_offset(16 + tr_row, tr_c + 16 * cb)));
       const auto vt = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      if constexpr (F16)
-        o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, vt), __builtin_bit_cast(v8h, pk), o[cb],
-                                                        0, 0, 0);
-      else
-        o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, vt), __builtin_bit_cast(v8bf, pk),
-                                                         o[cb], 0, 0, 0);
+#pragma unroll
+      for (int hb = 0; hb < kHB; ++hb) {
+        if constexpr (F16)
+          o[hb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, vt),
+                                                             __builtin_bit_cast(v8h, pk[hb]), o[hb][cb], 0, 0, 0);
+        else
+          o[hb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, vt),
+                                                              __builtin_bit_cast(v8bf, pk[hb]), o[hb][cb], 0, 0, 0);
+      }
     }
   };
-  auto qk_win = [&](int n, const RawWin& r) {
-    qk(n, r.ok, Bf16Tag{}, [&](int ks) { return decode_window<SWA8>(r, ks); });
+  auto rest = [&](auto f16_tag) {  // after qk: the two barriers, softmax and pv
+    __syncthreads();
+    if (smax) softmax(f16_tag);
+    __syncthreads();
+    pv(f16_tag);
   };
-  auto qk_lat = [&](int n, const RawLat& r) {
-    qk(n, r.ok, F16Tag{}, [&](int ks) { return decode_latent(r, ks); });
+  auto qk_win = [&](const RawWin& r) {
+    qk(r.ok0, r.ok1, Bf16Tag{}, [&](int sb, int ks) { return decode_window<SWA8>(r, sb, ks); });
+  };
+  auto qk_lat = [&](const RawLat& r) {
+    LatScale ls[2][2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const bool ok = sb ? r.ok1 : r.ok0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) ls[sb][h] = lat_scale(ok ? ((sb ? r.s1 : r.s0) >> (16 * (g & 1) + 8 * h)) & 0xFFu : 0u);
+    }
+    qk(r.ok0, r.ok1, F16Tag{}, [&](int sb, int ks) { return decode_latent(sb ? r.c1[ks] : r.c0[ks], ls[sb][ks >> 1]); });
   };
 
-  // tiles: window n = 0..nw-1 (at most four, straight-line code, qk() then
-  // sv() per tile: the two 128-byte window buffers per lane leave no room
-  // for a second tile's state), then latent n = nw + i, i = 0..nl-1 (latent
-  // tile l0 + i in ring slot i & 3), software-pipelined. Every ring load is
-  // issued unconditionally (positions past the list flagged invalid), so
-  // each wait counts exactly the loads it needs.
+  // tiles: window n = 0..nw-1 (at most four, straight-line code), then
+  // latent i = 0..nl-1 (latent tile l0 + i in ring slot i % kRing). Ring
+  // loads past the list are issued all the same (positions past it flagged
+  // invalid).
   static_assert(CSA2_MAX_SWA <= 4 * TILE, "at most four window tiles");
   const int nw = w1 - w0, nl = l1 - l0;
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
     if (n < nw) {
-      qk_win(n, (n & 1) ? rwB : rwA);
-      if (n + 2 < nw) load_window<SWA8>(a, q, (w0 + n + 2) * TILE + my_slot, ch, g, (n & 1) ? rwB : rwA);
-      __syncthreads();
-      sv(n, Bf16Tag{});
+      qk_win((n & 1) ? rwB : rwA);
+      if (n + 2 < nw) load_window<SWA8>(a, q, w0 + n + 2, w, g, r16, (n & 1) ? rwB : rwA);
+      rest(Bf16Tag{});
     }
   }
+  // The first latent tiles' bytes are requested only now: with no load
+  // issued under a condition between these and the loop, every wait in the
+  // loop counts exactly the loads issued after the slot it needs.
+  RawLat ring[kRing];
+#pragma unroll
+  for (int j = 0; j < kRing; ++j) load_latent(a, sh, q, l0 + j, w, g, r16, ring[j]);
   if (nl > 0) {
-    make_qh();
-    qk_lat(nw, ring[0]);
-    load_latent(a, sh, q, (l0 + kRing) * TILE + my_slot, ch, g, ring[0]);
-    __syncthreads();
+    // q to fp16, scaled per head
+#pragma unroll
+    for (int hb = 0; hb < kHB; ++hb) {
+      const float qs = __uint_as_float((unsigned)(head_k2(16 * hb + r16) + 127) << 23);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qr[hb][ks][j] = bf16x2_to_f16x2(qr[hb][ks][j], qs);
+    }
   }
-  for (int i0 = 0; i0 < nl; i0 += kRing) {
+  // Whole groups of kRing tiles run without conditions, so that each wait
+  // for a ring slot counts exactly the loads issued after it (a load under a
+  // condition makes the wait at the next join count conservatively, which
+  // here means waiting for every tile in flight); the last nl % kRing tiles
+  // follow.
+  int i0 = 0;
+  for (; i0 + kRing <= nl; i0 += kRing) {
 #pragma unroll
     for (int j = 0; j < kRing; ++j) {
-      const int i = i0 + j;
-      if (i < nl) {
-        if (i + 1 < nl) qk_lat(nw + i + 1, ring[(j + 1) & (kRing - 1)]);
-        load_latent(a, sh, q, (l0 + i + 1 + kRing) * TILE + my_slot, ch, g, ring[(j + 1) & (kRing - 1)]);
-        sv(nw + i, F16Tag{});
-        __syncthreads();
-      }
+      qk_lat(ring[j]);
+      load_latent(a, sh, q, l0 + i0 + j + kRing, w, g, r16, ring[j]);
+      rest(F16Tag{});
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kRing - 1; ++j) {
+    if (i0 + j < nl) {
+      qk_lat(ring[j]);
+      rest(F16Tag{});
     }
   }
 
-  const int head = HEADS_WG * hb + r16;
+  // ---- every head's reference max and sum to all waves
+  if (smax && g == 0) {
+    sh.ml[0][16 * shb + r16] = m_ref;
+    sh.ml[1][16 * shb + r16] = l_run;
+  }
+  __syncthreads();
   if (a.n_split > 1) {
-    // ---- partial record: m, l and O / l of this slot range
-    float* part = a.partial + (((int64_t)q * kHeadBlocks + hb) * a.n_split + split) * kPartFloats;
-    if (cq == 0 && g == 0) {
-      part[r16] = m_ref;
-      part[HEADS_WG + r16] = l_run;
+    // ---- partial record (shared by the two head halves): m, l and O / l
+    // of this slot range
+    float* part = a.partial + ((int64_t)q * ns + split) * kPartFloats;
+    if (w == 0 && lane < kHeadsWg) {
+      part[h0 + lane] = sh.ml[0][lane];
+      part[kHeads + h0 + lane] = sh.ml[1][lane];
     }
-    const float pinv = (l_run > 0.f) ? 1.f / l_run : 0.f;
-    uint16_t* orow = (uint16_t*)(part + 2 * HEADS_WG) + r16 * kDim + 128 * cq + 4 * g;
+    uint16_t* orec = (uint16_t*)(part + 2 * kHeads);
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) {
-      v2u pk;
-      pk.x = (unsigned)__builtin_bit_cast(uint16_t, (__bf16)(o[cb][0] * pinv)) |
-             ((unsigned)__builtin_bit_cast(uint16_t, (__bf16)(o[cb][1] * pinv)) << 16);
-      pk.y = (unsigned)__builtin_bit_cast(uint16_t, (__bf16)(o[cb][2] * pinv)) |
-             ((unsigned)__builtin_bit_cast(uint16_t, (__bf16)(o[cb][3] * pinv)) << 16);
-      *(v2u*)(orow + 16 * cb) = pk;
+    for (int hb = 0; hb < kHB; ++hb) {
+      const float lh = sh.ml[1][16 * hb + r16];
+      const float pinv = (lh > 0.f) ? 1.f / lh : 0.f;
+      uint16_t* orow = orec + (h0 + 16 * hb + r16) * kDim + 128 * w + 4 * g;
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) {
+        v2u pk;
+        pk.x = pack_bf16x2(o[hb][cb][0] * pinv, o[hb][cb][1] * pinv);
+        pk.y = pack_bf16x2(o[hb][cb][2] * pinv, o[hb][cb][3] * pinv);
+        *(v2u*)(orow + 16 * cb) = pk;
+      }
     }
     return;
   }
 
   // ---- epilogue: O / l as bf16 (rotary channels rotated back when a table
-  // is given); lane (head r16, g) holds channels 128*cq + 16*cb + 4*g .. +3
-  const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
-  if (a.lse && cq == 0 && g == 0)
-    a.lse[(int64_t)q * kHeads + head] = (l_run > 0.f) ? (m_ref + __log2f(l_run)) * kLn2 : -__builtin_inff();
-  const float* rope = (a.rope && cq == 3) ? a.rope + (int64_t)q * 64 : nullptr;
-  uint16_t* orow = a.out + ((int64_t)q * kHeads + head) * kDim + 128 * cq + 4 * g;
+  // is given); lane (head h0 + 16hb + r16, g) holds channels 128w + 16cb + 4g .. +3
+  if (a.lse && smax && g == 0)
+    a.lse[(int64_t)q * kHeads + h0 + 16 * shb + r16] =
+        (l_run > 0.f) ? (m_ref + __log2f(l_run)) * kLn2 : -__builtin_inff();
+  const float* rope = (a.rope && w == kWaves - 1) ? a.rope + (int64_t)q * 64 : nullptr;
 #pragma unroll
-  for (int cb = 0; cb < 8; ++cb) {
-    float v0 = o[cb][0] * inv, v1 = o[cb][1] * inv, v2 = o[cb][2] * inv, v3 = o[cb][3] * inv;
-    if (cb >= 4 && rope) {  // channels 384 + 16*cb + 4*g >= 448: pairs (16*cb + 4*g - 64) / 2 and +1
-      const int c0 = 16 * cb + 4 * g - 64;
-      unrotate(v0, v1, *(const float2*)(rope + c0));  // the table is 8-B aligned
-      unrotate(v2, v3, *(const float2*)(rope + c0 + 2));
+  for (int hb = 0; hb < kHB; ++hb) {
+    const float lh = sh.ml[1][16 * hb + r16];
+    const float inv = (lh > 0.f) ? 1.f / lh : 0.f;
+    uint16_t* orow = a.out + ((int64_t)q * kHeads + h0 + 16 * hb + r16) * kDim + 128 * w + 4 * g;
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+      float v0 = o[hb][cb][0] * inv, v1 = o[hb][cb][1] * inv, v2 = o[hb][cb][2] * inv, v3 = o[hb][cb][3] * inv;
+      if (cb >= 4 && rope) {  // channels 384 + 16*cb + 4*g >= 448: pairs (16*cb + 4*g - 64) / 2 and +1
+        const int c0 = 16 * cb + 4 * g - 64;
+        unrotate(v0, v1, *(const float2*)(rope + c0));  // the table is 8-B aligned
+        unrotate(v2, v3, *(const float2*)(rope + c0 + 2));
+      }
+      v2u pk;
+      pk.x = pack_bf16x2(v0, v1);
+      pk.y = pack_bf16x2(v2, v3);
+      __builtin_nontemporal_store(pk, (v2u*)(orow + 16 * cb));
     }
-    v2u pk;
-    pk.x = (unsigned)__builtin_bit_cast(uint16_t, (__bf16)v0) | ((unsigned)__builtin_bit_cast(uint16_t, (__bf16)v1) << 16);
-    pk.y = (unsigned)__builtin_bit_cast(uint16_t, (__bf16)v2) | ((unsigned)__builtin_bit_cast(uint16_t, (__bf16)v3) << 16);
-    __builtin_nontemporal_store(pk, (v2u*)(orow + 16 * cb));
   }
 }
 
-// Merge the slot ranges of one (query, head block): with partial (m_s, l_s,
+// Merge the slot ranges of one query's head: with partial (m_s, l_s,
 // P_s = O_s / l_s), out = sum_s P_s l_s 2^(m_s - M) / sum_s l_s 2^(m_s - M),
 // M = max_s m_s, in range order. grid (Q * 64): workgroup -> (query, head),
 // 64 threads -> 8 channels each. Every range's record is requested before
@@ -518,16 +648,16 @@ __global__ __launch_bounds__(64) void k_attn_merge(const float* __restrict__ par
                                                    const float* __restrict__ rope, uint16_t* __restrict__ out,
                                                    float* __restrict__ lse) {
   const int q = blockIdx.x >> 6, h = blockIdx.x & 63;
-  const int hb = h >> 4, hl = h & 15, c0 = threadIdx.x * 8;
-  const float* base = partial + ((int64_t)q * kHeadBlocks + hb) * n_split * kPartFloats;
+  const int c0 = threadIdx.x * 8;
+  const float* base = partial + (int64_t)q * n_split * kPartFloats;
   float ms[MS], ls[MS];
   v4u x[MS];
 #pragma unroll
   for (int sp = 0; sp < MS; ++sp) {
     const float* pr = base + (int64_t)min(sp, n_split - 1) * kPartFloats;
-    ms[sp] = pr[hl];
-    ls[sp] = pr[HEADS_WG + hl];
-    x[sp] = *(const v4u*)((const uint16_t*)(pr + 2 * HEADS_WG) + hl * kDim + c0);
+    ms[sp] = pr[h];
+    ls[sp] = pr[kHeads + h];
+    x[sp] = *(const v4u*)((const uint16_t*)(pr + 2 * kHeads) + h * kDim + c0);
   }
   float M = -__builtin_inff();
 #pragma unroll
@@ -556,10 +686,7 @@ __global__ __launch_bounds__(64) void k_attn_merge(const float* __restrict__ par
   }
   v4u pk;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    __bf16 lo = (__bf16)acc[2 * j], hi = (__bf16)acc[2 * j + 1];
-    pk[j] = (unsigned)__builtin_bit_cast(uint16_t, lo) | ((unsigned)__builtin_bit_cast(uint16_t, hi) << 16);
-  }
+  for (int j = 0; j < 4; ++j) pk[j] = pack_bf16x2(acc[2 * j], acc[2 * j + 1]);
   __builtin_nontemporal_store(pk, (v4u*)(out + ((int64_t)q * kHeads + h) * kDim + c0));
   if (lse && threadIdx.x == 0)
     lse[(int64_t)q * kHeads + h] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
@@ -567,13 +694,13 @@ __global__ __launch_bounds__(64) void k_attn_merge(const float* __restrict__ par
 
 AttnPlan plan_attn(int Q, int k_sel, int n_swa) {
   // Window rows and selected latents are tiled apart. The slot list is split
-  // only when the launch would hold fewer than two workgroups per CU: into as
-  // many ranges as bring it to about kTargetWgs workgroups, each of at least
+  // only when the launch would hold fewer workgroups than CUs: into as many
+  // ranges as bring it to about kTargetWgs workgroups, each of at least
   // kMinTilesPerSplit tiles.
   AttnPlan p;
   p.n_tiles = (k_sel + TILE - 1) / TILE + (n_swa + TILE - 1) / TILE;
   int ns = 1;
-  if (Q > 0 && kHeadBlocks * Q < kTargetWgs) ns = kTargetWgs / (kHeadBlocks * Q);
+  if (Q > 0 && Q < kTargetWgs) ns = kTargetWgs / Q;
   ns = max(1, min(ns, min(kMaxSplits, p.n_tiles / kMinTilesPerSplit)));
   p.tiles_per_split = p.n_tiles > 0 ? (p.n_tiles + ns - 1) / ns : 1;
   p.n_splits = p.n_tiles > 0 ? (p.n_tiles + p.tiles_per_split - 1) / p.tiles_per_split : 1;
@@ -582,9 +709,9 @@ AttnPlan plan_attn(int Q, int k_sel, int n_swa) {
 
 size_t attn_partial_bytes(int Q, const AttnPlan& plan) {
   if (plan.n_splits <= 1) return 0;
-  // a split launch has kHeadBlocks * Q * n_splits <= kTargetWgs workgroups,
-  // so this stays within kAttnPartialMaxBytes
-  return (size_t)Q * kHeadBlocks * plan.n_splits * kPartFloats * sizeof(float);
+  // a split launch has Q * n_splits <= kTargetWgs workgroups, so this stays
+  // within kAttnPartialMaxBytes
+  return (size_t)Q * plan.n_splits * kPartFloats * sizeof(float);
 }
 
 hipError_t launch_attn(const AttnLaunch& L, const AttnPlan& plan, float* partial, hipStream_t s) {
@@ -630,7 +757,7 @@ hipError_t launch_attn(const AttnLaunch& L, const AttnPlan& plan, float* partial
   }
   if (plan.n_splits > 1 && partial == nullptr) return hipErrorInvalidValue;
   const int q8 = (L.Q + 7) / 8 * 8;
-  const dim3 grid((unsigned)(kHeadBlocks * plan.n_splits * q8));
+  const dim3 grid((unsigned)(kHalves * plan.n_splits * q8));
   const bool fused = L.sel_counts != nullptr;
   if (L.swa_fp8) {
     if (fused)
@@ -655,6 +782,10 @@ hipError_t launch_attn(const AttnLaunch& L, const AttnPlan& plan, float* partial
       k_attn_merge<8><<<mg, 64, 0, s>>>(partial, plan.n_splits, L.rope, L.out, L.lse);
     else if (plan.n_splits <= 12)
       k_attn_merge<12><<<mg, 64, 0, s>>>(partial, plan.n_splits, L.rope, L.out, L.lse);
+    else if (plan.n_splits <= 16)
+      k_attn_merge<16><<<mg, 64, 0, s>>>(partial, plan.n_splits, L.rope, L.out, L.lse);
+    else if (plan.n_splits <= 24)
+      k_attn_merge<24><<<mg, 64, 0, s>>>(partial, plan.n_splits, L.rope, L.out, L.lse);
     else
       k_attn_merge<kMaxSplits><<<mg, 64, 0, s>>>(partial, plan.n_splits, L.rope, L.out, L.lse);
   }

@@ -278,7 +278,7 @@ CSA2_API int csa2_sparse_attn(const csa2_attn_args* args, void* workspace, size_
  * partial records of small batches (the only scratch csa2_sparse_attn uses)
  * go to a device array the library holds on every GPU it runs on, of
  * CSA2_ATTN_SCRATCH_BYTES, until the process ends. Any valid args fit in it
- * (a split launch has at most 512 partial records of 16,512 B); a call that
+ * (a split launch has at most 128 partial records of 66,048 B); a call that
  * would need more returns CSA2_ERR_SCRATCH before any work is enqueued. The
  * call allocates nothing; the array's address on the current device is
  * looked up once per device (hipGetSymbolAddress) on the first call there,
