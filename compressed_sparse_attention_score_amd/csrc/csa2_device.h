@@ -175,4 +175,25 @@ __device__ __forceinline__ unsigned umax_xor16(unsigned x) {
   return r[0] > r[1] ? r[0] : r[1];
 }
 
+// Unsigned maximum / minimum over the 64 lanes of a wave, left in every lane:
+// quad permutations and row rotations by 4 and 8 (DPP), then the two lane
+// swaps. No LDS traffic, unlike a shuffle.
+__device__ __forceinline__ unsigned wave_umax(unsigned x) {
+  x = max(x, (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false));   // [1,0,3,2]
+  x = max(x, (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false));   // [2,3,0,1]
+  x = max(x, (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x124, 0xF, 0xF, false));  // row_ror:4
+  x = max(x, (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, false));  // row_ror:8
+  return umax_xor32(umax_xor16(x));
+}
+__device__ __forceinline__ unsigned wave_umin(unsigned x) {
+  x = min(x, (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false));
+  x = min(x, (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false));
+  x = min(x, (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x124, 0xF, 0xF, false));
+  x = min(x, (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, false));
+  auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = r[0] < r[1] ? r[0] : r[1];
+  auto t = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return t[0] < t[1] ? t[0] : t[1];
+}
+
 }  // namespace csa2

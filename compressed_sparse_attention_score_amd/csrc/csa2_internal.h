@@ -26,7 +26,7 @@ struct IndexLaunch {
 // Work decomposition of the scoring pass, shared by the selection pass.
 struct ScorePlan {
   int wave_span;    // entries per wave (power of two, multiple of 16)
-  int group;        // sub-chunk size whose maximum key is recorded (16..wave_span)
+  int group;        // sub-chunk size whose maximum key is recorded (4..wave_span)
   int64_t n_groups; // sub-chunks per query
   int n_wg;         // scoring workgroups per query
 };

@@ -185,10 +185,11 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
   const int span = (int)(w1p - w0p);
   for (int i = lane; i < span; i += 64) out[w0p + i] = s_score[wave][i];
   if (a.gmax) {
-    // Sub-chunk maxima (sub-chunks start at multiples of the group size, and
-    // so does the wave's range). In each pass over 256 staged scores lane l
-    // takes scores 4l..4l+3, and the group/4 lanes of a sub-chunk reduce into
-    // its first lane; a 512-entry sub-chunk spans two passes. Invalid entries
+    // Sub-chunk maxima (sub-chunks of 4 to 512 entries start at multiples of
+    // the group size, and so does the wave's range). In each pass over 256
+    // staged scores lane l takes scores 4l..4l+3, and the group/4 lanes of a
+    // sub-chunk reduce into its first lane; a 512-entry sub-chunk spans two
+    // passes. Invalid entries
     // are -inf and a NaN score is passed over by the maximum, which can only
     // lower it and so keeps the selection bound valid. Order key 0 = empty.
     const int lpg = a.group >> 2;
@@ -203,8 +204,8 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
 #pragma unroll
         for (int e = 1; e < 4; ++e) m = (i + e < span) ? fmaxf(m, x[e]) : m;
       }
-      m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, false)));  // lane ^ 1
-      m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, false)));  // lane ^ 2
+      if (lpg >= 2) m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, false)));  // lane ^ 1
+      if (lpg >= 4) m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, false)));  // lane ^ 2
       // row rotations: the first lane of each 8- or 16-lane group collects it
       if (lpg >= 8) m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x124, 0xF, 0xF, false)));
       if (lpg >= 16) m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x128, 0xF, 0xF, false)));
@@ -447,7 +448,7 @@ __global__ __launch_bounds__(256) void k_score_maxima(const float* __restrict__ 
     }
     if (e >= 0 && e < limit) m = max(m, score_key(scores[(int64_t)q * n_cand + p]));
   }
-  for (int o = 32; o >= 1; o >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, o, 64));
+  m = wave_umax(m);
   if (lane == 0) gmax[(int64_t)q * n_groups + gi] = m;
 }
 
@@ -462,8 +463,13 @@ ScorePlan plan_score(int64_t n_cand, int Q, int k) {
   int W = 512;
   while (W > 64 && (int64_t)Q * ((n_cand + 4 * W - 1) / (4 * W)) < 1024) W /= 2;
   p.wave_span = W;
+  // Sub-chunks of about n / 2k entries, so that at least k of them exist
+  // and the threshold is informative. The query-tiled scan (32 queries or
+  // more over a shared cache) forms maxima per 16-entry step, so there the
+  // smallest sub-chunk is 16; the per-query scan goes down to 4.
   int64_t g = floor_pow2(n_cand / (2 * (int64_t)(k > 0 ? k : 1)));
-  if (g < 16) g = 16;
+  const int64_t gmin = (Q >= 16 * kQSets) ? 16 : 4;
+  if (g < gmin) g = gmin;
   if (g > W) g = W;
   p.group = (int)g;
   p.n_groups = (n_cand + g - 1) / g;

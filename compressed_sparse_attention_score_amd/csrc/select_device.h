@@ -210,11 +210,8 @@ __device__ __forceinline__ void shared_top_bits(const T (&v)[REG], unsigned* ext
       kmin = min(kmin, key);
     }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    kmax = max(kmax, (unsigned)__shfl_xor((int)kmax, o, 64));
-    kmin = min(kmin, (unsigned)__shfl_xor((int)kmin, o, 64));
-  }
+  kmax = wave_umax(kmax);
+  kmin = wave_umin(kmin);
   if (lane == 0) {
     ext[2 * wv] = kmax;
     ext[2 * wv + 1] = kmin;

@@ -60,6 +60,11 @@ constexpr int kThetaPasses = 2;
 // and the coarser bound let enough more through to cost the 4,096-query
 // prefill selection over 100 us.
 constexpr int kCompactThetaPasses = 1;
+// The per-query kernel of small batches (1,024 threads) also takes one: each
+// pass costs it about 2,000 cycles of barrier-bound work, and the coarser
+// bound adds a few hundred survivors to a final selection whose cost hardly
+// depends on their number.
+constexpr int kSmallThetaPasses = 1;
 
 // Threshold + compaction: grid (n_chunks, Q). Writes cand[q][c0 .. c0+cnt) in
 // position order and counts[q][chunk] = cnt.
@@ -283,27 +288,51 @@ __global__ __launch_bounds__(NQ) __attribute__((amdgpu_waves_per_eu(NQ >= 1024 ?
   // are read. The maxima pass over NaN and give an all-invalid or all -inf
   // sub-chunk key 0, so they bound every key above that of -inf; skipping is
   // taken only with theta above the key of +0, where NaN and -inf cannot pass.
-  const bool can_skip = !POOL && gmax && n_groups >= k && n_groups <= 4 * NQ && group >= RUN &&
+  // A list read in one pass is read whole, its loads in flight during the
+  // threshold search; skipping pays when it saves passes.
+  const bool can_skip = !POOL && gmax && n_cand > kStep && n_groups >= k && n_groups <= 4 * NQ && group >= RUN &&
                         (group & (group - 1)) == 0;
   const bool pre = n_full > 0 && !can_skip;
-  if (pre) load_full(scA, bkA, 0);  // in flight during the threshold search
+  // Ragged or unaligned passes: positions past the end load the last score
+  // (clamped, so every load is issued at once instead of one guarded round
+  // trip after another) and are dropped by process(). A list that is one such
+  // pass is requested before the threshold search, like the full passes.
+  auto load_ragged = [&](float* sc, int32_t* blk, int64_t p0) {
+#pragma unroll
+    for (int g = 0; g < kQGrp; ++g) {
+      const int64_t pb = p0 + g * kGrpLen + RUN * tid;
+#pragma unroll
+      for (int i = 0; i < RUN; ++i) sc[RUN * g + i] = srow[min(pb + i, n_cand - 1)];
+#pragma unroll
+      for (int b = 0; b < kBlk; ++b)
+        blk[kBlk * g + b] = POOL ? cand_blocks[(int64_t)q * n_blocks + min((pb >> 3) + b, (int64_t)n_blocks - 1)] : 0;
+    }
+  };
+  const bool pre_ragged = n_full == 0 && n_cand > 0 && n_cand <= kStep && !can_skip;
 
   // ---- theta = k-th largest sub-chunk maximum (1 = keep every valid candidate)
   unsigned theta = 1u;
   unsigned g[4] = {0u, 0u, 0u, 0u};  // maxima of sub-chunks j*NQ + tid
+  const bool theta_regs = gmax && n_groups >= k && n_groups <= 4 * NQ;
+  if (theta_regs) {  // requested first: the threshold search waits on these, not on the scores
+    const unsigned* gm = gmax + (int64_t)q * n_groups;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t i = (int64_t)j * NQ + tid;
+      g[j] = (i < n_groups) ? gm[i] : 0u;
+    }
+  }
+  if (pre) load_full(scA, bkA, 0);  // in flight during the threshold search
+  if (pre_ragged) load_ragged(scA, bkA, 0);
   if (gmax && n_groups >= k) {
     const unsigned* gm = gmax + (int64_t)q * n_groups;
     unsigned t;
-    if (n_groups <= 4 * NQ) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t i = (int64_t)j * NQ + tid;
-        g[j] = (i < n_groups) ? gm[i] : 0u;
-      }
+    if (theta_regs) {
       int top;
       unsigned prefix;
       shared_top_bits<NQ, unsigned, 4>(g, sh.ext, &top, &prefix);
-      t = radix_kth_regs<NQ, unsigned, 4>(g, (unsigned)k, sh.hist, sh.res, kThetaPasses, top, prefix);
+      t = radix_kth_regs<NQ, unsigned, 4>(g, (unsigned)k, sh.hist, sh.res, NQ >= 1024 ? kSmallThetaPasses : kThetaPasses,
+                                          top, prefix);
     } else {
       t = radix_kth_stream<NQ, unsigned>(gm, n_groups, (unsigned)k, sh.hist, sh.res, kThetaPasses);
     }
@@ -319,7 +348,7 @@ __global__ __launch_bounds__(NQ) __attribute__((amdgpu_waves_per_eu(NQ >= 1024 ?
   // score, -0 and NaN has u > 0x7F800000 and a key below theta. One subtract
   // and one unsigned compare per score; the composite is built for the
   // survivors only.
-  const bool fast = !POOL && theta > 0x80000000u;
+  const bool fast = theta > 0x80000000u;
   const unsigned tlo = theta & 0x7FFFFFFFu, tspan = 0x7F800000u - tlo;
   const int64_t vlim = min(n_cand, limit);  // valid positions of the plain range
   // Each group's count (at most RUN per thread, NQ*RUN <= 16,384 per
@@ -368,9 +397,9 @@ __global__ __launch_bounds__(NQ) __attribute__((amdgpu_waves_per_eu(NQ >= 1024 ?
   auto process_at = [&](const float* sc, const int32_t* blk, auto&& run_pos) {
     unsigned cnt[kQGrp], pos[kQGrp];
     unsigned keep = 0;  // bit RUN*g+i: position RUN*t+i of group g survives
-    // Pools with one group (runs of 16): the composites are built once,
-    // before the scan, and held (32 VGPRs, which that variant has to spare);
-    // otherwise they are rebuilt at the store.
+    // Pools with one group (runs of 16), without the fast filter: the
+    // composites are built once, before the scan, and held (32 VGPRs, which
+    // that variant has to spare); otherwise they are rebuilt at the store.
     constexpr bool kHold = POOL && kQGrp == 1;
     unsigned long long comp[kHold ? kQPer : 1];
 #pragma unroll
@@ -378,10 +407,19 @@ __global__ __launch_bounds__(NQ) __attribute__((amdgpu_waves_per_eu(NQ >= 1024 ?
       const int64_t pb = run_pos(g);
       unsigned kg = 0;
       if (fast) {
-        const int nv = (int)max((int64_t)0, min(vlim - pb, (int64_t)RUN));
+        const int nv = (int)max((int64_t)0, min((POOL ? n_cand : vlim) - pb, (int64_t)RUN));
 #pragma unroll
         for (int i = 0; i < RUN; ++i)
           kg |= (i < nv && __float_as_uint(sc[RUN * g + i]) - tlo <= tspan) ? (1u << i) : 0u;
+        if constexpr (POOL) {
+          // a pool position holds a candidate when its block id is valid and
+          // the entry lies below the limit: checked for the few that pass
+          for (unsigned rest = kg; rest; rest &= rest - 1) {
+            const int i = __builtin_ctz(rest);
+            const int64_t e = entry_of(blk, g, i, pb + i);
+            if (e < 0 || e >= limit) kg &= ~(1u << i);
+          }
+        }
       } else {
 #pragma unroll
         for (int i = 0; i < RUN; ++i) {
@@ -397,7 +435,7 @@ __global__ __launch_bounds__(NQ) __attribute__((amdgpu_waves_per_eu(NQ >= 1024 ?
       keep |= kg << (RUN * g);
     }
     place(cnt, pos);
-    if constexpr (kHold) {
+    if (kHold && !fast) {
 #pragma unroll
       for (int i = 0; i < kQPer; ++i)
         if (comp[i]) put(pos[0]++, comp[i]);
@@ -409,10 +447,10 @@ __global__ __launch_bounds__(NQ) __attribute__((amdgpu_waves_per_eu(NQ >= 1024 ?
 #pragma unroll
       for (int i = 0; i < RUN; ++i) {
         if (keep & (1u << (RUN * g + i))) {
-          // in the fast filter every survivor is a non-negative score of the
-          // plain range: key = bits with the sign bit set, entry = position
+          // in the fast filter every survivor is a non-negative score: key =
+          // bits with the sign bit set
           const unsigned key = fast ? (__float_as_uint(sc[RUN * g + i]) | 0x80000000u) : score_key(sc[RUN * g + i]);
-          const unsigned e = fast ? (unsigned)(pb + i) : (unsigned)entry_of(blk, g, i, pb + i);
+          const unsigned e = (unsigned)entry_of(blk, g, i, pb + i);
           put(pos[g]++, ((unsigned long long)key << 32) | (unsigned long long)(~e));
         }
       }
@@ -485,19 +523,7 @@ __global__ __launch_bounds__(NQ) __attribute__((amdgpu_waves_per_eu(NQ >= 1024 ?
       process(scB, bkB, (i + 1) * kStep);
     }
     for (int64_t p0 = n_full * kStep; p0 < n_cand; p0 += kStep) {  // ragged or unaligned passes
-      // positions past the end load the last score (clamped, so every load is
-      // issued at once instead of one guarded round trip after another) and
-      // are dropped by process()
-  #pragma unroll
-      for (int g = 0; g < kQGrp; ++g) {
-        const int64_t pb = p0 + g * kGrpLen + RUN * tid;
-  #pragma unroll
-        for (int i = 0; i < RUN; ++i) scA[RUN * g + i] = srow[min(pb + i, n_cand - 1)];
-  #pragma unroll
-        for (int b = 0; b < kBlk; ++b)
-          bkA[kBlk * g + b] =
-              POOL ? cand_blocks[(int64_t)q * n_blocks + min((pb >> 3) + b, (int64_t)n_blocks - 1)] : 0;
-      }
+      if (!(pre_ragged && p0 == 0)) load_ragged(scA, bkA, p0);
       process(scA, bkA, p0);
     }
   }
