@@ -323,6 +323,18 @@ __global__ __launch_bounds__(256) void k_index_score_qtile(ScoreArgs a, int rang
   const int steps_per_group = a.group >> 4;
   int step_in_group = 0;
   int64_t gidx = e_begin / a.group;
+  constexpr int kBatch = 16 * BB;  // entries per batch (compute() call)
+  const bool batch_groups = a.group >= kBatch;
+  // the sub-chunk maximum of each of this lane's query sets, over the 16
+  // entries of its row group, to gmax[query][g]; then restart
+  auto flush_max = [&](int64_t g) {
+#pragma unroll
+    for (int s = 0; s < QSETS; ++s) {
+      const float m = row16_max(gm[s]);
+      if (r16 == 0 && qok[s]) a.gmax[(int64_t)(q0 + 4 * s + kb) * a.n_groups + g] = (m == ninf) ? 0u : score_key(m);
+      gm[s] = ninf;
+    }
+  };
 
   // cooperative batch loads: batch = BB*16 entries; thread t loads code chunks
   // t and t+256 (16 B each: entry c/4, quarter c%4) and, t < BB*16, one scale dword
@@ -396,21 +408,20 @@ __global__ __launch_bounds__(256) void k_index_score_qtile(ScoreArgs a, int rang
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sv), orsrc[s], boff, 0, kNonTemporal);
         if (GMAX) gm[s] = fmaxf(gm[s], sv);  // lim <= span, so sv is -inf outside the range
       }
-      if (GMAX) {
+      if (GMAX && !batch_groups) {  // sub-chunks shorter than a batch: flushed by step
         ++step_in_group;
         if (step_in_group == steps_per_group || off + 16 >= span) {
-#pragma unroll
-          for (int s = 0; s < QSETS; ++s) {
-            const float m = row16_max(gm[s]);
-            if (r16 == 0 && qok[s])
-              a.gmax[(int64_t)(q0 + 4 * s + kb) * a.n_groups + gidx] = (m == ninf) ? 0u : score_key(m);
-            gm[s] = ninf;
-          }
+          flush_max(gidx);
           step_in_group = 0;
           ++gidx;
         }
       }
     }
+    // Sub-chunks of a batch or more (ranges start on sub-chunk boundaries):
+    // flushed after the batch that ends one, outside the step loop, so that
+    // no branch splits the steps' interleaved MFMA and vector work.
+    if (GMAX && batch_groups && (((off0 + kBatch) & (a.group - 1)) == 0 || off0 + kBatch >= span))
+      flush_max((e_begin + off0) / a.group);
   };
   constexpr int kStep = 16 * BB;
   gload(0);
