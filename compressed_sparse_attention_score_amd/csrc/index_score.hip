@@ -18,10 +18,19 @@
 #include "csa2_device.h"
 #include "csa2_internal.h"
 
+#include <type_traits>
+
 namespace csa2 {
 
 namespace {
-constexpr int kUnroll = 4;  // 16-entry groups per load batch (two batches in flight per wave)
+constexpr int kUnroll = 4;  // 16-entry groups per load batch
+constexpr int kScanRing = 2;  // load batches in flight per wave
+// Buffer resource word 3 for untyped dword access on gfx9-family parts, the
+// nontemporal cache-policy bit of a buffer access, and an offset that is
+// past every resource these kernels build (their sizes stay below 2 GiB).
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kNonTemporal = 2;
+constexpr unsigned kStoreDrop = 0x80000000u;
 constexpr int kMaxWaveSpan = 512;  // entries per wave (the plan picks 64..512)
 
 struct ScoreArgs {
@@ -56,8 +65,17 @@ __device__ __forceinline__ int64_t cand_entry(const ScoreArgs& a, const int32_t*
   return (e >= 0 && e < limit) ? e : -1;
 }
 
-template <bool POOL, int UNROLL = kUnroll>
+// BUF (plain ranges whose key bytes stay below 2 GiB per query): the keys
+// are read through buffer resources that end at the query's last valid
+// entry, so one 32-bit offset per lane, stepped by the batch, addresses every
+// load (the group's 1 KiB and 64 B strides are instruction offsets) and the
+// hardware returns zeros past the end instead of a clamped row.
+// NB: batches of 64 entries per wave (the wave span is 64*NB); the batch
+// loop is unrolled in full, so every wait names the exact load it needs.
+template <bool POOL, bool BUF, int NB, int UNROLL = kUnroll>
 __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
+  static_assert(!(POOL && BUF), "pools take per-entry addresses");
+  static_assert(NB >= 1 && 64 * NB <= kMaxWaveSpan, "wave span");
   static_assert(UNROLL == 4, "a batch is 64 entries: one staged score per lane");
   const int q = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -90,15 +108,15 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
   const int64_t base_row = (int64_t)q * a.cache_q_stride;
   float* out = a.scores + (int64_t)q * a.n_cand;
 
-  const int64_t w0p = ((int64_t)blockIdx.x * 4 + wave) * a.wave_span;
+  const int64_t w0p = ((int64_t)blockIdx.x * 4 + wave) * (64 * NB);
   if (w0p >= a.n_cand) return;
-  const int64_t w1p = min(w0p + a.wave_span, a.n_cand);
+  const int64_t w1p = min(w0p + 64 * NB, a.n_cand);
 
-  // Key loads run one batch of UNROLL groups ahead of the matrix cores (two
-  // statically indexed buffers, alternated by a 2x unrolled loop). Loads are
-  // unconditional so that the compiler keeps the second batch in flight:
-  // lanes without a valid candidate read row 0 of their cache and are masked
-  // at compute time.
+  // Key loads run kScanRing - 1 batches of UNROLL groups ahead of the matrix
+  // cores (statically indexed buffers). Loads are unconditional so that the
+  // compiler keeps the second batch in flight: lanes without a valid
+  // candidate read nothing (buffer resources) or row 0 of their cache, and
+  // are masked at compute time.
   if (limit <= 0) {  // no valid candidate in this query's list
     for (int64_t p = w0p + lane; p < w1p; p += 64) out[p] = -__builtin_inff();
     if (a.gmax && lane == 0)
@@ -113,10 +131,33 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
     // in order, and this keeps the compiler from moving the reads above
     __builtin_amdgcn_wave_barrier();
   }
-  v4u bcA[UNROLL], bcB[UNROLL];
-  unsigned bsA[UNROLL], bsB[UNROLL];
-  bool okA[UNROLL], okB[UNROLL];
+  v4u bcr[kScanRing][UNROLL];
+  unsigned bsr[kScanRing][UNROLL];
+  bool okr[kScanRing][UNROLL];
+  __amdgpu_buffer_rsrc_t crs, srs;
+  int64_t lim_w = 0;  // BUF: valid positions of the wave's range end here
+  if constexpr (BUF) {
+    const int64_t lim = min(limit, a.n_cand);
+    lim_w = min(lim, w1p);
+    crs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.key_codes + base_row * 64), 0, (int)(lim * 64), kBufferWord3);
+    srs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.key_scales + base_row * 4), 0, (int)(lim * 4), kBufferWord3);
+  }
   auto issue = [&](v4u* bc, unsigned* bs, bool* ok, int64_t g0) {
+    if constexpr (BUF) {
+      // a batch past the range (the one the loop issues after its last)
+      // reads nothing: its offsets are past every resource
+      const unsigned p = (unsigned)g0 + (unsigned)r16;
+      const bool in = g0 < w1p;
+      const unsigned co = in ? 64u * p + 16u * (unsigned)kb : kStoreDrop;
+      const unsigned so = in ? 4u * p : kStoreDrop;
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        ok[u] = g0 + 16 * u + r16 < lim_w;
+        bc[u] = __builtin_amdgcn_raw_buffer_load_b128(crs, (int)(co + 1024u * u), 0, kNonTemporal);
+        bs[u] = __builtin_amdgcn_raw_buffer_load_b32(srs, (int)(so + 64u * u), 0, kNonTemporal);
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int64_t p = g0 + 16 * u + r16;
@@ -173,13 +214,20 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
     s_score[wave][g0 - w0p + lane] = mine;
   };
   constexpr int64_t kStep = 16 * UNROLL;
-  issue(bcA, bsA, okA, w0p);
-  for (int64_t g0 = w0p; g0 < w1p; g0 += 2 * kStep) {
-    if (g0 + kStep < w1p) issue(bcB, bsB, okB, g0 + kStep);
-    compute(bcA, bsA, okA, g0);
-    if (g0 + kStep >= w1p) break;
-    if (g0 + 2 * kStep < w1p) issue(bcA, bsA, okA, g0 + 2 * kStep);
-    compute(bcB, bsB, okB, g0 + kStep);
+  // Both batches are issued without conditions (a batch past the range is
+  // masked: no bytes through the buffer resources, row 0 of the cache
+  // otherwise), so that the wait before each group counts only the loads
+  // issued after it and the other batch stays in flight meanwhile; a load
+  // under a condition would make those waits cover both batches.
+  // Each buffer is refilled right after its batch is computed. Batches past
+  // the range (a wave at the list end) are computed on masked lanes too.
+#pragma unroll
+  for (int b = 0; b < kScanRing && b < NB; ++b) issue(bcr[b], bsr[b], okr[b], w0p + b * kStep);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    constexpr int R = kScanRing;
+    compute(bcr[b % R], bsr[b % R], okr[b % R], w0p + b * kStep);
+    if (b + R < NB) issue(bcr[b % R], bsr[b % R], okr[b % R], w0p + (b + R) * kStep);
   }
   // flush this wave's staged scores (wave-private LDS rows)
   const int span = (int)(w1p - w0p);
@@ -242,12 +290,6 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
 namespace {
 constexpr int kQSets = 2;  // 4-query sets per wave
 constexpr int kTileUnroll = 4;  // 16-entry steps per load batch
-// Buffer resource word 3 for untyped dword access on gfx9-family parts, the
-// nontemporal cache-policy bit of a buffer store, and an offset that is past
-// every resource this kernel builds (their sizes stay below 2 GiB).
-constexpr int kBufferWord3 = 0x00020000;
-constexpr int kNonTemporal = 2;
-constexpr unsigned kStoreDrop = 0x80000000u;
 }  // namespace
 
 template <bool GMAX, int QSETS = kQSets, int BB = kTileUnroll>
@@ -532,10 +574,23 @@ hipError_t launch_index_score(const IndexLaunch& L, const ScorePlan& plan, float
     return hipGetLastError();
   }
   dim3 grid((unsigned)plan.n_wg, (unsigned)L.Q);
-  if (L.cand_blocks)
-    k_index_score<true><<<grid, 256, 0, s>>>(a);
-  else
-    k_index_score<false><<<grid, 256, 0, s>>>(a);
+  const bool buf = L.n_cand < (1ll << 25);  // key bytes of a query's list below 2 GiB
+  auto go = [&](auto nb_tag) {
+    constexpr int NB = decltype(nb_tag)::value;
+    if (L.cand_blocks)
+      k_index_score<true, false, NB><<<grid, 256, 0, s>>>(a);
+    else if (buf)
+      k_index_score<false, true, NB><<<grid, 256, 0, s>>>(a);
+    else
+      k_index_score<false, false, NB><<<grid, 256, 0, s>>>(a);
+  };
+  switch (plan.wave_span) {
+    case 64: go(std::integral_constant<int, 1>{}); break;
+    case 128: go(std::integral_constant<int, 2>{}); break;
+    case 256: go(std::integral_constant<int, 4>{}); break;
+    case 512: go(std::integral_constant<int, 8>{}); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

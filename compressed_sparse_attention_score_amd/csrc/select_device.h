@@ -18,12 +18,15 @@ namespace csa2 {
 constexpr int kRadixBits = 8;
 constexpr int kBins = 1 << kRadixBits;
 constexpr int kRegCand = 16;  // default candidates per thread held in registers by the final selection
+// Candidates per thread once the final selection has spread a short joined
+// list evenly over the workgroup (lists of at most NTH * kBalCand).
+constexpr int kBalCand = 4;
 
 // LDS scratch of the selection steps below.
 template <int NTH>
 struct SelScratch {
   alignas(16) unsigned hist[2][kBins];
-  alignas(16) unsigned wsum[NTH / 64];
+  alignas(16) unsigned wsum[2 * (NTH / 64)];
   unsigned res[4];
   unsigned off[NTH + 1];  // exclusive offsets of the chunk regions in the joined list
   unsigned ext[2 * (NTH / 64)];  // per-wave largest and smallest key
@@ -271,13 +274,17 @@ __device__ __forceinline__ unsigned select_regs(const unsigned long long (&v)[RE
 //
 // Three paths, by what fits: (1) each chunk's survivors fit the threads'
 // register slots of that chunk: the slots are loaded together with the
-// counts (one memory round trip) and masked by the counts; (2) the joined
-// list fits the registers: each thread locates its elements through an
-// offset table; (3) otherwise the chunk regions are streamed.
+// counts (one memory round trip) and masked by the counts; a joined list of
+// at most NTH * kBalCand is then spread evenly over the threads through
+// `list` (LDS, that many composites), so that every radix pass and the
+// ordered write loop over kBalCand values instead of REG; (2) the joined list
+// fits the registers: each thread locates its elements through an offset
+// table; (3) otherwise the chunk regions are streamed.
 template <int NTH, int REG = kRegCand, typename Emit>
 __device__ __forceinline__ void select_from_regions(const unsigned* __restrict__ cq, int n_chunks, int chunk,
                                                     int64_t n_cand, int k, const unsigned long long* __restrict__ lq,
-                                                    SelScratch<NTH>& sc, int lo, int hi, Emit emit) {
+                                                    SelScratch<NTH>& sc, unsigned long long* list, int lo, int hi,
+                                                    Emit emit) {
   const int tid = threadIdx.x;
   unsigned written = 0;
   bool done = false;
@@ -286,25 +293,48 @@ __device__ __forceinline__ void select_from_regions(const unsigned* __restrict__
     // Chunk c's region starts at c*chunk whatever the counts, so each thread
     // loads REG fixed slots of one chunk (threads c*tpc .. c*tpc+tpc-1
     // take chunk c in order, so thread order is list order) together with
-    // the counts, and masks the slots past its chunk's count afterwards.
+    // its chunk's count, and masks the slots past that count afterwards.
     const int tpc = NTH / n_chunks;
     const int c_t = tid / tpc, sub = tid - c_t * tpc;
     const bool own = c_t < n_chunks;
     const unsigned slot0 = (unsigned)sub * REG;
-    cnt_c = (tid < n_chunks) ? cq[tid] : 0u;
     const unsigned my_cnt = own ? cq[c_t] : 0u;
     const int64_t rb = (own ? (int64_t)c_t * chunk : 0) + slot0;
     unsigned long long v[REG];
 #pragma unroll
     for (int j = 0; j < REG; ++j) v[j] = lq[min(rb + j, n_cand - 1)];  // slots past the list: dropped below
-    incl_c = block_incl_scan<NTH>(cnt_c, sc.wsum, &m);
-    const bool fits = __syncthreads_and(!own || my_cnt <= (unsigned)tpc * REG) != 0;
-    if (fits) {
+    // survivors this thread holds, and whether its chunk has more than its
+    // threads' slots: one scan gives every thread its list position and the
+    // list length, and tells whether the registers hold the whole list
+    const unsigned held = (own && my_cnt > slot0) ? min(my_cnt - slot0, (unsigned)REG) : 0u;
+    unsigned incl = held, over = (own && sub == 0 && my_cnt > (unsigned)tpc * REG) ? 1u : 0u, n_over;
+    block_incl_scan2<NTH>(incl, over, sc.wsum, &m, &n_over);
+    if (n_over == 0) {
 #pragma unroll
-      for (int j = 0; j < REG; ++j) v[j] = (own && slot0 + j < my_cnt) ? v[j] : 0ull;
-      written = select_regs<NTH, REG>(v, m, k, sc, lo, hi, emit);
+      for (int j = 0; j < REG; ++j) v[j] = ((unsigned)j < held) ? v[j] : 0ull;
+      if (m <= (unsigned)(NTH * kBalCand)) {
+        const unsigned p = incl - held;
+#pragma unroll
+        for (int j = 0; j < REG; ++j)
+          if ((unsigned)j < held) list[p + j] = v[j];
+        __syncthreads();
+        unsigned long long b[kBalCand];
+#pragma unroll
+        for (int j = 0; j < kBalCand; ++j) {
+          const unsigned e = (unsigned)(tid * kBalCand + j);
+          b[j] = (e < m) ? list[e] : 0ull;
+        }
+        written = select_regs<NTH, kBalCand>(b, m, k, sc, lo, hi, emit);
+      } else {
+        written = select_regs<NTH, REG>(v, m, k, sc, lo, hi, emit);
+      }
       done = true;
     }
+  }
+  if (done) {
+  } else if (n_chunks <= NTH && n_cand > 0) {
+    cnt_c = (tid < n_chunks) ? cq[tid] : 0u;
+    incl_c = block_incl_scan<NTH>(cnt_c, sc.wsum, &m);
   } else {
     for (int c0 = 0; c0 < n_chunks; c0 += NTH) {
       const unsigned x = (c0 + tid < n_chunks) ? cq[c0 + tid] : 0u;

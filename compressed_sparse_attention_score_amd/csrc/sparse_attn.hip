@@ -114,7 +114,10 @@ struct AttnArgs {
 struct AttnShared {
   union {
     uint16_t v[TILE * kDim];  // the tile's rows (16-bit), swizzled (v_offset)
-    SelScratch<NT> sel;       // prologue: finishing the selection
+    struct {
+      SelScratch<NT> sc;
+      alignas(16) unsigned long long list[NT * kBalCand];
+    } sel;                    // prologue: finishing the selection
   };
   v4f sx[kWaves][kHB][2][64];   // partial S^T: [channel quarter][head block][slot block][lane]
   v4u px[kHB][64];              // P^T operands: [head block][lane]
@@ -338,8 +341,8 @@ __global__ __launch_bounds__(NT, 2) void k_sparse_attn(AttnArgs a) {
     if (sbeg < send) {  // uniform over the workgroup
       int32_t* io = (a.idx_out && hh == 0) ? a.idx_out + (int64_t)q * a.k_sel : nullptr;
       select_from_regions<NT, kSelReg>(a.sel_counts + (int64_t)q * a.sel_chunks, a.sel_chunks, a.sel_chunk,
-                                       a.sel_n_cand, a.k_sel, a.sel_cand + (int64_t)q * a.sel_n_cand, sh.sel, sbeg,
-                                       send, [&](unsigned pos, unsigned long long x) {
+                                       a.sel_n_cand, a.k_sel, a.sel_cand + (int64_t)q * a.sel_n_cand, sh.sel.sc,
+                                       sh.sel.list, sbeg, send, [&](unsigned pos, unsigned long long x) {
                                          const int32_t id = x ? (int32_t)(~(unsigned)(x & 0xFFFFFFFFull)) : -1;
                                          sh.ids[pos] = id;
                                          if (io) io[pos] = id;
@@ -588,11 +591,13 @@ __global__ __launch_bounds__(NT, 2) void k_sparse_attn(AttnArgs a) {
   __syncthreads();
   if (a.n_split > 1) {
     // ---- partial record (shared by the two head halves): m, l and O / l
-    // of this slot range
+    // of this slot range, with nontemporal stores (the merge, in the next
+    // kernel, is the only reader; at 16 queries x 65,536 entries these
+    // stores took about 2 us off the step against ordinary ones)
     float* part = a.partial + ((int64_t)q * ns + split) * kPartFloats;
     if (w == 0 && lane < kHeadsWg) {
-      part[h0 + lane] = sh.ml[0][lane];
-      part[kHeads + h0 + lane] = sh.ml[1][lane];
+      __builtin_nontemporal_store(sh.ml[0][lane], part + h0 + lane);
+      __builtin_nontemporal_store(sh.ml[1][lane], part + kHeads + h0 + lane);
     }
     uint16_t* orec = (uint16_t*)(part + 2 * kHeads);
 #pragma unroll
@@ -605,7 +610,7 @@ __global__ __launch_bounds__(NT, 2) void k_sparse_attn(AttnArgs a) {
         v2u pk;
         pk.x = pack_bf16x2(o[hb][cb][0] * pinv, o[hb][cb][1] * pinv);
         pk.y = pack_bf16x2(o[hb][cb][2] * pinv, o[hb][cb][3] * pinv);
-        *(v2u*)(orow + 16 * cb) = pk;
+        __builtin_nontemporal_store(pk, (v2u*)(orow + 16 * cb));
       }
     }
     return;

@@ -186,11 +186,12 @@ __global__ __launch_bounds__(NT) void k_select_final(const unsigned* __restrict_
                                                      int64_t n_cand, int k, const unsigned long long* __restrict__ cand,
                                                      int32_t* __restrict__ idx, float* __restrict__ top_scores) {
   __shared__ SelScratch<NT> sc;
+  __shared__ __attribute__((aligned(16))) unsigned long long list[NT * kBalCand];
   const int q = blockIdx.x;
   int32_t* iq = idx + (int64_t)q * k;
   float* tq = top_scores ? top_scores + (int64_t)q * k : nullptr;
   select_from_regions<NT>(counts + (int64_t)q * n_chunks, n_chunks, kChunk, n_cand, k, cand + (int64_t)q * n_cand, sc,
-                          0, k, [&](unsigned pos, unsigned long long x) {
+                          list, 0, k, [&](unsigned pos, unsigned long long x) {
                             iq[pos] = x ? (int32_t)(~(unsigned)(x & 0xFFFFFFFFull)) : -1;
                             if (tq) tq[pos] = x ? key_score((unsigned)(x >> 32)) : -__builtin_inff();
                           });
