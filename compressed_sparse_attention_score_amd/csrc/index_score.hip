@@ -25,6 +25,12 @@ namespace csa2 {
 namespace {
 constexpr int kUnroll = 4;  // 16-entry groups per load batch
 constexpr int kScanRing = 2;  // load batches in flight per wave
+// Plain ranges: the four waves of a workgroup take the 64-entry batches of
+// its range in turn (wave w: batches w, w+4, ...), so that at any time they
+// read one contiguous stretch of the cache; the scores meet in LDS. (This
+// took about 2 us off the 4 x 1,048,576 decode scan; pools, whose rows are
+// scattered anyway, keep one contiguous range per wave.)
+constexpr bool kScanInterleave = true;
 // Buffer resource word 3 for untyped dword access on gfx9-family parts, the
 // nontemporal cache-policy bit of a buffer access, and an offset that is
 // past every resource these kernels build (their sizes stay below 2 GiB).
@@ -77,6 +83,7 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
   static_assert(!(POOL && BUF), "pools take per-entry addresses");
   static_assert(NB >= 1 && 64 * NB <= kMaxWaveSpan, "wave span");
   static_assert(UNROLL == 4, "a batch is 64 entries: one staged score per lane");
+  constexpr bool IL = kScanInterleave && !POOL;  // pools keep one range per wave
   const int q = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, kb = lane >> 4;
@@ -108,9 +115,23 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
   const int64_t base_row = (int64_t)q * a.cache_q_stride;
   float* out = a.scores + (int64_t)q * a.n_cand;
 
-  const int64_t w0p = ((int64_t)blockIdx.x * 4 + wave) * (64 * NB);
-  if (w0p >= a.n_cand) return;
-  const int64_t w1p = min(w0p + 64 * NB, a.n_cand);
+  constexpr int kSpan = 64 * NB;  // entries per wave
+  const int64_t wg0 = (int64_t)blockIdx.x * 4 * kSpan;
+  if (wg0 >= a.n_cand) return;  // uniform over the workgroup
+  const int64_t wg1 = min(wg0 + 4 * kSpan, a.n_cand);
+  // the wave's share of the scores to write and reduce: [w0p, w1p)
+  const int64_t w0p = wg0 + (int64_t)wave * kSpan;
+  const int64_t w1p = max(w0p, min(w0p + kSpan, a.n_cand));
+  // the positions the wave scores: batch b at bpos(b), inside [r0, r1)
+  const int64_t r0 = IL ? wg0 : w0p, r1 = IL ? wg1 : w1p;
+  auto bpos = [&](int b) -> int64_t {
+    return IL ? wg0 + (int64_t)(4 * b + wave) * 64 : w0p + (int64_t)b * 64;
+  };
+  // LDS rows: staged score of position p at s_flat[p - r0 + soff]; the
+  // wave's share starts at s_flat[sown]
+  float* s_flat = &s_score[0][0];
+  const int soff = IL ? 0 : wave * kMaxWaveSpan;
+  const int sown = IL ? wave * kSpan : wave * kMaxWaveSpan;
 
   // Key loads run kScanRing - 1 batches of UNROLL groups ahead of the matrix
   // cores (statically indexed buffers). Loads are unconditional so that the
@@ -123,10 +144,11 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
       for (int64_t g = w0p / a.group; g * a.group < w1p; ++g) a.gmax[(int64_t)q * a.n_groups + g] = 0u;
     return;
   }
-  if (POOL) {  // the range starts on a block boundary (wave spans are multiples of 64)
-    const int nb = (int)((w1p - w0p + 7) >> 3);
-    const int32_t* src = a.cand_blocks + (int64_t)q * a.n_blocks + (w0p >> 3);
-    for (int i = lane; i < nb; i += 64) s_blk[wave][i] = src[i];
+  int32_t* s_blkp = &s_blk[0][0] + wave * (kMaxWaveSpan / 8);
+  if (POOL) {  // the range starts on a block boundary (spans are multiples of 64)
+    const int nb = (int)((r1 - r0 + 7) >> 3);
+    const int32_t* src = a.cand_blocks + (int64_t)q * a.n_blocks + (r0 >> 3);
+    for (int i = lane; i < nb; i += 64) s_blkp[i] = src[i];
     // read back by other lanes of this wave only: its LDS accesses complete
     // in order, and this keeps the compiler from moving the reads above
     __builtin_amdgcn_wave_barrier();
@@ -138,7 +160,7 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
   int64_t lim_w = 0;  // BUF: valid positions of the wave's range end here
   if constexpr (BUF) {
     const int64_t lim = min(limit, a.n_cand);
-    lim_w = min(lim, w1p);
+    lim_w = min(lim, r1);
     crs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.key_codes + base_row * 64), 0, (int)(lim * 64), kBufferWord3);
     srs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.key_scales + base_row * 4), 0, (int)(lim * 4), kBufferWord3);
   }
@@ -147,7 +169,7 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
       // a batch past the range (the one the loop issues after its last)
       // reads nothing: its offsets are past every resource
       const unsigned p = (unsigned)g0 + (unsigned)r16;
-      const bool in = g0 < w1p;
+      const bool in = g0 < r1;
       const unsigned co = in ? 64u * p + 16u * (unsigned)kb : kStoreDrop;
       const unsigned so = in ? 4u * p : kStoreDrop;
 #pragma unroll
@@ -161,7 +183,7 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int64_t p = g0 + 16 * u + r16;
-      const int64_t e = (p < w1p) ? cand_entry<POOL>(a, s_blk[wave], w0p, p, limit) : -1;
+      const int64_t e = (p < r1) ? cand_entry<POOL>(a, s_blkp, r0, p, limit) : -1;
       ok[u] = e >= 0;
       const int64_t row = base_row + (e >= 0 ? e : 0);
       bc[u] = __builtin_nontemporal_load((const v4u*)(a.key_codes + row * 64 + kb * 16));
@@ -211,9 +233,8 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
     float mine = sv[0];
 #pragma unroll
     for (int u = 1; u < UNROLL; ++u) mine = (kb == u) ? sv[u] : mine;
-    s_score[wave][g0 - w0p + lane] = mine;
+    s_flat[soff + (int)(g0 - r0) + lane] = mine;
   };
-  constexpr int64_t kStep = 16 * UNROLL;
   // Both batches are issued without conditions (a batch past the range is
   // masked: no bytes through the buffer resources, row 0 of the cache
   // otherwise), so that the wait before each group counts only the loads
@@ -222,16 +243,18 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
   // Each buffer is refilled right after its batch is computed. Batches past
   // the range (a wave at the list end) are computed on masked lanes too.
 #pragma unroll
-  for (int b = 0; b < kScanRing && b < NB; ++b) issue(bcr[b], bsr[b], okr[b], w0p + b * kStep);
+  for (int b = 0; b < kScanRing && b < NB; ++b) issue(bcr[b], bsr[b], okr[b], bpos(b));
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     constexpr int R = kScanRing;
-    compute(bcr[b % R], bsr[b % R], okr[b % R], w0p + b * kStep);
-    if (b + R < NB) issue(bcr[b % R], bsr[b % R], okr[b % R], w0p + (b + R) * kStep);
+    compute(bcr[b % R], bsr[b % R], okr[b % R], bpos(b));
+    if (b + R < NB) issue(bcr[b % R], bsr[b % R], okr[b % R], bpos(b + R));
   }
-  // flush this wave's staged scores (wave-private LDS rows)
+  if (IL) __syncthreads();  // every wave's staged scores in LDS
+  // flush this wave's share of the staged scores
+  const float* srow = s_flat + sown;
   const int span = (int)(w1p - w0p);
-  for (int i = lane; i < span; i += 64) out[w0p + i] = s_score[wave][i];
+  for (int i = lane; i < span; i += 64) out[w0p + i] = srow[i];
   if (a.gmax) {
     // Sub-chunk maxima (sub-chunks of 4 to 512 entries start at multiples of
     // the group size, and so does the wave's range). In each pass over 256
@@ -247,7 +270,7 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
       const int i = base + 4 * lane;
       float m = -__builtin_inff();
       if (i < span) {
-        const v4f x = *(const v4f*)&s_score[wave][i];
+        const v4f x = *(const v4f*)&srow[i];
         m = x[0];
 #pragma unroll
         for (int e = 1; e < 4; ++e) m = (i + e < span) ? fmaxf(m, x[e]) : m;
