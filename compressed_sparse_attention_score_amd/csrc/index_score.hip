@@ -540,10 +540,13 @@ ScorePlan plan_score(int64_t n_cand, int Q, int k) {
   while (W > 64 && (int64_t)Q * ((n_cand + 4 * W - 1) / (4 * W)) < 1024) W /= 2;
   p.wave_span = W;
   // Sub-chunks of about n / 2k entries, so that at least k of them exist
-  // and the threshold is informative. The query-tiled scan (32 queries or
-  // more over a shared cache) forms maxima per 16-entry step, so there the
-  // smallest sub-chunk is 16; the per-query scan goes down to 4.
-  int64_t g = floor_pow2(n_cand / (2 * (int64_t)(k > 0 ? k : 1)));
+  // and the threshold is informative; n / 4k for 1,024 queries or more,
+  // whose selection reads only the sub-chunks that reach the threshold
+  // (about k of them, so half the scores of n / 2k). The query-tiled scan
+  // (32 queries or more over a shared cache) forms maxima per 16-entry step,
+  // so there the smallest sub-chunk is 16; the per-query scan goes down to 4.
+  const int64_t kk = k > 0 ? k : 1;
+  int64_t g = floor_pow2(n_cand / ((Q >= 1024 ? 4 : 2) * kk));
   const int64_t gmin = (Q >= 16 * kQSets) ? 16 : 4;
   if (g < gmin) g = gmin;
   if (g > W) g = W;

@@ -213,9 +213,13 @@ constexpr int kQPer = 16;           // positions per thread per pass
 constexpr int64_t kQMaxCand = 1 << 18;
 constexpr int kQSmallBatch = 1024;  // queries from which the 256-thread workgroup is used
 
-// Survivors held in LDS: 8 per thread at 1,024 threads, 16 per thread below.
+// Survivors held in LDS: 8 per thread at 1,024 threads, 15 per thread below
+// (a selection keeps k and a few percent more).
 template <int NQ>
-constexpr int q_cap() { return NQ >= 1024 ? 8192 : 16 * NQ; }
+constexpr int q_cap() { return NQ >= 1024 ? 8192 : 15 * NQ; }
+// Sub-chunk maxima held per thread for the threshold search and the
+// sub-chunk skipping (lists of up to kQMaxPer * NQ sub-chunks).
+constexpr int kQMaxPer = 8;
 
 template <int NQ>
 struct QSelShared {
@@ -223,7 +227,7 @@ struct QSelShared {
   alignas(16) unsigned wsum[2 * (NQ / 64)];
   unsigned res[4];
   unsigned ext[2 * (NQ / 64)];
-  unsigned short glist[4 * NQ];  // sub-chunks that can hold survivors, ascending
+  unsigned short glist[kQMaxPer * NQ];  // sub-chunks that can hold survivors, ascending
   unsigned long long cand[q_cap<NQ>() + q_cap<NQ>() / 16];  // survivor i at q_slot(i)
 };
 
@@ -291,7 +295,7 @@ __global__ __launch_bounds__(NQ) __attribute__((amdgpu_waves_per_eu(NQ >= 1024 ?
   // taken only with theta above the key of +0, where NaN and -inf cannot pass.
   // A list read in one pass is read whole, its loads in flight during the
   // threshold search; skipping pays when it saves passes.
-  const bool can_skip = !POOL && gmax && n_cand > kStep && n_groups >= k && n_groups <= 4 * NQ && group >= RUN &&
+  const bool can_skip = !POOL && gmax && n_cand > kStep && n_groups >= k && n_groups <= kQMaxPer * NQ && group >= RUN &&
                         (group & (group - 1)) == 0;
   const bool pre = n_full > 0 && !can_skip;
   // Ragged or unaligned passes: positions past the end load the last score
@@ -313,12 +317,14 @@ __global__ __launch_bounds__(NQ) __attribute__((amdgpu_waves_per_eu(NQ >= 1024 ?
 
   // ---- theta = k-th largest sub-chunk maximum (1 = keep every valid candidate)
   unsigned theta = 1u;
-  unsigned g[4] = {0u, 0u, 0u, 0u};  // maxima of sub-chunks j*NQ + tid
-  const bool theta_regs = gmax && n_groups >= k && n_groups <= 4 * NQ;
+  unsigned g[kQMaxPer];  // maxima of sub-chunks j*NQ + tid
+#pragma unroll
+  for (int j = 0; j < kQMaxPer; ++j) g[j] = 0u;
+  const bool theta_regs = gmax && n_groups >= k && n_groups <= kQMaxPer * NQ;
   if (theta_regs) {  // requested first: the threshold search waits on these, not on the scores
     const unsigned* gm = gmax + (int64_t)q * n_groups;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kQMaxPer; ++j) {
       const int64_t i = (int64_t)j * NQ + tid;
       g[j] = (i < n_groups) ? gm[i] : 0u;
     }
@@ -331,9 +337,9 @@ __global__ __launch_bounds__(NQ) __attribute__((amdgpu_waves_per_eu(NQ >= 1024 ?
     if (theta_regs) {
       int top;
       unsigned prefix;
-      shared_top_bits<NQ, unsigned, 4>(g, sh.ext, &top, &prefix);
-      t = radix_kth_regs<NQ, unsigned, 4>(g, (unsigned)k, sh.hist, sh.res, NQ >= 1024 ? kSmallThetaPasses : kThetaPasses,
-                                          top, prefix);
+      shared_top_bits<NQ, unsigned, kQMaxPer>(g, sh.ext, &top, &prefix);
+      t = radix_kth_regs<NQ, unsigned, kQMaxPer>(g, (unsigned)k, sh.hist, sh.res,
+                                                 NQ >= 1024 ? kSmallThetaPasses : kThetaPasses, top, prefix);
     } else {
       t = radix_kth_stream<NQ, unsigned>(gm, n_groups, (unsigned)k, sh.hist, sh.res, kThetaPasses);
     }
@@ -462,24 +468,31 @@ __global__ __launch_bounds__(NQ) __attribute__((amdgpu_waves_per_eu(NQ >= 1024 ?
   };
   if (can_skip && fast) {
     // ordered list of the sub-chunks with maximum >= theta (sub-chunk
-    // j*NQ + t is this thread's g[j]; at most NQ per j, so 16-bit fields)
+    // j*NQ + t is this thread's g[j]; at most NQ per j, so 16-bit fields,
+    // two to a scanned word)
     const int lg = __builtin_ctz((unsigned)group);
-    unsigned f[4];
+    static_assert(kQMaxPer % 4 == 0, "maxima are listed four at a time");
+    unsigned base = 0;  // listed sub-chunks of the rounds before
 #pragma unroll
-    for (int j = 0; j < 4; ++j) f[j] = ((int64_t)j * NQ + tid < n_groups && g[j] >= theta) ? 1u : 0u;
-    unsigned w0 = f[0] | (f[1] << 16), w1 = f[2] | (f[3] << 16);
-    const unsigned e0 = w0, e1 = w1;
-    unsigned t0, t1;
-    block_incl_scan2<NQ>(w0, w1, sh.wsum, &t0, &t1);
-    w0 -= e0;
-    w1 -= e1;
-    const unsigned T0 = t0 & 0xFFFFu, T1 = t0 >> 16, T2 = t1 & 0xFFFFu;
-    const unsigned at[4] = {w0 & 0xFFFFu, T0 + (w0 >> 16), T0 + T1 + (w1 & 0xFFFFu), T0 + T1 + T2 + (w1 >> 16)};
+    for (int r = 0; r < kQMaxPer; r += 4) {
+      unsigned f[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (f[j]) sh.glist[at[j]] = (unsigned short)(j * NQ + tid);
+      for (int j = 0; j < 4; ++j) f[j] = ((int64_t)(r + j) * NQ + tid < n_groups && g[r + j] >= theta) ? 1u : 0u;
+      unsigned w0 = f[0] | (f[1] << 16), w1 = f[2] | (f[3] << 16);
+      const unsigned e0 = w0, e1 = w1;
+      unsigned t0, t1;
+      block_incl_scan2<NQ>(w0, w1, sh.wsum, &t0, &t1);
+      w0 -= e0;
+      w1 -= e1;
+      const unsigned T0 = t0 & 0xFFFFu, T1 = t0 >> 16, T2 = t1 & 0xFFFFu;
+      const unsigned at[4] = {w0 & 0xFFFFu, T0 + (w0 >> 16), T0 + T1 + (w1 & 0xFFFFu), T0 + T1 + T2 + (w1 >> 16)};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (f[j]) sh.glist[base + at[j]] = (unsigned short)((r + j) * NQ + tid);
+      base += T0 + T1 + T2 + (t1 >> 16);
+    }
     __syncthreads();
-    const int64_t V = (int64_t)(T0 + T1 + T2 + (t1 >> 16)) << lg;  // positions of the listed sub-chunks
+    const int64_t V = (int64_t)base << lg;  // positions of the listed sub-chunks
     const bool vec = (n_cand & 3) == 0;
     // virtual position v -> position: listed sub-chunk v >> lg, offset
     // v & (group-1); a run never crosses a sub-chunk (group >= RUN, both
