@@ -126,6 +126,7 @@ struct AttnShared {
   alignas(16) float mask[TILE];  // per slot of the tile: 0 (valid) or -inf, added to its logits
   unsigned qmax[kWaves][kHeadsWg];  // per channel quarter, each head's largest |q| (bf16 bits)
   float ml[2][kHeadsWg];        // end: each head's reference max and sum
+  alignas(16) float rope[64];   // the query's (cos, sin) table (final outputs with a table)
   int32_t ids[kMaxSelected];    // the query's selected ids (by list position)
 };
 
@@ -315,6 +316,9 @@ __global__ __launch_bounds__(NT, 2) void k_sparse_attn(AttnArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) qr[hb][ks] = *(const v4u*)(qrow + (int64_t)16 * hb * kDim + 8 * ks);
   }
+  // the query's RoPE table, for the epilogue (a load without a condition:
+  // the first floats of q stand in when there is no table)
+  const float rope_v = (a.rope ? a.rope + (int64_t)q * 64 : (const float*)a.q)[lane];
   RawWin rwA, rwB;
   if (w1 > w0) load_window<SWA8>(a, q, w0, w, g, r16, rwA);
   if (w1 > w0 + 1) load_window<SWA8>(a, q, w0 + 1, w, g, r16, rwB);
@@ -352,6 +356,7 @@ __global__ __launch_bounds__(NT, 2) void k_sparse_attn(AttnArgs a) {
     for (int sl = sbeg + tid; sl < send; sl += NT) sh.ids[sl] = a.idx[(int64_t)q * a.k_sel + sl];
   }
   __syncthreads();  // ids and q maxima in LDS; the selection scratch (over the tile area) is free
+  if (w == 0) sh.rope[lane] = rope_v;  // read after the barrier that ends the tiles
 
   // q scaled into fp16's range for the latent products: 2^k with the head's
   // largest |q| times 2^k in [2^14, 2^15) (k clamped to +-100); logits of
@@ -589,9 +594,40 @@ __global__ __launch_bounds__(NT, 2) void k_sparse_attn(AttnArgs a) {
     sh.ml[1][16 * shb + r16] = l_run;
   }
   __syncthreads();
-  if (a.n_split > 1) {
-    // ---- partial record (shared by the two head halves): m, l and O / l
-    // of this slot range, with nontemporal stores (the merge, in the next
+  // ---- epilogue: O / l rounded once to bf16 (the rotary channels of a
+  // final output rotated back first), staged by each wave in its own
+  // quarter of the tile rows (which every wave has finished reading) as
+  // [32 heads][its 128 channels], so that each store then writes 256
+  // contiguous bytes of four rows instead of 32 bytes of sixteen. Lane
+  // (head h0 + 16hb + r16, g) holds channels 128w + 16cb + 4g .. +3; the
+  // rotary pairs (448 + 2i, 449 + 2i) lie in wave 3's cb >= 4. A row's
+  // sixteen 16-byte granules sit XOR-swizzled by the row (bank spread).
+  uint16_t* stg = sh.v + w * (kHeadsWg * 128);
+  auto stg_at = [](int row, int gran) { return row * 128 + ((gran ^ (row & 15)) << 3); };
+  const bool split_out = a.n_split > 1;
+  const bool rot = !split_out && a.rope != nullptr && w == kWaves - 1;
+#pragma unroll
+  for (int hb = 0; hb < kHB; ++hb) {
+    const float lh = sh.ml[1][16 * hb + r16];
+    const float inv = (lh > 0.f) ? 1.f / lh : 0.f;
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+      float v0 = o[hb][cb][0] * inv, v1 = o[hb][cb][1] * inv, v2 = o[hb][cb][2] * inv, v3 = o[hb][cb][3] * inv;
+      if (cb >= 4 && rot) {  // pairs (16*cb + 4*g - 64) / 2 and +1
+        const int c0 = 16 * cb + 4 * g - 64;
+        unrotate(v0, v1, *(const float2*)&sh.rope[c0]);
+        unrotate(v2, v3, *(const float2*)&sh.rope[c0 + 2]);
+      }
+      v2u pk;
+      pk.x = pack_bf16x2(v0, v1);
+      pk.y = pack_bf16x2(v2, v3);
+      *(v2u*)(stg + stg_at(16 * hb + r16, 2 * cb + (g >> 1)) + 4 * (g & 1)) = pk;
+    }
+  }
+  uint16_t* dst;
+  if (split_out) {
+    // partial record (shared by the two head halves): m, l and O / l of
+    // this slot range, with nontemporal stores (the merge, in the next
     // kernel, is the only reader; at 16 queries x 65,536 entries these
     // stores took about 2 us off the step against ordinary ones)
     float* part = a.partial + ((int64_t)q * ns + split) * kPartFloats;
@@ -599,47 +635,22 @@ __global__ __launch_bounds__(NT, 2) void k_sparse_attn(AttnArgs a) {
       __builtin_nontemporal_store(sh.ml[0][lane], part + h0 + lane);
       __builtin_nontemporal_store(sh.ml[1][lane], part + kHeads + h0 + lane);
     }
-    uint16_t* orec = (uint16_t*)(part + 2 * kHeads);
-#pragma unroll
-    for (int hb = 0; hb < kHB; ++hb) {
-      const float lh = sh.ml[1][16 * hb + r16];
-      const float pinv = (lh > 0.f) ? 1.f / lh : 0.f;
-      uint16_t* orow = orec + (h0 + 16 * hb + r16) * kDim + 128 * w + 4 * g;
-#pragma unroll
-      for (int cb = 0; cb < 8; ++cb) {
-        v2u pk;
-        pk.x = pack_bf16x2(o[hb][cb][0] * pinv, o[hb][cb][1] * pinv);
-        pk.y = pack_bf16x2(o[hb][cb][2] * pinv, o[hb][cb][3] * pinv);
-        __builtin_nontemporal_store(pk, (v2u*)(orow + 16 * cb));
-      }
-    }
-    return;
+    dst = (uint16_t*)(part + 2 * kHeads) + h0 * kDim;
+  } else {
+    if (a.lse && smax && g == 0)
+      a.lse[(int64_t)q * kHeads + h0 + 16 * shb + r16] =
+          (l_run > 0.f) ? (m_ref + __log2f(l_run)) * kLn2 : -__builtin_inff();
+    dst = a.out + ((int64_t)q * kHeads + h0) * kDim;
   }
-
-  // ---- epilogue: O / l as bf16 (rotary channels rotated back when a table
-  // is given); lane (head h0 + 16hb + r16, g) holds channels 128w + 16cb + 4g .. +3
-  if (a.lse && smax && g == 0)
-    a.lse[(int64_t)q * kHeads + h0 + 16 * shb + r16] =
-        (l_run > 0.f) ? (m_ref + __log2f(l_run)) * kLn2 : -__builtin_inff();
-  const float* rope = (a.rope && w == kWaves - 1) ? a.rope + (int64_t)q * 64 : nullptr;
+  // the staged block is read back by lanes of the same wave only (its LDS
+  // accesses complete in order): lane l takes granule l & 15 of row
+  // 4i + l/16
+  __builtin_amdgcn_wave_barrier();
 #pragma unroll
-  for (int hb = 0; hb < kHB; ++hb) {
-    const float lh = sh.ml[1][16 * hb + r16];
-    const float inv = (lh > 0.f) ? 1.f / lh : 0.f;
-    uint16_t* orow = a.out + ((int64_t)q * kHeads + h0 + 16 * hb + r16) * kDim + 128 * w + 4 * g;
-#pragma unroll
-    for (int cb = 0; cb < 8; ++cb) {
-      float v0 = o[hb][cb][0] * inv, v1 = o[hb][cb][1] * inv, v2 = o[hb][cb][2] * inv, v3 = o[hb][cb][3] * inv;
-      if (cb >= 4 && rope) {  // channels 384 + 16*cb + 4*g >= 448: pairs (16*cb + 4*g - 64) / 2 and +1
-        const int c0 = 16 * cb + 4 * g - 64;
-        unrotate(v0, v1, *(const float2*)(rope + c0));  // the table is 8-B aligned
-        unrotate(v2, v3, *(const float2*)(rope + c0 + 2));
-      }
-      v2u pk;
-      pk.x = pack_bf16x2(v0, v1);
-      pk.y = pack_bf16x2(v2, v3);
-      __builtin_nontemporal_store(pk, (v2u*)(orow + 16 * cb));
-    }
+  for (int i = 0; i < kHeadsWg / 4; ++i) {
+    const int row = 4 * i + (lane >> 4), gran = lane & 15;
+    const v4u x = *(const v4u*)(stg + stg_at(row, gran));
+    __builtin_nontemporal_store(x, (v4u*)(dst + row * kDim + 128 * w + 8 * gran));
   }
 }
 
