@@ -666,6 +666,14 @@ __global__ __launch_bounds__(64) void k_attn_merge(const float* __restrict__ par
   const int q = blockIdx.x >> 6, h = blockIdx.x & 63;
   const int c0 = threadIdx.x * 8;
   const float* base = partial + (int64_t)q * n_split * kPartFloats;
+  // the (cos, sin) of this thread's four rotary pairs, requested with the
+  // records (a load without a condition: another thread's or the first
+  // pairs stand in where they are not needed)
+  const bool rot = rope != nullptr && c0 >= kRopeFirst;
+  const float* csp = (rope ? rope : partial) + (rope ? (int64_t)q * 64 + max(c0 - kRopeFirst, 0) : 0);
+  float2 cs[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) cs[j] = *(const float2*)(csp + 2 * j);
   float ms[MS], ls[MS];
   v4u x[MS];
 #pragma unroll
@@ -695,10 +703,9 @@ __global__ __launch_bounds__(64) void k_attn_merge(const float* __restrict__ par
   const float inv = (L > 0.f) ? 1.f / L : 0.f;
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] *= inv;
-  if (rope && c0 >= kRopeFirst) {  // pairs (c0 - 448) / 2 .. +3
-    const float* cs = rope + (int64_t)q * 64 + (c0 - kRopeFirst);
+  if (rot) {  // pairs (c0 - 448) / 2 .. +3
 #pragma unroll
-    for (int j = 0; j < 4; ++j) unrotate(acc[2 * j], acc[2 * j + 1], *(const float2*)(cs + 2 * j));
+    for (int j = 0; j < 4; ++j) unrotate(acc[2 * j], acc[2 * j + 1], cs[j]);
   }
   v4u pk;
 #pragma unroll
