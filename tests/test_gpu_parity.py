@@ -256,9 +256,15 @@ def test_quantize_empty_and_errors():
 
 # ------------------------------------------------------------ index scores
 
-@pytest.mark.parametrize("Q,N", [(3, 5000), (1, 17), (2, 16), (1, 4096 + 37)])
+@pytest.mark.parametrize("Q,N", [(3, 5000), (1, 17), (2, 16), (1, 4096 + 37), (4, 131072 + 37), (16, 65536 + 37),
+                                 (16, 131072 + 37)])
 def test_index_score_full(Q, N):
+    """Per-query scans. The last three sizes take 2, 4 and 8 batches of 64
+    entries per wave (128-, 256- and 512-entry wave spans, the four waves of
+    a workgroup interleaving their batches), each with a last workgroup
+    range holding 37 entries."""
     wl = synth.full_decode(Q, N, seed=N)
+    announce(f"full scores Q={Q} N={N}")
     ref, dots = oracle.index_score(wl, want_dots=True)
     got = gpu_scores(to_device(wl))
     check_scores(got, ref, dots, wl.w, f"full Q{Q} N{N}")
@@ -737,6 +743,24 @@ def test_decode_chunked_selection_paths():
     ref = oracle.decode(wl, queries=[0, 1])
     assert np.array_equal(gidx[0], np.arange(512, dtype=np.int32))
     assert np.array_equal(np.sort(gidx[1]), np.sort(ref["idx"][1][:512]))
+
+
+def test_decode_chunked_long_tie_list():
+    """2 queries x 65,536 entries (16 compaction chunks). In query 0 every
+    32nd entry carries the query's best key: 2,048 tied candidates survive
+    the compaction, 128 per chunk, which the attention kernel's final
+    selection holds in registers but cannot spread over its threads (more
+    than 1,024); the lowest 512 ids of the tie set win. Query 1 is random
+    (its few hundred survivors take the spread path)."""
+    wl = synth.full_decode(2, 65536, seed=35)
+    s0 = oracle.index_score(wl, queries=[0])[0]
+    best = int(np.argmax(s0))
+    ties = np.arange(0, 65536, 32)
+    wl.key_codes[ties] = wl.key_codes[best]
+    wl.key_scales[ties] = wl.key_scales[best]
+    announce("chunked long tie list")
+    gidx = _check_decode(wl, what="chunked tie list")
+    assert np.array_equal(gidx[0], np.sort(np.union1d(ties, [best]))[:512].astype(np.int32))
 
 
 @pytest.mark.parametrize("k", [7, 1024])
