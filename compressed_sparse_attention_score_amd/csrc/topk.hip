@@ -29,6 +29,8 @@
 #include "csa2_internal.h"
 #include "select_device.h"
 
+#include <type_traits>
+
 namespace csa2 {
 
 namespace {
@@ -544,29 +546,31 @@ __global__ __launch_bounds__(NQ) __attribute__((amdgpu_waves_per_eu(NQ >= 1024 ?
   __syncthreads();
 
   unsigned written = 0;
-  if (m <= (unsigned)kQCap) {
-    // ---- survivors in LDS: thread t holds list elements PER*t..PER*t+PER-1
-    constexpr int PER = kQCap / NQ;
-    unsigned long long v[PER];
+  // ---- survivors in LDS: thread t takes list elements P*t..P*t+P-1, P the
+  // fewest per thread that hold the list (2, 4 or all kQCap/NQ), so that the
+  // radix passes and the ordered write loop over no more slots than needed
+  auto final_select = [&](auto p_tag) {
+    constexpr int P = decltype(p_tag)::value;
+    unsigned long long v[P];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const unsigned e = (unsigned)tid * PER + j;
+    for (int j = 0; j < P; ++j) {
+      const unsigned e = (unsigned)tid * P + j;
       v[j] = (e < m) ? sh.cand[q_slot(e)] : 0ull;
     }
     unsigned long long T = 0ull;
     if (m > (unsigned)k) {
       int top;
       unsigned long long prefix;
-      shared_top_bits<NQ, unsigned long long, PER>(v, sh.ext, &top, &prefix);
-      T = radix_kth_regs<NQ, unsigned long long, PER>(v, (unsigned)k, sh.hist, sh.res, 64, top, prefix);
+      shared_top_bits<NQ, unsigned long long, P>(v, sh.ext, &top, &prefix);
+      T = radix_kth_regs<NQ, unsigned long long, P>(v, (unsigned)k, sh.hist, sh.res, 64, top, prefix);
     }
     unsigned c = 0;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) c += (v[j] != 0ull && v[j] >= T) ? 1u : 0u;
+    for (int j = 0; j < P; ++j) c += (v[j] != 0ull && v[j] >= T) ? 1u : 0u;
     unsigned all;
     unsigned pos = block_incl_scan<NQ>(c, sh.wsum, &all) - c;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
+    for (int j = 0; j < P; ++j) {
       if (v[j] != 0ull && v[j] >= T && pos < (unsigned)k) {
         iq[pos] = (int32_t)(~(unsigned)(v[j] & 0xFFFFFFFFull));
         if (tq) tq[pos] = key_score((unsigned)(v[j] >> 32));
@@ -574,6 +578,14 @@ __global__ __launch_bounds__(NQ) __attribute__((amdgpu_waves_per_eu(NQ >= 1024 ?
       }
     }
     written = min(all, (unsigned)k);
+  };
+  constexpr int kPerAll = kQCap / NQ;
+  if (m <= (unsigned)(2 * NQ)) {
+    final_select(std::integral_constant<int, 2>{});
+  } else if (kPerAll > 4 && m <= (unsigned)(4 * NQ)) {
+    final_select(std::integral_constant<int, (kPerAll > 4 ? 4 : kPerAll)>{});
+  } else if (m <= (unsigned)kQCap) {
+    final_select(std::integral_constant<int, kPerAll>{});
   } else {
     // ---- long survivor lists (heavy ties): move the LDS part to global and
     // select from there
