@@ -71,11 +71,12 @@ __device__ __forceinline__ int64_t cand_entry(const ScoreArgs& a, const int32_t*
   return (e >= 0 && e < limit) ? e : -1;
 }
 
-// BUF (plain ranges whose key bytes stay below 2 GiB per query): the keys
-// are read through buffer resources that end at the query's last valid
-// entry, so one 32-bit offset per lane, stepped by the batch, addresses every
-// load (the group's 1 KiB and 64 B strides are instruction offsets) and the
-// hardware returns zeros past the end instead of a clamped row.
+// BUF (plain ranges): the keys are read through buffer resources that span
+// the workgroup's positions up to the query's last valid entry, so one
+// 32-bit offset per lane, stepped by the batch, addresses every load (the
+// group's 1 KiB and 64 B strides are instruction offsets) and the hardware
+// returns zeros past the end instead of a clamped row. Pools (BUF false)
+// take per-entry addresses and clamp to row 0.
 // NB: batches of 64 entries per wave (the wave span is 64*NB); the batch
 // loop is unrolled in full, so every wait names the exact load it needs.
 template <bool POOL, bool BUF, int NB, int UNROLL = kUnroll>
@@ -159,16 +160,19 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
   __amdgpu_buffer_rsrc_t crs, srs;
   int64_t lim_w = 0;  // BUF: valid positions of the wave's range end here
   if constexpr (BUF) {
+    // resources based at the start of this workgroup's positions, so that
+    // their sizes and offsets stay small whatever the list length
     const int64_t lim = min(limit, a.n_cand);
     lim_w = min(lim, r1);
-    crs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.key_codes + base_row * 64), 0, (int)(lim * 64), kBufferWord3);
-    srs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.key_scales + base_row * 4), 0, (int)(lim * 4), kBufferWord3);
+    const int nrec = (int)max((int64_t)0, lim_w - r0);  // valid positions from r0 on (at most 2,048)
+    crs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.key_codes + (base_row + r0) * 64), 0, nrec * 64, kBufferWord3);
+    srs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.key_scales + (base_row + r0) * 4), 0, nrec * 4, kBufferWord3);
   }
   auto issue = [&](v4u* bc, unsigned* bs, bool* ok, int64_t g0) {
     if constexpr (BUF) {
       // a batch past the range (the one the loop issues after its last)
       // reads nothing: its offsets are past every resource
-      const unsigned p = (unsigned)g0 + (unsigned)r16;
+      const unsigned p = (unsigned)(g0 - r0) + (unsigned)r16;
       const bool in = g0 < r1;
       const unsigned co = in ? 64u * p + 16u * (unsigned)kb : kStoreDrop;
       const unsigned so = in ? 4u * p : kStoreDrop;
@@ -600,15 +604,12 @@ hipError_t launch_index_score(const IndexLaunch& L, const ScorePlan& plan, float
     return hipGetLastError();
   }
   dim3 grid((unsigned)plan.n_wg, (unsigned)L.Q);
-  const bool buf = L.n_cand < (1ll << 25);  // key bytes of a query's list below 2 GiB
   auto go = [&](auto nb_tag) {
     constexpr int NB = decltype(nb_tag)::value;
     if (L.cand_blocks)
       k_index_score<true, false, NB><<<grid, 256, 0, s>>>(a);
-    else if (buf)
-      k_index_score<false, true, NB><<<grid, 256, 0, s>>>(a);
     else
-      k_index_score<false, false, NB><<<grid, 256, 0, s>>>(a);
+      k_index_score<false, true, NB><<<grid, 256, 0, s>>>(a);
   };
   switch (plan.wave_span) {
     case 64: go(std::integral_constant<int, 1>{}); break;
