@@ -433,18 +433,24 @@ int csa2_decode(const csa2_decode_args* a, void* ws, size_t ws_bytes, void* stre
   auto mark = [&](int i) {
     return a->stage_events[i] ? hipEventRecord((hipEvent_t)a->stage_events[i], s) : hipSuccess;
   };
+  // Few queries over a short plain list: the attention kernel selects
+  // straight from the scores (no selection launch, no sub-chunk maxima).
+  const bool raw = a->index.cand_blocks == nullptr && n_cand <= kRawSelectMax && Q < 64;
   // 1. scores + sub-chunk maxima
   hipError_t e = mark(0);
-  if (e == hipSuccess) e = launch_index_score(L, sp, w.scores, w.tk.gmax, s);
+  if (e == hipSuccess) e = launch_index_score(L, sp, w.scores, raw ? nullptr : w.tk.gmax, s);
   if (e == hipSuccess) e = mark(1);
   if (e != hipSuccess) return CSA2_ERR_HIP;
   // 2. threshold + compaction, exact top-k. In the chunk-parallel form the
   // final selection runs inside the attention kernel, whose every split
   // finishes its query's selection from the compacted candidates: one kernel
-  // boundary and one id round trip fewer.
+  // boundary and one id round trip fewer. In the raw form the attention
+  // kernel makes the whole selection from the scores.
   const SelectPlan pl = plan_select(n_cand);
-  const bool fused = select_is_chunked(Q, n_cand) && pl.n_chunks <= kFusedSelectMaxChunks;
-  if (fused)
+  const bool fused = !raw && select_is_chunked(Q, n_cand) && pl.n_chunks <= kFusedSelectMaxChunks;
+  if (raw)
+    e = hipSuccess;
+  else if (fused)
     e = launch_select_compact(w.scores, Q, n_cand, a->index.n_entries, a->index.cand_blocks, a->index.n_blocks,
                               a->index.n_valid, a->k, sp, w.tk.gmax, w.tk.counts, w.tk.cand, s);
   else
@@ -458,7 +464,12 @@ int csa2_decode(const csa2_decode_args* a, void* ws, size_t ws_bytes, void* stre
                w.idx,  a->k,               a->q,                    a->swa,
                a->swa_q_stride, a->n_swa, a->softmax_scale,        a->out,
                a->lse, a->swa_format == CSA2_SWA_FP8, a->rope_cos_sin};
-  if (fused) {
+  if (raw) {
+    A.sel_scores = w.scores;
+    A.sel_n_valid = a->index.n_valid;
+    A.sel_n_cand = n_cand;
+    A.idx_out = a->idx_out;
+  } else if (fused) {
     A.sel_counts = w.tk.counts;
     A.sel_cand = w.tk.cand;
     A.sel_n_cand = n_cand;

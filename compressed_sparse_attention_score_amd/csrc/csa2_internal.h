@@ -130,14 +130,22 @@ struct AttnLaunch {
   int swa_fp8;
   const float* rope;  // [Q][32][2] (cos, sin) or nullptr
   // Selection finished by the attention kernel (decode): the compaction's
-  // counts [Q][sel_chunks] and composites [Q][sel_n_cand], or sel_counts =
-  // nullptr to read the ids from idx. idx_out receives the ids (or nullptr).
+  // counts [Q][sel_chunks] and composites [Q][sel_n_cand], or (sel_scores
+  // given) the plain range's raw scores [Q][sel_n_cand] with the causal
+  // limits sel_n_valid (or nullptr); with neither the ids are read from idx.
+  // idx_out receives the ids (or nullptr).
   const unsigned* sel_counts;
   const unsigned long long* sel_cand;
   int64_t sel_n_cand;
   int sel_chunks, sel_chunk;
   int32_t* idx_out;
+  const float* sel_scores;
+  const int32_t* sel_n_valid;
 };
+
+// Longest plain candidate list whose selection the attention kernel makes
+// straight from the scores (16 per thread).
+constexpr int kRawSelectMax = 4096;
 
 // partial: workspace for the per-range records (plan.n_splits > 1); the
 // merge runs as a second kernel.

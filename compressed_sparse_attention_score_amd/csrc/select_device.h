@@ -419,4 +419,33 @@ __device__ __forceinline__ void select_from_regions(const unsigned* __restrict__
   for (int j = max((int)written, lo) + tid; j < hi; j += NTH) emit((unsigned)j, 0ull);
 }
 
+
+// Exact top-k of a plain candidate range straight from its scores: position
+// p (< n_cand) is a candidate when p < limit; thread t takes positions
+// PER*t .. PER*t+PER-1 (thread order is list order) as composites, and the
+// selection and ordered write are those of select_regs. emit as for
+// select_from_regions, including emit(pos, 0) past the number selected.
+template <int NTH, int PER, typename Emit>
+__device__ __forceinline__ void select_from_scores(const float* __restrict__ sq, int64_t n_cand, int64_t limit, int k,
+                                                   SelScratch<NTH>& sc, int lo, int hi, Emit emit) {
+  const int tid = threadIdx.x;
+  const int64_t p0 = (int64_t)tid * PER;
+  const int64_t vlim = min(n_cand, limit);
+  unsigned long long v[PER];
+  unsigned cnt = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int64_t p = p0 + j;
+    // a load without a condition (the last score stands in past the list)
+    const float s = sq[n_cand > 0 ? min(p, n_cand - 1) : 0];
+    const bool ok = p < vlim;
+    v[j] = ok ? (((unsigned long long)score_key(s) << 32) | (unsigned long long)(~(unsigned)p)) : 0ull;
+    cnt += ok ? 1u : 0u;
+  }
+  unsigned m;
+  block_incl_scan<NTH>(cnt, sc.wsum, &m);
+  const unsigned written = select_regs<NTH, PER>(v, m, k, sc, lo, hi, emit);
+  for (int j = max((int)written, lo) + tid; j < hi; j += NTH) emit((unsigned)j, 0ull);
+}
+
 }  // namespace csa2

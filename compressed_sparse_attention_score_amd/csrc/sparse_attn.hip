@@ -106,6 +106,9 @@ struct AttnArgs {
   int64_t sel_n_cand;
   int sel_chunks, sel_chunk;
   int32_t* idx_out;  // selected ids [Q][k_sel], or nullptr
+  // or straight from the raw scores of a short plain range (sel_scores)
+  const float* sel_scores;
+  const int32_t* sel_n_valid;
   int64_t n_entries, cache_q_stride, swa_q_stride;
   int Q, k_sel, n_swa, n_split, tps;
   float scale_log2;
@@ -344,13 +347,21 @@ __global__ __launch_bounds__(NT, 2) void k_sparse_attn(AttnArgs a) {
   if (FUSED) {
     if (sbeg < send) {  // uniform over the workgroup
       int32_t* io = (a.idx_out && hh == 0) ? a.idx_out + (int64_t)q * a.k_sel : nullptr;
-      select_from_regions<NT, kSelReg>(a.sel_counts + (int64_t)q * a.sel_chunks, a.sel_chunks, a.sel_chunk,
-                                       a.sel_n_cand, a.k_sel, a.sel_cand + (int64_t)q * a.sel_n_cand, sh.sel.sc,
-                                       sh.sel.list, sbeg, send, [&](unsigned pos, unsigned long long x) {
-                                         const int32_t id = x ? (int32_t)(~(unsigned)(x & 0xFFFFFFFFull)) : -1;
-                                         sh.ids[pos] = id;
-                                         if (io) io[pos] = id;
-                                       });
+      auto emit = [&](unsigned pos, unsigned long long x) {
+        const int32_t id = x ? (int32_t)(~(unsigned)(x & 0xFFFFFFFFull)) : -1;
+        sh.ids[pos] = id;
+        if (io) io[pos] = id;
+      };
+      if (a.sel_scores) {
+        int64_t limit = a.n_entries;
+        if (a.sel_n_valid) limit = min(limit, (int64_t)a.sel_n_valid[q]);
+        select_from_scores<NT, kRawSelectMax / NT>(a.sel_scores + (int64_t)q * a.sel_n_cand, a.sel_n_cand, limit,
+                                                   a.k_sel, sh.sel.sc, sbeg, send, emit);
+      } else {
+        select_from_regions<NT, kSelReg>(a.sel_counts + (int64_t)q * a.sel_chunks, a.sel_chunks, a.sel_chunk,
+                                         a.sel_n_cand, a.k_sel, a.sel_cand + (int64_t)q * a.sel_n_cand, sh.sel.sc,
+                                         sh.sel.list, sbeg, send, emit);
+      }
     }
   } else {
     for (int sl = sbeg + tid; sl < send; sl += NT) sh.ids[sl] = a.idx[(int64_t)q * a.k_sel + sl];
@@ -755,6 +766,8 @@ hipError_t launch_attn(const AttnLaunch& L, const AttnPlan& plan, float* partial
   a.sel_chunks = L.sel_chunks;
   a.sel_chunk = L.sel_chunk;
   a.idx_out = L.idx_out;
+  a.sel_scores = L.sel_scores;
+  a.sel_n_valid = L.sel_n_valid;
   a.n_entries = L.n_entries;
   a.cache_q_stride = L.cache_q_stride;
   a.swa_q_stride = L.swa_q_stride;
@@ -781,7 +794,7 @@ hipError_t launch_attn(const AttnLaunch& L, const AttnPlan& plan, float* partial
   if (plan.n_splits > 1 && partial == nullptr) return hipErrorInvalidValue;
   const int q8 = (L.Q + 7) / 8 * 8;
   const dim3 grid((unsigned)(kHalves * plan.n_splits * q8));
-  const bool fused = L.sel_counts != nullptr;
+  const bool fused = L.sel_counts != nullptr || L.sel_scores != nullptr;
   if (L.swa_fp8) {
     if (fused)
       k_sparse_attn<true, true><<<grid, NT, 0, s>>>(a);
