@@ -802,6 +802,28 @@ def test_decode_prefill_from_position_zero(T, t0):
     _check_decode(synth.prefill(T, 65536, t0, seed=60 + T + t0), what=f"prefill from t0={t0} T={T}")
 
 
+@pytest.mark.parametrize("T,n,t0", [(40, 3001, 0), (9, 4096, 9000)])
+def test_decode_raw_selection(T, n, t0):
+    """Fewer than 64 queries over a plain list of at most 4,096 entries: the
+    attention kernel selects straight from the scores. t0 = 0: causal limits
+    from 0 up (queries with fewer than k valid entries pad with -1, one with
+    none attends over its window only), a list that is not a multiple of 16;
+    t0 past the cache end: every entry valid, the longest such list."""
+    announce(f"raw selection T={T} n={n} t0={t0}")
+    _check_decode(synth.prefill(T, n, t0, seed=70 + T), what=f"raw selection T={T}")
+
+
+def test_decode_raw_selection_ties():
+    """Raw-score selection with query 0's 4,096 keys all equal: every score
+    ties and the lowest 512 ids win. Query 1 is random."""
+    wl = synth.full_decode(2, 4096, seed=36)
+    wl.key_codes[0:4096] = wl.key_codes[0]
+    wl.key_scales[0:4096] = wl.key_scales[0]
+    announce("raw selection ties")
+    gidx = _check_decode(wl, what="raw ties")
+    assert np.array_equal(gidx[0], np.arange(512, dtype=np.int32))
+
+
 def test_decode_fewer_than_k_entries():
     _check_decode(synth.full_decode(2, 300, seed=24), what="n<k")
 
