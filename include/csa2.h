@@ -323,7 +323,9 @@ typedef struct csa2_decode_args {
                                  selection kernels that precede attention [2]
                                  and after attention [3]; NULL = skip. For few
                                  long lists the last selection step runs inside
-                                 the attention kernel, so [2]..[3] includes it. */
+                                 the attention kernel, and for few short plain
+                                 lists (< 64 queries, <= 4,096 candidates) the
+                                 whole selection does, so [2]..[3] includes it. */
   int32_t swa_format;         /* CSA2_SWA_BF16 or CSA2_SWA_FP8                   */
   const float* rope_cos_sin;  /* [Q][32][2] or NULL, as in csa2_attn_args        */
 } csa2_decode_args;
