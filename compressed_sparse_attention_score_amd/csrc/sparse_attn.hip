@@ -26,10 +26,10 @@
 //    keeps it in fp16's range, taken back out of the logits. Window rows stay
 //    bf16 (exact). The decoded values also go to LDS (the tile's rows,
 //    swizzled) as the values, and the partial sums go to LDS.
-//  * Softmax: two waves, one per block of 16 heads, add the four partial
-//    sums and run the online softmax for those heads over the 32 slots; P^T
-//    goes to LDS in the layout the PV product takes (lane = head, slots
-//    4g..4g+3 and 16+4g..16+4g+3). The running maximum is a reference that
+//  * Softmax: each wave takes 8 heads, adds the four partial sums and runs
+//    the online softmax for those heads over the 32 slots (lane = head, one
+//    run of 4 slots); P^T goes to LDS in the layout the PV product takes
+//    (lane = head, slots 4g..4g+3 and 16+4g..16+4g+3). The running maximum is a reference that
 //    moves only when a head's tile maximum exceeds it by more than 2^8 (log2
 //    units), so O is rescaled a handful of times per query; the factor goes
 //    to LDS with P.
@@ -58,7 +58,7 @@ constexpr int NT = 256;     // threads per workgroup (4 waves)
 constexpr int kWaves = NT / 64;
 constexpr int kHalves = 2;                 // workgroups per (query, slot range)
 constexpr int kHeadsWg = kHeads / kHalves;  // heads per workgroup
-constexpr int kHB = kHeadsWg / 16;          // head blocks of 16 (two waves run their softmax)
+constexpr int kHB = kHeadsWg / 16;          // head blocks of 16 (MFMA columns)
 constexpr float kRescaleSlack = 8.f;  // log2 units
 constexpr float kRefFloor = -0x1p126f;  // initial reference max (log2 units)
 constexpr float kLog2e = 1.4426950408889634f;
@@ -122,10 +122,10 @@ struct AttnShared {
       alignas(16) unsigned long long list[NT * kBalCand];
     } sel;                    // prologue: finishing the selection
   };
-  v4f sx[kWaves][kHB][2][64];   // partial S^T: [channel quarter][head block][slot block][lane]
+  v4f sx[kWaves][kHB][2][64];   // partial S^T: [channel quarter][head block][slot block][sx_idx]
   v4u px[kHB][64];              // P^T operands: [head block][lane]
   float alpha[kHB][16];         // O rescale factor per head (1 when unchanged)
-  unsigned resc[kHB];           // nonzero when some head of the block rescales
+  unsigned resc[kHB][2];        // nonzero when some head of the block's half rescales
   alignas(16) float mask[TILE];  // per slot of the tile: 0 (valid) or -inf, added to its logits
   unsigned qmax[kWaves][kHeadsWg];  // per channel quarter, each head's largest |q| (bf16 bits)
   float ml[2][kHeadsWg];        // end: each head's reference max and sum
@@ -377,12 +377,21 @@ __global__ __launch_bounds__(NT, 2) void k_sparse_attn(AttnArgs a) {
     const int qe = (qmh == 0u) ? 127 : (int)(qmh >> 7);  // bf16 biased exponent
     return min(100, max(-100, 14 - (qe - 127)));
   };
-  // softmax role: head block shb = w - 2*hh (waves 0 and 1 in the first
-  // head half, 2 and 3 in the second, so that two workgroups of different
-  // halves on one CU load its four SIMDs evenly), head h0 + 16*shb + r16
-  const int shb = w - kHB * hh;
-  const bool smax = (unsigned)shb < (unsigned)kHB;
-  const float lat_log2 = a.scale_log2 * __uint_as_float((unsigned)(127 - head_k2((16 * shb + r16) & 31)) << 23);
+  // softmax role: wave w takes heads h0 + 16*shb + 8*shalf .. +7 (shb = w/2,
+  // shalf = w%2); lane (sr8, sgq, ssb) holds head shead's slots
+  // 16*ssb + 4*sgq .. +3, and the 8 lanes of a head reduce by lane swaps.
+  // (Two waves of 16 heads each left the other two idle between the
+  // barriers: prefill attention took 652 us against 623 us.)
+  const int shb = w >> 1, shalf = w & 1;
+  const int sr8 = lane & 7, sgq = (lane >> 3) & 3, ssb = lane >> 5;
+  const int shead = 16 * shb + 8 * shalf + sr8;
+  const bool slead = (lane >> 3) == 0;
+  const float lat_log2 = a.scale_log2 * __uint_as_float((unsigned)(127 - head_k2(shead)) << 23);
+  // position in a [head block][slot block] row of sx of the MFMA output of
+  // lane (g, r16 = 8*half + r8): the 8 heads of a softmax wave's lane group
+  // sit together, XOR-swizzled so that 16 consecutive lanes of either side
+  // touch 16 distinct 16-byte bank groups
+  auto sx_idx = [](int half, int gg, int r8) { return (32 * half + 8 * gg + r8) ^ (8 * half); };
 
   // O^T accumulators: channels 128w + 16cb + 4g + j, head h0 + 16hb + r16
   v4f o[kHB][8];
@@ -401,7 +410,7 @@ __global__ __launch_bounds__(NT, 2) void k_sparse_attn(AttnArgs a) {
 
   // Per tile, between two barriers:
   //  qk: decode + partial S^T of this wave's channels -> sx, rows -> v
-  //  softmax (two waves): head block shb over the tile -> px, alpha, resc
+  //  softmax (8 heads per wave) over the tile -> px, alpha, resc
   //  pv: O rescale (when flagged) and O += V^T P^T
   // Each buffer is single: a wave rewrites its own rows of v only after its
   // pv has read them, sx only after the barrier that ends every softmax
@@ -436,7 +445,7 @@ __global__ __launch_bounds__(NT, 2) void k_sparse_attn(AttnArgs a) {
 #pragma unroll
     for (int hb = 0; hb < kHB; ++hb)
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) sh.sx[w][hb][sb][lane] = s[sb][hb];
+      for (int sb = 0; sb < 2; ++sb) sh.sx[w][hb][sb][sx_idx(r16 >> 3, g, r16 & 7)] = s[sb][hb];
     if (w == 0 && g == 0) {
       sh.mask[r16] = ok0 ? 0.f : -__builtin_inff();
       sh.mask[16 + r16] = ok1 ? 0.f : -__builtin_inff();
@@ -444,24 +453,18 @@ __global__ __launch_bounds__(NT, 2) void k_sparse_attn(AttnArgs a) {
   };
   auto softmax = [&](auto f16_tag) {
     constexpr bool F16 = decltype(f16_tag)::value;
-    // lane (head h0 + 16*shb + r16, g) holds slots 4g..4g+3 and 16+4g..16+4g+3
+    // lane: head h0 + shead, slots 16*ssb + 4*sgq .. +3
     const float sl2 = F16 ? lat_log2 : a.scale_log2;
-    v4f s0 = sh.sx[0][shb][0][lane], s1 = sh.sx[0][shb][1][lane];
+    const int si = sx_idx(shalf, sgq, sr8);
+    v4f s0 = sh.sx[0][shb][ssb][si];
 #pragma unroll
-    for (int c = 1; c < kWaves; ++c) {
-      s0 += sh.sx[c][shb][0][lane];
-      s1 += sh.sx[c][shb][1][lane];
-    }
-    const v4f mk0 = *(const v4f*)&sh.mask[4 * g], mk1 = *(const v4f*)&sh.mask[16 + 4 * g];
-    float x[8];
+    for (int c = 1; c < kWaves; ++c) s0 += sh.sx[c][shb][ssb][si];
+    const v4f mk0 = *(const v4f*)&sh.mask[16 * ssb + 4 * sgq];
+    float x[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[j] = fmaf(s0[j], sl2, mk0[j]);
-      x[4 + j] = fmaf(s1[j], sl2, mk1[j]);
-    }
-    float mt = x[0];
-#pragma unroll
-    for (int j = 1; j < 8; ++j) mt = fmaxf(mt, x[j]);
+    for (int j = 0; j < 4; ++j) x[j] = fmaf(s0[j], sl2, mk0[j]);
+    float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mt = max_xor8(mt);
     mt = max_xor16(mt);
     mt = max_xor32(mt);
     // the reference moves (also from the floor, when the first valid slot
@@ -474,33 +477,34 @@ __global__ __launch_bounds__(NT, 2) void k_sparse_attn(AttnArgs a) {
       l_run *= al;
       m_ref = mt;
     }
-    float p[8], ps = 0.f;
+    float p[4], ps = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 4; ++j) {
       p[j] = __builtin_amdgcn_exp2f(x[j] - m_ref);
       ps += p[j];
     }
+    ps = add_xor8(ps);
     ps = add_xor16(ps);
     ps = add_xor32(ps);
     l_run += ps;
-    v4u pk;
+    v2u pk;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
       if constexpr (F16)
         pk[j] = __builtin_bit_cast(unsigned, v2h{(_Float16)p[2 * j], (_Float16)p[2 * j + 1]});
       else
         pk[j] = pack_bf16x2(p[2 * j], p[2 * j + 1]);
     }
-    sh.px[shb][lane] = pk;
-    if (g == 0) sh.alpha[shb][r16] = al;
+    *((v2u*)&sh.px[shb][16 * sgq + 8 * shalf + sr8] + ssb) = pk;
+    if (slead) sh.alpha[shb][8 * shalf + sr8] = al;
     const bool any = __builtin_amdgcn_ballot_w64(moved) != 0ull;
-    if (lane == 0) sh.resc[shb] = any ? 1u : 0u;
+    if (lane == 0) sh.resc[shb][shalf] = any ? 1u : 0u;
   };
   auto pv = [&](auto f16_tag) {
     constexpr bool F16 = decltype(f16_tag)::value;
 #pragma unroll
     for (int hb = 0; hb < kHB; ++hb) {
-      if (__builtin_amdgcn_readfirstlane(sh.resc[hb])) {
+      if (__builtin_amdgcn_readfirstlane(sh.resc[hb][0] | sh.resc[hb][1])) {
         const float al = sh.alpha[hb][r16];
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb) o[hb][cb] *= al;
@@ -528,7 +532,7 @@ __global__ __launch_bounds__(NT, 2) void k_sparse_attn(AttnArgs a) {
   };
   auto rest = [&](auto f16_tag) {  // after qk: the two barriers, softmax and pv
     __syncthreads();
-    if (smax) softmax(f16_tag);
+    softmax(f16_tag);
     __syncthreads();
     pv(f16_tag);
   };
@@ -600,9 +604,9 @@ __global__ __launch_bounds__(NT, 2) void k_sparse_attn(AttnArgs a) {
   }
 
   // ---- every head's reference max and sum to all waves
-  if (smax && g == 0) {
-    sh.ml[0][16 * shb + r16] = m_ref;
-    sh.ml[1][16 * shb + r16] = l_run;
+  if (slead) {
+    sh.ml[0][shead] = m_ref;
+    sh.ml[1][shead] = l_run;
   }
   __syncthreads();
   // ---- epilogue: O / l rounded once to bf16 (the rotary channels of a
@@ -648,8 +652,8 @@ __global__ __launch_bounds__(NT, 2) void k_sparse_attn(AttnArgs a) {
     }
     dst = (uint16_t*)(part + 2 * kHeads) + h0 * kDim;
   } else {
-    if (a.lse && smax && g == 0)
-      a.lse[(int64_t)q * kHeads + h0 + 16 * shb + r16] =
+    if (a.lse && slead)
+      a.lse[(int64_t)q * kHeads + h0 + shead] =
           (l_run > 0.f) ? (m_ref + __log2f(l_run)) * kLn2 : -__builtin_inff();
     dst = a.out + ((int64_t)q * kHeads + h0) * kDim;
   }
