@@ -166,14 +166,6 @@ __device__ __forceinline__ float max_xor16(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-// x + x[lane ^ 8] and max(x, x[lane ^ 8]): a rotation by 8 within each row
-// of 16 lanes (DPP row_ror:8).
-__device__ __forceinline__ float add_xor8(float x) {
-  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float max_xor8(float x) {
-  return fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false)));
-}
 __device__ __forceinline__ unsigned umax_xor32(unsigned x) {
   auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
   return r[0] > r[1] ? r[0] : r[1];

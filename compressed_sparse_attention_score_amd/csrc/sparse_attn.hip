@@ -151,6 +151,15 @@ struct RawWin {
   unsigned s0, s1;
   bool ok0, ok1;
 };
+// x + x[lane ^ 8] and max(x, x[lane ^ 8]): a rotation by 8 within each row
+// of 16 lanes (DPP row_ror:8).
+__device__ __forceinline__ float add_xor8(float x) {
+  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float max_xor8(float x) {
+  return fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false)));
+}
+
 // Latent tiles whose bytes are in flight ahead of the one being processed
 // (register ring; the loop is unrolled by this so every index is static).
 constexpr int kRing = 2;
