@@ -526,9 +526,11 @@ def test_sparse_attn_with_oracle_ids():
     check_lse(glse, lse, "attn lse")
 
 
-@pytest.mark.parametrize("Q", [1, 40, 700])
+@pytest.mark.parametrize("Q", [1, 12, 40, 700])
 def test_sparse_attn_split_layouts(Q):
-    """Q=1 splits the slot list over many workgroups, Q=700 over one."""
+    """Q=1 splits the slot list into 10 ranges, Q=12 too (120 (query, range)
+    pairs, the queries in two groups of 8 with 4 idle places), Q=40 into 3,
+    Q=700 not at all."""
     wl = synth.full_decode(Q, 600, seed=Q)
     rng = np.random.default_rng(Q)
     idx = np.stack([rng.choice(600, 512, replace=False) for _ in range(Q)]).astype(np.int32)
