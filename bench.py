@@ -277,8 +277,8 @@ def cpu_baseline(wl, seconds):
     first, done, calls, dt = _time_oracle(wl, view, per_call, seconds)
     what = "the whole batch" if per_call == wl.Q else f"strided subsets of {per_call} queries"
     res = dict(value=round(done / dt, 3), unit="queries/s", cores=int(min(threads, per_call)), kind="oracle",
-               sample=f"{calls} oracle decode call(s) on {what} of this workload ({done} queries, "
-                      f"{wl.n_cand} candidates each), fp64, {dt:.1f} s wall",
+               sample=f"{calls} oracle decode call(s) on {what} of this workload ({wl.Q} queries, "
+                      f"{wl.n_cand} candidates each; {done} queries in all), fp64, {dt:.1f} s wall",
                cpu_model=_cpu_model(), host_threads=int(threads))
     oracle.set_threads(1)
     try:
