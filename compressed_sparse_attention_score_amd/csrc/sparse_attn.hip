@@ -29,10 +29,10 @@
 //  * Softmax: each wave takes 8 heads, adds the four partial sums and runs
 //    the online softmax for those heads over the 32 slots (lane = head, one
 //    run of 4 slots); P^T goes to LDS in the layout the PV product takes
-//    (lane = head, slots 4g..4g+3 and 16+4g..16+4g+3). The running maximum is a reference that
-//    moves only when a head's tile maximum exceeds it by more than 2^8 (log2
-//    units), so O is rescaled a handful of times per query; the factor goes
-//    to LDS with P.
+//    (lane = head, slots 4g..4g+3 and 16+4g..16+4g+3). The running maximum
+//    is a reference that moves only when a head's tile maximum exceeds it
+//    by more than 2^8 (log2 units), so O is rescaled a handful of times per
+//    query; the factor goes to LDS with P.
 //  * PV: wave w owns channels 128w..128w+127 of the 32 heads:
 //    O^T[128 x 32] += V^T P^T, the V^T operand read back from the rows it
 //    decoded itself by gfx950's transposing LDS read (ds_read_b64_tr_b16:
