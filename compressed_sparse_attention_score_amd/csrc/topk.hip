@@ -68,16 +68,25 @@ constexpr int kCompactThetaPasses = 1;
 // depends on their number.
 constexpr int kSmallThetaPasses = 1;
 
-// Threshold + compaction: grid (n_chunks, Q). Writes cand[q][c0 .. c0+cnt) in
-// position order and counts[q][chunk] = cnt.
+// Threshold + compaction: grid (n_chunks, Q), or with qx a 1-D grid of
+// n_chunks * Q whose workgroups of query q sit 8 ids apart from q & 7 on, so
+// that they share an XCD with the query's scan and attention workgroups (Q a
+// multiple of 8). Writes cand[q][c0 .. c0+cnt) in position order and
+// counts[q][chunk] = cnt.
 __global__ __launch_bounds__(NT) void k_select_compact(const float* __restrict__ scores, int64_t n_cand,
                                                        int64_t n_entries, const int32_t* __restrict__ cand_blocks,
                                                        int n_blocks, const int32_t* __restrict__ n_valid, int k,
                                                        const unsigned* __restrict__ gmax, int64_t n_groups,
                                                        int n_chunks, unsigned* __restrict__ counts,
-                                                       unsigned long long* __restrict__ cand) {
+                                                       unsigned long long* __restrict__ cand, int qx) {
   __shared__ SelShared sh;
-  const int q = blockIdx.y, tid = threadIdx.x;
+  int q = blockIdx.y, cx = blockIdx.x;  // query, chunk
+  if (qx) {
+    const int lin = blockIdx.x;
+    q = ((lin / (8 * n_chunks)) << 3) | (lin & 7);
+    cx = (lin >> 3) % n_chunks;
+  }
+  const int tid = threadIdx.x;
   int64_t limit = n_entries;
   if (n_valid) limit = min(limit, (int64_t)n_valid[q]);
 
@@ -86,7 +95,7 @@ __global__ __launch_bounds__(NT) void k_select_compact(const float* __restrict__
   // whose rows are not 16-B aligned takes 4-B loads in the same order) and
   // staged in LDS before the threshold work; the thread picks its 16 up after
   // it, whose barriers order the stores before the reads.
-  const int64_t c0 = (int64_t)blockIdx.x * kChunk;
+  const int64_t c0 = (int64_t)cx * kChunk;
   const int64_t p0 = c0 + (int64_t)tid * kPer;
   const float* srow = scores + (int64_t)q * n_cand;
   {
@@ -180,7 +189,7 @@ __global__ __launch_bounds__(NT) void k_select_compact(const float* __restrict__
 #pragma unroll
   for (int j = 0; j < kPer; ++j)
     if (comp[j]) dst[pos++] = comp[j];
-  if (tid == 0) counts[(int64_t)q * n_chunks + blockIdx.x] = total;
+  if (tid == 0) counts[(int64_t)q * n_chunks + cx] = total;
 }
 
 // Exact top-k of each query's candidate list: grid (Q). Output in list order.
@@ -631,8 +640,10 @@ hipError_t launch_select_compact(const float* scores, int Q, int64_t n_cand, int
                                  hipStream_t s) {
   if (Q <= 0) return hipSuccess;
   SelectPlan pl = plan_select(n_cand);
-  k_select_compact<<<dim3((unsigned)pl.n_chunks, (unsigned)Q), NT, 0, s>>>(
-      scores, n_cand, n_entries, cand_blocks, n_blocks, n_valid, k, gmax, sp.n_groups, pl.n_chunks, counts, cand);
+  const bool qx = Q % 8 == 0 && (int64_t)pl.n_chunks * Q * NT < ((int64_t)1 << 31);  // 1-D grid size
+  const dim3 cg = qx ? dim3((unsigned)(pl.n_chunks * Q)) : dim3((unsigned)pl.n_chunks, (unsigned)Q);
+  k_select_compact<<<cg, NT, 0, s>>>(
+      scores, n_cand, n_entries, cand_blocks, n_blocks, n_valid, k, gmax, sp.n_groups, pl.n_chunks, counts, cand, qx ? 1 : 0);
   return hipGetLastError();
 }
 
