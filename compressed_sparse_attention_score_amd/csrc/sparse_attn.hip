@@ -288,8 +288,12 @@ __device__ __forceinline__ unsigned bf16x2_to_f16x2(unsigned u, float f) {
   return __builtin_bit_cast(unsigned, h);
 }
 
+// Two fp32 values rounded (to nearest even) into bf16x2, lo in bits 15:0:
+// one paired conversion (two single conversions, a shift and an or when
+// written as two scalar casts).
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
-  return (unsigned)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((unsigned)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((v2f){lo, hi}, v2bf16));
 }
 
 template <bool SWA8, bool FUSED>
