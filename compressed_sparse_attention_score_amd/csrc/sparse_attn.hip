@@ -369,7 +369,8 @@ __global__ __launch_bounds__(NT, 2) void k_sparse_attn(AttnArgs a) {
         int64_t limit = a.n_entries;
         if (a.sel_n_valid) limit = min(limit, (int64_t)a.sel_n_valid[q]);
         select_from_scores<NT, kRawSelectMax / NT>(a.sel_scores + (int64_t)q * a.sel_n_cand, a.sel_n_cand, limit,
-                                                   a.k_sel, sh.sel.sc, sbeg, send, emit);
+                                                   a.k_sel, sh.sel.sc, sbeg, send, emit,
+                                                   (unsigned (*)[kBins])sh.sel.list);  // unused on this path
       } else {
         select_from_regions<NT, kSelReg>(a.sel_counts + (int64_t)q * a.sel_chunks, a.sel_chunks, a.sel_chunk,
                                          a.sel_n_cand, a.k_sel, a.sel_cand + (int64_t)q * a.sel_n_cand, sh.sel.sc,
