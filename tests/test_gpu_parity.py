@@ -340,6 +340,18 @@ def test_topk_exact_random(n, k):
     _assert_topk_exact(s, k, n, what=f"n{n} k{k}")
 
 
+def test_topk_chunked_query_major_layout():
+    """16 queries x 70,001 scores take the chunk-parallel selection with its
+    compaction laid out query-major (the batch is a multiple of 8), then the
+    per-query final selection; rows under causal limits from 0 to the whole
+    list."""
+    rng = np.random.default_rng(1616)
+    s = rng.standard_normal((16, 70001)).astype(np.float32)
+    nv = np.array([70001, 65536, 4099, 512, 511, 40, 1, 0, 70000, 30000, 20000, 16384, 16383, 1000, 513, 2],
+                  np.int32)
+    _assert_topk_exact(s, 512, 70001, n_valid=nv, what="chunked 16 x 70,001")
+
+
 @pytest.mark.parametrize("n", [20000, 16000])
 def test_topk_ties_nan_negzero(n):
     """n=20000 with 4 queries takes the chunk-parallel selection, n=16000 the
