@@ -13,10 +13,15 @@
  * Conventions for every entry point
  *  - All data pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors),
  *    C-contiguous, owned by the caller. The library allocates nothing, keeps no
- *    pointer after a call returns and holds no mutable global state; calls are
- *    thread-safe and reentrant.
+ *    pointer after a call returns and holds no mutable global state (apart
+ *    from the static device scratch of csa2_sparse_attn_noalloc, below); calls
+ *    are thread-safe and reentrant.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work
  *    is enqueued asynchronously on it; outputs are valid once it synchronises.
+ *    A call only enqueues kernels (and the event records a caller asks for;
+ *    no allocation, memset or synchronisation), so it can be captured in a
+ *    HIP graph on that stream; replays reproduce the eager results bit for
+ *    bit (csa2_decode is tested that way).
  *  - Arguments are validated on the host before anything is enqueued: a
  *    non-zero status means no work was launched. Data contents (NaN scores,
  *    unsorted block lists) are preconditions and are not checked on the host;

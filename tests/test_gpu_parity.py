@@ -851,6 +851,47 @@ def test_decode_deterministic():
         assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
 
 
+
+@pytest.mark.parametrize("Q,n", [(1, 4096), (3, 20000), (16, 3000)])
+def test_decode_graph_capture_replays(Q, n):
+    """csa2_decode captured in a HIP graph on the caller's stream: three
+    replays, each after eager work and a synchronisation, must reproduce the
+    eager outputs bit for bit (1 x 4,096: the selection from raw scores
+    inside attention; 3 x 20,000: compaction and the fused final selection;
+    16 x 3,000: raw selection with the query-major scan)."""
+    announce(f"graph capture Q={Q} n={n}")
+    wl = synth.full_decode(Q, n, seed=Q + n)
+    db = to_device(wl)
+    out, lse, idx = db.new_outputs()
+    da = db.decode_args(out, lse, idx)
+    ws = torch.empty(max(1, csa.csa2_workspace_size(csa.CSA2_WS_DECODE, da)), dtype=torch.uint8, device="cuda")
+    csa.csa2_decode(da, ws)
+    torch.cuda.synchronize()
+    ref = [out.clone(), lse.clone(), idx.clone()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        csa.csa2_decode(da, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        csa.csa2_decode(da, ws)
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.fill_(0)
+        lse.fill_(0)
+        idx.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((out, lse, idx), ref):
+            assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), f"replay {r}"
+        csa.csa2_decode(da, ws)  # eager work between the replays
+        torch.cuda.synchronize()
+    del g
+
+
 # ------------------------------------------------- full-size workload shapes
 
 def test_decode_1x4096_full():
